@@ -1,0 +1,328 @@
+/*
+ * sdm_oracle.c -- plain, slow CPU oracle for the Sparse Delta Memory (SDM)
+ * hot path: product-key top-k addressing, softmax weights and the sparse
+ * gated delta-rule scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP kernels.
+ *
+ * Sources (web pages on the method; cited by title and section):
+ *   [P]  "Sparse Delta Memory: Scaling the State of Linear RNNs through
+ *        Sparsity" -- the paper text.
+ *          Sec. 2  (Product-Key Memories): scores of the N = n_sub^2 slots are
+ *                  the outer sum of two half-score vectors; the top-k can be
+ *                  found without materialising all N scores.
+ *          Sec. 3.1, step 1 (Sparse Key Selection): keys/queries are split in
+ *                  two halves; top-W of the write scores and top-R of the read
+ *                  scores select the slots.
+ *          Sec. 3.1, step 2 (Gated Delta Write, Eq. 4): selected rows only;
+ *                  unselected slots stay unchanged.
+ *          Sec. 3.1, step 3 (Sparse Read): weighted sum of the selected read
+ *                  rows, after the write.
+ *          Sec. 3.1, "Learned Initial State": M0 copied into every sequence.
+ *          Sec. 4 (SDM Configuration): read and write activations use
+ *                  softmax normalisation.
+ *   [B]  "Sparse Delta Memory: Scaling Linear RNN States to 1M Tokens via
+ *        Sparsity" -- blog summary, "Methodology", item 2 (Gated Delta
+ *        Updates): M_t[i] <- a_t M_{t-1}[i] + b_t k^(i) (v_t - a_t M_{t-1}^T k_t).
+ *
+ * Readings where the pages are silent or garbled (each is also listed in the
+ * design notes of the repository):
+ *   - The prediction is M_{t-1}^T k_t = sum over the W selected slots of
+ *     w_j M_{t-1}[slot_j], formed on the pre-write state before any row is
+ *     written (this is what makes W = N reduce to the Gated DeltaNet rule of
+ *     [P] Sec. 2, Eq. 2, as [P] Sec. 3.1 states).
+ *   - The read uses the post-write state of the same token.
+ *   - Decay applies to the written rows only.
+ *   - Each half is scored against its own sub-key codebook C[h][c] of shape
+ *     [n_sub, d_k/2]; slot = i1 * n_sub + i2 with i1 from the first half.
+ *   - Weights are a softmax over the selected slot scores, no temperature.
+ *   - Scores are fp32 values (the kernel's precision for the selection):
+ *     a half score is the fp32 rounding of the exact (fp64) dot product, and
+ *     a slot score is the fp32 sum of its two half scores.  Every order is by
+ *     score descending, ties to the lower index (sub-key index in the halves,
+ *     flat slot index in the merge).
+ *   - Memory state is fp32; the scan accumulates in fp64 and rounds each
+ *     stored row element and each output element once to fp32.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    int64_t B, T, H, d_k, n_sub, d_v, k_prime, W, R;
+    int32_t in_bf16; /* 1: k, q, v and codebooks are bf16 bit patterns; 0: fp32 */
+    int32_t pad_;
+} orc_dims;
+
+enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ENOMEM = -2, ORC_EINDEX = -3, ORC_ENONFINITE = -4 };
+
+/* ---- input decoding (bf16 -> fp64 is exact) ------------------------------ */
+static double dec_bf16(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double load_in(const void *p, int bf16, int64_t i)
+{
+    return bf16 ? dec_bf16(((const uint16_t *)p)[i]) : (double)((const float *)p)[i];
+}
+
+static int check_dims(const orc_dims *d)
+{
+    if (!d) return ORC_EINVAL;
+    if (d->B < 0 || d->T < 0 || d->H < 1 || d->d_k < 2 || (d->d_k & 1) || d->n_sub < 1 ||
+        d->d_v < 1 || d->k_prime < 1 || d->k_prime > d->n_sub || d->W < 1 || d->R < 1 ||
+        d->W > d->k_prime * d->k_prime || d->R > d->k_prime * d->k_prime)
+        return ORC_EINVAL;
+    if (d->n_sub > 46340) return ORC_EINVAL; /* N must fit in int32 */
+    return ORC_OK;
+}
+
+/* ---- scores -------------------------------------------------------------- */
+/* Half scores of one token-head row for half c: s[u] = fp32(<x_c, C[h][c][u]>),
+ * the dot product taken in fp64.  [P] Sec. 2 (PKM) and Sec. 3.1 step 1. */
+static int half_scores(const void *x, const void *C, const orc_dims *d, int64_t row, int64_t h,
+                       int c, float *s)
+{
+    const int64_t half = d->d_k / 2;
+    const int bf = d->in_bf16;
+    for (int64_t u = 0; u < d->n_sub; ++u) {
+        double acc = 0.0;
+        const int64_t cbase = ((h * 2 + c) * d->n_sub + u) * half;
+        const int64_t xbase = row * d->d_k + (int64_t)c * half;
+        for (int64_t e = 0; e < half; ++e)
+            acc += load_in(x, bf, xbase + e) * load_in(C, bf, cbase + e);
+        if (!isfinite(acc)) return ORC_ENONFINITE;
+        s[u] = (float)acc;
+    }
+    return ORC_OK;
+}
+
+typedef struct {
+    float s;
+    int32_t i;
+} scored;
+
+/* score descending, then index ascending: a total order on distinct indices */
+static int cmp_scored(const void *pa, const void *pb)
+{
+    const scored *a = (const scored *)pa, *b = (const scored *)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+/* One addressing problem: top-n slots of x against codebook C, with weights.
+ * Step order of [P] Sec. 2: top-k' per half, then the k' x k' outer-sum
+ * candidates, then top-n of those.  Then the softmax of [P] Sec. 4. */
+static int address_one(const void *x, const void *C, const orc_dims *d, int64_t row, int64_t h,
+                       int64_t n, scored *work, int32_t *idx_out, float *wt_out, float *sc_out)
+{
+    const int64_t ns = d->n_sub, kp = d->k_prime;
+    scored *h0 = work, *h1 = work + ns, *cand = work + 2 * ns;
+    float *tmp = (float *)(work + 2 * ns + kp * kp);
+    int rc;
+    for (int c = 0; c < 2; ++c) {
+        scored *hc = c ? h1 : h0;
+        if ((rc = half_scores(x, C, d, row, h, c, tmp)) != ORC_OK) return rc;
+        for (int64_t u = 0; u < ns; ++u) {
+            hc[u].s = tmp[u];
+            hc[u].i = (int32_t)u;
+        }
+        qsort(hc, (size_t)ns, sizeof(scored), cmp_scored); /* first k' are the top-k' */
+    }
+    for (int64_t a = 0; a < kp; ++a)
+        for (int64_t b = 0; b < kp; ++b) {
+            scored *e = &cand[a * kp + b];
+            e->s = h0[a].s + h1[b].s; /* fp32 addition */
+            e->i = (int32_t)(h0[a].i * ns + h1[b].i);
+        }
+    qsort(cand, (size_t)(kp * kp), sizeof(scored), cmp_scored);
+    double z = 0.0;
+    const double m = (double)cand[0].s;
+    for (int64_t j = 0; j < n; ++j) z += exp((double)cand[j].s - m);
+    for (int64_t j = 0; j < n; ++j) {
+        idx_out[j] = cand[j].i;
+        wt_out[j] = (float)(exp((double)cand[j].s - m) / z);
+        if (sc_out) sc_out[j] = cand[j].s;
+    }
+    return ORC_OK;
+}
+
+/* Addressing for every token-head row of k (write) and q (read).
+ *   k, q   [B,T,H,d_k]; C_w, C_r [H,2,n_sub,d_k/2]
+ *   widx, wwt [B,T,H,W]; ridx, rwt [B,T,H,R]; wsc, rsc optional selected scores */
+int orc_address(const void *k, const void *q, const void *C_w, const void *C_r, const orc_dims *d,
+                int32_t *widx, float *wwt, int32_t *ridx, float *rwt, float *wsc, float *rsc,
+                int nthreads)
+{
+    int rc = check_dims(d);
+    if (rc) return rc;
+    const int64_t rows = d->B * d->T * d->H;
+    const int64_t kp = d->k_prime, ns = d->n_sub;
+    const size_t wbytes = sizeof(scored) * (size_t)(2 * ns + kp * kp) + sizeof(float) * (size_t)ns;
+    int err = ORC_OK;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        scored *work = (scored *)malloc(wbytes + 16);
+        if (!work) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t r = 0; r < rows; ++r) {
+            if (!work || err) continue;
+            const int64_t h = r % d->H;
+            int e1 = address_one(k, C_w, d, r, h, d->W, work, widx + r * d->W, wwt + r * d->W,
+                                 wsc ? wsc + r * d->W : NULL);
+            int e2 = address_one(q, C_r, d, r, h, d->R, work, ridx + r * d->R, rwt + r * d->R,
+                                 rsc ? rsc + r * d->R : NULL);
+            if (e1 || e2) {
+#pragma omp atomic write
+                err = e1 ? e1 : e2;
+            }
+        }
+        free(work);
+    }
+    return err;
+}
+
+/* Half scores for every row and both halves: out [rows, 2, n_sub]. */
+int orc_half_scores(const void *x, const void *C, const orc_dims *d, float *out, int nthreads)
+{
+    int rc = check_dims(d);
+    if (rc) return rc;
+    const int64_t rows = d->B * d->T * d->H;
+    int err = ORC_OK;
+#pragma omp parallel for num_threads(nthreads > 0 ? nthreads : 1) schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int c = 0; c < 2; ++c) {
+            int e = half_scores(x, C, d, r, r % d->H, c, out + (r * 2 + c) * d->n_sub);
+            if (e) {
+#pragma omp atomic write
+                err = e;
+            }
+        }
+    }
+    return err;
+}
+
+/* fp32 slot score fp32(s1[i1]) + fp32(s2[i2]) of given (row, slot) pairs. */
+int orc_slot_scores(const void *x, const void *C, const orc_dims *d, int64_t nq,
+                    const int64_t *rows, const int32_t *slots, float *out)
+{
+    int rc = check_dims(d);
+    if (rc) return rc;
+    float *s = (float *)malloc(sizeof(float) * (size_t)(2 * d->n_sub));
+    if (!s) return ORC_ENOMEM;
+    const int64_t N = d->n_sub * d->n_sub;
+    for (int64_t i = 0; i < nq; ++i) {
+        if (slots[i] < 0 || slots[i] >= N || rows[i] < 0 || rows[i] >= d->B * d->T * d->H) {
+            free(s);
+            return ORC_EINDEX;
+        }
+        const int64_t h = rows[i] % d->H;
+        if ((rc = half_scores(x, C, d, rows[i], h, 0, s)) ||
+            (rc = half_scores(x, C, d, rows[i], h, 1, s + d->n_sub))) {
+            free(s);
+            return rc;
+        }
+        out[i] = s[slots[i] / d->n_sub] + s[d->n_sub + slots[i] % d->n_sub];
+    }
+    free(s);
+    return ORC_OK;
+}
+
+/* ---- the scan ------------------------------------------------------------ */
+/* Sequence-serial sparse gated delta rule, [P] Sec. 3.1 steps 2-3 and [B]
+ * item 2.  For every (b, h), tokens in order:
+ *     p   = sum_j w_j M[widx_j]                  (pre-write rows, fp64)
+ *     u   = v_t - a_t p
+ *     M[widx_j] = fp32(a_t M[widx_j] + b_t w_j u)    for all j at once
+ *     o_t = fp32(sum_j r_j M[ridx_j])              (post-write rows)
+ * Rows not in widx are untouched.
+ *   M [B,H,N,d_v] fp32 in/out; widx, wwt [B,T,H,W]; ridx, rwt [B,T,H,R];
+ *   v [B,T,H,d_v]; a, b [B,T,H]; o [B,T,H,d_v] */
+int orc_scan(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx, const float *rwt,
+             const void *v, const float *a, const float *b, float *o, const orc_dims *d,
+             int nthreads)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->n_sub < 1 || d->d_v < 1 || d->W < 1 ||
+        d->R < 1 || d->n_sub > 46340)
+        return ORC_EINVAL;
+    const int64_t N = d->n_sub * d->n_sub, dv = d->d_v, W = d->W, R = d->R;
+    const int64_t chains = d->B * d->H;
+    int err = ORC_OK;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(2 * dv));
+        if (!p) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t ch = 0; ch < chains; ++ch) {
+            if (!p || err) continue;
+            double *u = p + dv;
+            const int64_t bb = ch / d->H, h = ch % d->H;
+            float *Mc = M + ch * N * dv;
+            for (int64_t t = 0; t < d->T && !err; ++t) {
+                const int64_t row = (bb * d->T + t) * d->H + h;
+                const int32_t *wi = widx + row * W, *ri = ridx + row * R;
+                const float *ww = wwt + row * W, *rw = rwt + row * R;
+                int bad = 0;
+                for (int64_t j = 0; j < W; ++j) {
+                    if (wi[j] < 0 || wi[j] >= N) bad = 1;
+                    for (int64_t jj = 0; jj < j; ++jj)
+                        if (wi[jj] == wi[j]) bad = 1; /* write slots must be distinct */
+                }
+                for (int64_t j = 0; j < R; ++j)
+                    if (ri[j] < 0 || ri[j] >= N) bad = 1;
+                if (bad) {
+#pragma omp atomic write
+                    err = ORC_EINDEX;
+                    break;
+                }
+                const double at = (double)a[row], bt = (double)b[row];
+                for (int64_t c = 0; c < dv; ++c) p[c] = 0.0;
+                for (int64_t j = 0; j < W; ++j) {
+                    const float *Mr = Mc + (int64_t)wi[j] * dv;
+                    for (int64_t c = 0; c < dv; ++c) p[c] += (double)ww[j] * (double)Mr[c];
+                }
+                for (int64_t c = 0; c < dv; ++c)
+                    u[c] = load_in(v, d->in_bf16, row * dv + c) - at * p[c];
+                for (int64_t j = 0; j < W; ++j) {
+                    float *Mr = Mc + (int64_t)wi[j] * dv;
+                    const double bw = bt * (double)ww[j];
+                    for (int64_t c = 0; c < dv; ++c)
+                        Mr[c] = (float)(at * (double)Mr[c] + bw * u[c]);
+                }
+                for (int64_t c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < R; ++j)
+                        acc += (double)rw[j] * (double)Mc[(int64_t)ri[j] * dv + c];
+                    o[row * dv + c] = (float)acc;
+                }
+            }
+        }
+        free(p);
+    }
+    return err;
+}
+
+/* Learned initial state copied into every sequence, [P] Sec. 3.1:
+ * M[b][h] = M0[h].  M [B,H,N,d_v], M0 [H,N,d_v]. */
+int orc_state_init(float *M, const float *M0, const orc_dims *d)
+{
+    if (!d || d->B < 0 || d->H < 1 || d->n_sub < 1 || d->d_v < 1) return ORC_EINVAL;
+    const size_t per_seq = (size_t)(d->H * d->n_sub * d->n_sub * d->d_v);
+    for (int64_t b = 0; b < d->B; ++b) memcpy(M + (size_t)b * per_seq, M0, per_seq * sizeof(float));
+    return ORC_OK;
+}
