@@ -1,0 +1,164 @@
+/*
+ * sdm.h -- C ABI of the Sparse Delta Memory (SDM) hot path on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (cited by page title and section):
+ *   [P] "Sparse Delta Memory: Scaling the State of Linear RNNs through
+ *       Sparsity"
+ *       Sec. 2, Product-Key Memories: N = n_sub^2 slot scores are the outer
+ *               sum of two half-score vectors; top-k is found without
+ *               materialising the N scores.
+ *       Sec. 3.1, step 1 (Sparse Key Selection), step 2 (Gated Delta Write,
+ *               Eq. 4), step 3 (Sparse Read), "Learned Initial State".
+ *       Sec. 4, SDM Configuration: read and write activations use softmax
+ *               normalisation.
+ *   [B] "Sparse Delta Memory: Scaling Linear RNN States to 1M Tokens via
+ *       Sparsity", Methodology, item 2 (Gated Delta Updates):
+ *       M_t[i] <- a_t M_{t-1}[i] + b_t k^(i) (v_t - a_t M_{t-1}^T k_t).
+ *
+ * Conventions shared by every call:
+ *   - Layouts are row-major and contiguous.  A "token-head" is one (b, t, h).
+ *       k, q       [B, T, H, d_k]        bf16 (in_dtype SDM_BF16) or fp32
+ *       v          [B, T, H, d_v]        same dtype as k
+ *       C_w, C_r   [H, 2, n_sub, d_k/2]  sub-key codebooks (half 0, half 1)
+ *       a, b       [B, T, H]             fp32 forget gate a_t and input gate b_t
+ *       widx, wwt  [B, T, H, W]          int32 write slots, fp32 weights
+ *       ridx, rwt  [B, T, H, R]          int32 read slots, fp32 weights
+ *       M          [B, H, N, d_v]        fp32 memory state, N = n_sub^2
+ *       M0         [H, N, d_v]           fp32 learned initial state
+ *       o          [B, T, H, d_v]        fp32 read-out
+ *   - Slot numbering: slot = i1 * n_sub + i2, i1 from half 0 of the key.
+ *   - Slot lists are sorted by score descending, ties to the lower slot; a
+ *     half score is an fp32 dot product and a slot score is the fp32 sum of
+ *     its two half scores.  Weights are the softmax of the selected scores.
+ *   - All pointers are device pointers (hipMalloc'd or equivalent) unless
+ *     stated.  The caller owns every buffer; the library keeps no pointer
+ *     after a call returns and allocates no device memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Arguments are validated on the host before anything
+ *     is launched; on a validation error nothing is written.  A launch
+ *     failure returns SDM_ERR_HIP.  No C++ exception crosses this boundary.
+ *   - Calls that overlap on the same buffers race; order them on one stream.
+ *   - sdm_last_error() returns a per-thread message describing the last
+ *     non-OK status.
+ */
+#ifndef SDM_H_
+#define SDM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SDM_OK = 0,
+    SDM_ERR_INVALID_ARG = -1, /* bad pointer, size or dimension */
+    SDM_ERR_UNSUPPORTED = -2, /* legal for the method, outside what the kernels implement */
+    SDM_ERR_HIP = -3          /* the HIP runtime reported an error */
+} sdm_status;
+
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+
+typedef void *sdm_stream_t; /* a hipStream_t */
+
+typedef struct {
+    int64_t B;       /* sequences */
+    int64_t T;       /* tokens per sequence in this call (1 for sdm_decode_step) */
+    int64_t H;       /* SDM heads */
+    int64_t d_k;     /* key/query width, even; each half is d_k/2 */
+    int64_t n_sub;   /* sub-keys per half; N = n_sub^2 slots per head */
+    int64_t d_v;     /* value / memory row width */
+    int64_t k_prime; /* candidates kept per half before the merge */
+    int64_t W;       /* write slots per token */
+    int64_t R;       /* read slots per token */
+    int32_t in_dtype;/* sdm_dtype of k, q, v, C_w, C_r */
+    int32_t reserved;/* must be 0 */
+} sdm_dims;
+
+/* Limits of this implementation (SDM_ERR_UNSUPPORTED beyond them):
+ *   W, R <= 64;  k_prime <= 64;  k_prime <= n_sub <= 4096;
+ *   d_v a multiple of 32 and <= 1024;  bf16: d_k/2 a multiple of 32, d_k <= 512;
+ *   fp32: d_k <= 512.
+ * Method constraints (SDM_ERR_INVALID_ARG): d_k even; 1 <= W, R <= k_prime^2. */
+
+/* ---------------------------------------------------------------------------
+ * sdm_state_init -- [P] Sec. 3.1 "Learned Initial State"; [B] item 3.
+ * Copies the learned initial memory into every sequence: M[b][h] = M0[h].
+ *   M  [B,H,N,d_v] fp32, written.   M0 [H,N,d_v] fp32, read.
+ * Only B, H, n_sub and d_v of dims are used.  M and M0 must not overlap.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_state_init(float *M, const float *M0, const sdm_dims *dims, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * sdm_pkm_address -- [P] Sec. 2 (PKM) and Sec. 3.1 step 1; softmax of Sec. 4.
+ * For every token-head and each kind (write: x = k against C_w, read: x = q
+ * against C_r):
+ *   s_c[u] = <x[c*d_k/2 : (c+1)*d_k/2], C[h][c][u]>   c = 0, 1   (fp32 result)
+ *   top-k_prime of s_0 and of s_1; the k_prime^2 outer-sum candidates
+ *   s_0[i1] + s_1[i2] at slot i1*n_sub + i2; the top W (write) / R (read)
+ *   of those, sorted; weights = softmax of their scores.
+ * With k_prime >= W (resp. R) the result is the exact top-W over all N slots.
+ * C_r may equal C_w (one shared codebook).  Outputs: widx, wwt [B,T,H,W];
+ * ridx, rwt [B,T,H,R].  Uses B, T, H, d_k, n_sub, k_prime, W, R, in_dtype.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const void *C_r,
+                           const sdm_dims *dims, int32_t *widx, float *wwt, int32_t *ridx,
+                           float *rwt, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * sdm_scan_workspace_size -- bytes of device workspace sdm_scan_forward needs
+ * for these dims (0 if none).  Host-only; never fails (returns 0 on bad dims).
+ * ------------------------------------------------------------------------- */
+size_t sdm_scan_workspace_size(const sdm_dims *dims);
+
+/* ---------------------------------------------------------------------------
+ * sdm_scan_forward -- [P] Sec. 3.1 steps 2-3 (Eq. 4) and [B] item 2.
+ * For every (b, h), tokens t = 0..T-1 in order, on the state M in place:
+ *   p   = sum_j wwt_j M[widx_j]                    (rows before this write)
+ *   M[widx_j] = a_t M[widx_j] + b_t wwt_j (v_t - a_t p)   for all j at once
+ *   o_t = sum_j rwt_j M[ridx_j]                    (rows after this write)
+ * Rows not in widx are untouched.  Write slots of one token must be distinct
+ * and every slot must lie in [0, N); out-of-range slots are dropped by the
+ * hardware bounds check of the buffer access instead of faulting (results
+ * are then undefined, never out-of-bounds memory traffic).
+ * workspace: device memory of at least sdm_scan_workspace_size(dims) bytes
+ * (may be NULL when that is 0); its contents on entry are ignored.
+ * o must not alias M, the slot lists or the weights.
+ * Uses B, T, H, n_sub, d_v, W, R, in_dtype (v's dtype).
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                            const float *rwt, const void *v, const float *a, const float *b,
+                            float *o, void *workspace, size_t workspace_bytes,
+                            const sdm_dims *dims, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * sdm_decode_step -- one new token for each of B sequences: the addressing of
+ * sdm_pkm_address and one step of sdm_scan_forward fused in one launch
+ * ([P] Sec. 3.1 steps 1-3 for T = 1).
+ *   M [B,H,N,d_v] in/out;  k, q [B,H,d_k];  v [B,H,d_v];  a, b [B,H];
+ *   o [B,H,d_v] written;  widx_out [B,H,W], ridx_out [B,H,R] optional (NULL
+ *   skips them) -- the selected slots, for inspection.
+ * dims->T must be 1.  Results equal sdm_pkm_address followed by
+ * sdm_scan_forward on the same token.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C_w,
+                           const void *C_r, const void *v, const float *a, const float *b,
+                           float *o, int32_t *widx_out, int32_t *ridx_out, const sdm_dims *dims,
+                           sdm_stream_t stream);
+
+/* Static description of a status code. */
+const char *sdm_status_string(sdm_status status);
+
+/* Per-thread detail message of the last non-OK status ("" if none). */
+const char *sdm_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int sdm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H_ */

@@ -1,0 +1,17 @@
+"""Sparse Delta Memory hot path on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libsdm.so`` (C ABI in ``include/sdm.h``).  The
+binding only marshals arguments: torch tensors provide device memory and
+streams, and every step of the path runs in the HIP kernels of the library.
+If the library has not been built, the first call raises ImportError; there
+is no fallback implementation.
+"""
+from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP, SDM_F32,
+                      SDM_BF16, SdmDims, SdmError, dims_from, lib_path, load_library,
+                      sdm_state_init, sdm_pkm_address, sdm_scan_workspace_size, sdm_scan_forward,
+                      sdm_decode_step, sdm_status_string, sdm_last_error, sdm_version,
+                      state_init, pkm_address, scan_forward, decode_step)
+
+__all__ = [n for n in dir() if n.startswith(("sdm_", "SDM_", "Sdm")) or n in (
+    "dims_from", "lib_path", "load_library", "state_init", "pkm_address", "scan_forward",
+    "decode_step")]

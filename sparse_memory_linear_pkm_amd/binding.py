@@ -1,0 +1,260 @@
+"""ctypes binding of the C ABI declared in ``include/sdm.h``.
+
+Low-level functions carry the C names and take raw device pointers (ints) or
+torch tensors; the convenience wrappers (``state_init``, ``pkm_address``,
+``scan_forward``, ``decode_step``) allocate outputs with torch and check
+shapes, dtypes and devices before calling the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libsdm.so"
+
+SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP = 0, -1, -2, -3
+SDM_F32, SDM_BF16 = 0, 1
+
+
+class SdmError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what}: {sdm_status_string(status)} ({status}): {detail}")
+        self.status = status
+
+
+class SdmDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("B", "T", "H", "d_k", "n_sub", "d_v", "k_prime", "W", "R")] + \
+               [("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def lib_path() -> str:
+    return os.environ.get("SDM_LIBRARY", os.path.join(HERE, _LIB_NAME))
+
+
+_lib = None
+
+
+def load_library():
+    """Load libsdm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m sparse_memory_linear_pkm_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32 = ctypes.c_void_p, ctypes.c_int
+    D = ctypes.POINTER(SdmDims)
+    sigs = {
+        "sdm_state_init": [P, P, D, P],
+        "sdm_pkm_address": [P, P, P, P, D, P, P, P, P, P],
+        "sdm_scan_forward": [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
+        "sdm_decode_step": [P, P, P, P, P, P, P, P, P, P, P, D, P],
+    }
+    for name, args in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = I32
+    lib.sdm_scan_workspace_size.argtypes = [D]
+    lib.sdm_scan_workspace_size.restype = ctypes.c_size_t
+    lib.sdm_status_string.argtypes = [I32]
+    lib.sdm_status_string.restype = ctypes.c_char_p
+    lib.sdm_last_error.argtypes = []
+    lib.sdm_last_error.restype = ctypes.c_char_p
+    lib.sdm_version.argtypes = []
+    lib.sdm_version.restype = I32
+    _lib = lib
+    return lib
+
+
+def dims_from(d=None, **kw) -> SdmDims:
+    """SdmDims from an object with B, T, H, d_k, n_sub, d_v, k_prime, W, R and
+    in_dtype ("bf16"/"f32" or SDM_BF16/SDM_F32) attributes, or keywords."""
+    vals = {}
+    for n in ("B", "T", "H", "d_k", "n_sub", "d_v", "k_prime", "W", "R", "in_dtype"):
+        if n in kw:
+            vals[n] = kw[n]
+        elif d is not None:
+            vals[n] = getattr(d, n)
+        else:
+            raise TypeError(f"missing dimension {n}")
+    dt = vals["in_dtype"]
+    if isinstance(dt, str):
+        dt = {"bf16": SDM_BF16, "f32": SDM_F32}[dt]
+    out = SdmDims(*(int(vals[n]) for n in ("B", "T", "H", "d_k", "n_sub", "d_v", "k_prime", "W", "R")),
+                  int(dt), int(kw.get("reserved", 0)))
+    return out
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != SDM_OK:
+        raise SdmError(status, what, sdm_last_error())
+
+
+# ---------------------------------------------------------------------------
+# the C calls, same names
+# ---------------------------------------------------------------------------
+def sdm_status_string(status: int) -> str:
+    return load_library().sdm_status_string(int(status)).decode()
+
+
+def sdm_last_error() -> str:
+    return load_library().sdm_last_error().decode()
+
+
+def sdm_version() -> int:
+    return load_library().sdm_version()
+
+
+def sdm_scan_workspace_size(dims: SdmDims) -> int:
+    return int(load_library().sdm_scan_workspace_size(ctypes.byref(dims)))
+
+
+def sdm_state_init(M, M0, dims: SdmDims, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_state_init(_ptr(M), _ptr(M0), ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_state_init")
+    return st
+
+
+def sdm_pkm_address(k, q, C_w, C_r, dims: SdmDims, widx, wwt, ridx, rwt, stream=None, *,
+                    check: bool = True) -> int:
+    st = load_library().sdm_pkm_address(_ptr(k), _ptr(q), _ptr(C_w), _ptr(C_r), ctypes.byref(dims),
+                                        _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _stream(stream))
+    if check:
+        _check(st, "sdm_pkm_address")
+    return st
+
+
+def sdm_scan_forward(M, widx, wwt, ridx, rwt, v, a, b, o, workspace, workspace_bytes: int,
+                     dims: SdmDims, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_scan_forward(_ptr(M), _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _ptr(v),
+                                         _ptr(a), _ptr(b), _ptr(o), _ptr(workspace),
+                                         int(workspace_bytes), ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_scan_forward")
+    return st
+
+
+def sdm_decode_step(M, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, dims: SdmDims, stream=None, *,
+                    check: bool = True) -> int:
+    st = load_library().sdm_decode_step(_ptr(M), _ptr(k), _ptr(q), _ptr(C_w), _ptr(C_r), _ptr(v), _ptr(a),
+                                        _ptr(b), _ptr(o), _ptr(widx_out), _ptr(ridx_out),
+                                        ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_decode_step")
+    return st
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences (allocation + shape checks only)
+# ---------------------------------------------------------------------------
+def _expect(t, shape, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} dtype {t.dtype} != {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _in_dtype(d: SdmDims):
+    import torch
+    return torch.bfloat16 if d.in_dtype == SDM_BF16 else torch.float32
+
+
+def state_init(M0, dims: SdmDims, M=None, stream=None):
+    import torch
+    N = dims.n_sub * dims.n_sub
+    _expect(M0, (dims.H, N, dims.d_v), torch.float32, "M0")
+    if M is None:
+        M = torch.empty((dims.B, dims.H, N, dims.d_v), dtype=torch.float32, device=M0.device)
+    _expect(M, (dims.B, dims.H, N, dims.d_v), torch.float32, "M")
+    sdm_state_init(M, M0, dims, stream)
+    return M
+
+
+def pkm_address(k, q, C_w, C_r, dims: SdmDims, out=None, stream=None):
+    import torch
+    dt = _in_dtype(dims)
+    B, T, H = dims.B, dims.T, dims.H
+    for n, t in (("k", k), ("q", q)):
+        _expect(t, (B, T, H, dims.d_k), dt, n)
+    for n, t in (("C_w", C_w), ("C_r", C_r)):
+        _expect(t, (H, 2, dims.n_sub, dims.d_k // 2), dt, n)
+    if out is None:
+        dev = k.device
+        out = (torch.empty((B, T, H, dims.W), dtype=torch.int32, device=dev),
+               torch.empty((B, T, H, dims.W), dtype=torch.float32, device=dev),
+               torch.empty((B, T, H, dims.R), dtype=torch.int32, device=dev),
+               torch.empty((B, T, H, dims.R), dtype=torch.float32, device=dev))
+    widx, wwt, ridx, rwt = out
+    sdm_pkm_address(k, q, C_w, C_r, dims, widx, wwt, ridx, rwt, stream)
+    return widx, wwt, ridx, rwt
+
+
+def scan_forward(M, widx, wwt, ridx, rwt, v, a, b, dims: SdmDims, o=None, workspace=None, stream=None):
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    N = dims.n_sub * dims.n_sub
+    _expect(M, (B, H, N, dims.d_v), torch.float32, "M")
+    _expect(widx, (B, T, H, dims.W), torch.int32, "widx")
+    _expect(wwt, (B, T, H, dims.W), torch.float32, "wwt")
+    _expect(ridx, (B, T, H, dims.R), torch.int32, "ridx")
+    _expect(rwt, (B, T, H, dims.R), torch.float32, "rwt")
+    _expect(v, (B, T, H, dims.d_v), _in_dtype(dims), "v")
+    _expect(a, (B, T, H), torch.float32, "a")
+    _expect(b, (B, T, H), torch.float32, "b")
+    if o is None:
+        o = torch.empty((B, T, H, dims.d_v), dtype=torch.float32, device=M.device)
+    _expect(o, (B, T, H, dims.d_v), torch.float32, "o")
+    need = sdm_scan_workspace_size(dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=M.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sdm_scan_forward(M, widx, wwt, ridx, rwt, v, a, b, o, workspace, ws_bytes, dims, stream)
+    return o
+
+
+def decode_step(M, k, q, C_w, C_r, v, a, b, dims: SdmDims, o=None, widx_out=None, ridx_out=None,
+                stream=None):
+    import torch
+    B, H = dims.B, dims.H
+    N = dims.n_sub * dims.n_sub
+    dt = _in_dtype(dims)
+    _expect(M, (B, H, N, dims.d_v), torch.float32, "M")
+    _expect(k, (B, H, dims.d_k), dt, "k")
+    _expect(q, (B, H, dims.d_k), dt, "q")
+    _expect(C_w, (H, 2, dims.n_sub, dims.d_k // 2), dt, "C_w")
+    _expect(C_r, (H, 2, dims.n_sub, dims.d_k // 2), dt, "C_r")
+    _expect(v, (B, H, dims.d_v), dt, "v")
+    _expect(a, (B, H), torch.float32, "a")
+    _expect(b, (B, H), torch.float32, "b")
+    if o is None:
+        o = torch.empty((B, H, dims.d_v), dtype=torch.float32, device=M.device)
+    sdm_decode_step(M, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, dims, stream)
+    return o

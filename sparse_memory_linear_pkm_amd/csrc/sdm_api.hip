@@ -1,0 +1,235 @@
+// sdm_api.hip -- the C ABI declared in include/sdm.h: host-side validation,
+// error reporting and kernel launches.  No device memory is allocated here
+// and no pointer is kept after a call returns.
+#include "../../include/sdm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sdm_status fail(sdm_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+sdm_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(SDM_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+constexpr int64_t kMaxList = 64;      // W, R, k' per wave-level selection
+constexpr int64_t kMaxNsub = 2048;    // 16 x n_sub fp32 score tile in LDS
+constexpr int64_t kMaxDv = 1024;
+
+// Checks shared by every call that uses the memory geometry.
+sdm_status check_memory_dims(const sdm_dims *d)
+{
+    if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
+    if (d->reserved != 0) return fail(SDM_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->B < 0 || d->H < 1 || d->n_sub < 1 || d->d_v < 1)
+        return fail(SDM_ERR_INVALID_ARG, "need B >= 0, H >= 1, n_sub >= 1, d_v >= 1 (got B=%lld H=%lld n_sub=%lld d_v=%lld)",
+                    (long long)d->B, (long long)d->H, (long long)d->n_sub, (long long)d->d_v);
+    if (d->n_sub > 46340) return fail(SDM_ERR_INVALID_ARG, "n_sub^2 must fit in int32");
+    if (d->d_v % 32 != 0 || d->d_v > kMaxDv)
+        return fail(SDM_ERR_UNSUPPORTED, "d_v must be a multiple of 32 and <= %lld (got %lld)",
+                    (long long)kMaxDv, (long long)d->d_v);
+    const uint64_t row_bytes = (uint64_t)d->d_v * 4u;
+    if ((uint64_t)d->n_sub * (uint64_t)d->n_sub * row_bytes >= (1ull << 32))
+        return fail(SDM_ERR_UNSUPPORTED, "one (sequence, head) memory must be < 4 GiB");
+    return SDM_OK;
+}
+
+sdm_status check_method_dims(const sdm_dims *d, bool need_T)
+{
+    sdm_status st = check_memory_dims(d);
+    if (st != SDM_OK) return st;
+    if (need_T && d->T < 0) return fail(SDM_ERR_INVALID_ARG, "T must be >= 0");
+    if (d->in_dtype != SDM_F32 && d->in_dtype != SDM_BF16)
+        return fail(SDM_ERR_INVALID_ARG, "in_dtype must be SDM_F32 or SDM_BF16");
+    if (d->d_k < 2 || (d->d_k & 1)) return fail(SDM_ERR_INVALID_ARG, "d_k must be even and >= 2");
+    if (d->k_prime < 1 || d->k_prime > d->n_sub)
+        return fail(SDM_ERR_INVALID_ARG, "need 1 <= k_prime <= n_sub");
+    if (d->W < 1 || d->R < 1 || d->W > d->k_prime * d->k_prime || d->R > d->k_prime * d->k_prime)
+        return fail(SDM_ERR_INVALID_ARG, "need 1 <= W, R <= k_prime^2");
+    if (d->W > kMaxList || d->R > kMaxList || d->k_prime > kMaxList)
+        return fail(SDM_ERR_UNSUPPORTED, "W, R and k_prime must be <= %lld", (long long)kMaxList);
+    if (d->n_sub > kMaxNsub) return fail(SDM_ERR_UNSUPPORTED, "n_sub must be <= %lld", (long long)kMaxNsub);
+    if (d->d_k > 512) return fail(SDM_ERR_UNSUPPORTED, "d_k must be <= 512");
+    if (d->in_dtype == SDM_BF16 && ((d->d_k / 2) % 32) != 0)
+        return fail(SDM_ERR_UNSUPPORTED, "bf16 inputs need d_k/2 to be a multiple of 32 (MFMA K)");
+    return SDM_OK;
+}
+
+hipStream_t as_stream(sdm_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+size_t in_size(const sdm_dims *d) { return d->in_dtype == SDM_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+const char *sdm_status_string(sdm_status st)
+{
+    switch (st) {
+    case SDM_OK: return "ok";
+    case SDM_ERR_INVALID_ARG: return "invalid argument";
+    case SDM_ERR_UNSUPPORTED: return "unsupported by this implementation";
+    case SDM_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *sdm_last_error(void) { return g_last_error.c_str(); }
+
+int sdm_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+sdm_status sdm_state_init(float *M, const float *M0, const sdm_dims *d, sdm_stream_t stream)
+{
+    sdm_status st = check_memory_dims(d);
+    if (st != SDM_OK) return st;
+    if (!M || !M0) return fail(SDM_ERR_INVALID_ARG, "M and M0 must be non-NULL");
+    if (!aligned(M, 16) || !aligned(M0, 16)) return fail(SDM_ERR_INVALID_ARG, "M and M0 must be 16-byte aligned");
+    const int64_t per_seq = d->H * d->n_sub * d->n_sub * d->d_v;
+    if (overlap(M, sizeof(float) * per_seq * d->B, M0, sizeof(float) * per_seq))
+        return fail(SDM_ERR_INVALID_ARG, "M and M0 overlap");
+    sdm::InitArgs A{M, M0, d->B, per_seq};
+    hipError_t e = sdm::launch_state_init(A, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_state_init launch");
+}
+
+sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const void *C_r,
+                           const sdm_dims *d, int32_t *widx, float *wwt, int32_t *ridx, float *rwt,
+                           sdm_stream_t stream)
+{
+    sdm_status st = check_method_dims(d, true);
+    if (st != SDM_OK) return st;
+    if (!k || !q || !C_w || !C_r || !widx || !wwt || !ridx || !rwt)
+        return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t al = d->in_dtype == SDM_BF16 ? 16 : 4;
+    if (!aligned(k, al) || !aligned(q, al) || !aligned(C_w, al) || !aligned(C_r, al))
+        return fail(SDM_ERR_INVALID_ARG, "k, q, C_w, C_r must be %zu-byte aligned", al);
+    if (!aligned(widx, 4) || !aligned(wwt, 4) || !aligned(ridx, 4) || !aligned(rwt, 4))
+        return fail(SDM_ERR_INVALID_ARG, "slot and weight outputs must be 4-byte aligned");
+    const int64_t rows = d->B * d->T * d->H;
+    if (overlap(widx, 4 * rows * d->W, ridx, 4 * rows * d->R) ||
+        overlap(wwt, 4 * rows * d->W, rwt, 4 * rows * d->R) ||
+        overlap(widx, 4 * rows * d->W, wwt, 4 * rows * d->W) ||
+        overlap(ridx, 4 * rows * d->R, rwt, 4 * rows * d->R))
+        return fail(SDM_ERR_INVALID_ARG, "output buffers overlap");
+    if (rows == 0) return SDM_OK;
+    sdm::AddressArgs A{};
+    A.kind[0] = {k, C_w, widx, wwt, (int)d->W};
+    A.kind[1] = {q, C_r, ridx, rwt, (int)d->R};
+    A.BT = d->B * d->T;
+    A.H = (int)d->H;
+    A.d_k = (int)d->d_k;
+    A.n_sub = (int)d->n_sub;
+    A.k_prime = (int)d->k_prime;
+    hipError_t e = sdm::launch_pkm_address(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_pkm_address launch");
+}
+
+size_t sdm_scan_workspace_size(const sdm_dims *d)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->W < 1 || d->R < 1 || d->d_v < 1) return 0;
+    return sdm::scan_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v);
+}
+
+sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                            const float *rwt, const void *v, const float *a, const float *b,
+                            float *o, void *workspace, size_t workspace_bytes, const sdm_dims *d,
+                            sdm_stream_t stream)
+{
+    sdm_status st = check_memory_dims(d);
+    if (st != SDM_OK) return st;
+    if (d->T < 0) return fail(SDM_ERR_INVALID_ARG, "T must be >= 0");
+    if (d->in_dtype != SDM_F32 && d->in_dtype != SDM_BF16)
+        return fail(SDM_ERR_INVALID_ARG, "in_dtype must be SDM_F32 or SDM_BF16");
+    if (d->W < 1 || d->R < 1) return fail(SDM_ERR_INVALID_ARG, "need W, R >= 1");
+    if (d->W > d->n_sub * d->n_sub || d->R > d->n_sub * d->n_sub)
+        return fail(SDM_ERR_INVALID_ARG, "W and R must not exceed N");
+    if (d->W > kMaxList || d->R > kMaxList)
+        return fail(SDM_ERR_UNSUPPORTED, "W and R must be <= %lld", (long long)kMaxList);
+    if (!M || !widx || !wwt || !ridx || !rwt || !v || !a || !b || !o)
+        return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(M, 16) || !aligned(o, 16)) return fail(SDM_ERR_INVALID_ARG, "M and o must be 16-byte aligned");
+    if (!aligned(v, d->in_dtype == SDM_BF16 ? 8 : 16)) return fail(SDM_ERR_INVALID_ARG, "v is misaligned");
+    if (!aligned(widx, 4) || !aligned(wwt, 4) || !aligned(ridx, 4) || !aligned(rwt, 4) ||
+        !aligned(a, 4) || !aligned(b, 4))
+        return fail(SDM_ERR_INVALID_ARG, "slot lists, weights and gates must be 4-byte aligned");
+    const int64_t N = d->n_sub * d->n_sub;
+    const int64_t rows = d->B * d->T * d->H;
+    const size_t msz = sizeof(float) * (size_t)(d->B * d->H * N * d->d_v);
+    const size_t osz = sizeof(float) * (size_t)(rows * d->d_v);
+    if (overlap(o, osz, M, msz)) return fail(SDM_ERR_INVALID_ARG, "o overlaps M");
+    if (overlap(o, osz, widx, 4 * rows * d->W) || overlap(o, osz, ridx, 4 * rows * d->R) ||
+        overlap(o, osz, wwt, 4 * rows * d->W) || overlap(o, osz, rwt, 4 * rows * d->R))
+        return fail(SDM_ERR_INVALID_ARG, "o overlaps a slot list or weight array");
+    if (overlap(M, msz, widx, 4 * rows * d->W) || overlap(M, msz, ridx, 4 * rows * d->R) ||
+        overlap(M, msz, wwt, 4 * rows * d->W) || overlap(M, msz, rwt, 4 * rows * d->R))
+        return fail(SDM_ERR_INVALID_ARG, "M overlaps a slot list or weight array");
+    const size_t need = sdm::scan_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(SDM_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (rows == 0) return SDM_OK;
+    sdm::ScanArgs A{M, widx, wwt, ridx, rwt, v, a, b, o, d->B, d->T, (int)d->H, (int)N, (int)d->d_v,
+                    (int)d->W, (int)d->R};
+    hipError_t e = sdm::launch_scan(A, d->in_dtype == SDM_BF16, workspace, workspace_bytes,
+                                    as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan_forward launch");
+}
+
+sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C_w, const void *C_r,
+                           const void *v, const float *a, const float *b, float *o, int32_t *widx_out,
+                           int32_t *ridx_out, const sdm_dims *d, sdm_stream_t stream)
+{
+    sdm_status st = check_method_dims(d, false);
+    if (st != SDM_OK) return st;
+    if (d->T != 1) return fail(SDM_ERR_INVALID_ARG, "sdm_decode_step needs dims.T == 1");
+    if (!M || !k || !q || !C_w || !C_r || !v || !a || !b || !o)
+        return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t al = d->in_dtype == SDM_BF16 ? 16 : 4;
+    if (!aligned(k, al) || !aligned(q, al) || !aligned(C_w, al) || !aligned(C_r, al))
+        return fail(SDM_ERR_INVALID_ARG, "k, q, C_w, C_r must be %zu-byte aligned", al);
+    if (!aligned(M, 16) || !aligned(o, 16)) return fail(SDM_ERR_INVALID_ARG, "M and o must be 16-byte aligned");
+    if (!aligned(v, d->in_dtype == SDM_BF16 ? 8 : 16)) return fail(SDM_ERR_INVALID_ARG, "v is misaligned");
+    if (!aligned(a, 4) || !aligned(b, 4) || !aligned(widx_out, 4) || !aligned(ridx_out, 4))
+        return fail(SDM_ERR_INVALID_ARG, "gates and slot outputs must be 4-byte aligned");
+    const int64_t N = d->n_sub * d->n_sub;
+    const size_t msz = sizeof(float) * (size_t)(d->B * d->H * N * d->d_v);
+    if (overlap(o, sizeof(float) * d->B * d->H * d->d_v, M, msz)) return fail(SDM_ERR_INVALID_ARG, "o overlaps M");
+    if (d->B * d->H > 0x7fffffff) return fail(SDM_ERR_UNSUPPORTED, "B*H too large");
+    if (d->B == 0) return SDM_OK;
+    sdm::DecodeArgs A{};
+    A.M = M; A.k = k; A.q = q; A.C_w = C_w; A.C_r = C_r; A.v = v; A.a = a; A.b = b; A.o = o;
+    A.widx_out = widx_out; A.ridx_out = ridx_out;
+    A.B = (int)d->B; A.H = (int)d->H; A.d_k = (int)d->d_k; A.n_sub = (int)d->n_sub;
+    A.d_v = (int)d->d_v; A.k_prime = (int)d->k_prime; A.W = (int)d->W; A.R = (int)d->R; A.N = (int)N;
+    hipError_t e = sdm::launch_decode(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_decode_step launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/sdm.h declares, and rejects bad arguments on the host
+before anything reaches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_memory_linear_pkm_amd as sdm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sdm.load_library()
+    names = declared_functions()
+    assert {"sdm_state_init", "sdm_pkm_address", "sdm_scan_forward", "sdm_decode_step",
+            "sdm_scan_workspace_size", "sdm_status_string", "sdm_last_error", "sdm_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = os.popen(f"nm -D --defined-only {sdm.lib_path()}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", nm), f"{n} not exported"
+
+
+def test_status_strings_and_version():
+    assert sdm.sdm_status_string(sdm.SDM_OK) == "ok"
+    assert "invalid" in sdm.sdm_status_string(sdm.SDM_ERR_INVALID_ARG)
+    assert "unsupported" in sdm.sdm_status_string(sdm.SDM_ERR_UNSUPPORTED)
+    assert "HIP" in sdm.sdm_status_string(sdm.SDM_ERR_HIP)
+    assert sdm.sdm_version() >= 10000
+
+
+def good_dims(**kw):
+    base = dict(B=2, T=8, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=8, R=8, in_dtype="bf16")
+    base.update(kw)
+    return sdm.dims_from(**base)
+
+
+FAKE = 1 << 40  # never dereferenced: every case below fails validation first
+
+
+def addr(dims, **ptrs):
+    p = dict(k=FAKE, q=FAKE, C_w=FAKE, C_r=FAKE, widx=FAKE, wwt=FAKE + (1 << 30), ridx=FAKE + (2 << 30),
+             rwt=FAKE + (3 << 30))
+    p.update(ptrs)
+    return sdm.sdm_pkm_address(p["k"], p["q"], p["C_w"], p["C_r"], dims, p["widx"], p["wwt"], p["ridx"],
+                               p["rwt"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_k=127), sdm.SDM_ERR_INVALID_ARG),
+    (dict(k_prime=17), sdm.SDM_ERR_INVALID_ARG),        # k' > n_sub
+    (dict(W=65, k_prime=16), sdm.SDM_ERR_UNSUPPORTED),  # W <= k'^2 but above the kernel cap
+    (dict(W=0), sdm.SDM_ERR_INVALID_ARG),
+    (dict(R=100, k_prime=8), sdm.SDM_ERR_INVALID_ARG),  # R > k'^2
+    (dict(d_v=48), sdm.SDM_ERR_UNSUPPORTED),
+    (dict(d_k=96), sdm.SDM_ERR_UNSUPPORTED),            # bf16 MFMA needs d_k/2 % 32 == 0
+    (dict(in_dtype=7), sdm.SDM_ERR_INVALID_ARG),
+    (dict(reserved=1), sdm.SDM_ERR_INVALID_ARG),
+    (dict(H=0), sdm.SDM_ERR_INVALID_ARG),
+])
+def test_address_rejects_bad_dims(kw, status):
+    assert addr(good_dims(**kw)) == status
+    assert sdm.sdm_last_error() != ""
+
+
+def test_address_rejects_null_and_misaligned():
+    assert addr(good_dims(), k=None) == sdm.SDM_ERR_INVALID_ARG
+    assert addr(good_dims(), q=FAKE + 2) == sdm.SDM_ERR_INVALID_ARG
+    # overlapping outputs
+    assert addr(good_dims(), ridx=FAKE) == sdm.SDM_ERR_INVALID_ARG
+
+
+def scan(dims, **ptrs):
+    base = FAKE
+    step = 1 << 34
+    p = dict(M=base, widx=base + step, wwt=base + 2 * step, ridx=base + 3 * step, rwt=base + 4 * step,
+             v=base + 5 * step, a=base + 6 * step, b=base + 7 * step, o=base + 8 * step, ws=None, ws_bytes=0)
+    p.update(ptrs)
+    return sdm.sdm_scan_forward(p["M"], p["widx"], p["wwt"], p["ridx"], p["rwt"], p["v"], p["a"], p["b"],
+                                p["o"], p["ws"], p["ws_bytes"], dims, stream=0, check=False)
+
+
+def test_scan_rejects_bad_arguments():
+    d = good_dims()
+    assert scan(d, o=FAKE + 64) == sdm.SDM_ERR_INVALID_ARG          # o overlaps M
+    assert scan(d, M=None) == sdm.SDM_ERR_INVALID_ARG
+    assert scan(d, M=FAKE + 4) == sdm.SDM_ERR_INVALID_ARG           # misaligned M
+    assert scan(good_dims(W=70)) == sdm.SDM_ERR_UNSUPPORTED
+    assert scan(good_dims(T=-1)) == sdm.SDM_ERR_INVALID_ARG
+    assert scan(good_dims(n_sub=46341)) == sdm.SDM_ERR_INVALID_ARG
+    # one (b, h) memory must stay below 4 GiB for 32-bit buffer offsets
+    assert scan(good_dims(n_sub=4096, d_v=128)) == sdm.SDM_ERR_UNSUPPORTED
+    need = sdm.sdm_scan_workspace_size(d)
+    if need:
+        assert scan(d, ws=None, ws_bytes=0) == sdm.SDM_ERR_INVALID_ARG
+
+
+def test_decode_rejects_bad_arguments():
+    d = good_dims(T=2)
+    st = sdm.sdm_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + (1 << 36), None, None, d,
+                             stream=0, check=False)
+    assert st == sdm.SDM_ERR_INVALID_ARG
+    d = good_dims(T=1)
+    st = sdm.sdm_decode_step(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + (1 << 36), None, None, d,
+                             stream=0, check=False)
+    assert st == sdm.SDM_ERR_INVALID_ARG
+
+
+def test_state_init_rejects_overlap():
+    d = good_dims()
+    assert sdm.sdm_state_init(FAKE, FAKE + 16, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
+    assert sdm.sdm_state_init(None, FAKE, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
+
+
+def test_workspace_size_is_host_only():
+    assert sdm.sdm_scan_workspace_size(good_dims()) >= 0
+    bad = good_dims(W=0)
+    assert sdm.sdm_scan_workspace_size(bad) == 0
+
+
+def test_binding_raises_with_detail():
+    with pytest.raises(sdm.SdmError) as ei:
+        sdm.sdm_pkm_address(None, FAKE, FAKE, FAKE, good_dims(), FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert ei.value.status == sdm.SDM_ERR_INVALID_ARG
+    assert "NULL" in str(ei.value)
