@@ -1,0 +1,307 @@
+"""Benchmark of the SDM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload small]
+
+One step is one pass of the whole hot path over one batch of synthetic input
+of the named layer: copy the learned M0 into every sequence, PKM addressing
+of all B*T*H token-heads (write and read), the prefill scan over the T tokens,
+and one decode step (a new token for every sequence).  The "decode" workload
+instead times 1024 consecutive decode steps of 32 sequences.
+
+Prints one JSON line: whole-step tokens/s, the roofline of the dominant
+kernel (the scan; HBM-bound) measured with HIP events on the launch stream,
+a per-kernel breakdown, and the CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+PREFILL_WORKLOADS = ("tiny", "small", "prefill_1p4b", "long_context")
+KERNEL_SOURCES = ("sdm_scan.hip", "scan_step.h", "device_common.h")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="small",
+                   choices=list(PREFILL_WORKLOADS) + ["decode"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum CPU time spent on the oracle baseline (0 disables it)")
+    p.add_argument("--decode-steps", type=int, default=1024, help="decode steps per step (decode workload)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one plain 1 GiB device copy (for counter calibration) and exit")
+    return p.parse_args()
+
+
+def scan_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_memory_linear_pkm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per scan launch from the committed counter summary, if it was
+    taken on the current scan kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"sdm_scan_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("scan_source_sha256_16") != scan_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def device_inputs(name, d, seed):
+    import numpy as np
+    import torch
+    import sdm_synth as synth
+    p = synth.PRESETS[name]
+    if d.B * d.T * d.H <= 1 << 20 and d.H * d.N * d.d_v <= 1 << 28:
+        x = synth.make_inputs(d, seed, reuse_frac=p.reuse_frac, recall_frac=p.recall_frac)
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(a).cuda()
+        return {k: dev(v) for k, v in x.items()}, x
+    return synth.make_inputs_torch(d, seed, reuse_frac=p.reuse_frac, recall_frac=p.recall_frac), None
+
+
+def cpu_baseline(name, d, host_x, seed, min_seconds):
+    """The oracle (as it stands) on the host cores, whole steps of the same
+    workload (or a stated sample of it), reported in tokens/s."""
+    import numpy as np
+    import oracle
+    import sdm_synth as synth
+    threads = oracle.default_threads()
+    if name == "decode":
+        # 8 (b, h) pairs x a few hundred steps: the 137 GB state does not fit host RAM
+        ds = d.replace(B=1, H=8, T=256)
+        x = synth.make_inputs(ds, seed)
+        sample = f"decode: 1 sequence x 8 heads x {ds.T} steps of the decode layer (N=1,048,576)"
+        tokens = ds.T
+    elif host_x is not None:
+        ds, x = d, host_x
+        sample = f"full step of the {name} workload (B={d.B}, T={d.T}, H={d.H})"
+        tokens = d.B * d.T + d.B
+    else:
+        Ts = min(d.T, 2048)
+        ds = d.replace(B=1, T=Ts)
+        x = synth.make_inputs(ds, seed)
+        sample = f"{name}: 1 sequence x {Ts} tokens x all {d.H} heads (prefix of the workload)"
+        tokens = Ts
+    total_tokens, elapsed, reps = 0, 0.0, 0
+    while elapsed < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        M = oracle.state_init(x["M0"], ds)
+        ad = oracle.address(x["k"], x["q"], x["C_w"], x["C_r"], ds, nthreads=threads)
+        oracle.scan(M, *ad, x["v"], x["a"], x["b"], ds, nthreads=threads)
+        if name != "decode" and host_x is not None:
+            k1 = np.ascontiguousarray(x["k"][:, -1])
+            q1 = np.ascontiguousarray(x["q"][:, -1])
+            v1 = np.ascontiguousarray(x["v"][:, -1])
+            oracle.decode_step(M, k1, q1, x["C_w"], x["C_r"], v1, x["a"][:, -1].copy(),
+                               x["b"][:, -1].copy(), ds, nthreads=threads)
+        elapsed += time.perf_counter() - t0
+        total_tokens += tokens
+        reps += 1
+        if reps >= 50:
+            break
+    return {"value": total_tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample}; {reps} repetition(s), {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (sequence, head) chain is independent; see the sharding notes in DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sdm_synth as synth
+    import sparse_memory_linear_pkm_amd as sdm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sdm.load_library()
+
+    if args.copy_calibration:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
+        return
+
+    name = args.workload
+    d = synth.PRESETS[name].dims
+    decode_mode = name == "decode"
+    dx, host_x = device_inputs(name, d, args.seed)
+    N = d.N
+    stream = torch.cuda.current_stream()
+
+    if decode_mode:
+        d1 = d.replace(T=1)
+        dims1 = sdm.dims_from(d1)
+        M = torch.empty((d.B, d.H, N, d.d_v), dtype=torch.float32, device="cuda")
+        sdm.state_init(dx["M0"], dims1, M=M)
+        o = torch.empty((d.B, d.H, d.d_v), dtype=torch.float32, device="cuda")
+        per = {key: [dx[key][:, t].contiguous() for t in range(d.T)] for key in ("k", "q", "v", "a", "b")}
+        nsteps = min(args.decode_steps, d.T)
+
+        def step(timers=None):
+            ev = []
+            for t in range(nsteps):
+                if timers is not None and t == 0:
+                    e = torch.cuda.Event(enable_timing=True); e.record(stream); ev.append(e)
+                sdm.sdm_decode_step(M, per["k"][t], per["q"][t], dx["C_w"], dx["C_r"], per["v"][t], per["a"][t],
+                                    per["b"][t], o, None, None, dims1, stream)
+            if timers is not None:
+                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev.append(e)
+                timers.append(ev)
+        tokens_per_step = d.B * nsteps
+    else:
+        dims = sdm.dims_from(d)
+        d1 = d.replace(T=1)
+        dims1 = sdm.dims_from(d1)
+        B, T, H = d.B, d.T, d.H
+        M = torch.empty((B, H, N, d.d_v), dtype=torch.float32, device="cuda")
+        widx = torch.empty((B, T, H, d.W), dtype=torch.int32, device="cuda")
+        wwt = torch.empty((B, T, H, d.W), dtype=torch.float32, device="cuda")
+        ridx = torch.empty((B, T, H, d.R), dtype=torch.int32, device="cuda")
+        rwt = torch.empty((B, T, H, d.R), dtype=torch.float32, device="cuda")
+        o = torch.empty((B, T, H, d.d_v), dtype=torch.float32, device="cuda")
+        o1 = torch.empty((B, H, d.d_v), dtype=torch.float32, device="cuda")
+        ws_bytes = sdm.sdm_scan_workspace_size(dims)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        # the decode token of each step: the last prefill token's inputs reused
+        dec = {key: dx[key][:, -1].contiguous() for key in ("k", "q", "v", "a", "b")}
+
+        def step(timers=None):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timers is not None else None
+            if ev: ev[0].record(stream)
+            sdm.sdm_state_init(M, dx["M0"], dims, stream)
+            if ev: ev[1].record(stream)
+            sdm.sdm_pkm_address(dx["k"], dx["q"], dx["C_w"], dx["C_r"], dims, widx, wwt, ridx, rwt, stream)
+            if ev: ev[2].record(stream)
+            sdm.sdm_scan_forward(M, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], o, ws, ws_bytes, dims,
+                                 stream)
+            if ev: ev[3].record(stream)
+            sdm.sdm_decode_step(M, dec["k"], dec["q"], dx["C_w"], dx["C_r"], dec["v"], dec["a"], dec["b"], o1,
+                                None, None, dims1, stream)
+            if ev:
+                ev[4].record(stream)
+                timers.append(ev)
+        tokens_per_step = B * T + B
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(timers)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    value = tokens_per_step / (ms_per_step / 1e3)
+
+    result = {
+        "metric": "SDM layer tokens/sec (prefill scan + decode) and % of HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": name, "B": d.B, "T": d.T, "H": d.H, "d_k": d.d_k, "n_sub": d.n_sub, "N": N,
+                   "d_v": d.d_v, "k_prime": d.k_prime, "W": d.W, "R": d.R, "inputs": d.in_dtype,
+                   "state": "fp32", "tokens_per_step": tokens_per_step,
+                   "step": ("1024 decode steps" if decode_mode else
+                            "state init + PKM addressing + prefill scan + 1 decode token per sequence")},
+        "wall_s_timed_region": wall,
+    }
+
+    if decode_mode:
+        per_step_ms = [ev[0].elapsed_time(ev[1]) for ev in timers]
+        avg = sum(per_step_ms) / len(per_step_ms)
+        dec_ms = avg / nsteps
+        bytes_per_launch = d.B * d.H * (2 * d.W + d.R) * d.d_v * 4
+        achieved = bytes_per_launch / (dec_ms * 1e-3) / 1e9
+        result["kernels_ms"] = {"sdm_decode_step": dec_ms}
+        result["roofline"] = {"kernel": "sdm_decode_kernel", "bound": "hbm", "achieved": achieved,
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                              "traffic": None, "algorithmic_bytes_per_launch": bytes_per_launch,
+                              "avg_launch_ms": dec_ms}
+    else:
+        names = ("sdm_state_init", "sdm_pkm_address", "sdm_scan_forward", "sdm_decode_step")
+        avg = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in timers) / len(timers) for i, n in enumerate(names)}
+        result["kernels_ms"] = avg
+        th = d.B * d.T * d.H
+        scan_bytes = th * (2 * d.W + d.R) * d.d_v * 4
+        scan_s = avg["sdm_scan_forward"] * 1e-3
+        achieved = scan_bytes / scan_s / 1e9
+        traffic = measured_traffic(name)
+        result["roofline"] = {"kernel": "sdm_scan (sdm_scan_forward)", "bound": "hbm", "achieved": achieved,
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                              "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
+                              "avg_launch_ms": avg["sdm_scan_forward"]}
+        flops = th * 4 * d.n_sub * d.d_k
+        addr_tflops = flops / (avg["sdm_pkm_address"] * 1e-3) / 1e12
+        result["pkm_scoring"] = {"kernel": "pkm_score_topk", "bound": "mfma", "achieved": addr_tflops,
+                                 "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": addr_tflops / BF16_DENSE_PEAK_TFLOPS,
+                                 "algorithmic_flops_per_launch": flops}
+        init_bytes = (1 + d.B) * d.H * N * d.d_v * 4
+        result["state_init"] = {"GB/s": init_bytes / (avg["sdm_state_init"] * 1e-3) / 1e9,
+                                "bytes_per_launch": init_bytes}
+        result["scan_tokens_per_s"] = d.B * d.T / scan_s
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(name, d, host_x, args.seed, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

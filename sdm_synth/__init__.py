@@ -192,6 +192,55 @@ def make_preset_inputs(name: str, seed: int = 0, **overrides) -> dict:
     return make_inputs(d, seed, reuse_frac=p.reuse_frac, recall_frac=p.recall_frac)
 
 
+def make_inputs_torch(d: Dims, seed: int = 0, *, reuse_frac: float = 0.0, recall_frac: float = 0.0,
+                      m0: bool = True, device: str = "cuda") -> dict:
+    """Same tensors and distributions as make_inputs, drawn on the GPU with a
+    seeded torch generator (for layers too large to draw on the host).
+    Returns torch tensors on `device` (bf16 inputs as torch.bfloat16)."""
+    import torch
+    g = torch.Generator(device=device)
+    half = d.d_k // 2
+    dt = torch.bfloat16 if d.in_dtype == "bf16" else torch.float32
+
+    def normal(shape, std=1.0, mean=0.0, sub=0):
+        g.manual_seed(int(seed) * 1000003 + sub)
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        if mean != 0.0:
+            x.add_(mean)
+        return x
+
+    out = {}
+    out["C_w"] = normal((d.H, 2, d.n_sub, half), std=1.0 / math.sqrt(half), sub=1).to(dt)
+    out["C_r"] = out["C_w"]
+    k = normal((d.B, d.T, d.H, d.d_k), sub=2)
+    q = normal((d.B, d.T, d.H, d.d_k), sub=3)
+    out["v"] = normal((d.B, d.T, d.H, d.d_v), sub=4).to(dt)
+    out["a"] = torch.sigmoid(normal((d.B, d.T, d.H), mean=3.0, sub=5))
+    out["b"] = torch.sigmoid(normal((d.B, d.T, d.H), sub=6))
+    if m0:
+        out["M0"] = normal((d.H, d.N, d.d_v), std=math.sqrt(0.02), sub=7)
+    g.manual_seed(int(seed) * 1000003 + 8)
+    if reuse_frac > 0 and d.T > 1:
+        mask = torch.rand((d.B, d.T, d.H), generator=g, device=device) < reuse_frac
+        mask[:, 0, :] = False
+        # k_t := k_{t-1}; a run of reuses copies the key at the run's start
+        tidx = torch.arange(d.T, device=device).view(1, d.T, 1).expand(d.B, d.T, d.H)
+        src = torch.where(mask, torch.zeros_like(tidx), tidx)
+        src = torch.cummax(src, dim=1).values
+        k = torch.gather(k, 1, src.unsqueeze(-1).expand(-1, -1, -1, d.d_k))
+    if recall_frac > 0 and d.T > 1:
+        mask = torch.rand((d.B, d.T, d.H), generator=g, device=device) < recall_frac
+        mask[:, 0, :] = False
+        bb, tt, hh = torch.nonzero(mask, as_tuple=True)
+        srct = torch.floor(torch.rand(tt.shape, generator=g, device=device) * tt).long()
+        q[bb, tt, hh, :] = k[bb, srct, hh, :]
+    out["k"] = k.to(dt)
+    out["q"] = q.to(dt)
+    return out
+
+
 def random_addressing(d: Dims, seed: int = 0, *, hazard_slots: Optional[int] = None) -> dict:
     """Random (not PKM-derived) slot lists and weights for scan-only tests.
 

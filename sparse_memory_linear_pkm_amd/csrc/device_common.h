@@ -10,6 +10,7 @@ namespace sdm {
 constexpr int kWave = 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Buffer resource word 3 for raw (untyped) buffer access on gfx9 parts.

@@ -35,6 +35,15 @@ struct ScanArgs {
     int H, N, d_v, W, R;
 };
 
+struct HazardArgs {
+    const int32_t *widx;
+    const int32_t *ridx;
+    uint16_t *codes;   // [B,T,H,W+R]
+    uint32_t *flags;   // [B,T,H]
+    int64_t B, T, H;
+    int W, R, window;
+};
+
 struct DecodeArgs {
     float *M;
     const void *k, *q, *C_w, *C_r, *v;
@@ -56,6 +65,10 @@ size_t address_smem_bytes(int n_sub);
 hipError_t launch_scan(const ScanArgs &args, bool bf16, void *workspace, size_t ws_bytes,
                        hipStream_t stream);
 size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int d_v);
+hipError_t launch_scan_hazard(const HazardArgs &args, hipStream_t stream);
+int scan_pipe_depth(int W, int R);
+hipError_t launch_scan_pipe(const ScanArgs &args, bool bf16, const uint16_t *codes, const uint32_t *flags,
+                            hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, bool bf16, hipStream_t stream);
 size_t decode_smem_bytes(int n_sub);
 hipError_t launch_state_init(const InitArgs &args, hipStream_t stream);

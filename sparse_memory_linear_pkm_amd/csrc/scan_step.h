@@ -41,13 +41,29 @@ __device__ __forceinline__ f32x4 shfl_xor4(f32x4 x, int m)
     return y;
 }
 
+// x[l] + x[l ^ 8] + x[l ^ 16] + x[l ^ 24] + ... : the sum over the 8 lanes
+// that share (l & 7), left in every one of them.  Lane exchanges run on the
+// VALU: DPP row_ror:8 pairs l with l ^ 8 inside each 16-lane row, and the
+// gfx950 permlane16/32 swaps pair l with l ^ 16 and l ^ 32.
+__device__ __forceinline__ float rowgroup_sum1(float x)
+{
+    constexpr int kRowRor8 = 0x128;
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kRowRor8, 0xf, 0xf, false));
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
 // Sum over the 8 row groups (lanes with equal lane & 7).
 __device__ __forceinline__ f32x4 rowgroup_sum(f32x4 x)
 {
-    x += shfl_xor4(x, 8);
-    x += shfl_xor4(x, 16);
-    x += shfl_xor4(x, 32);
-    return x;
+    f32x4 r;
+    r.x = rowgroup_sum1(x.x);
+    r.y = rowgroup_sum1(x.y);
+    r.z = rowgroup_sum1(x.z);
+    r.w = rowgroup_sum1(x.w);
+    return r;
 }
 
 template <bool BF16>

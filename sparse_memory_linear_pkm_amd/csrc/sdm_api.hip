@@ -57,8 +57,8 @@ sdm_status check_memory_dims(const sdm_dims *d)
         return fail(SDM_ERR_UNSUPPORTED, "d_v must be a multiple of 32 and <= %lld (got %lld)",
                     (long long)kMaxDv, (long long)d->d_v);
     const uint64_t row_bytes = (uint64_t)d->d_v * 4u;
-    if ((uint64_t)d->n_sub * (uint64_t)d->n_sub * row_bytes >= (1ull << 32))
-        return fail(SDM_ERR_UNSUPPORTED, "one (sequence, head) memory must be < 4 GiB");
+    if ((uint64_t)d->n_sub * (uint64_t)d->n_sub * row_bytes > (1ull << 31))
+        return fail(SDM_ERR_UNSUPPORTED, "one (sequence, head) memory must be <= 2 GiB");
     return SDM_OK;
 }
 

@@ -33,12 +33,32 @@ __global__ void __launch_bounds__(64) sdm_scan_serial_kernel(ScanArgs A)
     }
 }
 
-size_t scan_workspace_bytes(int64_t, int64_t, int64_t, int, int, int) { return 0; }
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-hipError_t launch_scan(const ScanArgs &A, bool bf16, void *, size_t, hipStream_t stream)
+// Workspace of the pipelined scan: forwarding codes [B,T,H,W+R] (uint16) and
+// per-token hazard flags [B,T,H] (uint32).  The serial kernel needs none.
+size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int)
+{
+    if (scan_pipe_depth(W, R) == 0) return 0;
+    const size_t rows = (size_t)(B * T * H);
+    return align256(rows * (size_t)(W + R) * 2) + align256(rows * 4);
+}
+
+hipError_t launch_scan(const ScanArgs &A, bool bf16, void *ws, size_t, hipStream_t stream)
 {
     const int64_t units = A.B * A.H * (A.d_v / 32);
     if (units == 0 || A.T == 0) return hipSuccess;
+    const int D = scan_pipe_depth(A.W, A.R);
+    if (D > 0) {
+        const size_t rows = (size_t)(A.B * A.T * A.H);
+        uint16_t *codes = static_cast<uint16_t *>(ws);
+        uint32_t *flags = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) +
+                                                       align256(rows * (size_t)(A.W + A.R) * 2));
+        HazardArgs hz{A.widx, A.ridx, codes, flags, A.B, A.T, A.H, A.W, A.R, D - 1};
+        hipError_t e = launch_scan_hazard(hz, stream);
+        if (e != hipSuccess) return e;
+        return launch_scan_pipe(A, bf16, codes, flags, stream);
+    }
     if (bf16)
         hipLaunchKernelGGL(sdm_scan_serial_kernel<true>, dim3((unsigned)units), dim3(64), 0, stream, A);
     else

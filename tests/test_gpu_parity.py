@@ -114,6 +114,10 @@ SCAN_CASES = {
     "ragged_lists": (Dims(B=3, T=77, H=1, d_k=128, n_sub=32, d_v=96, k_prime=8, W=5, R=3), 40),
     "W64_R1": (Dims(B=1, T=50, H=2, d_k=128, n_sub=64, d_v=32, k_prime=8, W=64, R=1), 500),
     "no_hazard_pool": (Dims(B=2, T=200, H=2, d_k=128, n_sub=256, d_v=64, k_prime=16, W=16, R=16), None),
+    "W8_R8_f32": (Dims(B=2, T=90, H=2, d_k=32, n_sub=16, d_v=64, k_prime=8, W=8, R=8, in_dtype="f32"), 60),
+    "W64_R64": (Dims(B=1, T=70, H=2, d_k=128, n_sub=64, d_v=64, k_prime=8, W=64, R=64), 400),
+    "W32_T1": (Dims(B=3, T=1, H=2, d_k=128, n_sub=64, d_v=128, k_prime=32, W=32, R=32), None),
+    "W32_T17_dv32": (Dims(B=2, T=17, H=1, d_k=128, n_sub=64, d_v=32, k_prime=32, W=32, R=32), 100),
 }
 
 
