@@ -10,54 +10,64 @@
 //     the slot, and the position j' of the slot in that token's write list.
 // code = delta * 64 + j'  (0xFFFF: none), and flag[u] = 1 if any code is present.
 // Slots are compared exactly (integers), so the codes are exact.
+//
+// One workgroup per (b, h, block of 32 tokens); one thread per (token,
+// position).  The write lists of the block and of the `window` tokens before
+// it sit in LDS; each thread scans the window from the farthest token to the
+// nearest, so the last match it records is the latest writer, with no
+// data-dependent loop exits.
 #include "kernels.h"
 #include "device_common.h"
 
 namespace sdm {
 
-constexpr int kHzBlock = 16;     // tokens per workgroup
+constexpr int kHzBlock = 32;     // tokens per workgroup
 constexpr int kHzMaxWin = 15;    // largest supported window
+constexpr int kHzThreads = 256;
 
-__global__ void __launch_bounds__(64) scan_hazard_kernel(HazardArgs A)
+__global__ void __launch_bounds__(kHzThreads) scan_hazard_kernel(HazardArgs A)
 {
-    __shared__ int32_t wl[(kHzBlock + kHzMaxWin) * 64];
-    const int lane = lane_id();
+    __shared__ int32_t wl[(kHzBlock + kHzMaxWin) * 64];   // write lists, row stride 64
+    __shared__ uint32_t anyhz[kHzBlock];
+    const int tid = threadIdx.x;
     const int nblk = (int)((A.T + kHzBlock - 1) / kHzBlock);
     const int64_t ch = blockIdx.x / nblk;
     const int64_t t0 = (int64_t)(blockIdx.x % nblk) * kHzBlock;
     const int bb = (int)(ch / A.H), h = (int)(ch % A.H);
-    const int W = A.W, R = A.R, win = A.window;
+    const int W = A.W, R = A.R, P = W + R, win = A.window;
     const int64_t tlo = t0 - win > 0 ? t0 - win : 0;
     const int64_t thi = t0 + kHzBlock < A.T ? t0 + kHzBlock : A.T;
-    // write lists of tokens [tlo, thi) into LDS, row i <-> token tlo + i
-    for (int64_t t = tlo; t < thi; ++t) {
+    const int nrows = (int)(thi - tlo);
+    for (int e = tid; e < nrows * W; e += kHzThreads) {
+        const int r = e / W, j = e - r * W;
+        const int64_t row = ((int64_t)bb * A.T + tlo + r) * A.H + h;
+        wl[r * 64 + j] = A.widx[row * W + j];
+    }
+    if (tid < kHzBlock) anyhz[tid] = 0;
+    __syncthreads();
+    const int ntok = (int)(thi - t0);
+    for (int e = tid; e < ntok * P; e += kHzThreads) {
+        const int tl = e / P, p = e - tl * P;
+        const int64_t t = t0 + tl;
         const int64_t row = ((int64_t)bb * A.T + t) * A.H + h;
-        if (lane < W) wl[(t - tlo) * 64 + lane] = A.widx[row * W + lane];
+        const int32_t slot = p < W ? wl[(t - tlo) * 64 + p] : A.ridx[row * R + (p - W)];
+        const int dmin = p < W ? 1 : 0;
+        int dmax = win;
+        if (t - dmax < 0) dmax = (int)t;
+        uint32_t code = 0xFFFFu;
+        for (int d = dmax; d >= dmin; --d) {
+            const int32_t *lst = wl + (t - d - tlo) * 64;
+            int jm = -1;
+            for (int j = 0; j < W; ++j) jm = lst[j] == slot ? j : jm;
+            code = jm >= 0 ? (uint32_t)(d * 64 + jm) : code;
+        }
+        A.codes[row * P + p] = (uint16_t)code;
+        if (code != 0xFFFFu) atomicOr(&anyhz[tl], 1u);
     }
     __syncthreads();
-    const int P = W + R;
-    for (int64_t t = t0; t < thi; ++t) {
-        const int64_t row = ((int64_t)bb * A.T + t) * A.H + h;
-        bool any = false;
-        for (int p = lane; p < P; p += kWave) {
-            const int32_t slot = p < W ? wl[(t - tlo) * 64 + p] : A.ridx[row * R + (p - W)];
-            uint32_t code = 0xFFFFu;
-            const int dmin = p < W ? 1 : 0;
-            for (int d = dmin; d <= win && code == 0xFFFFu; ++d) {
-                const int64_t ts = t - d;
-                if (ts < 0) break;
-                const int32_t *lst = wl + (ts - tlo) * 64;
-                for (int j = 0; j < W; ++j)
-                    if (lst[j] == slot) {
-                        code = (uint32_t)(d * 64 + j);
-                        break;
-                    }
-            }
-            A.codes[row * P + p] = (uint16_t)code;
-            any |= code != 0xFFFFu;
-        }
-        const bool f = __ballot(any) != 0;
-        if (lane == 0) A.flags[row] = f ? 1 : 0;
+    if (tid < ntok) {
+        const int64_t row = ((int64_t)bb * A.T + t0 + tid) * A.H + h;
+        A.flags[row] = anyhz[tid];
     }
 }
 
@@ -67,7 +77,7 @@ hipError_t launch_scan_hazard(const HazardArgs &A, hipStream_t stream)
     const int64_t nblk = (A.T + kHzBlock - 1) / kHzBlock;
     const int64_t grid = A.B * A.H * nblk;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(scan_hazard_kernel, dim3((unsigned)grid), dim3(64), 0, stream, A);
+    hipLaunchKernelGGL(scan_hazard_kernel, dim3((unsigned)grid), dim3(kHzThreads), 0, stream, A);
     return hipGetLastError();
 }
 
