@@ -30,16 +30,21 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h)
 }
 
 // Total order used by every selection: score descending, then index
-// ascending.  key = (monotone bits of score) << 32 | ~index, so a larger key
-// is a better candidate.  -0.0 is folded into +0.0 first so that the order
-// agrees with IEEE comparison (where the two are equal).  Finite scores map
-// to keys > 0; key 0 means "no candidate".
-__device__ __forceinline__ uint64_t score_key(float s, uint32_t idx)
+// ascending.  score_bits maps a float to an unsigned integer in the same
+// order (-0.0 is folded into +0.0 first, so that equal floats map to equal
+// bits), and key = score_bits << 32 | ~index, so a larger key is a better
+// candidate.  Finite scores have score_bits > 0, so key 0 means "no
+// candidate".
+__device__ __forceinline__ uint32_t score_bits(float s)
 {
     s = s + 0.0f;
-    uint32_t u = __float_as_uint(s);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint64_t)(~idx);
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t score_key(float s, uint32_t idx)
+{
+    return ((uint64_t)score_bits(s) << 32) | (uint64_t)(~idx);
 }
 
 __device__ __forceinline__ float key_score(uint64_t key)
@@ -51,14 +56,6 @@ __device__ __forceinline__ float key_score(uint64_t key)
 
 __device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m)
-{
-    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
-    lo = (uint32_t)__shfl_xor((int)lo, m, kWave);
-    hi = (uint32_t)__shfl_xor((int)hi, m, kWave);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l)
 {
     uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
@@ -66,114 +63,187 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l)
     return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x)
+__device__ __forceinline__ int mbcnt64(uint64_t mask)
 {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        uint64_t y = shfl_xor_u64(x, m);
-        x = y > x ? y : x;
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// LDS ordering among the lanes of one wave (no workgroup barrier needed).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Lane exchanges on the VALU (no LDS crossbar): x[lane ^ J] for J = 1..32.
+// DPP quad_perm for 1 and 2, row_shl:4 / row_shr:4 for 4, row_ror:8 for 8,
+// and the gfx950 v_permlane16_swap / v_permlane32_swap for 16 and 32.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x)
+{
+    static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "xor distance");
+    if constexpr (J == 1) {
+        return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    } else if constexpr (J == 4) {
+        const uint32_t up = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0xF, false);  // row_shl:4
+        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+        return (lane_id() & 4) ? dn : up;
+    } else if constexpr (J == 8) {
+        return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (J == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane_id() & 16) ? s[0] : s[1];
+    } else {
+        const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane_id() & 32) ? s[0] : s[1];
     }
-    return x;
 }
 
-__device__ __forceinline__ int wave_sum_i32(int x)
+template <int J>
+__device__ __forceinline__ uint64_t lane_xor(uint64_t x)
 {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
-    return x;
+    const uint32_t lo = lane_xor<J>((uint32_t)x), hi = lane_xor<J>((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
 }
 
+// Butterfly sum across the wave.  Every lane ends with the same value, and
+// the order of additions is fixed, so the result is deterministic.
 __device__ __forceinline__ float wave_sum_f32(float x)
 {
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
+    x += __uint_as_float(lane_xor<1>(__float_as_uint(x)));
+    x += __uint_as_float(lane_xor<2>(__float_as_uint(x)));
+    x += __uint_as_float(lane_xor<4>(__float_as_uint(x)));
+    x += __uint_as_float(lane_xor<8>(__float_as_uint(x)));
+    x += __uint_as_float(lane_xor<16>(__float_as_uint(x)));
+    x += __uint_as_float(lane_xor<32>(__float_as_uint(x)));
     return x;
 }
 
-// Exclusive prefix sum across the wave.
-__device__ __forceinline__ int wave_excl_prefix_i32(int x)
+template <class T>
+__device__ __forceinline__ T wave_max(T x)
 {
-    const int lane = lane_id();
-    int incl = x;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-        int y = __shfl_up(incl, m, kWave);
-        if (lane >= m) incl += y;
-    }
-    return incl - x;
+    T y;
+    y = lane_xor<1>(x);  x = y > x ? y : x;
+    y = lane_xor<2>(x);  x = y > x ? y : x;
+    y = lane_xor<4>(x);  x = y > x ? y : x;
+    y = lane_xor<8>(x);  x = y > x ? y : x;
+    y = lane_xor<16>(x); x = y > x ? y : x;
+    y = lane_xor<32>(x); x = y > x ? y : x;
+    return x;
 }
 
-// Bitonic sort of one key per lane, descending across lanes 0..63.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key)
+// Descending bitonic sort across the 64 lanes of NR independent values per
+// lane (NR sorts interleaved, so their dependency chains overlap).  One
+// compare-exchange stage: block size K, partner distance J.
+template <int K, int J, int NR, class T>
+__device__ __forceinline__ void bitonic_stage(T (&x)[NR])
 {
-    const int lane = lane_id();
+    if constexpr (J >= 1) {
+        const int lane = lane_id();
+        const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
 #pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t other = shfl_xor_u64(key, j);
-            const bool lower = (lane & j) == 0;
-            const bool desc_block = (lane & k) == 0;
-            const bool keep_max = (lower == desc_block);
-            const uint64_t mx = key > other ? key : other;
-            const uint64_t mn = key > other ? other : key;
-            key = keep_max ? mx : mn;
+        for (int r = 0; r < NR; ++r) {
+            const T other = lane_xor<J>(x[r]);
+            // equal values: taking either is the same
+            const bool take = (other > x[r]) == keep_max;
+            x[r] = take ? other : x[r];
         }
+        bitonic_stage<K, J / 2, NR>(x);
     }
-    return key;
 }
 
-// Exact top-n (n <= 64) of `len` candidates, one wave.  get(p) returns the key
-// of candidate p (p in [0, len)); keys are unique and > 0.  On return lane j
-// (j < n) holds the j-th best key, sorted descending; other lanes hold 0.
-// lds_scratch: 64 uint64 of per-wave LDS.
+template <int K, int NR, class T>
+__device__ __forceinline__ void bitonic_from(T (&x)[NR])
+{
+    if constexpr (K <= kWave) {
+        bitonic_stage<K, K / 2, NR>(x);
+        bitonic_from<K * 2, NR>(x);
+    }
+}
+
+template <int NR, class T>
+__device__ __forceinline__ void wave_sort_desc(T (&x)[NR])
+{
+    bitonic_from<2, NR>(x);
+}
+
+// Exact top-n (1 <= n <= 64, n <= len) of `len` candidates for each of NR
+// independent rows, one wave.  get(r, p) returns the key of candidate p of
+// row r (p in [0, len)); the keys of a row are distinct and > 0.  On return
+// lane j < n of res[r] holds the j-th best key of row r (descending); the
+// other lanes hold 0.  scratch: NR * 64 uint64 of this wave's LDS.
 //
-// Method: the n-th largest of the 64 per-lane maxima is a lower bound tau
-// with at least n candidates >= tau; the candidates >= tau are compacted and
-// sorted when they fit in one wave, otherwise the n best are extracted one by
-// one (exact in both cases).
-template <class Get>
-__device__ __forceinline__ uint64_t wave_topn(int len, int n, Get get, uint64_t *lds_scratch)
+// Per row: tau = the n-th largest per-lane maximum score (compared on the
+// score bits only) bounds the answer from below, since at least n candidates
+// (one per lane above it) reach it.  The candidates whose score reaches tau
+// are compacted with ballots and sorted as 64-bit keys.  When more than 64
+// reach tau (ties, or n close to 64), that row is instead extracted one best
+// key at a time, which is exact as well.
+template <int NR, class Get>
+__device__ __forceinline__ void wave_topn(int len, int n, Get get, uint64_t *scratch,
+                                          uint64_t (&res)[NR])
 {
     const int lane = lane_id();
-    uint64_t lmax = 0;
+    uint32_t m[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) m[r] = 0;
     for (int p = lane; p < len; p += kWave) {
-        uint64_t k = get(p);
-        lmax = k > lmax ? k : lmax;
-    }
-    const uint64_t sorted_max = wave_sort_desc(lmax);
-    const uint64_t tau = readlane_u64(sorted_max, n - 1);
-    int cnt = 0;
-    for (int p = lane; p < len; p += kWave) cnt += get(p) >= tau ? 1 : 0;
-    const int total = wave_sum_i32(cnt);
-    uint64_t result = 0;
-    if (total <= kWave) {
-        int pos = wave_excl_prefix_i32(cnt);
-        for (int p = lane; p < len; p += kWave) {
-            uint64_t k = get(p);
-            if (k >= tau) lds_scratch[pos++] = k;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const uint32_t hi = (uint32_t)(get(r, p) >> 32);
+            m[r] = hi > m[r] ? hi : m[r];
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint64_t mine = lane < total ? lds_scratch[lane] : 0;
-        __builtin_amdgcn_wave_barrier();
-        result = wave_sort_desc(mine);
-        if (lane >= n) result = 0;
-    } else {
-        uint64_t prev = ~0ull;
-        for (int j = 0; j < n; ++j) {
-            uint64_t best = 0;
-            for (int p = lane; p < len; p += kWave) {
-                uint64_t k = get(p);
-                if (k < prev && k > best) best = k;
+    }
+    wave_sort_desc<NR>(m);
+    uint32_t tau[NR];
+    int total[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        tau[r] = (uint32_t)__builtin_amdgcn_readlane((int)m[r], n - 1);
+        total[r] = 0;
+    }
+    const int iters = (len + kWave - 1) / kWave;
+    for (int i = 0; i < iters; ++i) {
+        const int p = lane + i * kWave;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const uint64_t k = p < len ? get(r, p) : 0ull;
+            const bool f = (uint32_t)(k >> 32) >= tau[r];   // tau > 0, so k != 0
+            const uint64_t ball = __ballot(f);
+            const int pos = total[r] + mbcnt64(ball);
+            if (f && pos < kWave) scratch[r * kWave + pos] = k;
+            total[r] += __popcll(ball);
+        }
+    }
+    wave_lds_sync();
+    uint64_t c[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) c[r] = lane < total[r] ? scratch[r * kWave + lane] : 0ull;
+    __builtin_amdgcn_wave_barrier();
+    wave_sort_desc<NR>(c);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        res[r] = lane < n ? c[r] : 0ull;
+        if (total[r] > kWave) {
+            uint64_t prev = ~0ull, out = 0;
+            for (int j = 0; j < n; ++j) {
+                uint64_t best = 0;
+                for (int p = lane; p < len; p += kWave) {
+                    const uint64_t k = get(r, p);
+                    best = (k < prev && k > best) ? k : best;
+                }
+                best = wave_max(best);
+                out = lane == j ? best : out;
+                prev = best;
             }
-            best = wave_max_u64(best);
-            if (lane == j) result = best;
-            prev = best;
+            res[r] = out;
         }
     }
-    return result;
 }
 
 }  // namespace sdm

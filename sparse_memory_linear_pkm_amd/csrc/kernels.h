@@ -61,7 +61,7 @@ struct InitArgs {
 };
 
 hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream);
-size_t address_smem_bytes(int n_sub);
+size_t address_smem_bytes(int n_sub, int k_prime);
 hipError_t launch_scan(const ScanArgs &args, bool bf16, void *workspace, size_t ws_bytes,
                        hipStream_t stream);
 size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int d_v);
@@ -70,7 +70,7 @@ int scan_pipe_depth(int W, int R);
 hipError_t launch_scan_pipe(const ScanArgs &args, bool bf16, const uint16_t *codes, const uint32_t *flags,
                             hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, bool bf16, hipStream_t stream);
-size_t decode_smem_bytes(int n_sub);
+size_t decode_smem_bytes(int n_sub, int k_prime);
 hipError_t launch_state_init(const InitArgs &args, hipStream_t stream);
 
 }  // namespace sdm

@@ -8,26 +8,28 @@
 // Sec. 4 (SDM Configuration): the selected scores are softmax-normalised.
 //
 // Used by the prefill addressing kernel and by the fused decode kernel, so
-// both select bit-identical slots from identical scores.
+// both select bit-identical slots and weights from identical scores.
 #pragma once
 
 #include "device_common.h"
 
 namespace sdm {
 
-constexpr int kTileRows = 16;  // token rows scored together (MFMA M dimension)
+constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimension)
+constexpr int kMaxStair = 288;    // >= max over k', n <= 64 of the staircase size (280)
 
 // fp32 half scores S[r][u] = <x_r[c*half : (c+1)*half], C[h][c][u]> for the
-// rows r < nrows of one tile, written to LDS (row stride n_sub).  bf16 inputs
-// use the gfx950 MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation (rows
-// >= nrows enter the MFMA as zero vectors and are not stored); every output
-// element depends only on its own row, so a row's scores do not depend on
-// which other rows share the tile.  All threads of the block take part; the caller
-// synchronises before reading S.
+// first `srows` rows of one 16-row tile, written to LDS (row stride n_sub).
+// Rows >= nrows are scored as zero vectors (so stored rows past the real ones
+// hold zeros).  bf16 inputs use the gfx950 MFMA v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation; every output element depends only on its own row, so a
+// row's scores do not depend on which other rows share the tile.  All threads
+// of the block take part; the caller synchronises before reading S.
 //   x: base of the tile's first row; consecutive tile rows are row_stride
 //      elements apart.
 template <bool BF16>
 __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_stride, int nrows,
+                                                int srows,
                                                 const void *Cc /* [n_sub, half] of (h, c) */,
                                                 int c, int half, int n_sub, float *S)
 {
@@ -41,77 +43,150 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
         const int kg = lane >> 4;         // which 8-wide k group of the 32
         const uint16_t *xr = static_cast<const uint16_t *>(x) + (int64_t)r * row_stride + c * half;
         const uint16_t *C16 = static_cast<const uint16_t *>(Cc);
-        const int nk = half / 32;
+        const int nk = half / 32;         // <= 8 (d_k <= 512)
+        bf16x8 av[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            av[kk] = (bf16x8){};
+            if (kk < nk && r < nrows) av[kk] = *reinterpret_cast<const bf16x8 *>(xr + kk * 32 + kg * 8);
+        }
         for (int st = wave; st * 16 < n_sub; st += nwaves) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             const int u = st * 16 + r;    // sub-key (B column) of this lane
             const uint16_t *cr = C16 + (int64_t)u * half;
-            for (int kk = 0; kk < nk; ++kk) {
-                bf16x8 av = (bf16x8){}, bv = (bf16x8){};
-                if (r < nrows) av = *reinterpret_cast<const bf16x8 *>(xr + kk * 32 + kg * 8);
-                if (u < n_sub) bv = *reinterpret_cast<const bf16x8 *>(cr + kk * 32 + kg * 8);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                if (kk < nk) {
+                    bf16x8 bv = (bf16x8){};
+                    if (u < n_sub) bv = *reinterpret_cast<const bf16x8 *>(cr + kk * 32 + kg * 8);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], bv, acc, 0, 0, 0);
+                }
             }
             // D[i][j]: lane holds column j = lane & 15 (sub-key), rows 4*(lane>>4) + e
             if (u < n_sub) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = 4 * kg + e;
-                    if (row < nrows) S[row * n_sub + u] = acc[e];
+                    if (row < srows) S[row * n_sub + u] = acc[e];
                 }
             }
         }
     } else {
         const float *xf = static_cast<const float *>(x);
         const float *Cf = static_cast<const float *>(Cc);
-        for (int e = tid; e < nrows * n_sub; e += nthreads) {
+        for (int e = tid; e < srows * n_sub; e += nthreads) {
             const int row = e / n_sub, u = e - row * n_sub;
-            const float *xr = xf + (int64_t)row * row_stride + c * half;
-            const float *cr = Cf + (int64_t)u * half;
             float acc = 0.f;
-            for (int d = 0; d < half; ++d) acc = __builtin_fmaf(xr[d], cr[d], acc);
+            if (row < nrows) {
+                const float *xr = xf + (int64_t)row * row_stride + c * half;
+                const float *cr = Cf + (int64_t)u * half;
+                for (int d = 0; d < half; ++d) acc = __builtin_fmaf(xr[d], cr[d], acc);
+            }
             S[e] = acc;
         }
     }
 }
 
-// Top-k' of one row of half scores (n_sub values in LDS) by one wave.
-// Lane j < k' receives the key of the j-th best sub-key.
-__device__ __forceinline__ uint64_t half_topk(const float *Srow, int n_sub, int kp, uint64_t *scratch)
+// An entry of a selected half list: the raw fp32 score bits and the sub-key.
+struct HalfEntry {
+    uint32_t score;
+    uint32_t index;
+};
+
+// The staircase of the k' x k' merge: pairs (a, b) of half-list ranks with
+// (a + 1)(b + 1) <= n.  Each of the (a + 1)(b + 1) pairs (a' <= a, b' <= b)
+// scores at least as high as (a, b) (fp32 addition is monotone), so outside
+// ties the top n lie inside it.  Entries (a << 8 | b) grouped by a; the
+// count (>= n for every k', n <= 64) is returned in every thread.  Called
+// by all threads of the block (a = the thread's index in it); the caller
+// synchronises before use.
+__device__ __forceinline__ int build_staircase(int kp, int n, uint16_t *stair, int a)
 {
-    return wave_topn(n_sub, kp,
-                     [&](int p) { return score_key(Srow[p], (uint32_t)p); }, scratch);
+    int total = 0, off = 0;
+    for (int i = 0; i < kp; ++i) {
+        const int cnt = min(kp, n / (i + 1));
+        if (i < a) off += cnt;
+        total += cnt;
+    }
+    if (a < kp) {
+        const int cnt = min(kp, n / (a + 1));
+        for (int b = 0; b < cnt; ++b) stair[off + b] = (uint16_t)((a << 8) | b);
+    }
+    return total;
 }
 
-// Merge of two per-half lists (keys in lane j < kp, sorted) into the top-n
-// slots, then softmax weights.  lists: per-wave LDS of 2*64 uint64.
-// Lane j < n ends with (slot_j, weight_j).
-__device__ __forceinline__ void merge_softmax(uint64_t k0, uint64_t k1, int kp, int n_sub, int n,
-                                              uint64_t *lists, uint64_t *scratch, int &slot,
-                                              float &weight)
+// Top-k' of NR rows of half scores, one wave.  Row r's n_sub scores are at
+// S + rows[r] * n_sub; lane j < k' of keys[r] receives the j-th best
+// (score desc, sub-key asc).
+template <int NR>
+__device__ __forceinline__ void half_topk(const float *S, const int (&rows)[NR], int n_sub, int kp,
+                                          uint64_t *scratch, uint64_t (&keys)[NR])
+{
+    wave_topn<NR>(n_sub, kp,
+                  [&](int r, int p) { return score_key(S[rows[r] * n_sub + p], (uint32_t)p); },
+                  scratch, keys);
+}
+
+// Merge of the two half lists of NR rows into the top-n slots and their
+// softmax weights, one wave.  L0[r], L1[r]: the k' entries of row r's half 0
+// and half 1 lists, best first.  The slot of pair (a, b) is
+// L0[a].index * n_sub + L1[b].index and its score the fp32 sum of the two
+// half scores.
+//
+// The top n are taken over the staircase first.  The result is exact when
+// the n-th score found is strictly above every pair just outside the
+// staircase, (a, floor(n / (a + 1))) for each a, which bound all pairs
+// outside it; otherwise (a tie at the border) that row is redone over all
+// k'^2 pairs.  Lane j < n ends with slot[r] and wt[r] of the j-th best.
+template <int NR>
+__device__ __forceinline__ void merge_softmax(const HalfEntry *const (&L0)[NR],
+                                              const HalfEntry *const (&L1)[NR], int kp, int n_sub,
+                                              int n, const uint16_t *stair, int nstair,
+                                              uint64_t *scratch, int (&slot)[NR], float (&wt)[NR])
 {
     const int lane = lane_id();
-    lists[lane] = k0;
-    lists[kWave + lane] = k1;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint64_t *l0 = lists, *l1 = lists + kWave;
-    auto get = [&](int p) {
-        const int ia = p / kp, ib = p - ia * kp;
-        const uint64_t ka = l0[ia], kb = l1[ib];
-        const float s = key_score(ka) + key_score(kb);
-        const uint32_t idx = key_index(ka) * (uint32_t)n_sub + key_index(kb);
-        return score_key(s, idx);
+    auto pair_key = [&](int r, int a, int b) {
+        const HalfEntry e0 = L0[r][a], e1 = L1[r][b];
+        const float s = __uint_as_float(e0.score) + __uint_as_float(e1.score);
+        return score_key(s, e0.index * (uint32_t)n_sub + e1.index);
     };
-    const uint64_t best = wave_topn(kp * kp, n, get, scratch);
-    const float s = key_score(best);
-    const float smax = __shfl(s, 0, kWave);
-    const float e = lane < n ? expf(s - smax) : 0.f;
-    const float z = wave_sum_f32(e);
-    weight = e / z;
-    slot = (int)key_index(best);
-    __builtin_amdgcn_wave_barrier();
+    uint64_t best[NR];
+    wave_topn<NR>(nstair, n,
+                  [&](int r, int p) {
+                      const uint32_t ab = stair[p];
+                      return pair_key(r, (int)(ab >> 8), (int)(ab & 0xff));
+                  },
+                  scratch, best);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        uint32_t fb = 0;
+        const int b0 = n / (lane + 1);
+        if (lane < kp && b0 < kp) {
+            const float s = __uint_as_float(L0[r][lane].score) + __uint_as_float(L1[r][b0].score);
+            fb = score_bits(s);
+        }
+        fb = wave_max(fb);
+        const uint32_t nth = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(best[r] >> 32), n - 1);
+        if (!(nth > fb)) {
+            uint64_t one[1];
+            wave_topn<1>(kp * kp, n,
+                         [&](int, int p) {
+                             const int a = p / kp;
+                             return pair_key(r, a, p - a * kp);
+                         },
+                         scratch, one);
+            best[r] = one[0];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const float s = key_score(best[r]);
+        const float smax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(s), 0));
+        const float e = lane < n ? expf(s - smax) : 0.f;
+        const float z = wave_sum_f32(e);
+        wt[r] = e / z;
+        slot[r] = (int)key_index(best[r]);
+    }
 }
 
 }  // namespace sdm

@@ -16,6 +16,24 @@
 
 namespace sdm {
 
+struct DecodeLds {
+    // byte offsets into dynamic LDS
+    size_t S, L, scratch, stair, fidx, fwt, total;
+};
+
+__host__ __device__ inline DecodeLds decode_lds_layout(int n_sub, int kp)
+{
+    DecodeLds o;
+    o.S = 0;                                                      // float [4][n_sub]
+    o.L = o.S + sizeof(float) * 4 * (size_t)n_sub;                // HalfEntry [4][kp]
+    o.scratch = o.L + sizeof(HalfEntry) * 4 * (size_t)kp;         // u64 [4][64]
+    o.stair = o.scratch + sizeof(uint64_t) * 4 * kWave;           // u16 [2][kMaxStair]
+    o.fidx = o.stair + sizeof(uint16_t) * 2 * kMaxStair;          // int32 [2][64]
+    o.fwt = o.fidx + sizeof(int32_t) * 2 * kWave;                 // float [2][64]
+    o.total = o.fwt + sizeof(float) * 2 * kWave;
+    return o;
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
 {
@@ -27,11 +45,13 @@ __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
     const int n_sub = A.n_sub, half = A.d_k / 2, kp = A.k_prime;
     const size_t esz = BF16 ? 2 : 4;
 
-    float *S = reinterpret_cast<float *>(smem);                          // [4][n_sub]
-    uint64_t *lists = reinterpret_cast<uint64_t *>(S + 4 * n_sub);       // [4][64]
-    uint64_t *wscr = lists + 4 * kWave + wave * (3 * kWave);             // per wave
-    int32_t *fidx = reinterpret_cast<int32_t *>(lists + 4 * kWave + 4 * 3 * kWave);  // [2][64]
-    float *fwt = reinterpret_cast<float *>(fidx + 2 * kWave);                          // [2][64]
+    const DecodeLds lay = decode_lds_layout(n_sub, kp);
+    float *S = reinterpret_cast<float *>(smem + lay.S);                 // [4][n_sub]
+    HalfEntry *L = reinterpret_cast<HalfEntry *>(smem + lay.L);         // [4][kp]
+    uint64_t *wscr = reinterpret_cast<uint64_t *>(smem + lay.scratch) + wave * kWave;
+    uint16_t *stair = reinterpret_cast<uint16_t *>(smem + lay.stair);   // [2][kMaxStair]
+    int32_t *fidx = reinterpret_cast<int32_t *>(smem + lay.fidx);       // [2][64]
+    float *fwt = reinterpret_cast<float *>(smem + lay.fwt);             // [2][64]
 
     // A. scores (row 0 of a 16-row tile is this token; the others are zero)
 #pragma unroll
@@ -42,25 +62,39 @@ __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
         const unsigned char *Cb = static_cast<const unsigned char *>(C) +
                                   (size_t)h * 2 * n_sub * half * esz;
         for (int c = 0; c < 2; ++c)
-            score_half_tile<BF16>(xb, A.d_k, 1, Cb + (size_t)c * n_sub * half * esz, c, half, n_sub,
-                                  S + (kind * 2 + c) * n_sub);
+            score_half_tile<BF16>(xb, A.d_k, 1, 1, Cb + (size_t)c * n_sub * half * esz, c, half,
+                                  n_sub, S + (kind * 2 + c) * n_sub);
     }
+    const int nstair_w = build_staircase(kp, (int)A.W, stair, threadIdx.x);
+    const int nstair_r = build_staircase(kp, (int)A.R, stair + kMaxStair, threadIdx.x);
     __syncthreads();
-    // B. per-half top-k'
-    lists[wave * kWave + lane] = half_topk(S + wave * n_sub, n_sub, kp, wscr);
+    // B. per-half top-k': wave w takes list w (kind w / 2, half w % 2)
+    {
+        const int rows[1] = {wave};
+        uint64_t key[1];
+        half_topk<1>(S, rows, n_sub, kp, wscr, key);
+        if (lane < kp) {
+            HalfEntry e;
+            e.score = __float_as_uint(key_score(key[0]));
+            e.index = key_index(key[0]);
+            L[wave * kp + lane] = e;
+        }
+    }
     __syncthreads();
     // C. merge + softmax
     if (wave < 2) {
         const int kind = wave;
-        const int n = kind ? A.R : A.W;
-        int slot;
-        float wt;
-        merge_softmax(lists[(kind * 2) * kWave + lane], lists[(kind * 2 + 1) * kWave + lane], kp,
-                      n_sub, n, wscr + kWave, wscr, slot, wt);
-        fidx[kind * kWave + lane] = slot;
-        fwt[kind * kWave + lane] = wt;
+        const int n = kind ? (int)A.R : (int)A.W;
+        const HalfEntry *const L0[1] = {L + (kind * 2) * kp};
+        const HalfEntry *const L1[1] = {L + (kind * 2 + 1) * kp};
+        int slot[1];
+        float wt[1];
+        merge_softmax<1>(L0, L1, kp, n_sub, n, stair + kind * kMaxStair, kind ? nstair_r : nstair_w,
+                         wscr, slot, wt);
+        fidx[kind * kWave + lane] = slot[0];
+        fwt[kind * kWave + lane] = wt[0];
         int32_t *out = kind ? A.ridx_out : A.widx_out;
-        if (out && lane < n) out[(size_t)bh * n + lane] = slot;
+        if (out && lane < n) out[(size_t)bh * n + lane] = slot[0];
     }
     __syncthreads();
     // D. the write and the read, one wave per 32-column slice
@@ -75,17 +109,13 @@ __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
     }
 }
 
-size_t decode_smem_bytes(int n_sub)
-{
-    return sizeof(float) * 4 * (size_t)n_sub + sizeof(uint64_t) * (4 * kWave + 12 * kWave) +
-           sizeof(int32_t) * 2 * kWave + sizeof(float) * 2 * kWave;
-}
+size_t decode_smem_bytes(int n_sub, int k_prime) { return decode_lds_layout(n_sub, k_prime).total; }
 
 hipError_t launch_decode(const DecodeArgs &A, bool bf16, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)A.B * A.H;
     if (blocks == 0) return hipSuccess;
-    const size_t smem = decode_smem_bytes(A.n_sub);
+    const size_t smem = decode_smem_bytes(A.n_sub, A.k_prime);
     if (bf16) {
         hipError_t e = hipFuncSetAttribute((const void *)sdm_decode_kernel<true>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
