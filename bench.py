@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 
 PREFILL_WORKLOADS = ("tiny", "small", "prefill_1p4b", "long_context")
-KERNEL_SOURCES = ("sdm_scan.hip", "sdm_scan_pipe.hip", "scan_hazard.hip", "scan_step.h", "device_common.h",
+KERNEL_SOURCES = ("sdm_scan.hip", "sdm_scan_lanes.hip", "scan_prep.hip", "scan_lanes.h", "device_common.h",
                   "kernels.h")
 
 
@@ -282,7 +282,7 @@ def main():
         scan_s = avg["sdm_scan_forward"] * 1e-3
         achieved = scan_bytes / scan_s / 1e9
         traffic = measured_traffic(name)
-        result["roofline"] = {"kernel": "sdm_scan_forward (scan_hazard_kernel + sdm_scan_pipe_kernel)",
+        result["roofline"] = {"kernel": "sdm_scan_forward (scan_prep_kernel + sdm_scan_lanes_kernel)",
                               "bound": "hbm", "achieved": achieved,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                               "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,

@@ -69,12 +69,16 @@ __device__ __forceinline__ int mbcnt64(uint64_t mask)
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// LDS ordering among the lanes of one wave (no workgroup barrier needed).
+// Orders LDS accesses among the lanes of one wave (a write by one lane, then
+// a read of it by another).  The LDS executes one wave's instructions in
+// issue order, so only the compiler must be kept from reordering; a memory
+// fence here would also make the compiler wait for outstanding loads that
+// target LDS directly (buffer_load ... lds), which never alias these arrays.
 __device__ __forceinline__ void wave_lds_sync()
 {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------

@@ -35,13 +35,24 @@ struct ScanArgs {
     int H, N, d_v, W, R;
 };
 
-struct HazardArgs {
-    const int32_t *widx;
-    const int32_t *ridx;
-    uint16_t *codes;   // [B,T,H,W+R]
-    uint32_t *flags;   // [B,T,H]
+
+// The per-(sequence, head) streams the lane-parallel scan reads (written by
+// the preparation pass, scan_prep.hip).  Streams are ordered [chain][token]
+// with chain = b * H + h, so one chain's records are contiguous.
+struct ScanStreams {
+    uint4 *lane;        // [chain][t][Q]: {~codes, w_j, r_j, b_t * w_j}
+    uint2 *gofs;        // [chain][t][Q]: biased byte offsets of write / read row j
+    uint4 *tok;         // [chain][t][d_v / 4]: {a_t, v chunk (bf16: 2 words, 0) | (f32: 0,0,0 + 4 words)}
+};
+
+struct PrepArgs {
+    const int32_t *widx, *ridx;
+    const float *wwt, *rwt, *a, *b;
+    const void *v;
+    ScanStreams st;
     int64_t B, T, H;
-    int W, R, window;
+    int W, R, Q, K, window, hash_log2, d_v, bf16;   // K = tokens per scan step
+    int lookahead;   // D * K - 1: superseded writes are looked for up to the end of step + D - 1
 };
 
 struct DecodeArgs {
@@ -64,11 +75,12 @@ hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t st
 size_t address_smem_bytes(int n_sub, int k_prime);
 hipError_t launch_scan(const ScanArgs &args, bool bf16, void *workspace, size_t ws_bytes,
                        hipStream_t stream);
-size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int d_v);
-hipError_t launch_scan_hazard(const HazardArgs &args, hipStream_t stream);
-int scan_pipe_depth(int W, int R);
-hipError_t launch_scan_pipe(const ScanArgs &args, bool bf16, const uint16_t *codes, const uint32_t *flags,
-                            hipStream_t stream);
+size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int d_v, bool bf16);
+bool scan_chain_fits(int64_t T, int W, int R, int d_v, bool bf16);
+hipError_t launch_scan_prep(const PrepArgs &args, hipStream_t stream);
+int scan_prep_hash_log2(int W, int window, int lookahead);
+hipError_t launch_scan_lanes(const ScanArgs &args, bool bf16, const ScanStreams &st, int Q, int D,
+                             hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, bool bf16, hipStream_t stream);
 size_t decode_smem_bytes(int n_sub, int k_prime);
 hipError_t launch_state_init(const InitArgs &args, hipStream_t stream);

@@ -154,8 +154,11 @@ sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const 
 
 size_t sdm_scan_workspace_size(const sdm_dims *d)
 {
-    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->W < 1 || d->R < 1 || d->d_v < 1) return 0;
-    return sdm::scan_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v);
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->W < 1 || d->R < 1 || d->d_v < 1 || d->W > kMaxList ||
+        d->R > kMaxList)
+        return 0;
+    return sdm::scan_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v,
+                                     d->in_dtype == SDM_BF16);
 }
 
 sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
@@ -191,9 +194,22 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
     if (overlap(M, msz, widx, 4 * rows * d->W) || overlap(M, msz, ridx, 4 * rows * d->R) ||
         overlap(M, msz, wwt, 4 * rows * d->W) || overlap(M, msz, rwt, 4 * rows * d->R))
         return fail(SDM_ERR_INVALID_ARG, "M overlaps a slot list or weight array");
-    const size_t need = sdm::scan_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v);
+    if (!sdm::scan_chain_fits(d->T, (int)d->W, (int)d->R, (int)d->d_v, d->in_dtype == SDM_BF16))
+        return fail(SDM_ERR_UNSUPPORTED, "T too large: one (sequence, head) stream of the scan must stay below 2 GiB");
+    const size_t need = sdm::scan_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v,
+                                                  d->in_dtype == SDM_BF16);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(SDM_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    if (need > 0 && !aligned(workspace, 16)) return fail(SDM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    {
+        const size_t vsz = (size_t)(rows * d->d_v) * (d->in_dtype == SDM_BF16 ? 2 : 4);
+        if (overlap(workspace, need, M, msz) || overlap(workspace, need, o, osz) ||
+            overlap(workspace, need, v, vsz) || overlap(workspace, need, widx, 4 * rows * d->W) ||
+            overlap(workspace, need, ridx, 4 * rows * d->R) || overlap(workspace, need, wwt, 4 * rows * d->W) ||
+            overlap(workspace, need, rwt, 4 * rows * d->R) || overlap(workspace, need, a, 4 * rows) ||
+            overlap(workspace, need, b, 4 * rows))
+            return fail(SDM_ERR_INVALID_ARG, "workspace overlaps an input or output");
+    }
     if (rows == 0) return SDM_OK;
     sdm::ScanArgs A{M, widx, wwt, ridx, rwt, v, a, b, o, d->B, d->T, (int)d->H, (int)N, (int)d->d_v,
                     (int)d->W, (int)d->R};

@@ -9,10 +9,14 @@
 //      the selected slots, are bit-identical to a prefill of the same token);
 //   B. wave w selects the top-k' of list w;
 //   C. waves 0 and 1 merge and softmax the write and read lists;
-//   D. one wave per 32-column slice applies the write and the read.
+//   D. the write and the read in the lane layout of the prefill scan (lane
+//      (i, j) of a wave: column chunk i of the pass, write row j and read row
+//      j), with the same arithmetic, so a decode step reproduces the prefill
+//      scan of the same token bit for bit.  The read rows are loaded after
+//      the stores of the write (same wave, so they see the new rows).
 #include "kernels.h"
 #include "pkm_address.h"
-#include "scan_step.h"
+#include "scan_lanes.h"
 
 namespace sdm {
 
@@ -34,7 +38,7 @@ __host__ __device__ inline DecodeLds decode_lds_layout(int n_sub, int kp)
     return o;
 }
 
-template <bool BF16>
+template <int Q, bool BF16>
 __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -97,37 +101,74 @@ __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
         if (out && lane < n) out[(size_t)bh * n + lane] = slot[0];
     }
     __syncthreads();
-    // D. the write and the read, one wave per 32-column slice
+    // D. the write and the read
+    constexpr int K = kWave / Q;
+    constexpr uint32_t kOOB = 0x80000000u;
+    constexpr uint32_t vbytes = BF16 ? 8u : 16u;   // one 4-column chunk of v
+    const int i = lane / Q, j = lane % Q;
+    const uint32_t d_v = (uint32_t)A.d_v;
+    const int nchunk = A.d_v / 4;
     const __amdgpu_buffer_rsrc_t Mrs =
-        make_rsrc(A.M + (size_t)bh * A.N * A.d_v, (uint32_t)((uint64_t)A.N * A.d_v * 4u));
-    const unsigned char *vrow = static_cast<const unsigned char *>(A.v) + (size_t)bh * A.d_v * esz;
+        make_rsrc(A.M + (size_t)bh * A.N * d_v, (uint32_t)((uint64_t)A.N * d_v * 4u));
+    const __amdgpu_buffer_rsrc_t Vrs =
+        make_rsrc(static_cast<const unsigned char *>(A.v) + (size_t)bh * d_v * esz, d_v * (uint32_t)esz);
+    const __amdgpu_buffer_rsrc_t Ors = make_rsrc(A.o + (size_t)bh * d_v, d_v * 4u);
     const float at = A.a[bh], bt = A.b[bh];
-    for (int slice = wave; slice * 32 < A.d_v; slice += 4) {
-        const int col = slice * 32 + 4 * (lane & 7);
-        scan_token_slice<BF16>(Mrs, A.d_v, col, fidx, fwt, A.W, fidx + kWave, fwt + kWave, A.R,
-                               vrow, at, bt, A.o + (size_t)bh * A.d_v);
+    const float wj = j < A.W ? fwt[j] : 0.f;
+    const float rj = j < A.R ? fwt[kWave + j] : 0.f;
+    for (int c0 = wave * K; c0 < nchunk; c0 += 4 * K) {
+        const int chunk = c0 + i;
+        const bool live = chunk < nchunk;
+        const uint32_t col4 = (uint32_t)chunk * 16u;
+        const uint32_t offw = (live && j < A.W) ? (uint32_t)fidx[j] * d_v * 4u + col4 : kOOB;
+        const uint32_t offr = (live && j < A.R) ? (uint32_t)fidx[kWave + j] * d_v * 4u + col4 : kOOB;
+        const f32x4 xw = __builtin_amdgcn_raw_buffer_load_b128(Mrs, offw, 0, 0);
+        f32x4 v4;
+        if constexpr (BF16) {
+            const auto raw = __builtin_amdgcn_raw_buffer_load_b64(Vrs, live ? (uint32_t)chunk * vbytes : kOOB, 0, 0);
+            v4 = v_chunk((uint2){raw[0], raw[1]});
+        } else {
+            v4 = __builtin_amdgcn_raw_buffer_load_b128(Vrs, live ? (uint32_t)chunk * vbytes : kOOB, 0, 0);
+        }
+        const f32x4 p = weighted_rows<Q>(wj, xw);
+        const f32x4 nm = written_row(xw, at, bt * wj, v4, p);
+        __builtin_amdgcn_raw_buffer_store_b128(nm, Mrs, offw, 0, 0);
+        const f32x4 xr = __builtin_amdgcn_raw_buffer_load_b128(Mrs, offr, 0, 0);
+        const f32x4 o = weighted_rows<Q>(rj, xr);
+        __builtin_amdgcn_raw_buffer_store_b128(o, Ors, (live && j == 0) ? col4 : kOOB, 0, 0);
     }
 }
 
 size_t decode_smem_bytes(int n_sub, int k_prime) { return decode_lds_layout(n_sub, k_prime).total; }
 
-hipError_t launch_decode(const DecodeArgs &A, bool bf16, hipStream_t stream)
+template <int Q>
+static hipError_t launch_decode_q(const DecodeArgs &A, bool bf16, hipStream_t stream)
 {
     const int64_t blocks = (int64_t)A.B * A.H;
-    if (blocks == 0) return hipSuccess;
     const size_t smem = decode_smem_bytes(A.n_sub, A.k_prime);
-    if (bf16) {
-        hipError_t e = hipFuncSetAttribute((const void *)sdm_decode_kernel<true>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(sdm_decode_kernel<true>, dim3((unsigned)blocks), dim3(256), smem, stream, A);
-    } else {
-        hipError_t e = hipFuncSetAttribute((const void *)sdm_decode_kernel<false>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(sdm_decode_kernel<false>, dim3((unsigned)blocks), dim3(256), smem, stream, A);
-    }
+    const void *fn = bf16 ? (const void *)sdm_decode_kernel<Q, true> : (const void *)sdm_decode_kernel<Q, false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    if (bf16)
+        hipLaunchKernelGGL((sdm_decode_kernel<Q, true>), dim3((unsigned)blocks), dim3(256), smem, stream, A);
+    else
+        hipLaunchKernelGGL((sdm_decode_kernel<Q, false>), dim3((unsigned)blocks), dim3(256), smem, stream, A);
     return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &A, bool bf16, hipStream_t stream)
+{
+    if ((int64_t)A.B * A.H == 0) return hipSuccess;
+    int q = 4;   // the lane group of the prefill scan: power of two >= W, R
+    while (q < A.W || q < A.R) q *= 2;
+    switch (q) {
+    case 4: return launch_decode_q<4>(A, bf16, stream);
+    case 8: return launch_decode_q<8>(A, bf16, stream);
+    case 16: return launch_decode_q<16>(A, bf16, stream);
+    case 32: return launch_decode_q<32>(A, bf16, stream);
+    case 64: return launch_decode_q<64>(A, bf16, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace sdm

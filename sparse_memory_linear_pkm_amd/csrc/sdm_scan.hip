@@ -3,67 +3,83 @@
 // memory.  "Sparse Delta Memory: Scaling the State of Linear RNNs through
 // Sparsity", Sec. 3.1 steps 2-3 (Eq. 4).
 //
-// Work unit: one wave per (b, h, 32-column slice).  Columns never interact,
-// so the d_v/32 slices of one memory are independent recurrences over the
-// same slot lists; each wave walks its tokens in order.
+// Two launches on the caller's stream: the preparation pass (scan_prep.hip:
+// forwarding codes and the repacked per-chain input streams) and the
+// lane-parallel scan (sdm_scan_lanes.hip).
 #include "kernels.h"
-#include "scan_step.h"
 
 namespace sdm {
 
-template <bool BF16>
-__global__ void __launch_bounds__(64) sdm_scan_serial_kernel(ScanArgs A)
-{
-    const int nslice = A.d_v / 32;
-    const int unit = blockIdx.x;
-    const int slice = unit % nslice;
-    const int ch = unit / nslice;
-    const int bb = ch / A.H, h = ch - bb * A.H;
-    const int lane = lane_id();
-    const int col = slice * 32 + 4 * (lane & 7);
-    const size_t esz = BF16 ? 2 : 4;
-    const __amdgpu_buffer_rsrc_t Mrs =
-        make_rsrc(A.M + (size_t)ch * A.N * A.d_v, (uint32_t)((uint64_t)A.N * A.d_v * 4u));
-    for (int64_t t = 0; t < A.T; ++t) {
-        const int64_t row = (bb * A.T + t) * A.H + h;
-        scan_token_slice<BF16>(Mrs, A.d_v, col, A.widx + row * A.W, A.wwt + row * A.W, A.W,
-                               A.ridx + row * A.R, A.rwt + row * A.R, A.R,
-                               static_cast<const unsigned char *>(A.v) + row * A.d_v * esz,
-                               A.a[row], A.b[row], A.o + row * A.d_v);
-    }
-}
-
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of the pipelined scan: forwarding codes [B,T,H,W+R] (uint16) and
-// per-token hazard flags [B,T,H] (uint32).  The serial kernel needs none.
-size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int)
+// Lanes per token of the lane-parallel scan: the power of two >= max(W, R).
+static int scan_lanes_q(int W, int R)
 {
-    if (scan_pipe_depth(W, R) == 0) return 0;
+    int q = 4;
+    while (q < W || q < R) q *= 2;
+    return q;
+}
+
+// Pipeline depth D (steps in flight) of the lane-parallel scan.  A workgroup
+// (8 waves) holds 32 KB of LDS per unit of D (16 KB of gathered rows per step
+// in flight, and a ring of the rows written by the last 2D steps): with at
+// most one workgroup per CU D = 4 (128 KB); with more workgroups than CUs
+// two share a CU at D = 2.
+static int scan_lanes_depth(int64_t groups)
+{
+    return groups > 256 ? 2 : 4;
+}
+
+// Workspace: the three streams of the preparation pass, each 256-byte
+// aligned: lane records [B*H, T, Q] (16 bytes), row offsets [B*H, T, Q]
+// (8 bytes) and token records [B*H, T, d_v/4] (16 bytes, 32 for fp32 v).
+struct WsLayout {
+    size_t lane, gofs, tok, total;
+};
+
+static WsLayout ws_layout(int64_t B, int64_t T, int64_t H, int W, int R, int d_v, bool bf16)
+{
     const size_t rows = (size_t)(B * T * H);
-    return align256(rows * (size_t)(W + R) * 2) + align256(rows * 4);
+    const size_t q = (size_t)scan_lanes_q(W, R);
+    WsLayout L;
+    L.lane = 0;
+    L.gofs = L.lane + align256(rows * q * 16);
+    L.tok = L.gofs + align256(rows * q * 8);
+    L.total = L.tok + align256(rows * (size_t)(d_v / 4) * (bf16 ? 16 : 32));
+    return L;
+}
+
+size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int d_v, bool bf16)
+{
+    return ws_layout(B, T, H, W, R, d_v, bf16).total;
+}
+
+bool scan_chain_fits(int64_t T, int W, int R, int d_v, bool bf16)
+{
+    const uint64_t q = (uint64_t)scan_lanes_q(W, R);
+    const uint64_t lim = 1ull << 31;
+    return (uint64_t)T * q * 16 < lim && (uint64_t)T * (uint64_t)(d_v / 4) * (bf16 ? 16 : 32) < lim;
 }
 
 hipError_t launch_scan(const ScanArgs &A, bool bf16, void *ws, size_t, hipStream_t stream)
 {
-    const int64_t units = A.B * A.H * (A.d_v / 32);
+    const int64_t units = A.B * A.H * (A.d_v / 4);
     if (units == 0 || A.T == 0) return hipSuccess;
-    const int D = scan_pipe_depth(A.W, A.R);
-    if (D > 0) {
-        const size_t rows = (size_t)(A.B * A.T * A.H);
-        uint16_t *codes = static_cast<uint16_t *>(ws);
-        uint32_t *flags = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) +
-                                                       align256(rows * (size_t)(A.W + A.R) * 2));
-        HazardArgs hz{A.widx, A.ridx, codes, flags, A.B, A.T, A.H, A.W, A.R, D - 1};
-        hipError_t e = launch_scan_hazard(hz, stream);
-        if (e != hipSuccess) return e;
-        return launch_scan_pipe(A, bf16, codes, flags, stream);
-    }
-    if (bf16)
-        hipLaunchKernelGGL(sdm_scan_serial_kernel<true>, dim3((unsigned)units), dim3(64), 0, stream, A);
-    else
-        hipLaunchKernelGGL(sdm_scan_serial_kernel<false>, dim3((unsigned)units), dim3(64), 0, stream, A);
-    return hipGetLastError();
+    const int Q = scan_lanes_q(A.W, A.R);
+    const int D = scan_lanes_depth(A.B * A.H * (A.d_v / 32));
+    const int K = 64 / Q;
+    // rows written in the last 2D steps may not be visible to a gather yet
+    const int window = 2 * D * K - 1;
+    const WsLayout L = ws_layout(A.B, A.T, A.H, A.W, A.R, A.d_v, bf16);
+    unsigned char *base = static_cast<unsigned char *>(ws);
+    ScanStreams st{reinterpret_cast<uint4 *>(base + L.lane), reinterpret_cast<uint2 *>(base + L.gofs),
+                   reinterpret_cast<uint4 *>(base + L.tok)};
+    PrepArgs pa{A.widx, A.ridx, A.wwt, A.rwt, A.a, A.b, A.v, st, A.B, A.T, A.H,
+                A.W, A.R, Q, K, window, scan_prep_hash_log2(A.W, window, D * K - 1), A.d_v, bf16 ? 1 : 0,
+                D * K - 1};
+    hipError_t e = launch_scan_prep(pa, stream);
+    if (e != hipSuccess) return e;
+    return launch_scan_lanes(A, bf16, st, Q, D, stream);
 }
 
 }  // namespace sdm

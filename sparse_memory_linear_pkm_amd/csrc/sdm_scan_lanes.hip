@@ -1,0 +1,366 @@
+// sdm_scan_lanes.hip -- lane-parallel prefill scan.
+//
+// The recurrence is the sparse gated delta rule of "Sparse Delta Memory:
+// Scaling the State of Linear RNNs through Sparsity", Sec. 3.1 steps 2-3
+// (Eq. 4): per token, p = sum_j w_j M[s_j] over the W write rows, then
+// M[s_j] = a M[s_j] + b w_j (v - a p) for all j at once, then
+// o = sum_j r_j M[s'_j] over the R read rows after the write.
+//
+// Work unit: one wave per (sequence, head, 4-column chunk) -- columns never
+// interact, so every 16-byte column chunk of the memory is an independent
+// recurrence over the same slot lists.  The 8 waves of the chunks that make
+// up one 128-byte row segment (32 columns) form a workgroup and pass a
+// barrier once per step: they gather the same rows within a short window, so
+// each 128-byte line comes from HBM once and serves all 8 (without the
+// barrier the waves drift apart and the lines are evicted in between, which
+// multiplies the HBM traffic).  Within the wave, lane (i, j) =
+// (lane / Q, lane % Q) holds column chunk `chunk` of write row j and of read
+// row j of token i of the current step, Q = the power of two >= max(W, R):
+// a step advances K = 64 / Q consecutive tokens at once.  The sums over rows
+// are all-reductions over aligned groups of Q lanes (DPP quad_perm and
+// row_half_mirror / row_mirror adds, then the gfx950 permlane16/32 swaps).
+//
+// Tokens of one step run concurrently unless one of them needs a row that
+// an earlier token of the same step writes (forwarding code with 1 <= delta
+// <= its position in the step); such a step runs its K tokens one after the
+// other (exact, rare for scattered addressing).  Two tokens of a step never
+// store the same row: a write superseded later in the step is dropped.
+//
+// Latency: the gathers of step s + D are issued at the end of step s with the
+// LDS-destination form of buffer_load (one 1 KB instruction per row kind),
+// and the per-token metadata of step s + D (the slot lists of step s + 2D)
+// is loaded into a register ring at the same time.  Every step issues the
+// same fixed list of vector-memory instructions (lanes with nothing to do
+// use an offset past the buffer range: loads return zero, stores are
+// dropped), so the wait for a step's data is an exact compile-time vmcnt.
+// A gather issued D steps early misses the writes of the tokens in between;
+// those rows are taken from an LDS ring of recently written rows, following
+// exact forwarding codes computed beforehand (scan_hazard.hip).  Same-wave
+// stores are ordered before later loads of the same address, so every other
+// gather sees the current row.
+#include <type_traits>
+
+#include "kernels.h"
+#include "scan_lanes.h"
+
+namespace sdm {
+
+namespace {
+
+constexpr uint32_t kOOB = 0x80000000u;   // past every buffer range used here (all < 2 GiB)
+constexpr uint32_t kRowBias = 0x40000000u;   // row offsets are stored plus this (0: no row)
+constexpr int kWPG = 8;                  // waves per workgroup: the chunks of one 128-byte segment
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(K >= 0 && K <= 63, "vmcnt out of range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(K) : "memory");
+}
+
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T *)p;
+}
+
+// Reads this lane's 16 bytes of the gathered write row (at addr) and read
+// row (8192 bytes further) and waits for them inside the asm block (the
+// compiler would otherwise wait for every outstanding LDS-destination load
+// before an LDS read it cannot tell apart).
+constexpr int kReadRowsOffset = 8192;
+__device__ __forceinline__ void read_gathered(f32x4 &xw, f32x4 &xr, uint32_t addr)
+{
+    asm volatile("ds_read_b128 %0, %2\n\t"
+                 "ds_read_b128 %1, %2 offset:8192\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(xw), "=&v"(xr)
+                 : "v"(addr)
+                 : "memory");
+}
+
+// One 16-byte LDS read that waits for itself (see read_gathered).
+__device__ __forceinline__ f32x4 lds_read16(uint32_t addr)
+{
+    f32x4 x;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(addr) : "memory");
+    return x;
+}
+
+// Buffer resource over the records of tokens [u0, u0 + n) of one chain; token
+// u0 + i starts at base + i * tstride bytes and its record is rec bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t win_rsrc(const void *base, int64_t n, uint32_t tstride,
+                                                           uint32_t rec)
+{
+    return make_rsrc(base, n > 0 ? (uint32_t)(n - 1) * tstride + rec : 0u);
+}
+
+}  // namespace
+
+template <int Q, int D, bool BF16>
+__global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, ScanStreams S)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int K = kWave / Q;
+    constexpr int LQ = ilog2(Q), LK = ilog2(K);
+    static_assert((1 << LQ) == Q, "Q is a power of two");
+    constexpr int NTR = BF16 ? 1 : 2;            // 16-byte token records per chunk
+    constexpr int NVM = 6 + NTR;                 // vector-memory instructions per step (fixed)
+    static_assert((D - 1) * NVM <= 63, "pipeline deeper than the vmcnt range");
+
+    // Row r of a step is token r / Q, list position r % Q (r = the lane of
+    // the compute layout).  Row segments are 8 chunks of 16 bytes; chunk c of
+    // row r sits at position (c + r) % 8 (so that the compute waves, which
+    // read one chunk of 64 consecutive rows, spread over the LDS banks).
+    __shared__ f32x4 gath[D][2][kWave][kWPG];   // gathered write / read rows of the steps in flight
+    __shared__ f32x4 ring[2 * D][kWave][kWPG];  // rows written by the last 2D steps
+    __shared__ uint32_t supf[kWave];            // this step: write row superseded within the step
+    static_assert(sizeof(gath[0][0]) == kReadRowsOffset, "read rows follow the write rows");
+
+    const uint32_t nseg = (uint32_t)A.d_v / 32u;
+    const uint32_t chu = __builtin_amdgcn_readfirstlane(blockIdx.x / nseg);
+    const uint32_t seg = __builtin_amdgcn_readfirstlane(blockIdx.x - chu * nseg);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));   // compute chunk
+    const int64_t ch = chu;
+    const int64_t H = A.H, T = A.T;
+    const int64_t bb = ch / H, h = ch - bb * H;
+    const int lane = lane_id();
+    const int i = lane >> LQ;                                // compute layout: token of the step
+    const int rg = wave * 8 + (lane >> 3);                  // memory layout: row ...
+    const int pg = lane & 7;                                //   ... and its position
+    const uint32_t cg = (uint32_t)((pg - rg) & 7);          //   = chunk cg of that row
+    const uint32_t d_v = (uint32_t)A.d_v;
+    const uint32_t nchunk = d_v / 4u;
+    const uint32_t chunk = seg * 8u + (uint32_t)wave;
+    const uint32_t segb = seg * 128u;                       // byte offset of the segment in a row
+    const uint32_t colb = segb + (uint32_t)wave * 16u;      // byte offset of this wave's chunk
+    const __amdgpu_buffer_rsrc_t Mrs =
+        make_rsrc(A.M + (size_t)ch * A.N * d_v, (uint32_t)((uint64_t)A.N * d_v * 4u));
+    // this chain's streams (sizes checked on the host to be < 2 GiB)
+    const uint64_t tq = (uint64_t)T * Q;
+    const __amdgpu_buffer_rsrc_t R1 = make_rsrc(S.lane + ch * tq, (uint32_t)(tq * 16u));
+    const __amdgpu_buffer_rsrc_t R2 = make_rsrc(S.gofs + ch * tq, (uint32_t)(tq * 8u));
+    const uint64_t tc = (uint64_t)T * nchunk * NTR;
+    const __amdgpu_buffer_rsrc_t R3 = make_rsrc(S.tok + ch * tc, (uint32_t)(tc * 16u));
+    const int64_t nsteps = (T + K - 1) / K;
+
+    // running byte offsets of the next loads: lane records and token records
+    // of step s + D, row offsets of step s + 2D
+    uint32_t p1 = (uint32_t)lane * 16u;
+    uint32_t p2 = (uint32_t)rg * 8u;
+    uint32_t p3 = ((uint32_t)i * nchunk + chunk) * (16u * NTR);
+    constexpr uint32_t st1 = kWave * 16u, st2 = kWave * 8u;
+    const uint32_t st3 = (uint32_t)K * nchunk * (16u * NTR);
+    // output window of a step: K tokens from its first
+    const uint32_t otok = (uint32_t)(H * d_v * 4u);
+    const uint32_t offO = (lane & (Q - 1)) == 0 ? (uint32_t)i * otok + colb : kOOB;
+    float *obase = A.o + (size_t)(bb * T * H + h) * d_v;
+    const uint32_t orec = (uint32_t)(K - 1) * otok + d_v * 4u;
+
+    // register ring, slot = step % D
+    uint4 lr[D];              // lane record of step s
+    uint4 tr[D][NTR];         // token record (this wave's chunk) of step s
+    uint2 go[D];              // row offsets (memory layout) of step s + D
+    uint32_t ofw[D];          // write-row offsets (memory layout) of step s, for its store
+
+    auto idx_load = [&](int sl) __attribute__((always_inline)) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(R2, p2, 0, 0);
+        go[sl] = make_uint2(x[0], x[1]);
+        p2 += st2;
+    };
+    auto meta_load = [&](int sl) __attribute__((always_inline)) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(R1, p1, 0, 0);
+        lr[sl] = make_uint4(x[0], x[1], x[2], x[3]);
+#pragma unroll
+        for (int q = 0; q < NTR; ++q) {
+            const auto y = __builtin_amdgcn_raw_buffer_load_b128(R3, p3 + 16u * q, 0, 0);
+            tr[sl][q] = make_uint4(y[0], y[1], y[2], y[3]);
+        }
+        p1 += st1;
+        p3 += st3;
+    };
+    // this wave's share of the gathers of a step (rows 8w..8w+7 of the write
+    // and of the read rows, whole 128-byte segments) into gath[sl], from the
+    // row offsets in go[sl]; a zero offset record lands at or beyond 2^31
+    auto gathers = [&](int sl) __attribute__((always_inline)) {
+        ofw[sl] = go[sl].x - kRowBias + segb + cg * 16u;
+        const uint32_t ofr = go[sl].y - kRowBias + segb + cg * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][0][wave * 8][0], 16, ofw[sl], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][1][wave * 8][0], 16, ofr, 0, 0, 0);
+    };
+
+    // Rows past W or R are gathered from past the buffer range; make every
+    // LDS byte they could leave untouched a finite zero once.
+    for (uint32_t e = threadIdx.x; e < sizeof(gath) / 16; e += 64 * kWPG)
+        reinterpret_cast<f32x4 *>(&gath[0][0][0][0])[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+
+    // ---- prologue: row offsets of steps 0..D-1, then the steady-state issue
+    // order (gathers of s, row offsets of s + D, records of s) for s < D.
+    static_for<0, D>([&](auto s_c) __attribute__((always_inline)) { idx_load(decltype(s_c)::value); });
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    static_for<0, D>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int s = decltype(s_c)::value;
+        gathers(s);
+        idx_load(s);
+        meta_load(s);
+    });
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the loop starts with nothing pending
+    asm volatile("" ::: "memory");
+
+    const int pos_own = (wave + lane) & 7;   // position of this wave's chunk in row `lane`
+    for (int64_t s0 = 0; s0 < nsteps; s0 += D) {
+        static_for<0, D>([&](auto s_c) __attribute__((always_inline)) {
+            constexpr int s = decltype(s_c)::value;
+            const int64_t step = s0 + s;
+            const int rs = (int)((uint64_t)step % (2 * D));   // ring slot of this step
+            // ---- this step's gathers (every wave's share) and records ----
+            wait_vmcnt<(D - 1) * NVM>();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            f32x4 gw, gr;
+            read_gathered(gw, gr, lds_addr(&gath[s][0][lane][pos_own]));
+            const uint32_t code = ~lr[s].x;   // stored inverted: a load past the range reads "none"
+            const float wj = __uint_as_float(lr[s].y), rj = __uint_as_float(lr[s].z);
+            const float bwj = __uint_as_float(lr[s].w), at = __uint_as_float(tr[s][0].x);
+            f32x4 v4;
+            if constexpr (BF16)
+                v4 = v_chunk(make_uint2(tr[s][0].y, tr[s][0].z));
+            else
+                v4 = (f32x4){__uint_as_float(tr[s][NTR - 1].x), __uint_as_float(tr[s][NTR - 1].y),
+                             __uint_as_float(tr[s][NTR - 1].z), __uint_as_float(tr[s][NTR - 1].w)};
+            const uint32_t cw = code & 0x7FFFu, cr = code >> 16;
+            const int dw = (int)(cw >> 6), dr = (int)(cr >> 6);
+            const bool hw = cw != 0x7FFFu, hr = cr != 0xFFFFu;
+            const int64_t u = step * K + i;   // this lane's token
+            // this wave's chunk of the row written by token u - d at position c
+            auto ring_at = [&](int d, uint32_t c) -> f32x4 & {
+                const int64_t up = u - d;
+                const int r = (((int)up & (K - 1)) << LQ) | (int)(c & (Q - 1));
+                return ring[(uint32_t)(up >> LK) % (uint32_t)(2 * D)][r][(wave + r) & 7];
+            };
+            auto own_row = [&](uint32_t c) {   // this token's write at position c
+                const int r = (i << LQ) | (int)(c & (Q - 1));
+                return lds_read16(lds_addr(&ring[rs][r][(wave + r) & 7]));
+            };
+            const bool any_code = __builtin_amdgcn_ballot_w64(hw || hr) != 0;
+            const bool intra = __builtin_amdgcn_ballot_w64((hw && dw <= i) || (hr && dr >= 1 && dr <= i)) != 0;
+            const bool d0 = __builtin_amdgcn_ballot_w64(hr && dr == 0) != 0;
+            f32x4 o;
+            if (!intra) {
+                f32x4 xw = gw, xr = gr;
+                if (any_code) {
+                    if (hw) xw = ring_at(dw, cw);
+                    if (hr && dr >= 1) xr = ring_at(dr, cr);
+                }
+                const f32x4 p = weighted_rows<Q>(wj, xw);
+                o = weighted_rows<Q>(rj, xr);
+                ring[rs][lane][pos_own] = written_row(xw, at, bwj, v4, p);
+                if (d0) {
+                    wave_lds_sync();
+                    const f32x4 own = own_row(cr);
+                    if (hr && dr == 0) xr = own;
+                    o = weighted_rows<Q>(rj, xr);
+                }
+            } else {
+                // tokens of this step one at a time; lanes of token `it` commit
+                f32x4 ok = gr;
+                for (int it = 0; it < K; ++it) {
+                    f32x4 xw = gw, xr = gr;
+                    if (hw) xw = ring_at(dw, cw);
+                    if (hr && dr >= 1) xr = ring_at(dr, cr);
+                    const f32x4 p = weighted_rows<Q>(wj, xw);
+                    const f32x4 n2 = written_row(xw, at, bwj, v4, p);
+                    if (i == it) ring[rs][lane][pos_own] = n2;
+                    wave_lds_sync();
+                    const f32x4 own = own_row(cr);
+                    if (hr && dr == 0) xr = own;
+                    const f32x4 o2 = weighted_rows<Q>(rj, xr);
+                    if (i == it) ok = o2;
+                }
+                o = ok;
+            }
+            // a later token of this step writes the same row: its store is dropped
+            if (wave == 0) supf[lane] = code & 0x8000u;
+            // ---- stores: whole segments of the written rows (every wave's
+            // chunks), and this wave's chunk of the outputs ----
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            {
+                f32x4 x;
+                uint32_t sp;
+                asm volatile("ds_read_b128 %0, %2\n\t"
+                             "ds_read_b32 %1, %3\n\t"
+                             "s_waitcnt lgkmcnt(0)"
+                             : "=&v"(x), "=&v"(sp)
+                             : "v"(lds_addr(&ring[rs][rg][pg])), "v"(lds_addr(&supf[rg]))
+                             : "memory");
+                __builtin_amdgcn_raw_buffer_store_b128(x, Mrs, sp ? kOOB : ofw[s], 0, 0);
+            }
+            {
+                const int64_t rem = T - step * K;   // live tokens of this step: i < rem
+                const __amdgpu_buffer_rsrc_t Ors = make_rsrc(obase, orec);
+                __builtin_amdgcn_raw_buffer_store_b128(o, Ors, i < rem ? offO : kOOB, 0, 0);
+                obase += (size_t)K * H * d_v;
+            }
+            // ---- issue step + D (its gathers overwrite gath[s], read by
+            // every wave before the barrier above) ----
+            gathers(s);
+            idx_load(s);
+            meta_load(s);
+            asm volatile("" ::: "memory");
+        });
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int Q, int D, bool BF16>
+static hipError_t launch_lanes(const ScanArgs &A, const ScanStreams &S, hipStream_t st)
+{
+    const int64_t groups = A.B * A.H * (A.d_v / 32);
+    hipLaunchKernelGGL((sdm_scan_lanes_kernel<Q, D, BF16>), dim3((unsigned)groups), dim3(64 * kWPG), 0, st, A, S);
+    return hipGetLastError();
+}
+
+template <int Q, int D>
+static hipError_t launch_lanes_dt(const ScanArgs &A, bool bf16, const ScanStreams &S, hipStream_t st)
+{
+    return bf16 ? launch_lanes<Q, D, true>(A, S, st) : launch_lanes<Q, D, false>(A, S, st);
+}
+
+hipError_t launch_scan_lanes(const ScanArgs &A, bool bf16, const ScanStreams &S, int Q, int D, hipStream_t st)
+{
+    if (A.B * A.H * (A.d_v / 4) == 0 || A.T == 0) return hipSuccess;
+#define SDM_LANES_CASE(QV)                                                  \
+    case QV:                                                                \
+        return D == 2 ? launch_lanes_dt<QV, 2>(A, bf16, S, st)              \
+                      : launch_lanes_dt<QV, 4>(A, bf16, S, st);
+    switch (Q) {
+        SDM_LANES_CASE(4)
+        SDM_LANES_CASE(8)
+        SDM_LANES_CASE(16)
+        SDM_LANES_CASE(32)
+        SDM_LANES_CASE(64)
+    default: return hipErrorInvalidValue;
+    }
+#undef SDM_LANES_CASE
+}
+
+}  // namespace sdm

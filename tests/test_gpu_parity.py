@@ -118,6 +118,12 @@ SCAN_CASES = {
     "W64_R64": (Dims(B=1, T=70, H=2, d_k=128, n_sub=64, d_v=64, k_prime=8, W=64, R=64), 400),
     "W32_T1": (Dims(B=3, T=1, H=2, d_k=128, n_sub=64, d_v=128, k_prime=32, W=32, R=32), None),
     "W32_T17_dv32": (Dims(B=2, T=17, H=1, d_k=128, n_sub=64, d_v=32, k_prime=32, W=32, R=32), 100),
+    # moderate collision rates: steps of concurrent tokens mixed with steps
+    # whose tokens depend on each other, and reads of the token's own writes
+    "mixed_W16": (Dims(B=5, T=500, H=2, d_k=128, n_sub=64, d_v=64, k_prime=16, W=16, R=16), 3000),
+    "mixed_W32": (Dims(B=3, T=300, H=3, d_k=128, n_sub=128, d_v=128, k_prime=32, W=32, R=32), 6000),
+    "mixed_W4_K16": (Dims(B=9, T=700, H=1, d_k=32, n_sub=32, d_v=32, k_prime=4, W=4, R=4, in_dtype="f32"), 300),
+    "mixed_W12_R7": (Dims(B=2, T=333, H=5, d_k=128, n_sub=64, d_v=160, k_prime=8, W=12, R=7), 1500),
 }
 
 
