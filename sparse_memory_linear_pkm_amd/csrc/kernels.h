@@ -79,7 +79,7 @@ size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int d
 bool scan_chain_fits(int64_t T, int W, int R, int d_v, bool bf16);
 hipError_t launch_scan_prep(const PrepArgs &args, hipStream_t stream);
 int scan_prep_hash_log2(int W, int window, int lookahead);
-hipError_t launch_scan_lanes(const ScanArgs &args, bool bf16, const ScanStreams &st, int Q, int D,
+hipError_t launch_scan_lanes(const ScanArgs &args, bool bf16, const ScanStreams &st, int Q, int G, int D,
                              hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, bool bf16, hipStream_t stream);
 size_t decode_smem_bytes(int n_sub, int k_prime);

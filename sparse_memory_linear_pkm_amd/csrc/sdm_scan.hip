@@ -20,14 +20,23 @@ static int scan_lanes_q(int W, int R)
     return q;
 }
 
-// Pipeline depth D (steps in flight) of the lane-parallel scan.  A workgroup
-// (8 waves) holds 32 KB of LDS per unit of D (16 KB of gathered rows per step
-// in flight, and a ring of the rows written by the last 2D steps): with at
-// most one workgroup per CU D = 4 (128 KB); with more workgroups than CUs
-// two share a CU at D = 2.
-static int scan_lanes_depth(int64_t groups)
+// Shape of the lane-parallel scan: G waves per workgroup (one G*16-byte
+// row segment each) and pipeline depth D (steps in flight).  The widest
+// segment that still gives every CU a workgroup wins (whole 128-byte lines
+// per access); a workgroup holds D * G * 4 KB of LDS (16 KB of gathered rows
+// per step in flight and a ring of the rows written by the last 2D steps,
+// per 8 waves), so D = 2 lets two 8-wave workgroups share a CU.
+struct LanesShape {
+    int G, D;
+};
+
+static LanesShape scan_lanes_shape(int64_t chunks)   // chunks = B * H * d_v / 4
 {
-    return groups > 256 ? 2 : 4;
+    constexpr int64_t kCUs = 256;
+    if (chunks / 8 >= 2 * kCUs) return {8, 2};
+    if (chunks / 8 >= kCUs) return {8, 4};
+    if (chunks / 4 >= kCUs) return {4, 4};
+    return {2, 8};
 }
 
 // Workspace: the three streams of the preparation pass, each 256-byte
@@ -66,7 +75,8 @@ hipError_t launch_scan(const ScanArgs &A, bool bf16, void *ws, size_t, hipStream
     const int64_t units = A.B * A.H * (A.d_v / 4);
     if (units == 0 || A.T == 0) return hipSuccess;
     const int Q = scan_lanes_q(A.W, A.R);
-    const int D = scan_lanes_depth(A.B * A.H * (A.d_v / 32));
+    const LanesShape sh = scan_lanes_shape(units);
+    const int D = sh.D;
     const int K = 64 / Q;
     // rows written in the last 2D steps may not be visible to a gather yet
     const int window = 2 * D * K - 1;
@@ -79,7 +89,7 @@ hipError_t launch_scan(const ScanArgs &A, bool bf16, void *ws, size_t, hipStream
                 D * K - 1};
     hipError_t e = launch_scan_prep(pa, stream);
     if (e != hipSuccess) return e;
-    return launch_scan_lanes(A, bf16, st, Q, D, stream);
+    return launch_scan_lanes(A, bf16, st, Q, sh.G, D, stream);
 }
 
 }  // namespace sdm

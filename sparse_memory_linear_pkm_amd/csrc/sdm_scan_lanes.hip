@@ -8,12 +8,15 @@
 //
 // Work unit: one wave per (sequence, head, 4-column chunk) -- columns never
 // interact, so every 16-byte column chunk of the memory is an independent
-// recurrence over the same slot lists.  The 8 waves of the chunks that make
-// up one 128-byte row segment (32 columns) form a workgroup and pass a
-// barrier once per step: they gather the same rows within a short window, so
-// each 128-byte line comes from HBM once and serves all 8 (without the
-// barrier the waves drift apart and the lines are evicted in between, which
-// multiplies the HBM traffic).  Within the wave, lane (i, j) =
+// recurrence over the same slot lists.  The G waves (G = 2, 4 or 8) of the
+// chunks that make up one G*16-byte row segment form a workgroup.  Memory is
+// accessed cooperatively in whole segments: each wave gathers and stores
+// whole segments of 64/G of the step's rows (G consecutive lanes per row, so
+// a row segment is one coalesced access) through LDS, and computes on its
+// own chunk of every row; two barriers per step separate the phases.  When G
+// < 8, the 8/G workgroups that share 128-byte lines run on the same XCD,
+// whose L2 then serves each line once (the host picks the widest G that
+// still gives a workgroup to every CU).  Within the wave, lane (i, j) =
 // (lane / Q, lane % Q) holds column chunk `chunk` of write row j and of read
 // row j of token i of the current step, Q = the power of two >= max(W, R):
 // a step advances K = 64 / Q consecutive tokens at once.  The sums over rows
@@ -35,9 +38,14 @@
 // dropped), so the wait for a step's data is an exact compile-time vmcnt.
 // A gather issued D steps early misses the writes of the tokens in between;
 // those rows are taken from an LDS ring of recently written rows, following
-// exact forwarding codes computed beforehand (scan_hazard.hip).  Same-wave
-// stores are ordered before later loads of the same address, so every other
-// gather sees the current row.
+// exact forwarding codes computed beforehand (scan_prep.hip).  A row stored
+// by one wave is gathered by another only after the storing wave waited for
+// the store and both passed a barrier: a store of step s is complete before
+// its wave passes the first barrier of step s + D, and the gathers issued at
+// the end of step s' see it from s' >= s + D on, so the codes cover the
+// rows written by the last 2D steps, which the ring holds.  A write that is
+// written again within the next D - 1 steps is not stored at all (the later
+// one is), so stores of one row are at least D steps apart and land in order.
 #include <type_traits>
 
 #include "kernels.h"
@@ -49,7 +57,6 @@ namespace {
 
 constexpr uint32_t kOOB = 0x80000000u;   // past every buffer range used here (all < 2 GiB)
 constexpr uint32_t kRowBias = 0x40000000u;   // row offsets are stored plus this (0: no row)
-constexpr int kWPG = 8;                  // waves per workgroup: the chunks of one 128-byte segment
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
@@ -76,17 +83,17 @@ __device__ __forceinline__ uint32_t lds_addr(const T *p)
 }
 
 // Reads this lane's 16 bytes of the gathered write row (at addr) and read
-// row (8192 bytes further) and waits for them inside the asm block (the
+// row (OFF bytes further) and waits for them inside the asm block (the
 // compiler would otherwise wait for every outstanding LDS-destination load
 // before an LDS read it cannot tell apart).
-constexpr int kReadRowsOffset = 8192;
+template <int OFF>
 __device__ __forceinline__ void read_gathered(f32x4 &xw, f32x4 &xr, uint32_t addr)
 {
     asm volatile("ds_read_b128 %0, %2\n\t"
-                 "ds_read_b128 %1, %2 offset:8192\n\t"
+                 "ds_read_b128 %1, %2 offset:%3\n\t"
                  "s_waitcnt lgkmcnt(0)"
                  : "=&v"(xw), "=&v"(xr)
-                 : "v"(addr)
+                 : "v"(addr), "n"(OFF)
                  : "memory");
 }
 
@@ -106,10 +113,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t win_rsrc(const void *base, int
     return make_rsrc(base, n > 0 ? (uint32_t)(n - 1) * tstride + rec : 0u);
 }
 
+// (group, member) of workgroup `id` for ngroups groups of nmem members, such
+// that all members of a group run on the same XCD (workgroup ids are dealt to
+// the 8 XCDs round-robin).  Groups past the last multiple of 8 take plain order.
+__device__ __forceinline__ void xcd_decode(uint32_t id, uint32_t ngroups, uint32_t nmem, uint32_t &group,
+                                           uint32_t &member)
+{
+    constexpr uint32_t kX = 8;
+    const uint32_t full = ngroups / kX;
+    const uint32_t per_xcd = full * nmem;
+    const uint32_t k = id / kX;
+    if (k < per_xcd) {
+        group = (k / nmem) * kX + id % kX;
+        member = k % nmem;
+    } else {
+        const uint32_t rest = id - per_xcd * kX;
+        group = full * kX + rest / nmem;
+        member = rest % nmem;
+    }
+}
+
 }  // namespace
 
-template <int Q, int D, bool BF16>
-__global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, ScanStreams S)
+template <int Q, int D, int G, bool BF16>
+__global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, ScanStreams S)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int K = kWave / Q;
@@ -119,31 +146,36 @@ __global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, S
     constexpr int NVM = 6 + NTR;                 // vector-memory instructions per step (fixed)
     static_assert((D - 1) * NVM <= 63, "pipeline deeper than the vmcnt range");
 
-    // Row r of a step is token r / Q, list position r % Q (r = the lane of
-    // the compute layout).  Row segments are 8 chunks of 16 bytes; chunk c of
-    // row r sits at position (c + r) % 8 (so that the compute waves, which
-    // read one chunk of 64 consecutive rows, spread over the LDS banks).
-    __shared__ f32x4 gath[D][2][kWave][kWPG];   // gathered write / read rows of the steps in flight
-    __shared__ f32x4 ring[2 * D][kWave][kWPG];  // rows written by the last 2D steps
-    __shared__ uint32_t supf[kWave];            // this step: write row superseded within the step
-    static_assert(sizeof(gath[0][0]) == kReadRowsOffset, "read rows follow the write rows");
+    static_assert(G == 2 || G == 4 || G == 8, "2, 4 or 8 waves per workgroup");
+    constexpr int RPW = kWave / G;               // rows of a step each wave moves
 
-    const uint32_t nseg = (uint32_t)A.d_v / 32u;
-    const uint32_t chu = __builtin_amdgcn_readfirstlane(blockIdx.x / nseg);
-    const uint32_t seg = __builtin_amdgcn_readfirstlane(blockIdx.x - chu * nseg);
+    // Row r of a step is token r / Q, list position r % Q (r = the lane of
+    // the compute layout).  Row segments are G chunks of 16 bytes; chunk c of
+    // row r sits at position (c + r) % G (so that the compute waves, which
+    // read one chunk of 64 consecutive rows, spread over the LDS banks).
+    __shared__ f32x4 gath[D][2][kWave][G];      // gathered write / read rows of the steps in flight
+    __shared__ f32x4 ring[2 * D][kWave][G];     // rows written by the last 2D steps
+    __shared__ uint32_t supf[kWave];            // this step: write row superseded within the step
+    constexpr int kReadOff = (int)sizeof(gath[0][0]);   // read rows follow the write rows
+
+    const uint32_t d_v = (uint32_t)A.d_v;
+    const uint32_t nline = d_v / 32u;            // 128-byte lines per row
+    uint32_t grp, part;
+    xcd_decode(blockIdx.x, (uint32_t)(A.B * A.H) * nline, 8u / G, grp, part);
+    const uint32_t chu = __builtin_amdgcn_readfirstlane(grp / nline);
+    const uint32_t seg = __builtin_amdgcn_readfirstlane((grp - chu * nline) * (8u / G) + part);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));   // compute chunk
     const int64_t ch = chu;
     const int64_t H = A.H, T = A.T;
     const int64_t bb = ch / H, h = ch - bb * H;
     const int lane = lane_id();
     const int i = lane >> LQ;                                // compute layout: token of the step
-    const int rg = wave * 8 + (lane >> 3);                  // memory layout: row ...
-    const int pg = lane & 7;                                //   ... and its position
-    const uint32_t cg = (uint32_t)((pg - rg) & 7);          //   = chunk cg of that row
-    const uint32_t d_v = (uint32_t)A.d_v;
+    const int rg = wave * RPW + lane / G;                   // memory layout: row ...
+    const int pg = lane % G;                                //   ... and its position
+    const uint32_t cg = (uint32_t)((pg - rg) & (G - 1));    //   = chunk cg of that row
     const uint32_t nchunk = d_v / 4u;
-    const uint32_t chunk = seg * 8u + (uint32_t)wave;
-    const uint32_t segb = seg * 128u;                       // byte offset of the segment in a row
+    const uint32_t chunk = seg * G + (uint32_t)wave;
+    const uint32_t segb = seg * G * 16u;                    // byte offset of the segment in a row
     const uint32_t colb = segb + (uint32_t)wave * 16u;      // byte offset of this wave's chunk
     const __amdgpu_buffer_rsrc_t Mrs =
         make_rsrc(A.M + (size_t)ch * A.N * d_v, (uint32_t)((uint64_t)A.N * d_v * 4u));
@@ -190,21 +222,21 @@ __global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, S
         p1 += st1;
         p3 += st3;
     };
-    // this wave's share of the gathers of a step (rows 8w..8w+7 of the write
-    // and of the read rows, whole 128-byte segments) into gath[sl], from the
+    // this wave's share of the gathers of a step (rows RPW*w .. RPW*w+RPW-1 of
+    // the write and of the read rows, whole segments) into gath[sl], from the
     // row offsets in go[sl]; a zero offset record lands at or beyond 2^31
     auto gathers = [&](int sl) __attribute__((always_inline)) {
         ofw[sl] = go[sl].x - kRowBias + segb + cg * 16u;
         const uint32_t ofr = go[sl].y - kRowBias + segb + cg * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][0][wave * 8][0], 16, ofw[sl], 0, 0, 0);
+            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][0][wave * RPW][0], 16, ofw[sl], 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][1][wave * 8][0], 16, ofr, 0, 0, 0);
+            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][1][wave * RPW][0], 16, ofr, 0, 0, 0);
     };
 
     // Rows past W or R are gathered from past the buffer range; make every
     // LDS byte they could leave untouched a finite zero once.
-    for (uint32_t e = threadIdx.x; e < sizeof(gath) / 16; e += 64 * kWPG)
+    for (uint32_t e = threadIdx.x; e < sizeof(gath) / 16; e += 64 * G)
         reinterpret_cast<f32x4 *>(&gath[0][0][0][0])[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
@@ -222,7 +254,7 @@ __global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, S
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the loop starts with nothing pending
     asm volatile("" ::: "memory");
 
-    const int pos_own = (wave + lane) & 7;   // position of this wave's chunk in row `lane`
+    const int pos_own = (wave + lane) & (G - 1);   // position of this wave's chunk in row `lane`
     for (int64_t s0 = 0; s0 < nsteps; s0 += D) {
         static_for<0, D>([&](auto s_c) __attribute__((always_inline)) {
             constexpr int s = decltype(s_c)::value;
@@ -234,7 +266,7 @@ __global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, S
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             f32x4 gw, gr;
-            read_gathered(gw, gr, lds_addr(&gath[s][0][lane][pos_own]));
+            read_gathered<kReadOff>(gw, gr, lds_addr(&gath[s][0][lane][pos_own]));
             const uint32_t code = ~lr[s].x;   // stored inverted: a load past the range reads "none"
             const float wj = __uint_as_float(lr[s].y), rj = __uint_as_float(lr[s].z);
             const float bwj = __uint_as_float(lr[s].w), at = __uint_as_float(tr[s][0].x);
@@ -252,11 +284,11 @@ __global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, S
             auto ring_at = [&](int d, uint32_t c) -> f32x4 & {
                 const int64_t up = u - d;
                 const int r = (((int)up & (K - 1)) << LQ) | (int)(c & (Q - 1));
-                return ring[(uint32_t)(up >> LK) % (uint32_t)(2 * D)][r][(wave + r) & 7];
+                return ring[(uint32_t)(up >> LK) % (uint32_t)(2 * D)][r][(wave + r) & (G - 1)];
             };
             auto own_row = [&](uint32_t c) {   // this token's write at position c
                 const int r = (i << LQ) | (int)(c & (Q - 1));
-                return lds_read16(lds_addr(&ring[rs][r][(wave + r) & 7]));
+                return lds_read16(lds_addr(&ring[rs][r][(wave + r) & (G - 1)]));
             };
             const bool any_code = __builtin_amdgcn_ballot_w64(hw || hr) != 0;
             const bool intra = __builtin_amdgcn_ballot_w64((hw && dw <= i) || (hr && dr >= 1 && dr <= i)) != 0;
@@ -331,36 +363,40 @@ __global__ void __launch_bounds__(64 * kWPG) sdm_scan_lanes_kernel(ScanArgs A, S
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int Q, int D, bool BF16>
+template <int Q, int D, int G, bool BF16>
 static hipError_t launch_lanes(const ScanArgs &A, const ScanStreams &S, hipStream_t st)
 {
-    const int64_t groups = A.B * A.H * (A.d_v / 32);
-    hipLaunchKernelGGL((sdm_scan_lanes_kernel<Q, D, BF16>), dim3((unsigned)groups), dim3(64 * kWPG), 0, st, A, S);
+    const int64_t groups = A.B * A.H * (A.d_v / 4) / G;
+    hipLaunchKernelGGL((sdm_scan_lanes_kernel<Q, D, G, BF16>), dim3((unsigned)groups), dim3(64 * G), 0, st, A, S);
     return hipGetLastError();
 }
 
-template <int Q, int D>
-static hipError_t launch_lanes_dt(const ScanArgs &A, bool bf16, const ScanStreams &S, hipStream_t st)
+template <int Q>
+static hipError_t launch_lanes_q(const ScanArgs &A, bool bf16, const ScanStreams &S, int G, int D, hipStream_t st)
 {
-    return bf16 ? launch_lanes<Q, D, true>(A, S, st) : launch_lanes<Q, D, false>(A, S, st);
+#define SDM_LANES_GD(GV, DV)                                                                      \
+    if (G == GV && D == DV)                                                                        \
+        return bf16 ? launch_lanes<Q, DV, GV, true>(A, S, st) : launch_lanes<Q, DV, GV, false>(A, S, st);
+    SDM_LANES_GD(8, 2)
+    SDM_LANES_GD(8, 4)
+    SDM_LANES_GD(4, 4)
+    SDM_LANES_GD(2, 8)
+#undef SDM_LANES_GD
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_lanes(const ScanArgs &A, bool bf16, const ScanStreams &S, int Q, int D, hipStream_t st)
+hipError_t launch_scan_lanes(const ScanArgs &A, bool bf16, const ScanStreams &S, int Q, int G, int D,
+                             hipStream_t st)
 {
     if (A.B * A.H * (A.d_v / 4) == 0 || A.T == 0) return hipSuccess;
-#define SDM_LANES_CASE(QV)                                                  \
-    case QV:                                                                \
-        return D == 2 ? launch_lanes_dt<QV, 2>(A, bf16, S, st)              \
-                      : launch_lanes_dt<QV, 4>(A, bf16, S, st);
     switch (Q) {
-        SDM_LANES_CASE(4)
-        SDM_LANES_CASE(8)
-        SDM_LANES_CASE(16)
-        SDM_LANES_CASE(32)
-        SDM_LANES_CASE(64)
+    case 4: return launch_lanes_q<4>(A, bf16, S, G, D, st);
+    case 8: return launch_lanes_q<8>(A, bf16, S, G, D, st);
+    case 16: return launch_lanes_q<16>(A, bf16, S, G, D, st);
+    case 32: return launch_lanes_q<32>(A, bf16, S, G, D, st);
+    case 64: return launch_lanes_q<64>(A, bf16, S, G, D, st);
     default: return hipErrorInvalidValue;
     }
-#undef SDM_LANES_CASE
 }
 
 }  // namespace sdm
