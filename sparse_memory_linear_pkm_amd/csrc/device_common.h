@@ -161,19 +161,23 @@ __device__ __forceinline__ void bitonic_stage(T (&x)[NR])
     }
 }
 
-template <int K, int NR, class T>
+template <int K, int WIDTH, int NR, class T>
 __device__ __forceinline__ void bitonic_from(T (&x)[NR])
 {
-    if constexpr (K <= kWave) {
+    if constexpr (K <= WIDTH) {
         bitonic_stage<K, K / 2, NR>(x);
-        bitonic_from<K * 2, NR>(x);
+        bitonic_from<K * 2, WIDTH, NR>(x);
     }
 }
 
-template <int NR, class T>
+// Sorts lanes [0, WIDTH) of each of the NR values descending (WIDTH = 32
+// also sorts lanes 32..63 among themselves, ascending; callers that use it
+// keep every candidate in lanes 0..31).
+template <int NR, int WIDTH = kWave, class T>
 __device__ __forceinline__ void wave_sort_desc(T (&x)[NR])
 {
-    bitonic_from<2, NR>(x);
+    static_assert(WIDTH == 32 || WIDTH == 64, "sort width");
+    bitonic_from<2, WIDTH, NR>(x);
 }
 
 // Exact top-n (1 <= n <= 64, n <= len) of `len` candidates for each of NR
@@ -182,17 +186,31 @@ __device__ __forceinline__ void wave_sort_desc(T (&x)[NR])
 // lane j < n of res[r] holds the j-th best key of row r (descending); the
 // other lanes hold 0.  scratch: NR * 64 uint64 of this wave's LDS.
 //
-// Per row: tau = the n-th largest per-lane maximum score (compared on the
+// len <= 64: the candidates are sorted directly (one per lane).  Otherwise,
+// per row: tau = the n-th largest per-lane maximum score (compared on the
 // score bits only) bounds the answer from below, since at least n candidates
-// (one per lane above it) reach it.  The candidates whose score reaches tau
-// are compacted with ballots and sorted as 64-bit keys.  When more than 64
-// reach tau (ties, or n close to 64), that row is instead extracted one best
-// key at a time, which is exact as well.
+// (one per lane above it) reach it; the candidates whose score reaches tau
+// are compacted with ballots and sorted as 64-bit keys (over 32 lanes when
+// every row has at most 32 of them).  When more than 64 reach tau (ties, or
+// n close to 64), that row is instead extracted one best key at a time,
+// which is exact as well.
 template <int NR, class Get>
 __device__ __forceinline__ void wave_topn(int len, int n, Get get, uint64_t *scratch,
                                           uint64_t (&res)[NR])
 {
     const int lane = lane_id();
+    if (len <= kWave) {
+        uint64_t c[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) c[r] = lane < len ? get(r, lane) : 0ull;
+        if (len <= 32)
+            wave_sort_desc<NR, 32>(c);
+        else
+            wave_sort_desc<NR, 64>(c);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) res[r] = lane < n ? c[r] : 0ull;
+        return;
+    }
     uint32_t m[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) m[r] = 0;
@@ -226,10 +244,17 @@ __device__ __forceinline__ void wave_topn(int len, int n, Get get, uint64_t *scr
     }
     wave_lds_sync();
     uint64_t c[NR];
+    int most = 0;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) c[r] = lane < total[r] ? scratch[r * kWave + lane] : 0ull;
+    for (int r = 0; r < NR; ++r) {
+        c[r] = lane < total[r] ? scratch[r * kWave + lane] : 0ull;
+        most = total[r] > most ? total[r] : most;
+    }
     __builtin_amdgcn_wave_barrier();
-    wave_sort_desc<NR>(c);
+    if (most <= 32 && n <= 32)
+        wave_sort_desc<NR, 32>(c);
+    else
+        wave_sort_desc<NR, 64>(c);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         res[r] = lane < n ? c[r] : 0ull;

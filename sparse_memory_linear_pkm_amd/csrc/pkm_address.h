@@ -19,7 +19,8 @@ constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimensio
 constexpr int kMaxStair = 288;    // >= max over k', n <= 64 of the staircase size (280)
 
 // fp32 half scores S[r][u] = <x_r[c*half : (c+1)*half], C[h][c][u]> for the
-// first `srows` rows of one 16-row tile, written to LDS (row stride n_sub).
+// first `srows` rows of one 16-row tile, written to LDS (row stride n_sub) as
+// their order-preserving bits (score_bits), the form every comparison uses.
 // Rows >= nrows are scored as zero vectors (so stored rows past the real ones
 // hold zeros).  bf16 inputs use the gfx950 MFMA v_mfma_f32_16x16x32_bf16 with
 // fp32 accumulation; every output element depends only on its own row, so a
@@ -31,7 +32,7 @@ template <bool BF16>
 __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_stride, int nrows,
                                                 int srows,
                                                 const void *Cc /* [n_sub, half] of (h, c) */,
-                                                int c, int half, int n_sub, float *S)
+                                                int c, int half, int n_sub, uint32_t *S)
 {
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
@@ -67,7 +68,7 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = 4 * kg + e;
-                    if (row < srows) S[row * n_sub + u] = acc[e];
+                    if (row < srows) S[row * n_sub + u] = score_bits(acc[e]);
                 }
             }
         }
@@ -82,7 +83,7 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
                 const float *cr = Cf + (int64_t)u * half;
                 for (int d = 0; d < half; ++d) acc = __builtin_fmaf(xr[d], cr[d], acc);
             }
-            S[e] = acc;
+            S[e] = score_bits(acc);
         }
     }
 }
@@ -115,15 +116,15 @@ __device__ __forceinline__ int build_staircase(int kp, int n, uint16_t *stair, i
     return total;
 }
 
-// Top-k' of NR rows of half scores, one wave.  Row r's n_sub scores are at
-// S + rows[r] * n_sub; lane j < k' of keys[r] receives the j-th best
+// Top-k' of NR rows of half scores, one wave.  Row r's n_sub score bits are
+// at S + rows[r] * n_sub; lane j < k' of keys[r] receives the j-th best
 // (score desc, sub-key asc).
 template <int NR>
-__device__ __forceinline__ void half_topk(const float *S, const int (&rows)[NR], int n_sub, int kp,
+__device__ __forceinline__ void half_topk(const uint32_t *S, const int (&rows)[NR], int n_sub, int kp,
                                           uint64_t *scratch, uint64_t (&keys)[NR])
 {
     wave_topn<NR>(n_sub, kp,
-                  [&](int r, int p) { return score_key(S[rows[r] * n_sub + p], (uint32_t)p); },
+                  [&](int r, int p) { return ((uint64_t)S[rows[r] * n_sub + p] << 32) | (uint32_t)~p; },
                   scratch, keys);
 }
 
@@ -182,9 +183,9 @@ __device__ __forceinline__ void merge_softmax(const HalfEntry *const (&L0)[NR],
     for (int r = 0; r < NR; ++r) {
         const float s = key_score(best[r]);
         const float smax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(s), 0));
-        const float e = lane < n ? expf(s - smax) : 0.f;
+        const float e = lane < n ? __expf(s - smax) : 0.f;
         const float z = wave_sum_f32(e);
-        wt[r] = e / z;
+        wt[r] = __fdividef(e, z);
         slot[r] = (int)key_index(best[r]);
     }
 }

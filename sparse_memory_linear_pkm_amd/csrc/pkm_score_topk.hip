@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
     const int lane = lane_id();
 
     const AddrLds lay = addr_lds_layout(n_sub, kp);
-    float *S = reinterpret_cast<float *>(smem + lay.S);
+    uint32_t *S = reinterpret_cast<uint32_t *>(smem + lay.S);
     HalfEntry *L = reinterpret_cast<HalfEntry *>(smem + lay.L);
     uint64_t *wscr = reinterpret_cast<uint64_t *>(smem + lay.scratch) + wave * kRowsPerWave * kWave;
     uint16_t *stair = reinterpret_cast<uint16_t *>(smem + lay.stair);

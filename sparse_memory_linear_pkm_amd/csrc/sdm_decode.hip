@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
     const size_t esz = BF16 ? 2 : 4;
 
     const DecodeLds lay = decode_lds_layout(n_sub, kp);
-    float *S = reinterpret_cast<float *>(smem + lay.S);                 // [4][n_sub]
+    uint32_t *S = reinterpret_cast<uint32_t *>(smem + lay.S);                 // [4][n_sub]
     HalfEntry *L = reinterpret_cast<HalfEntry *>(smem + lay.L);         // [4][kp]
     uint64_t *wscr = reinterpret_cast<uint64_t *>(smem + lay.scratch) + wave * kWave;
     uint16_t *stair = reinterpret_cast<uint16_t *>(smem + lay.stair);   // [2][kMaxStair]
