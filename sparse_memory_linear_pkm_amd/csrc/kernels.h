@@ -40,9 +40,9 @@ struct ScanArgs {
 // the preparation pass, scan_prep.hip).  Streams are ordered [chain][token]
 // with chain = b * H + h, so one chain's records are contiguous.
 struct ScanStreams {
-    uint4 *lane;        // [chain][t][Q]: {~codes, w_j, r_j, b_t * w_j}
+    uint4 *lane;        // [chain][t][Q]: {~codes, w_j, r_j, biased write row offset}
     uint2 *gofs;        // [chain][t][Q]: biased byte offsets of write / read row j
-    uint4 *tok;         // [chain][t][d_v / 4]: {a_t, v chunk (bf16: 2 words, 0) | (f32: 0,0,0 + 4 words)}
+    uint4 *tok;         // [chain][t][d_v / 4]: {a_t, v chunk, b_t} (bf16) | {a_t, b_t, 0, 0}{v chunk} (f32)
 };
 
 struct PrepArgs {

@@ -22,18 +22,18 @@
 //
 // Streams (chain = b * H + h, one chain contiguous, tokens in order):
 //   lane[chain][t][j], j < Q:  {~(write code | read code << 16), w_j, r_j,
-//                               b_t * w_j}  (0 weights past W or R; the code
-//                               word is inverted so that a zero -- what a
-//                               load past the end of a buffer returns --
-//                               reads as "none")
+//                               write row offset}  (0 weights past W or R;
+//                               the code word is inverted so that a zero --
+//                               what a load past the end of a buffer returns
+//                               -- reads as "none")
 //   gofs[chain][t][j]:          byte offsets of write row j and read row j in
 //                               the (b, h) memory plus 2^30 (0: no row), so a
 //                               zero read past the end maps to an offset at
-//                               or beyond 2^31, outside every memory
-//   tok[chain][t][c], c < d_v/4: {a_t, v_t[4c .. 4c+3]} as one 16-byte record
-//                               (bf16 v: 2 words then 0) or two (fp32 v: a_t,
-//                               0, 0, 0, then the 4 values)
-// b_t * w_j is the same fp32 product the decode step forms.
+//                               or beyond 2^31, outside every memory (the
+//                               lane record repeats the write offset)
+//   tok[chain][t][c], c < d_v/4: {a_t, v_t[4c .. 4c+3], b_t} as one 16-byte
+//                               record (bf16 v: 2 words) or two (fp32 v:
+//                               {a_t, b_t, 0, 0}, then the 4 values)
 //
 // One workgroup per (b, h, block of 32 tokens).  The write lists of the block
 // and of the `window` tokens before it go into an LDS hash table keyed by
@@ -145,8 +145,7 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
             wr = A.rwt[row * R + j];
         }
         const int64_t s = (ch * A.T + t) * Q + j;
-        const float bw = A.b[row] * ww;
-        A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(ww), __float_as_uint(wr), __float_as_uint(bw));
+        A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(ww), __float_as_uint(wr), gw);
         A.st.gofs[s] = make_uint2(gw, gr);
     }
     // token records: a_t and the 4-column chunks of v_t
@@ -155,14 +154,14 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
         const int tl = e / nchunk, c = e - tl * nchunk;
         const int64_t t = t0 + tl;
         const int64_t row = row_of(t);
-        const uint32_t a = __float_as_uint(A.a[row]);
+        const uint32_t a = __float_as_uint(A.a[row]), b = __float_as_uint(A.b[row]);
         const int64_t s = (ch * A.T + t) * nchunk + c;
         if (A.bf16) {
             const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(A.v) + row * A.d_v + 4 * c);
-            A.st.tok[s] = make_uint4(a, v.x, v.y, 0u);
+            A.st.tok[s] = make_uint4(a, v.x, v.y, b);
         } else {
             const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const float *>(A.v) + row * A.d_v + 4 * c);
-            A.st.tok[2 * s] = make_uint4(a, 0u, 0u, 0u);
+            A.st.tok[2 * s] = make_uint4(a, b, 0u, 0u);
             A.st.tok[2 * s + 1] = v;
         }
     }

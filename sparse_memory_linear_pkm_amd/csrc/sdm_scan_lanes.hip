@@ -269,7 +269,8 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
             read_gathered<kReadOff>(gw, gr, lds_addr(&gath[s][0][lane][pos_own]));
             const uint32_t code = ~lr[s].x;   // stored inverted: a load past the range reads "none"
             const float wj = __uint_as_float(lr[s].y), rj = __uint_as_float(lr[s].z);
-            const float bwj = __uint_as_float(lr[s].w), at = __uint_as_float(tr[s][0].x);
+            const float at = __uint_as_float(tr[s][0].x);
+            const float bwj = __uint_as_float(BF16 ? tr[s][0].w : tr[s][0].y) * wj;   // b_t * w_j
             f32x4 v4;
             if constexpr (BF16)
                 v4 = v_chunk(make_uint2(tr[s][0].y, tr[s][0].z));
