@@ -89,16 +89,19 @@ template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t x)
 {
     static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "xor distance");
+    // mov_dpp has no "old" operand to initialise; every lane that is selected
+    // below reads a valid source lane
+    const int xi = (int)x;
     if constexpr (J == 1) {
-        return __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
     } else if constexpr (J == 2) {
-        return __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
     } else if constexpr (J == 4) {
-        const uint32_t up = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0xF, false);  // row_shl:4
-        const uint32_t dn = __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+        const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x104, 0xF, 0xF, true);  // row_shl:4
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x114, 0xF, 0xF, true);  // row_shr:4
         return (lane_id() & 4) ? dn : up;
     } else if constexpr (J == 8) {
-        return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, true);  // row_ror:8
     } else if constexpr (J == 16) {
         const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
         return (lane_id() & 16) ? s[0] : s[1];

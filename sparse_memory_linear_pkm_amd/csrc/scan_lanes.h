@@ -24,7 +24,7 @@ __device__ __forceinline__ f32x4 add_dpp(f32x4 x)
     f32x4 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        r[e] = x[e] + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[e]), C, 0xF, 0xF, false));
+        r[e] = x[e] + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[e]), C, 0xF, 0xF, true));
     return r;
 }
 
