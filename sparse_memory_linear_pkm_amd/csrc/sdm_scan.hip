@@ -25,7 +25,10 @@ static int scan_lanes_q(int W, int R)
 // segment that still gives every CU a workgroup wins (whole 128-byte lines
 // per access); a workgroup holds D * G * 4 KB of LDS (16 KB of gathered rows
 // per step in flight and a ring of the rows written by the last 2D steps,
-// per 8 waves), so D = 2 lets two 8-wave workgroups share a CU.
+// per 8 waves), so D = 2 lets two 8-wave workgroups share a CU.  Narrower
+// workgroups run one wave per SIMD, whose steps are long enough that D = 4
+// hides the gathers; a deeper pipeline would only widen the forwarding
+// window the preparation pass searches.
 struct LanesShape {
     int G, D;
 };
@@ -36,7 +39,7 @@ static LanesShape scan_lanes_shape(int64_t chunks)   // chunks = B * H * d_v / 4
     if (chunks / 8 >= 2 * kCUs) return {8, 2};
     if (chunks / 8 >= kCUs) return {8, 4};
     if (chunks / 4 >= kCUs) return {4, 4};
-    return {2, 8};
+    return {2, 4};
 }
 
 // Workspace: the three streams of the preparation pass, each 256-byte

@@ -381,7 +381,7 @@ static hipError_t launch_lanes_q(const ScanArgs &A, bool bf16, const ScanStreams
     SDM_LANES_GD(8, 2)
     SDM_LANES_GD(8, 4)
     SDM_LANES_GD(4, 4)
-    SDM_LANES_GD(2, 8)
+    SDM_LANES_GD(2, 4)
 #undef SDM_LANES_GD
     return hipErrorInvalidValue;
 }
