@@ -262,7 +262,9 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
             const int rs = (int)((uint64_t)step % (2 * D));   // ring slot of this step
             // ---- this step's gathers (every wave's share) and records ----
             wait_vmcnt<(D - 1) * NVM>();
-            asm volatile("" ::: "memory");
+            // this wave's LDS writes of the previous step complete before the
+            // barrier (a workgroup-scope publish of LDS needs lgkmcnt(0))
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             f32x4 gw, gr;
@@ -331,8 +333,9 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
             // a later token of this step writes the same row: its store is dropped
             if (wave == 0) supf[lane] = code & 0x8000u;
             // ---- stores: whole segments of the written rows (every wave's
-            // chunks), and this wave's chunk of the outputs ----
-            asm volatile("" ::: "memory");
+            // chunks), and this wave's chunk of the outputs; the ring rows
+            // and flags written above are complete before the barrier ----
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             {
