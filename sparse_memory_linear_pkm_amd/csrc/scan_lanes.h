@@ -66,6 +66,26 @@ __device__ __forceinline__ f32x4 weighted_rows(float w, f32x4 x)
     return group_sum<Q>(mul4(w, x));
 }
 
+// Bitwise OR over the aligned group of Q lanes that holds this lane, left in
+// every lane of the group.
+template <int Q>
+__device__ __forceinline__ uint32_t group_or(uint32_t x)
+{
+    if constexpr (Q >= 2) x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+    if constexpr (Q >= 4) x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
+    if constexpr (Q >= 8) x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true);
+    if constexpr (Q >= 16) x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, true);
+    if constexpr (Q >= 32) {
+        const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        x = s[0] | s[1];
+    }
+    if constexpr (Q >= 64) {
+        const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        x = s[0] | s[1];
+    }
+    return x;
+}
+
 // The new value of a written row x with weight w: a x + bw (v - a p), where
 // bw = b * w (one fp32 product, formed by the caller).
 __device__ __forceinline__ f32x4 written_row(f32x4 x, float a, float bw, f32x4 v, f32x4 p)

@@ -13,7 +13,7 @@
 //     wrote the slot, and the position j' of the slot in that token's write
 //     list: code = delta * 64 + j' (window <= 511, so code < 0x7FFF; 0x7FFF
 //     for write positions, 0xFFFF for read positions: none);
-// and, for write positions, bit 15: a later token up to the end of the scan
+// and, for write positions, whether a later token up to the end of the scan
 // step D - 1 steps after u's (tokens up to K*floor(u/K) + D*K - 1) writes the
 // same slot, so this write need not be stored (the later one is; rows read in
 // between are forwarded).  Stores of one row are then at least D steps apart,
@@ -29,8 +29,10 @@
 //   gofs[chain][t][j]:          byte offsets of write row j and read row j in
 //                               the (b, h) memory plus 2^30 (0: no row), so a
 //                               zero read past the end maps to an offset at
-//                               or beyond 2^31, outside every memory (the
-//                               lane record repeats the write offset)
+//                               or beyond 2^31, outside every memory; bit 31
+//                               of the write offset set: the write is
+//                               superseded (not stored).  The lane record
+//                               repeats the write offset without that bit.
 //   tok[chain][t][c], c < d_v/4: {a_t, v_t[4c .. 4c+3], b_t} as one 16-byte
 //                               record (bf16 v: 2 words) or two (fp32 v:
 //                               {a_t, b_t, 0, 0}, then the 4 values)
@@ -133,8 +135,8 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
             if (v >= 0) cw = (uint32_t)((ul - (v >> 6)) * 64 + (v & 63));
             const int64_t last = (t / A.K) * A.K + look;   // <= t + look
             const int hi = (int)((last < tend - 1 ? last : tend - 1) - tlo);
-            if (hi > ul && latest(slot, ul + 1, hi) >= 0) cw |= 0x8000u;
             gw = (uint32_t)slot * rowb + kRowBias;
+            if (hi > ul && latest(slot, ul + 1, hi) >= 0) gw |= 0x80000000u;
             ww = A.wwt[row * W + j];
         }
         if (j < R) {
@@ -145,7 +147,7 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
             wr = A.rwt[row * R + j];
         }
         const int64_t s = (ch * A.T + t) * Q + j;
-        A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(ww), __float_as_uint(wr), gw);
+        A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(ww), __float_as_uint(wr), gw & 0x7FFFFFFFu);
         A.st.gofs[s] = make_uint2(gw, gr);
     }
     // token records: a_t and the 4-column chunks of v_t

@@ -25,9 +25,12 @@
 //
 // Tokens of one step run concurrently unless one of them needs a row that
 // an earlier token of the same step writes (forwarding code with 1 <= delta
-// <= its position in the step); such a step runs its K tokens one after the
-// other (exact, rare for scattered addressing).  Two tokens of a step never
+// <= its position in the step); such a step runs in rounds, a token
+// committing once the tokens it takes rows from have (exact, rare for
+// scattered addressing, usually two rounds).  Two tokens of a step never
 // store the same row: a write superseded later in the step is dropped.
+// Every row a lane needs comes from one LDS read placed before the step's
+// compute: the gathered row, or the ring row of its latest writer.
 //
 // Latency: the gathers of step s + D are issued at the end of step s with the
 // LDS-destination form of buffer_load (one 1 KB instruction per row kind),
@@ -82,35 +85,24 @@ __device__ __forceinline__ uint32_t lds_addr(const T *p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T *)p;
 }
 
-// Reads this lane's 16 bytes of the gathered write row (at addr) and read
-// row (OFF bytes further) and waits for them inside the asm block (the
+// LDS reads written as asm blocks that wait for their own results: the
 // compiler would otherwise wait for every outstanding LDS-destination load
-// before an LDS read it cannot tell apart).
-template <int OFF>
-__device__ __forceinline__ void read_gathered(f32x4 &xw, f32x4 &xr, uint32_t addr)
+// before an LDS read it cannot tell apart from their targets.
+__device__ __forceinline__ void lds_read2(f32x4 &x, f32x4 &y, uint32_t ax, uint32_t ay)
 {
     asm volatile("ds_read_b128 %0, %2\n\t"
-                 "ds_read_b128 %1, %2 offset:%3\n\t"
+                 "ds_read_b128 %1, %3\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(xw), "=&v"(xr)
-                 : "v"(addr), "n"(OFF)
+                 : "=&v"(x), "=&v"(y)
+                 : "v"(ax), "v"(ay)
                  : "memory");
 }
 
-// One 16-byte LDS read that waits for itself (see read_gathered).
 __device__ __forceinline__ f32x4 lds_read16(uint32_t addr)
 {
     f32x4 x;
     asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(addr) : "memory");
     return x;
-}
-
-// Buffer resource over the records of tokens [u0, u0 + n) of one chain; token
-// u0 + i starts at base + i * tstride bytes and its record is rec bytes.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t win_rsrc(const void *base, int64_t n, uint32_t tstride,
-                                                           uint32_t rec)
-{
-    return make_rsrc(base, n > 0 ? (uint32_t)(n - 1) * tstride + rec : 0u);
 }
 
 // (group, member) of workgroup `id` for ngroups groups of nmem members, such
@@ -155,8 +147,6 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
     // read one chunk of 64 consecutive rows, spread over the LDS banks).
     __shared__ f32x4 gath[D][2][kWave][G];      // gathered write / read rows of the steps in flight
     __shared__ f32x4 ring[2 * D][kWave][G];     // rows written by the last 2D steps
-    __shared__ uint32_t supf[kWave];            // this step: write row superseded within the step
-    constexpr int kReadOff = (int)sizeof(gath[0][0]);   // read rows follow the write rows
 
     const uint32_t d_v = (uint32_t)A.d_v;
     const uint32_t nline = d_v / 32u;            // 128-byte lines per row
@@ -204,7 +194,7 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
     uint4 lr[D];              // lane record of step s
     uint4 tr[D][NTR];         // token record (this wave's chunk) of step s
     uint2 go[D];              // row offsets (memory layout) of step s + D
-    uint32_t ofw[D];          // write-row offsets (memory layout) of step s, for its store
+    uint32_t ofw[D];          // store offsets of the write rows (memory layout) of step s
 
     auto idx_load = [&](int sl) __attribute__((always_inline)) {
         const auto x = __builtin_amdgcn_raw_buffer_load_b64(R2, p2, 0, 0);
@@ -225,11 +215,18 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
     // this wave's share of the gathers of a step (rows RPW*w .. RPW*w+RPW-1 of
     // the write and of the read rows, whole segments) into gath[sl], from the
     // row offsets in go[sl]; a zero offset record lands at or beyond 2^31
+    // (bit 31 of a write-row offset marks a write superseded within the next
+    // D - 1 steps: its store offset lands past the range and is dropped)
     auto gathers = [&](int sl) __attribute__((always_inline)) {
         ofw[sl] = go[sl].x - kRowBias + segb + cg * 16u;
+        // formed here, so that the row offset register is free for the next
+        // load into the same ring slot (a copy at the loop edge would wait
+        // for that load)
+        asm volatile("" : "+v"(ofw[sl]));
+        const uint32_t ofg = (go[sl].x & 0x7FFFFFFFu) - kRowBias + segb + cg * 16u;
         const uint32_t ofr = go[sl].y - kRowBias + segb + cg * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][0][wave * RPW][0], 16, ofw[sl], 0, 0, 0);
+            Mrs, (__attribute__((address_space(3))) void *)&gath[sl][0][wave * RPW][0], 16, ofg, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             Mrs, (__attribute__((address_space(3))) void *)&gath[sl][1][wave * RPW][0], 16, ofr, 0, 0, 0);
     };
@@ -262,15 +259,35 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
             const int rs = (int)((uint64_t)step % (2 * D));   // ring slot of this step
             // ---- this step's gathers (every wave's share) and records ----
             wait_vmcnt<(D - 1) * NVM>();
+            const uint32_t code = ~lr[s].x;   // stored inverted: a load past the range reads "none"
+            const float wj = __uint_as_float(lr[s].y), rj = __uint_as_float(lr[s].z);
+            const uint32_t cw = code & 0x7FFFu, cr = code >> 16;
+            const int dw = (int)(cw >> 6), dr = (int)(cr >> 6);
+            const bool hw = cw != 0x7FFFu, hr = cr != 0xFFFFu;
+            // sources inside this step: the writer is an earlier token of it
+            const bool inw = hw && dw <= i, inr = hr && dr >= 1 && dr <= i;
+            const int64_t u = step * K + i;   // this lane's token
+            // LDS address of this wave's chunk of the row written by token
+            // u - d at list position c (ring slot of that token's step)
+            auto ring_addr = [&](int d, uint32_t c) {
+                const int64_t up = u - d;
+                const int r = (((int)up & (K - 1)) << LQ) | (int)(c & (Q - 1));
+                return lds_addr(&ring[(uint32_t)(up >> LK) % (uint32_t)(2 * D)][r][(wave + r) & (G - 1)]);
+            };
+            // where this lane's write and read rows come from: the gathered
+            // row, or the ring row of the latest earlier writer in the window
+            const uint32_t gaw = lds_addr(&gath[s][0][lane][pos_own]), gar = lds_addr(&gath[s][1][lane][pos_own]);
+            const uint32_t aw = hw && !inw ? ring_addr(dw, cw) : gaw;
+            const uint32_t ar = hr && dr > i ? ring_addr(dr, cr) : gar;
+            const bool intra = __builtin_amdgcn_ballot_w64(inw || inr) != 0;
+            const bool d0 = __builtin_amdgcn_ballot_w64(hr && dr == 0) != 0;
             // this wave's LDS writes of the previous step complete before the
             // barrier (a workgroup-scope publish of LDS needs lgkmcnt(0))
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            f32x4 gw, gr;
-            read_gathered<kReadOff>(gw, gr, lds_addr(&gath[s][0][lane][pos_own]));
-            const uint32_t code = ~lr[s].x;   // stored inverted: a load past the range reads "none"
-            const float wj = __uint_as_float(lr[s].y), rj = __uint_as_float(lr[s].z);
+            f32x4 xw, xr;
+            lds_read2(xw, xr, aw, ar);
             const float at = __uint_as_float(tr[s][0].x);
             const float bwj = __uint_as_float(BF16 ? tr[s][0].w : tr[s][0].y) * wj;   // b_t * w_j
             f32x4 v4;
@@ -279,30 +296,12 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
             else
                 v4 = (f32x4){__uint_as_float(tr[s][NTR - 1].x), __uint_as_float(tr[s][NTR - 1].y),
                              __uint_as_float(tr[s][NTR - 1].z), __uint_as_float(tr[s][NTR - 1].w)};
-            const uint32_t cw = code & 0x7FFFu, cr = code >> 16;
-            const int dw = (int)(cw >> 6), dr = (int)(cr >> 6);
-            const bool hw = cw != 0x7FFFu, hr = cr != 0xFFFFu;
-            const int64_t u = step * K + i;   // this lane's token
-            // this wave's chunk of the row written by token u - d at position c
-            auto ring_at = [&](int d, uint32_t c) -> f32x4 & {
-                const int64_t up = u - d;
-                const int r = (((int)up & (K - 1)) << LQ) | (int)(c & (Q - 1));
-                return ring[(uint32_t)(up >> LK) % (uint32_t)(2 * D)][r][(wave + r) & (G - 1)];
-            };
             auto own_row = [&](uint32_t c) {   // this token's write at position c
                 const int r = (i << LQ) | (int)(c & (Q - 1));
                 return lds_read16(lds_addr(&ring[rs][r][(wave + r) & (G - 1)]));
             };
-            const bool any_code = __builtin_amdgcn_ballot_w64(hw || hr) != 0;
-            const bool intra = __builtin_amdgcn_ballot_w64((hw && dw <= i) || (hr && dr >= 1 && dr <= i)) != 0;
-            const bool d0 = __builtin_amdgcn_ballot_w64(hr && dr == 0) != 0;
             f32x4 o;
             if (!intra) {
-                f32x4 xw = gw, xr = gr;
-                if (any_code) {
-                    if (hw) xw = ring_at(dw, cw);
-                    if (hr && dr >= 1) xr = ring_at(dr, cr);
-                }
                 const f32x4 p = weighted_rows<Q>(wj, xw);
                 o = weighted_rows<Q>(rj, xr);
                 ring[rs][lane][pos_own] = written_row(xw, at, bwj, v4, p);
@@ -313,42 +312,47 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
                     o = weighted_rows<Q>(rj, xr);
                 }
             } else {
-                // tokens of this step one at a time; lanes of token `it` commit
-                f32x4 ok = gr;
-                for (int it = 0; it < K; ++it) {
-                    f32x4 xw = gw, xr = gr;
-                    if (hw) xw = ring_at(dw, cw);
-                    if (hr && dr >= 1) xr = ring_at(dr, cr);
-                    const f32x4 p = weighted_rows<Q>(wj, xw);
-                    const f32x4 n2 = written_row(xw, at, bwj, v4, p);
-                    if (i == it) ring[rs][lane][pos_own] = n2;
+                // Rounds: a token commits (writes its rows, takes its output)
+                // once every earlier token of the step it takes a row from has
+                // committed; the first uncommitted token is always ready, so
+                // at most K rounds, usually two.  Rows from earlier steps keep
+                // the values read above (the ring slot of step s - 2D is this
+                // step's, and committing tokens overwrite it).
+                uint32_t dep = 0;   // tokens of the step this token waits for (bit per token)
+                if (inw) dep |= 1u << (i - dw);
+                if (inr) dep |= 1u << (i - dr);
+                dep = group_or<Q>(dep);
+                const uint32_t aw2 = inw ? ring_addr(dw, cw) : gaw, ar2 = inr ? ring_addr(dr, cr) : gar;
+                uint32_t done = 0;
+                f32x4 ok = xr;
+                while (true) {
+                    const bool ready = ((dep | (1u << i)) & ~done) == (1u << i);
+                    f32x4 yw, yr;
+                    lds_read2(yw, yr, aw2, ar2);
+                    if (!inw) yw = xw;
+                    if (!inr) yr = xr;
+                    const f32x4 p = weighted_rows<Q>(wj, yw);
+                    const f32x4 n2 = written_row(yw, at, bwj, v4, p);
+                    if (ready) ring[rs][lane][pos_own] = n2;
                     wave_lds_sync();
                     const f32x4 own = own_row(cr);
-                    if (hr && dr == 0) xr = own;
-                    const f32x4 o2 = weighted_rows<Q>(rj, xr);
-                    if (i == it) ok = o2;
+                    if (hr && dr == 0) yr = own;
+                    const f32x4 o2 = weighted_rows<Q>(rj, yr);
+                    if (ready) ok = o2;
+                    const uint64_t rb = __builtin_amdgcn_ballot_w64(ready);
+#pragma unroll
+                    for (int t = 0; t < K; ++t) done |= (uint32_t)((rb >> (t * Q)) & 1u) << t;
+                    if (done == (1u << K) - 1u) break;
                 }
                 o = ok;
             }
-            // a later token of this step writes the same row: its store is dropped
-            if (wave == 0) supf[lane] = code & 0x8000u;
             // ---- stores: whole segments of the written rows (every wave's
             // chunks), and this wave's chunk of the outputs; the ring rows
-            // and flags written above are complete before the barrier ----
+            // written above are complete before the barrier ----
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            {
-                f32x4 x;
-                uint32_t sp;
-                asm volatile("ds_read_b128 %0, %2\n\t"
-                             "ds_read_b32 %1, %3\n\t"
-                             "s_waitcnt lgkmcnt(0)"
-                             : "=&v"(x), "=&v"(sp)
-                             : "v"(lds_addr(&ring[rs][rg][pg])), "v"(lds_addr(&supf[rg]))
-                             : "memory");
-                __builtin_amdgcn_raw_buffer_store_b128(x, Mrs, sp ? kOOB : ofw[s], 0, 0);
-            }
+            __builtin_amdgcn_raw_buffer_store_b128(lds_read16(lds_addr(&ring[rs][rg][pg])), Mrs, ofw[s], 0, 0);
             {
                 const int64_t rem = T - step * K;   // live tokens of this step: i < rem
                 const __amdgpu_buffer_rsrc_t Ors = make_rsrc(obase, orec);

@@ -126,10 +126,12 @@ SCAN_CASES = {
     "mixed_W12_R7": (Dims(B=2, T=333, H=5, d_k=128, n_sub=64, d_v=160, k_prime=8, W=12, R=7), 1500),
     # B*H*d_v/4 column chunks select the workgroup shape of the scan: >= 4096
     # (8 waves per workgroup, depth 2), >= 2048 (8 waves, depth 4), >= 1024
-    # (4 waves, depth 4); the cases above run 2 waves per workgroup, depth 8
+    # (4 waves, depth 4); the cases above run 2 waves per workgroup, depth 4
     "shape_g8_d2": (Dims(B=4, T=45, H=8, d_k=128, n_sub=16, d_v=512, k_prime=16, W=32, R=32), 120),
     "shape_g8_d4": (Dims(B=2, T=70, H=8, d_k=128, n_sub=16, d_v=512, k_prime=16, W=16, R=16), 100),
     "shape_g4_d4": (Dims(B=2, T=90, H=4, d_k=128, n_sub=32, d_v=512, k_prime=8, W=8, R=8), 200),
+    "shape_g8_d4_f32": (Dims(B=2, T=70, H=8, d_k=32, n_sub=16, d_v=512, k_prime=8, W=8, R=8, in_dtype="f32"), 100),
+    "shape_g8_d2_f32": (Dims(B=4, T=40, H=8, d_k=32, n_sub=16, d_v=512, k_prime=4, W=4, R=3, in_dtype="f32"), 50),
 }
 
 
