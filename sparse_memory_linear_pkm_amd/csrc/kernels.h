@@ -7,12 +7,36 @@
 
 namespace sdm {
 
+// The staircase of the k' x k' merge: pairs (a, b) of half-list ranks with
+// (a + 1)(b + 1) <= n.  Each of the (a + 1)(b + 1) pairs (a' <= a, b' <= b)
+// scores at least as high as (a, b) (fp32 addition is monotone), so outside
+// ties the top n lie inside it.  Entries (a << 8 | b) grouped by a, b
+// ascending; the count is >= n for every k', n <= 64.  It depends only on
+// (k', n), so the host builds it once per call and passes it by value.
+constexpr int kMaxStair = 288;   // >= max over k', n <= 64 of the staircase size (280)
+
+struct Staircase {
+    uint16_t e[kMaxStair];
+    int count;
+};
+
+inline void make_staircase(int kp, int n, Staircase &st)
+{
+    int k = 0;
+    for (int a = 0; a < kp; ++a) {
+        const int cnt = n / (a + 1) < kp ? n / (a + 1) : kp;
+        for (int b = 0; b < cnt; ++b) st.e[k++] = (uint16_t)((a << 8) | b);
+    }
+    st.count = k;
+}
+
 struct AddressKind {
     const void *x;   // [B*T*H, d_k] keys (write) or queries (read)
     const void *C;   // [H, 2, n_sub, d_k/2] codebook
     int32_t *idx;    // [B*T*H, n_out]
     float *wt;       // [B*T*H, n_out]
     int n_out;       // W or R
+    Staircase stair; // merge candidates for (k', n_out)
 };
 
 struct AddressArgs {
@@ -62,6 +86,7 @@ struct DecodeArgs {
     float *o;
     int32_t *widx_out, *ridx_out;
     int B, H, d_k, n_sub, d_v, k_prime, W, R, N;
+    Staircase stair[2];   // merge candidates for (k', W) and (k', R)
 };
 
 struct InitArgs {

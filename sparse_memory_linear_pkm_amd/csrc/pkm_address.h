@@ -12,11 +12,11 @@
 #pragma once
 
 #include "device_common.h"
+#include "kernels.h"
 
 namespace sdm {
 
 constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimension)
-constexpr int kMaxStair = 288;    // >= max over k', n <= 64 of the staircase size (280)
 
 // fp32 half scores S[r][u] = <x_r[c*half : (c+1)*half], C[h][c][u]> for the
 // first `srows` rows of one 16-row tile, written to LDS (row stride n_sub) as
@@ -94,26 +94,11 @@ struct HalfEntry {
     uint32_t index;
 };
 
-// The staircase of the k' x k' merge: pairs (a, b) of half-list ranks with
-// (a + 1)(b + 1) <= n.  Each of the (a + 1)(b + 1) pairs (a' <= a, b' <= b)
-// scores at least as high as (a, b) (fp32 addition is monotone), so outside
-// ties the top n lie inside it.  Entries (a << 8 | b) grouped by a; the
-// count (>= n for every k', n <= 64) is returned in every thread.  Called
-// by all threads of the block (a = the thread's index in it); the caller
-// synchronises before use.
-__device__ __forceinline__ int build_staircase(int kp, int n, uint16_t *stair, int a)
+// Copy of a staircase into LDS by all threads of the block (the caller
+// synchronises before use).
+__device__ __forceinline__ void load_staircase(const Staircase &st, uint16_t *stair)
 {
-    int total = 0, off = 0;
-    for (int i = 0; i < kp; ++i) {
-        const int cnt = min(kp, n / (i + 1));
-        if (i < a) off += cnt;
-        total += cnt;
-    }
-    if (a < kp) {
-        const int cnt = min(kp, n / (a + 1));
-        for (int b = 0; b < cnt; ++b) stair[off + b] = (uint16_t)((a << 8) | b);
-    }
-    return total;
+    for (int e = threadIdx.x; e < st.count; e += blockDim.x) stair[e] = st.e[e];
 }
 
 // Top-k' of NR rows of half scores, one wave.  Row r's n_sub score bits are

@@ -87,7 +87,8 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
                               ((int64_t)h * 2 * n_sub * half) * esz;
     const int64_t row_stride = (int64_t)args.H * args.d_k;
 
-    const int nstair = build_staircase(kp, n, stair, threadIdx.x);
+    load_staircase(K.stair, stair);   // ordered before use by the barriers below
+    const int nstair = K.stair.count;
 
     int rows[kRowsPerWave];
 #pragma unroll

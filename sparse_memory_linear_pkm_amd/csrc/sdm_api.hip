@@ -141,8 +141,10 @@ sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const 
         return fail(SDM_ERR_INVALID_ARG, "output buffers overlap");
     if (rows == 0) return SDM_OK;
     sdm::AddressArgs A{};
-    A.kind[0] = {k, C_w, widx, wwt, (int)d->W};
-    A.kind[1] = {q, C_r, ridx, rwt, (int)d->R};
+    A.kind[0] = {k, C_w, widx, wwt, (int)d->W, {}};
+    A.kind[1] = {q, C_r, ridx, rwt, (int)d->R, {}};
+    sdm::make_staircase((int)d->k_prime, (int)d->W, A.kind[0].stair);
+    sdm::make_staircase((int)d->k_prime, (int)d->R, A.kind[1].stair);
     A.BT = d->B * d->T;
     A.H = (int)d->H;
     A.d_k = (int)d->d_k;
@@ -244,6 +246,8 @@ sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C
     A.widx_out = widx_out; A.ridx_out = ridx_out;
     A.B = (int)d->B; A.H = (int)d->H; A.d_k = (int)d->d_k; A.n_sub = (int)d->n_sub;
     A.d_v = (int)d->d_v; A.k_prime = (int)d->k_prime; A.W = (int)d->W; A.R = (int)d->R; A.N = (int)N;
+    sdm::make_staircase(A.k_prime, A.W, A.stair[0]);
+    sdm::make_staircase(A.k_prime, A.R, A.stair[1]);
     hipError_t e = sdm::launch_decode(A, d->in_dtype == SDM_BF16, as_stream(stream));
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_decode_step launch");
 }

@@ -69,8 +69,8 @@ __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
             score_half_tile<BF16>(xb, A.d_k, 1, 1, Cb + (size_t)c * n_sub * half * esz, c, half,
                                   n_sub, S + (kind * 2 + c) * n_sub);
     }
-    const int nstair_w = build_staircase(kp, (int)A.W, stair, threadIdx.x);
-    const int nstair_r = build_staircase(kp, (int)A.R, stair + kMaxStair, threadIdx.x);
+    load_staircase(A.stair[0], stair);
+    load_staircase(A.stair[1], stair + kMaxStair);
     __syncthreads();
     // B. per-half top-k': wave w takes list w (kind w / 2, half w % 2)
     {
@@ -93,8 +93,7 @@ __global__ void __launch_bounds__(256) sdm_decode_kernel(DecodeArgs A)
         const HalfEntry *const L1[1] = {L + (kind * 2 + 1) * kp};
         int slot[1];
         float wt[1];
-        merge_softmax<1>(L0, L1, kp, n_sub, n, stair + kind * kMaxStair, kind ? nstair_r : nstair_w,
-                         wscr, slot, wt);
+        merge_softmax<1>(L0, L1, kp, n_sub, n, stair + kind * kMaxStair, A.stair[kind].count, wscr, slot, wt);
         fidx[kind * kWave + lane] = slot[0];
         fwt[kind * kWave + lane] = wt[0];
         int32_t *out = kind ? A.ridx_out : A.widx_out;
