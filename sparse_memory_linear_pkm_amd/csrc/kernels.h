@@ -107,7 +107,6 @@ int scan_prep_hash_log2(int W, int window, int lookahead);
 hipError_t launch_scan_lanes(const ScanArgs &args, bool bf16, const ScanStreams &st, int Q, int G, int D,
                              hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, bool bf16, hipStream_t stream);
-size_t decode_smem_bytes(int n_sub, int k_prime);
 hipError_t launch_state_init(const InitArgs &args, hipStream_t stream);
 
 }  // namespace sdm

@@ -28,7 +28,10 @@ constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimensio
 // of the block take part; the caller synchronises before reading S.
 //   x: base of the tile's first row; consecutive tile rows are row_stride
 //      elements apart.
-template <bool BF16>
+//   NB: sub-key tiles whose codebook loads a wave issues together (a
+//      latency-bound caller with few waves wants many in flight; the result
+//      does not depend on NB).
+template <bool BF16, int NB = 1>
 __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_stride, int nrows,
                                                 int srows,
                                                 const void *Cc /* [n_sub, half] of (h, c) */,
@@ -51,24 +54,34 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
             av[kk] = (bf16x8){};
             if (kk < nk && r < nrows) av[kk] = *reinterpret_cast<const bf16x8 *>(xr + kk * 32 + kg * 8);
         }
-        for (int st = wave; st * 16 < n_sub; st += nwaves) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int u = st * 16 + r;    // sub-key (B column) of this lane
-            const uint16_t *cr = C16 + (int64_t)u * half;
+        for (int st0 = wave * NB; st0 * 16 < n_sub; st0 += nwaves * NB) {
+            f32x4 acc[NB];
+#pragma unroll
+            for (int t = 0; t < NB; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
                 if (kk < nk) {
-                    bf16x8 bv = (bf16x8){};
-                    if (u < n_sub) bv = *reinterpret_cast<const bf16x8 *>(cr + kk * 32 + kg * 8);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], bv, acc, 0, 0, 0);
+                    bf16x8 bv[NB];
+#pragma unroll
+                    for (int t = 0; t < NB; ++t) {
+                        const int u = (st0 + t) * 16 + r;   // sub-key (B column) of this lane
+                        bv[t] = (bf16x8){};
+                        if (u < n_sub) bv[t] = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)u * half + kk * 32 + kg * 8);
+                    }
+#pragma unroll
+                    for (int t = 0; t < NB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], bv[t], acc[t], 0, 0, 0);
                 }
             }
             // D[i][j]: lane holds column j = lane & 15 (sub-key), rows 4*(lane>>4) + e
-            if (u < n_sub) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 4 * kg + e;
-                    if (row < srows) S[row * n_sub + u] = score_bits(acc[e]);
+            for (int t = 0; t < NB; ++t) {
+                const int u = (st0 + t) * 16 + r;
+                if (u < n_sub) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = 4 * kg + e;
+                        if (row < srows) S[row * n_sub + u] = score_bits(acc[t][e]);
+                    }
                 }
             }
         }

@@ -281,6 +281,53 @@ def test_end_to_end_prefill(sdm, torch, name):
                 np.testing.assert_array_equal(M_gpu[b, h][~wm], x["M0"][h][~wm])
 
 
+def test_decode_reads_own_writes(sdm, torch):
+    """Tokens whose read slots are their own write slots (q = k with one
+    shared codebook): the read must see the new rows.  B = 5 also leaves a
+    partly filled tile of sequences.  Against the oracle and, bit for bit,
+    against the prefill of the same tokens."""
+    d = Dims(B=5, T=4, H=3, d_k=128, n_sub=32, d_v=96, k_prime=8, W=8, R=6)
+    note(f"decode own writes {d}")
+    x = synth.make_inputs(d, seed=34)
+    x["C_r"] = x["C_w"].copy()
+    x["q"][:, 0::2] = x["k"][:, 0::2]
+    d1 = d.replace(T=1)
+    dims1 = gpu_dims(d1)
+    dx = {k: to_dev(v) for k, v in x.items()}
+    M = sdm.state_init(dx["M0"], dims1)
+    outs, widxs, ridxs = [], [], []
+    import torch as T
+    for t in range(d.T):
+        wo = T.empty((d.B, d.H, d.W), dtype=T.int32, device="cuda")
+        ro = T.empty((d.B, d.H, d.R), dtype=T.int32, device="cuda")
+        args = [dx[k][:, t].contiguous() for k in ("k", "q")]
+        rest = [dx[k][:, t].contiguous() for k in ("v", "a", "b")]
+        outs.append(sdm.decode_step(M, *args, dx["C_w"], dx["C_r"], *rest, dims1, widx_out=wo, ridx_out=ro))
+        widxs.append(wo)
+        ridxs.append(ro)
+    T.cuda.synchronize()
+    o_dec = np.stack([to_host(o) for o in outs], 1)
+    w_dec = np.stack([to_host(w) for w in widxs], 1)
+    r_dec = np.stack([to_host(r) for r in ridxs], 1)
+    # every even token reads R of its own W write slots
+    assert all(np.isin(r_dec[b, t, h], w_dec[b, t, h]).all()
+               for b in range(d.B) for t in range(0, d.T, 2) for h in range(d.H))
+    ow, oww, orr, orw = oracle.address(x["k"], x["q"], x["C_w"], x["C_r"], d)
+    if np.array_equal(w_dec, ow) and np.array_equal(r_dec, orr):
+        Mo = np.broadcast_to(x["M0"][None], (d.B,) + x["M0"].shape).copy()
+        o_ref = oracle.scan(Mo, ow, oww, orr, orw, x["v"], x["a"], x["b"], d)
+        assert_close_rms(o_dec, o_ref, what="decode o")
+    dims = gpu_dims(d)
+    widx, wwt, ridx, rwt = sdm.pkm_address(dx["k"], dx["q"], dx["C_w"], dx["C_r"], dims)
+    M2 = sdm.state_init(dx["M0"], dims)
+    o2 = sdm.scan_forward(M2, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], dims)
+    T.cuda.synchronize()
+    np.testing.assert_array_equal(w_dec, to_host(widx))
+    np.testing.assert_array_equal(r_dec, to_host(ridx))
+    np.testing.assert_array_equal(o_dec, to_host(o2))
+    np.testing.assert_array_equal(to_host(M), to_host(M2))
+
+
 def test_decode_matches_oracle_and_prefill(sdm, torch):
     d = Dims(B=4, T=6, H=2, d_k=128, n_sub=64, d_v=64, k_prime=8, W=8, R=8)
     note(f"decode {d}")
