@@ -21,7 +21,14 @@ __global__ void __launch_bounds__(256) sdm_state_init_kernel(InitArgs A)
     f32x4 *dst = reinterpret_cast<f32x4 *>(A.M);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
         const f32x4 x = __builtin_nontemporal_load(src + i);
-        for (int64_t b = 0; b < A.B; ++b) __builtin_nontemporal_store(x, dst + b * n4 + i);
+        // copies in a block-rotated order, so that the stores in flight at
+        // any moment spread over all B copies (the copies of one chunk are
+        // a large power-of-two stride apart and would otherwise tend to hit
+        // the same HBM channel together)
+        for (int64_t k = 0; k < A.B; ++k) {
+            const int64_t b = (k + blockIdx.x) % A.B;
+            __builtin_nontemporal_store(x, dst + b * n4 + i);
+        }
     }
 }
 
@@ -30,7 +37,7 @@ hipError_t launch_state_init(const InitArgs &A, hipStream_t stream)
     if (A.B == 0 || A.per_seq == 0) return hipSuccess;
     const int64_t n4 = A.per_seq / 4;
     int64_t blocks = (n4 + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > (1 << 20)) blocks = 1 << 20;   // one 16-byte chunk per thread, then a grid-stride loop
     hipLaunchKernelGGL(sdm_state_init_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, A);
     return hipGetLastError();
 }
