@@ -31,7 +31,7 @@ constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimensio
 //   NB: sub-key tiles whose codebook loads a wave issues together (a
 //      latency-bound caller with few waves wants many in flight; the result
 //      does not depend on NB).
-template <bool BF16, int NB = 1>
+template <bool BF16, int NB = 1, int NK = 0>
 __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_stride, int nrows,
                                                 int srows,
                                                 const void *Cc /* [n_sub, half] of (h, c) */,
@@ -45,28 +45,38 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
         const int nwaves = nthreads / kWave;
         const int r = lane & 15;          // A row / B column handled by this lane
         const int kg = lane >> 4;         // which 8-wide k group of the 32
-        const uint16_t *xr = static_cast<const uint16_t *>(x) + (int64_t)r * row_stride + c * half;
+        // rows past nrows and sub-keys past n_sub load a valid neighbour and
+        // are zeroed (no branches around the loads)
+        const uint16_t *xr = static_cast<const uint16_t *>(x) + (int64_t)max(min(r, nrows - 1), 0) * row_stride + c * half;
+        const bool rlive = r < nrows;
         const uint16_t *C16 = static_cast<const uint16_t *>(Cc);
-        const int nk = half / 32;         // <= 8 (d_k <= 512)
-        bf16x8 av[8];
+        // k-steps of 32: a compile-time count when NK > 0 (d_k = 64 * NK), else half / 32 (<= 8)
+        constexpr int KMAX = NK > 0 ? NK : 8;
+        const int nk = NK > 0 ? NK : half / 32;
+        const bf16x8 zero = (bf16x8){};
+        bf16x8 av[KMAX];
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            av[kk] = (bf16x8){};
-            if (kk < nk && r < nrows) av[kk] = *reinterpret_cast<const bf16x8 *>(xr + kk * 32 + kg * 8);
+        for (int kk = 0; kk < KMAX; ++kk) {
+            av[kk] = zero;
+            if (NK > 0 || kk < nk) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xr + kk * 32 + kg * 8);
+                av[kk] = rlive ? a : zero;
+            }
         }
         for (int st0 = wave * NB; st0 * 16 < n_sub; st0 += nwaves * NB) {
             f32x4 acc[NB];
 #pragma unroll
             for (int t = 0; t < NB; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                if (kk < nk) {
+            for (int kk = 0; kk < KMAX; ++kk) {
+                if (NK > 0 || kk < nk) {
                     bf16x8 bv[NB];
 #pragma unroll
                     for (int t = 0; t < NB; ++t) {
                         const int u = (st0 + t) * 16 + r;   // sub-key (B column) of this lane
-                        bv[t] = (bf16x8){};
-                        if (u < n_sub) bv[t] = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)u * half + kk * 32 + kg * 8);
+                        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)min(u, n_sub - 1) * half +
+                                                                          kk * 32 + kg * 8);
+                        bv[t] = u < n_sub ? b : zero;
                     }
 #pragma unroll
                     for (int t = 0; t < NB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], bv[t], acc[t], 0, 0, 0);

@@ -42,7 +42,8 @@ __host__ __device__ inline AddrLds addr_lds_layout(int n_sub, int kp)
     return o;
 }
 
-template <bool BF16>
+// NK: compile-time k-steps of the scoring tile (d_k = 64 * NK), 0 = any d_k
+template <bool BF16, int NK>
 __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, int ntiles)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -96,7 +97,7 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
 
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        score_half_tile<BF16>(xb, row_stride, nrows, kTileRows,
+        score_half_tile<BF16, 1, NK>(xb, row_stride, nrows, kTileRows,
                               Cb + (int64_t)c * n_sub * half * esz, c, half, n_sub, S);
         __syncthreads();
         uint64_t keys[kRowsPerWave];
@@ -141,16 +142,20 @@ hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t st
     const int64_t grid = ntiles * 2 * args.H;
     if (ntiles > INT32_MAX || grid > UINT32_MAX) return hipErrorInvalidValue;
     const size_t smem = address_smem_bytes(args.n_sub, args.k_prime);
-    const void *fn = bf16 ? (const void *)pkm_score_topk_kernel<true>
-                          : (const void *)pkm_score_topk_kernel<false>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    if (bf16)
-        hipLaunchKernelGGL(pkm_score_topk_kernel<true>, dim3((unsigned)grid), dim3(256), smem, stream,
-                           args, (int)ntiles);
+    auto launch = [&](auto kern) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, stream, args, (int)ntiles);
+        return hipSuccess;
+    };
+    hipError_t e;
+    if (!bf16)
+        e = launch(pkm_score_topk_kernel<false, 0>);
+    else if (args.d_k == 128)
+        e = launch(pkm_score_topk_kernel<true, 2>);
     else
-        hipLaunchKernelGGL(pkm_score_topk_kernel<false>, dim3((unsigned)grid), dim3(256), smem,
-                           stream, args, (int)ntiles);
+        e = launch(pkm_score_topk_kernel<true, 0>);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -65,35 +65,38 @@ __device__ __forceinline__ f32x4 lane_fetch(f32x4 x, int src)
 // k-steps); larger keys take score_half_tile.
 //   x[kind]: the tile's first input row of that kind; S[kind]: its two
 //   half-score lists ([c][srows][n_sub]).
-template <int NKIND, int NB>
+template <int NKIND, int NB, int NK>
 __device__ __forceinline__ void score_batched(const uint16_t *const (&x)[NKIND], int64_t row_stride, int nrows,
                                               int srows, const uint16_t *C, int half, int n_sub,
                                               uint32_t *const (&S)[NKIND])
 {
+    static_assert(NK == 1 || NK == 2, "one or two k-steps (d_k = 64 * NK)");
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
     const int r = lane & 15, kg = lane >> 4;
-    const int nk = half / 32;   // 1 or 2
+    // rows past nrows and sub-keys past n_sub load a valid neighbour and are
+    // zeroed (no branches around the loads)
+    const int rr = max(min(r, nrows - 1), 0);
+    const bool rlive = r < nrows;
+    const bf16x8 zero = (bf16x8){};
     for (int st0 = wave * NB; st0 * 16 < n_sub; st0 += nwaves * NB) {
-        bf16x8 av[NKIND][2][2], bv[2][NB][2];
+        bf16x8 av[NKIND][2][NK], bv[2][NB][NK];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
+            for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
                 for (int q = 0; q < NKIND; ++q) {
-                    av[q][c][kk] = (bf16x8){};
-                    if (kk < nk && r < nrows)
-                        av[q][c][kk] =
-                            *reinterpret_cast<const bf16x8 *>(x[q] + (int64_t)r * row_stride + c * half + kk * 32 + kg * 8);
+                    const bf16x8 a =
+                        *reinterpret_cast<const bf16x8 *>(x[q] + (int64_t)rr * row_stride + c * half + kk * 32 + kg * 8);
+                    av[q][c][kk] = rlive ? a : zero;
                 }
 #pragma unroll
                 for (int t = 0; t < NB; ++t) {
                     const int u = (st0 + t) * 16 + r;
-                    bv[c][t][kk] = (bf16x8){};
-                    if (kk < nk && u < n_sub)
-                        bv[c][t][kk] =
-                            *reinterpret_cast<const bf16x8 *>(C + ((int64_t)c * n_sub + u) * half + kk * 32 + kg * 8);
+                    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(
+                        C + ((int64_t)c * n_sub + min(u, n_sub - 1)) * half + kk * 32 + kg * 8);
+                    bv[c][t][kk] = u < n_sub ? b : zero;
                 }
             }
         }
@@ -105,8 +108,8 @@ __device__ __forceinline__ void score_batched(const uint16_t *const (&x)[NKIND],
                 for (int t = 0; t < NB; ++t) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
-                        if (kk < nk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[q][c][kk], bv[c][t][kk], acc, 0, 0, 0);
+                    for (int kk = 0; kk < NK; ++kk)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[q][c][kk], bv[c][t][kk], acc, 0, 0, 0);
                     const int u = (st0 + t) * 16 + r;
                     if (u < n_sub) {
 #pragma unroll
@@ -151,16 +154,22 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
         const unsigned char *Cw = static_cast<const unsigned char *>(A.C_w) + coff;
         const unsigned char *Cr = static_cast<const unsigned char *>(A.C_r) + coff;
         const int64_t rs = (int64_t)A.H * A.d_k;
-        if (BF16 && half <= 64 && A.C_w == A.C_r) {
+        if (BF16 && (half == 32 || half == 64) && A.C_w == A.C_r) {
             const uint16_t *const xs[2] = {reinterpret_cast<const uint16_t *>(xk), reinterpret_cast<const uint16_t *>(xq)};
             uint32_t *const Ss[2] = {S, S + (size_t)2 * TS * n_sub};
-            score_batched<2, 2>(xs, rs, nb, TS, reinterpret_cast<const uint16_t *>(Cw), half, n_sub, Ss);
-        } else if (BF16 && half <= 64) {
+            if (half == 64)
+                score_batched<2, 2, 2>(xs, rs, nb, TS, reinterpret_cast<const uint16_t *>(Cw), half, n_sub, Ss);
+            else
+                score_batched<2, 2, 1>(xs, rs, nb, TS, reinterpret_cast<const uint16_t *>(Cw), half, n_sub, Ss);
+        } else if (BF16 && (half == 32 || half == 64)) {
             for (int kind = 0; kind < 2; ++kind) {
                 const uint16_t *const xs[1] = {reinterpret_cast<const uint16_t *>(kind ? xq : xk)};
                 uint32_t *const Ss[1] = {S + (size_t)kind * 2 * TS * n_sub};
-                score_batched<1, 4>(xs, rs, nb, TS, reinterpret_cast<const uint16_t *>(kind ? Cr : Cw), half, n_sub,
-                                    Ss);
+                const uint16_t *Ck = reinterpret_cast<const uint16_t *>(kind ? Cr : Cw);
+                if (half == 64)
+                    score_batched<1, 4, 2>(xs, rs, nb, TS, Ck, half, n_sub, Ss);
+                else
+                    score_batched<1, 4, 1>(xs, rs, nb, TS, Ck, half, n_sub, Ss);
             }
         } else {
             for (int l = 0; l < 4; ++l) {
