@@ -50,6 +50,7 @@ namespace sdm {
 
 constexpr int kPrBlock = 32;      // tokens per workgroup
 constexpr int kPrThreads = 256;
+constexpr int kPrBatch = 8;       // loads a thread issues together
 constexpr int32_t kPrEmpty = INT32_MIN;
 constexpr uint32_t kRowBias = 0x40000000u;
 
@@ -88,18 +89,37 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
     auto row_of = [&](int64_t t) { return (bb * A.T + t) * A.H + h; };
 
     for (uint32_t e = tid; e <= hmask; e += kPrThreads) keys[e] = kPrEmpty;
+    // each thread's slots of kPrBatch entries are loaded together before any
+    // of them is inserted (the loads are in flight at once); the first batch
+    // is loaded while the table is cleared
+    const int nins = nrows * W;
+    int32_t sl[kPrBatch];
+    auto load_batch = [&](int e0) {
+#pragma unroll
+        for (int u = 0; u < kPrBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            const int r = e / W, j = e - r * W;
+            sl[u] = e < nins ? A.widx[row_of(tlo + r) * W + j] : 0;
+        }
+    };
+    load_batch(tid);
     __syncthreads();
-    for (int e = tid; e < nrows * W; e += kPrThreads) {
-        const int r = e / W, j = e - r * W;
-        const int32_t slot = A.widx[row_of(tlo + r) * W + j];
-        uint32_t b = pr_hash(slot, lg);
-        while (true) {
-            const int32_t old = atomicCAS(&keys[b], kPrEmpty, slot);
-            if (old == kPrEmpty) {
-                vals[b] = ((uint32_t)r << 6) | (uint32_t)j;
-                break;
+    for (int e0 = tid; e0 < nins; e0 += kPrThreads * kPrBatch) {
+        if (e0 != tid) load_batch(e0);
+#pragma unroll
+        for (int u = 0; u < kPrBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            if (e >= nins) break;
+            const int r = e / W, j = e - r * W;
+            uint32_t b = pr_hash(sl[u], lg);
+            while (true) {
+                const int32_t old = atomicCAS(&keys[b], kPrEmpty, sl[u]);
+                if (old == kPrEmpty) {
+                    vals[b] = ((uint32_t)r << 6) | (uint32_t)j;
+                    break;
+                }
+                b = (b + 1) & hmask;
             }
-            b = (b + 1) & hmask;
         }
     }
     __syncthreads();
@@ -121,50 +141,84 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
         return best;
     };
     const int ntok = (int)(thi - t0);
-    for (int e = tid; e < ntok * Q; e += kPrThreads) {
-        const int tl = e / Q, j = e - tl * Q;
-        const int64_t t = t0 + tl;
-        const int ul = (int)(t - tlo);              // local index of this token
-        const int lo = ul - win > 0 ? ul - win : 0;
-        const int64_t row = row_of(t);
-        uint32_t cw = 0x7FFFu, cr = 0xFFFFu, gw = 0u, gr = 0u;
-        float ww = 0.f, wr = 0.f;
-        if (j < W) {
-            const int32_t slot = A.widx[row * W + j];
-            const int v = latest(slot, lo, ul - 1);
-            if (v >= 0) cw = (uint32_t)((ul - (v >> 6)) * 64 + (v & 63));
-            const int64_t last = (t / A.K) * A.K + look;   // <= t + look
-            const int hi = (int)((last < tend - 1 ? last : tend - 1) - tlo);
-            gw = (uint32_t)slot * rowb + kRowBias;
-            if (hi > ul && latest(slot, ul + 1, hi) >= 0) gw |= 0x80000000u;
-            ww = A.wwt[row * W + j];
+    // (token, position) queries, kPrBatch per thread at a time: their inputs
+    // are loaded together, then the table is probed and the records written
+    const int nq = ntok * Q;
+    for (int e0 = tid; e0 < nq; e0 += kPrThreads * kPrBatch) {
+        int32_t ws[kPrBatch], rs[kPrBatch];
+        float wv[kPrBatch], rv[kPrBatch];
+#pragma unroll
+        for (int u = 0; u < kPrBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            const int tl = e / Q, j = e - tl * Q;
+            const int64_t row = row_of(t0 + tl);
+            const bool okw = e < nq && j < W, okr = e < nq && j < R;
+            ws[u] = okw ? A.widx[row * W + j] : 0;
+            wv[u] = okw ? A.wwt[row * W + j] : 0.f;
+            rs[u] = okr ? A.ridx[row * R + j] : 0;
+            rv[u] = okr ? A.rwt[row * R + j] : 0.f;
         }
-        if (j < R) {
-            const int32_t slot = A.ridx[row * R + j];
-            const int v = latest(slot, lo, ul);
-            if (v >= 0) cr = (uint32_t)((ul - (v >> 6)) * 64 + (v & 63));
-            gr = (uint32_t)slot * rowb + kRowBias;
-            wr = A.rwt[row * R + j];
+#pragma unroll
+        for (int u = 0; u < kPrBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            if (e >= nq) break;
+            const int tl = e / Q, j = e - tl * Q;
+            const int64_t t = t0 + tl;
+            const int ul = (int)(t - tlo);              // local index of this token
+            const int lo = ul - win > 0 ? ul - win : 0;
+            uint32_t cw = 0x7FFFu, cr = 0xFFFFu, gw = 0u, gr = 0u;
+            if (j < W) {
+                const int v = latest(ws[u], lo, ul - 1);
+                if (v >= 0) cw = (uint32_t)((ul - (v >> 6)) * 64 + (v & 63));
+                const int64_t last = (t / A.K) * A.K + look;   // <= t + look
+                const int hi = (int)((last < tend - 1 ? last : tend - 1) - tlo);
+                gw = (uint32_t)ws[u] * rowb + kRowBias;
+                if (hi > ul && latest(ws[u], ul + 1, hi) >= 0) gw |= 0x80000000u;
+            }
+            if (j < R) {
+                const int v = latest(rs[u], lo, ul);
+                if (v >= 0) cr = (uint32_t)((ul - (v >> 6)) * 64 + (v & 63));
+                gr = (uint32_t)rs[u] * rowb + kRowBias;
+            }
+            const int64_t s = (ch * A.T + t) * Q + j;
+            A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(wv[u]), __float_as_uint(rv[u]),
+                                      gw & 0x7FFFFFFFu);
+            A.st.gofs[s] = make_uint2(gw, gr);
         }
-        const int64_t s = (ch * A.T + t) * Q + j;
-        A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(ww), __float_as_uint(wr), gw & 0x7FFFFFFFu);
-        A.st.gofs[s] = make_uint2(gw, gr);
     }
-    // token records: a_t and the 4-column chunks of v_t
+    // token records: a_t and the 4-column chunks of v_t (kPrBatch per thread
+    // at a time, loads first)
     const int nchunk = A.d_v / 4;
-    for (int e = tid; e < ntok * nchunk; e += kPrThreads) {
-        const int tl = e / nchunk, c = e - tl * nchunk;
-        const int64_t t = t0 + tl;
-        const int64_t row = row_of(t);
-        const uint32_t a = __float_as_uint(A.a[row]), b = __float_as_uint(A.b[row]);
-        const int64_t s = (ch * A.T + t) * nchunk + c;
-        if (A.bf16) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(A.v) + row * A.d_v + 4 * c);
-            A.st.tok[s] = make_uint4(a, v.x, v.y, b);
-        } else {
-            const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const float *>(A.v) + row * A.d_v + 4 * c);
-            A.st.tok[2 * s] = make_uint4(a, b, 0u, 0u);
-            A.st.tok[2 * s + 1] = v;
+    const int nt = ntok * nchunk;
+    for (int e0 = tid; e0 < nt; e0 += kPrThreads * kPrBatch) {
+        uint32_t av[kPrBatch], bv[kPrBatch];
+        uint4 vv[kPrBatch];
+#pragma unroll
+        for (int u = 0; u < kPrBatch; ++u) {
+            const int e = min(e0 + u * kPrThreads, nt - 1);
+            const int tl = e / nchunk, c = e - tl * nchunk;
+            const int64_t row = row_of(t0 + tl);
+            av[u] = __float_as_uint(A.a[row]);
+            bv[u] = __float_as_uint(A.b[row]);
+            if (A.bf16) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(A.v) + row * A.d_v + 4 * c);
+                vv[u] = make_uint4(v.x, v.y, 0u, 0u);
+            } else {
+                vv[u] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(A.v) + row * A.d_v + 4 * c);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPrBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            if (e >= nt) break;
+            const int tl = e / nchunk, c = e - tl * nchunk;
+            const int64_t s = (ch * A.T + t0 + tl) * nchunk + c;
+            if (A.bf16) {
+                A.st.tok[s] = make_uint4(av[u], vv[u].x, vv[u].y, bv[u]);
+            } else {
+                A.st.tok[2 * s] = make_uint4(av[u], bv[u], 0u, 0u);
+                A.st.tok[2 * s + 1] = vv[u];
+            }
         }
     }
 }
