@@ -281,6 +281,69 @@ def test_end_to_end_prefill(sdm, torch, name):
                 np.testing.assert_array_equal(M_gpu[b, h][~wm], x["M0"][h][~wm])
 
 
+def _full_path(sdm, torch, d, x):
+    """Addressing, state init and prefill scan of host inputs x; host outputs."""
+    dims = gpu_dims(d)
+    dx = {k: to_dev(v) for k, v in x.items()}
+    lists = sdm.pkm_address(dx["k"], dx["q"], dx["C_w"], dx["C_r"], dims)
+    M = sdm.state_init(dx["M0"], dims)
+    o = sdm.scan_forward(M, *lists, dx["v"], dx["a"], dx["b"], dims)
+    torch.cuda.synchronize()
+    return [to_host(t) for t in lists], to_host(o), to_host(M)
+
+
+def test_gpu_power_of_two_homogeneity_bit_exact(sdm, torch):
+    """Scaling M0 and v by 2 scales o and M by 2 exactly (every operation of
+    the update is exact under a power-of-two scale); the slots do not move."""
+    d = Dims(B=2, T=150, H=2, d_k=128, n_sub=32, d_v=64, k_prime=8, W=8, R=8)
+    note(f"homogeneity {d}")
+    x = synth.make_inputs(d, seed=41)
+    x2 = dict(x)
+    x2["M0"] = x["M0"] * np.float32(2)
+    x2["v"] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x["v"]) * np.float32(2))
+    l1, o1, M1 = _full_path(sdm, torch, d, x)
+    l2, o2, M2 = _full_path(sdm, torch, d, x2)
+    for a, b in zip(l1, l2):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(o2, o1 * np.float32(2))
+    np.testing.assert_array_equal(M2, M1 * np.float32(2))
+
+
+def test_gpu_permuting_sequences_permutes_outputs(sdm, torch):
+    """Sequences are independent: permuting the batch permutes every output
+    bit for bit (addressing tiles mix sequences, but each score depends only
+    on its own row)."""
+    d = Dims(B=5, T=37, H=3, d_k=128, n_sub=32, d_v=32, k_prime=8, W=8, R=5)
+    note(f"permutation {d}")
+    x = synth.make_inputs(d, seed=42)
+    perm = np.array([3, 0, 4, 2, 1])
+    xp = dict(x)
+    for k in ("k", "q", "v", "a", "b"):
+        xp[k] = np.ascontiguousarray(x[k][perm])
+    l1, o1, M1 = _full_path(sdm, torch, d, x)
+    l2, o2, M2 = _full_path(sdm, torch, d, xp)
+    for a, b in zip(l1, l2):
+        np.testing.assert_array_equal(b, a[perm])
+    np.testing.assert_array_equal(o2, o1[perm])
+    np.testing.assert_array_equal(M2, M1[perm])
+
+
+def test_gpu_superposition(sdm, torch):
+    """For fixed slots, weights and gates the scan is linear in (M0, v):
+    scan(M0, v) = scan(M0, 0) + scan(0, v) within the o/M tolerance."""
+    d = Dims(B=2, T=120, H=2, d_k=128, n_sub=32, d_v=64, k_prime=8, W=8, R=8)
+    note(f"superposition {d}")
+    x = synth.make_inputs(d, seed=43)
+    ad = synth.random_addressing(d, seed=43, hazard_slots=100)
+    zero_v = synth.f32_to_bf16_bits(np.zeros(x["v"].shape, np.float32))
+    M0b = np.broadcast_to(x["M0"][None], (d.B,) + x["M0"].shape).copy()
+    o_full, M_full = run_scan(sdm, torch, d, x, ad, M0b)
+    o_m, M_m = run_scan(sdm, torch, d, dict(x, v=zero_v), ad, M0b)
+    o_v, M_v = run_scan(sdm, torch, d, x, ad, np.zeros_like(M0b))
+    assert_close_rms(o_m + o_v, o_full, what="o superposition")
+    assert_close_rms(M_m + M_v, M_full, what="M superposition")
+
+
 def test_decode_reads_own_writes(sdm, torch):
     """Tokens whose read slots are their own write slots (q = k with one
     shared codebook): the read must see the new rows.  B = 5 also leaves a
