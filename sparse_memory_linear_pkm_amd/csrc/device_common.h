@@ -197,9 +197,15 @@ __device__ __forceinline__ void wave_sort_desc(T (&x)[NR])
 // every row has at most 32 of them).  When more than 64 reach tau (ties, or
 // n close to 64), that row is instead extracted one best key at a time,
 // which is exact as well.
+//
+// idx_bits > 0 declares that every key's low word is ~i for an index
+// i < 2^idx_bits; the survivors of a row are then sorted as 32-bit keys
+// ((score bits - tau + 1) << idx_bits | (2^idx_bits - 1 - i)), the same
+// order exactly, whenever every row's score bits above tau fit in the
+// remaining high bits (else as 64-bit keys).
 template <int NR, class Get>
 __device__ __forceinline__ void wave_topn(int len, int n, Get get, uint64_t *scratch,
-                                          uint64_t (&res)[NR])
+                                          uint64_t (&res)[NR], int idx_bits = 0)
 {
     const int lane = lane_id();
     if (len <= kWave) {
@@ -254,10 +260,37 @@ __device__ __forceinline__ void wave_topn(int len, int n, Get get, uint64_t *scr
         most = total[r] > most ? total[r] : most;
     }
     __builtin_amdgcn_wave_barrier();
-    if (most <= 32 && n <= 32)
+    // 32-bit keys when every row's score range above tau fits
+    bool narrow = idx_bits > 0;
+    uint32_t span[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)m[r], 0);   // the row's best score bits
+        span[r] = top - tau[r] + 1u;
+        narrow = narrow && (uint64_t)span[r] < (1ull << (32 - idx_bits));
+    }
+    if (narrow) {
+        const uint32_t imask = (1u << idx_bits) - 1u;
+        uint32_t c32[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const uint32_t hi = (uint32_t)(c[r] >> 32), i = ~(uint32_t)c[r];
+            c32[r] = c[r] ? ((hi - tau[r] + 1u) << idx_bits) | (imask - i) : 0u;
+        }
+        if (most <= 32 && n <= 32)
+            wave_sort_desc<NR, 32>(c32);
+        else
+            wave_sort_desc<NR, 64>(c32);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const uint32_t hi = (c32[r] >> idx_bits) + tau[r] - 1u, i = imask - (c32[r] & imask);
+            c[r] = c32[r] ? ((uint64_t)hi << 32) | (uint32_t)~i : 0ull;
+        }
+    } else if (most <= 32 && n <= 32) {
         wave_sort_desc<NR, 32>(c);
-    else
+    } else {
         wave_sort_desc<NR, 64>(c);
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         res[r] = lane < n ? c[r] : 0ull;

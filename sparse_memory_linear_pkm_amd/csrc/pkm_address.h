@@ -131,9 +131,11 @@ template <int NR>
 __device__ __forceinline__ void half_topk(const uint32_t *S, const int (&rows)[NR], int n_sub, int kp,
                                           uint64_t *scratch, uint64_t (&keys)[NR])
 {
+    int ib = 1;   // bits of a sub-key index
+    while ((1 << ib) < n_sub) ++ib;
     wave_topn<NR>(n_sub, kp,
                   [&](int r, int p) { return ((uint64_t)S[rows[r] * n_sub + p] << 32) | (uint32_t)~p; },
-                  scratch, keys);
+                  scratch, keys, ib);
 }
 
 // Merge of the two half lists of NR rows into the top-n slots and their
