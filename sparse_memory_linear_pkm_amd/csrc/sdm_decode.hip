@@ -74,23 +74,34 @@ __device__ __forceinline__ void score_batched(const uint16_t *const (&x)[NKIND],
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
     const int r = lane & 15, kg = lane >> 4;
-    // rows past nrows and sub-keys past n_sub load a valid neighbour and are
-    // zeroed (no branches around the loads)
-    const int rr = max(min(r, nrows - 1), 0);
-    const bool rlive = r < nrows;
+    // the input fragments are the same for every sub-key tile: loaded once,
+    // by the lanes of live rows only (the others hold zeros)
     const bf16x8 zero = (bf16x8){};
+    bf16x8 av[NKIND][2][NK];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+            for (int q = 0; q < NKIND; ++q) av[q][c][kk] = zero;
+    if (r < nrows) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+                for (int q = 0; q < NKIND; ++q)
+                    av[q][c][kk] =
+                        *reinterpret_cast<const bf16x8 *>(x[q] + (int64_t)r * row_stride + c * half + kk * 32 + kg * 8);
+    }
+    // sub-keys past n_sub load a valid neighbour and are zeroed (no branches
+    // around the codebook loads)
     for (int st0 = wave * NB; st0 * 16 < n_sub; st0 += nwaves * NB) {
-        bf16x8 av[NKIND][2][NK], bv[2][NB][NK];
+        bf16x8 bv[2][NB][NK];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
-#pragma unroll
-                for (int q = 0; q < NKIND; ++q) {
-                    const bf16x8 a =
-                        *reinterpret_cast<const bf16x8 *>(x[q] + (int64_t)rr * row_stride + c * half + kk * 32 + kg * 8);
-                    av[q][c][kk] = rlive ? a : zero;
-                }
 #pragma unroll
                 for (int t = 0; t < NB; ++t) {
                     const int u = (st0 + t) * 16 + r;
