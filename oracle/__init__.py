@@ -56,8 +56,10 @@ def _load():
         lib.orc_slot_scores.argtypes = [P, P, ctypes.POINTER(_Dims), I64, P, P, P]
         lib.orc_scan.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.POINTER(_Dims), I32]
         lib.orc_state_init.argtypes = [P, P, ctypes.POINTER(_Dims)]
+        lib.orc_gates.argtypes = [P, P, P, P, ctypes.POINTER(_Dims), P, P]
+        lib.orc_output_norm_gate.argtypes = [P, P, P, ctypes.c_double, ctypes.POINTER(_Dims), P]
         for f in (lib.orc_address, lib.orc_half_scores, lib.orc_slot_scores, lib.orc_scan,
-                  lib.orc_state_init):
+                  lib.orc_state_init, lib.orc_gates, lib.orc_output_norm_gate):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -190,3 +192,37 @@ def decode_step(M, k, q, C_w, C_r, v, a, b, d, *, nthreads: Optional[int] = None
     widx, wwt, ridx, rwt = address(ex(k), ex(q), C_w, C_r, d1, nthreads=nthreads)
     o = scan(M, widx, wwt, ridx, rwt, ex(v), ex(a), ex(b), d1, nthreads=nthreads)
     return o[:, 0], widx[:, 0], ridx[:, 0]
+
+
+def gates(a_raw, b_raw, A, dt_bias, d) -> Tuple[np.ndarray, np.ndarray]:
+    """Forget and input gates (a, b) [B,T,H] fp32 from their pre-activations
+    a_raw, b_raw [B,T,H] and the per-head decay A and time-step bias [H]."""
+    lib = _load()
+    a_raw, b_raw = (np.ascontiguousarray(x, np.float32) for x in (a_raw, b_raw))
+    A, dt_bias = (np.ascontiguousarray(x, np.float32) for x in (A, dt_bias))
+    if a_raw.shape != (d.B, d.T, d.H) or b_raw.shape != (d.B, d.T, d.H):
+        raise ValueError("a_raw / b_raw shape")
+    if A.shape != (d.H,) or dt_bias.shape != (d.H,):
+        raise ValueError("A / dt_bias shape")
+    a = np.empty((d.B, d.T, d.H), np.float32)
+    b = np.empty((d.B, d.T, d.H), np.float32)
+    dm = _dims(d)
+    _check(lib.orc_gates(_p(a_raw), _p(b_raw), _p(A), _p(dt_bias), ctypes.byref(dm), _p(a), _p(b)), "orc_gates")
+    return a, b
+
+
+def output_norm_gate(o, g, gamma, eps: float, d) -> np.ndarray:
+    """y [B,T,H,d_v] float64 (exact, before rounding to the output precision):
+    RMS norm of each o row with gain gamma [d_v], times silu(g)."""
+    lib = _load()
+    o = np.ascontiguousarray(o, np.float32)
+    g = _in(g, d)
+    gamma = np.ascontiguousarray(gamma, np.float32)
+    shp = (d.B, d.T, d.H, d.d_v)
+    if o.shape != shp or g.shape != shp or gamma.shape != (d.d_v,):
+        raise ValueError("o / g / gamma shape")
+    y = np.empty(shp, np.float64)
+    dm = _dims(d)
+    _check(lib.orc_output_norm_gate(_p(o), _p(g), _p(gamma), float(eps), ctypes.byref(dm), _p(y)),
+           "orc_output_norm_gate")
+    return y

@@ -326,3 +326,59 @@ int orc_state_init(float *M, const float *M0, const orc_dims *d)
     for (int64_t b = 0; b < d->B; ++b) memcpy(M + (size_t)b * per_seq, M0, per_seq * sizeof(float));
     return ORC_OK;
 }
+
+/* ---- around the path: the gates before it, the output norm after it ------ */
+/* The gates of one token-head, [P] Sec. 3.1 step 2 (a per-head forget gate
+ * a_t with a learnable decay A, and an input gate b_t) in the Gated DeltaNet
+ * parameterisation that [P] Sec. 4 says the decay and the time-step bias are
+ * initialised for (the pages print no formula; this is the reading):
+ *     a = exp(-A[h] * softplus(a_raw + dt_bias[h])),  softplus(z) = ln(1 + e^z)
+ *     b = 1 / (1 + e^(-b_raw))
+ * in fp64, each result rounded once to fp32.
+ *   a_raw, b_raw, a, b [B,T,H] fp32; A (>= 0), dt_bias [H] fp32. */
+static double softplus(double z)
+{
+    /* ln(1 + e^z) = z + ln(1 + e^-z): the form whose exponential cannot overflow */
+    return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
+}
+
+int orc_gates(const float *a_raw, const float *b_raw, const float *A, const float *dt_bias,
+              const orc_dims *d, float *a, float *b)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1) return ORC_EINVAL;
+    for (int64_t h = 0; h < d->H; ++h)
+        if (!isfinite(A[h]) || A[h] < 0.0f || !isfinite(dt_bias[h])) return ORC_ENONFINITE;
+    const int64_t n = d->B * d->T * d->H;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t h = i % d->H;
+        if (!isfinite(a_raw[i]) || !isfinite(b_raw[i])) return ORC_ENONFINITE;
+        a[i] = (float)exp(-(double)A[h] * softplus((double)a_raw[i] + (double)dt_bias[h]));
+        b[i] = (float)(1.0 / (1.0 + exp(-(double)b_raw[i])));
+    }
+    return ORC_OK;
+}
+
+/* The read-out's norm and output gate, [P] Sec. 3.1 step 4: each token-head's
+ * o row is RMS-normalised over its d_v features with the learned gain gamma,
+ * then multiplied element-wise by the gate activation of g (reading: the
+ * Gated DeltaNet output gate, silu(g) = g / (1 + e^-g)):
+ *     y[c] = o[c] / sqrt(mean_c' o[c']^2 + eps) * gamma[c] * silu(g[c])
+ * The exact value in fp64 (the caller rounds it to the output precision).
+ *   o [B,T,H,d_v] fp32; g [B,T,H,d_v] (bf16 bits or fp32); gamma [d_v] fp32;
+ *   y [B,T,H,d_v] fp64. */
+int orc_output_norm_gate(const float *o, const void *g, const float *gamma, double eps, const orc_dims *d,
+                         double *y)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->d_v < 1 || !(eps >= 0.0)) return ORC_EINVAL;
+    const int64_t rows = d->B * d->T * d->H, dv = d->d_v;
+    for (int64_t r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < dv; ++c) ss += (double)o[r * dv + c] * (double)o[r * dv + c];
+        const double inv = 1.0 / sqrt(ss / (double)dv + eps);
+        for (int64_t c = 0; c < dv; ++c) {
+            const double gc = load_in(g, d->in_bf16, r * dv + c);
+            y[r * dv + c] = (double)o[r * dv + c] * inv * (double)gamma[c] * (gc / (1.0 + exp(-gc)));
+        }
+    }
+    return ORC_OK;
+}
