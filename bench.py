@@ -12,6 +12,9 @@ instead times 1024 consecutive decode steps of 32 sequences.
 Prints one JSON line: whole-step tokens/s, the roofline of the dominant
 kernel (the scan; HBM-bound) measured with HIP events on the launch stream,
 a per-kernel breakdown, and the CPU oracle timed on the host as a baseline.
+After the timed region it also times the steps either side of the path (the
+gates, and the read-out's norm and output gate) on the same layer, reported
+under "layer_edges" and not counted in the step.
 """
 from __future__ import annotations
 
@@ -136,6 +139,44 @@ def cpu_baseline(name, d, host_x, seed, min_seconds):
             break
     return {"value": total_tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{sample}; {reps} repetition(s), {elapsed:.1f} s"}
+
+
+def layer_edges(sdm, synth, torch, d, dims, o, stream, seed, reps=20):
+    """The steps either side of the path, timed after the timed region (they
+    are not part of the step): the gates from their pre-activations, and the
+    norm and output gate of the scan's read-out o.  Per-launch time from HIP
+    events on the launch stream, against the HBM peak."""
+    x = synth.make_layer_edge_inputs_torch(d, seed)
+    a = torch.empty_like(x["a_raw"])
+    b = torch.empty_like(x["b_raw"])
+    y = torch.empty(o.shape, dtype=x["g"].dtype, device="cuda")
+
+    def once():
+        sdm.sdm_gates(x["a_raw"], x["b_raw"], x["A"], x["dt_bias"], dims, a, b, stream)
+        sdm.sdm_output_norm_gate(o, x["g"], x["gamma"], 1e-5, dims, y, stream)
+
+    once()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * reps)]
+    for r in range(reps):
+        ev[3 * r].record(stream)
+        sdm.sdm_gates(x["a_raw"], x["b_raw"], x["A"], x["dt_bias"], dims, a, b, stream)
+        ev[3 * r + 1].record(stream)
+        sdm.sdm_output_norm_gate(o, x["g"], x["gamma"], 1e-5, dims, y, stream)
+        ev[3 * r + 2].record(stream)
+    torch.cuda.synchronize()
+    g_ms = sum(ev[3 * r].elapsed_time(ev[3 * r + 1]) for r in range(reps)) / reps
+    n_ms = sum(ev[3 * r + 1].elapsed_time(ev[3 * r + 2]) for r in range(reps)) / reps
+    th = d.B * d.T * d.H
+    esz = 2 if d.in_dtype == "bf16" else 4
+    g_bytes = th * 16 + d.H * 8                       # a_raw, b_raw read; a, b written
+    n_bytes = th * d.d_v * (4 + 2 * esz) + d.d_v * 4   # o, g read; y written
+    out = {}
+    for name, ms, nb in (("sdm_gates", g_ms, g_bytes), ("sdm_output_norm_gate", n_ms, n_bytes)):
+        gbs = nb / (ms * 1e-3) / 1e9
+        out[name] = {"bound": "hbm", "ms": ms, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nb}
+    return out
 
 
 def main():
@@ -310,6 +351,7 @@ def main():
         result["state_init"] = {"GB/s": init_bytes / (avg["sdm_state_init"] * 1e-3) / 1e9,
                                 "bytes_per_launch": init_bytes}
         result["scan_tokens_per_s"] = d.B * d.T / scan_s
+        result["layer_edges"] = layer_edges(sdm, synth, torch, d, dims, o, stream, args.seed)
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(name, d, host_x, args.seed, args.cpu_seconds)

@@ -38,6 +38,9 @@
  *     default stream).  Arguments are validated on the host before anything
  *     is launched; on a validation error nothing is written.  A launch
  *     failure returns SDM_ERR_HIP.  No C++ exception crosses this boundary.
+ *   - A call with no work (B = 0, or T = 0 where a call takes T) returns
+ *     SDM_OK once dims are valid, touches no buffer and launches nothing;
+ *     its pointers may then be NULL (as empty torch tensors give).
  *   - Calls that overlap on the same buffers race; order them on one stream.
  *   - sdm_last_error() returns a per-thread message describing the last
  *     non-OK status.
@@ -148,6 +151,41 @@ sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C
                            const void *C_r, const void *v, const float *a, const float *b,
                            float *o, int32_t *widx_out, int32_t *ridx_out, const sdm_dims *dims,
                            sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * sdm_gates -- the scan's gates from their pre-activations: [P] Sec. 3.1
+ * step 2 (per-head forget gate a_t with a learnable decay A, input gate
+ * b_t) with the Gated DeltaNet parameterisation that [P] Sec. 4 initialises
+ * A and the time-step bias for (the pages print no formula; this is the
+ * reading the library implements):
+ *   a[b,t,h] = exp(-A[h] * softplus(a_raw[b,t,h] + dt_bias[h]))
+ *   b[b,t,h] = 1 / (1 + exp(-b_raw[b,t,h]))        softplus(z) = ln(1 + e^z)
+ *   a_raw, b_raw [B,T,H] fp32 (the token's gate projections);
+ *   A [H] fp32, >= 0 (the decay rate itself, not its logarithm);
+ *   dt_bias [H] fp32;  a, b [B,T,H] fp32 written.
+ * fp32 arithmetic.  a may be the same buffer as a_raw and b as b_raw (in
+ * place); any other overlap is SDM_ERR_INVALID_ARG.  Negative A or
+ * non-finite inputs are not checked (the results are then unspecified).
+ * Uses B, T, H of dims.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_gates(const float *a_raw, const float *b_raw, const float *A, const float *dt_bias,
+                     const sdm_dims *dims, float *a, float *b, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * sdm_output_norm_gate -- [P] Sec. 3.1 step 4: the read-out of each
+ * token-head is RMS-normalised over its d_v features with a learned gain and
+ * gated element-wise, before the head-mixing projection (reading: the
+ * Gated DeltaNet output gate, silu(g) = g / (1 + e^-g)):
+ *   y[b,t,h,c] = o[b,t,h,c] / sqrt(mean_c' o[b,t,h,c']^2 + eps) * gamma[c] * silu(g[b,t,h,c])
+ *   o [B,T,H,d_v] fp32 (sdm_scan_forward's read-out), 16-byte aligned;
+ *   g [B,T,H,d_v] in_dtype (the output-gate projection);
+ *   gamma [d_v] fp32, 16-byte aligned;  eps finite, >= 0;
+ *   y [B,T,H,d_v] in_dtype written (bf16: rounded to nearest even), must
+ *   not overlap o, g or gamma.
+ * fp32 arithmetic.  Uses B, T, H, d_v (a multiple of 32, <= 1024), in_dtype.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_output_norm_gate(const float *o, const void *g, const float *gamma, float eps,
+                                const sdm_dims *dims, void *y, sdm_stream_t stream);
 
 /* Static description of a status code. */
 const char *sdm_status_string(sdm_status status);

@@ -28,7 +28,8 @@ from typing import Dict, Optional
 
 import numpy as np
 
-__all__ = ["Dims", "PRESETS", "preset", "make_inputs", "f32_to_bf16_bits",
+__all__ = ["Dims", "PRESETS", "preset", "make_inputs", "make_layer_edge_inputs", "make_layer_edge_inputs_torch",
+           "f32_to_bf16_bits",
            "bf16_bits_to_f32", "random_addressing"]
 
 
@@ -239,6 +240,50 @@ def make_inputs_torch(d: Dims, seed: int = 0, *, reuse_frac: float = 0.0, recall
     out["k"] = k.to(dt)
     out["q"] = q.to(dt)
     return out
+
+
+def make_layer_edge_inputs(d: Dims, seed: int = 0) -> dict:
+    """Inputs of the steps either side of the path (numpy backend).
+
+      a_raw, b_raw : [B,T,H]        float32 gate pre-activations, N(0, 1)
+      A            : [H]            float32 decay rates, U(0, 16)
+      dt_bias      : [H]            float32 time-step bias, U(-6.9, -2.25) (the
+                                    inverse softplus of a time step in [1e-3, 0.1])
+      o            : [B,T,H,d_v]    float32 read-out, N(0, 0.5^2)
+      g            : [B,T,H,d_v]    output-gate pre-activation N(0, 1), bf16 bits
+                                    (or float32 when d.in_dtype == "f32")
+      gamma        : [d_v]          float32 norm gain, 1 + N(0, 0.1^2)
+    Drawn from sub-streams of their own, so the other inputs of a seed do not change.
+    """
+    names = ("a_raw", "b_raw", "A", "dt_bias", "o", "g", "gamma")
+    ss = np.random.SeedSequence([seed, 104729])
+    gs = {n: np.random.Generator(np.random.PCG64(s)) for n, s in zip(names, ss.spawn(len(names)))}
+    shp = (d.B, d.T, d.H)
+    g = _normal(gs["g"], shp + (d.d_v,))
+    return dict(a_raw=_normal(gs["a_raw"], shp), b_raw=_normal(gs["b_raw"], shp),
+                A=gs["A"].uniform(0.0, 16.0, d.H).astype(np.float32),
+                dt_bias=gs["dt_bias"].uniform(-6.9, -2.25, d.H).astype(np.float32),
+                o=_normal(gs["o"], shp + (d.d_v,), std=0.5),
+                g=f32_to_bf16_bits(g) if d.in_dtype == "bf16" else g,
+                gamma=_normal(gs["gamma"], (d.d_v,), std=0.1, mean=1.0))
+
+
+def make_layer_edge_inputs_torch(d: Dims, seed: int = 0, device: str = "cuda") -> dict:
+    """The distributions of make_layer_edge_inputs drawn on the GPU (torch
+    generator; for layers too large to draw on the host)."""
+    import torch
+    gen = torch.Generator(device=device)
+    dt = torch.bfloat16 if d.in_dtype == "bf16" else torch.float32
+    shp = (d.B, d.T, d.H)
+
+    def draw(sub, shape, kind="normal"):
+        gen.manual_seed(int(seed) * 1000003 + 100 + sub)
+        f = torch.randn if kind == "normal" else torch.rand
+        return f(shape, generator=gen, device=device, dtype=torch.float32)
+
+    return dict(a_raw=draw(0, shp), b_raw=draw(1, shp), A=draw(2, (d.H,), "uniform") * 16.0,
+                dt_bias=draw(3, (d.H,), "uniform") * 4.65 - 6.9, o=draw(4, shp + (d.d_v,)) * 0.5,
+                g=draw(5, shp + (d.d_v,)).to(dt), gamma=draw(6, (d.d_v,)) * 0.1 + 1.0)
 
 
 def random_addressing(d: Dims, seed: int = 0, *, hazard_slots: Optional[int] = None) -> dict:

@@ -52,6 +52,8 @@ def load_library():
         "sdm_pkm_address": [P, P, P, P, D, P, P, P, P, P],
         "sdm_scan_forward": [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
         "sdm_decode_step": [P, P, P, P, P, P, P, P, P, P, P, D, P],
+        "sdm_gates": [P, P, P, P, D, P, P, P],
+        "sdm_output_norm_gate": [P, P, P, ctypes.c_float, D, P, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -165,6 +167,22 @@ def sdm_decode_step(M, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, dims: Sdm
     return st
 
 
+def sdm_gates(a_raw, b_raw, A, dt_bias, dims: SdmDims, a, b, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_gates(_ptr(a_raw), _ptr(b_raw), _ptr(A), _ptr(dt_bias), ctypes.byref(dims), _ptr(a),
+                                  _ptr(b), _stream(stream))
+    if check:
+        _check(st, "sdm_gates")
+    return st
+
+
+def sdm_output_norm_gate(o, g, gamma, eps: float, dims: SdmDims, y, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_output_norm_gate(_ptr(o), _ptr(g), _ptr(gamma), float(eps), ctypes.byref(dims),
+                                             _ptr(y), _stream(stream))
+    if check:
+        _check(st, "sdm_output_norm_gate")
+    return st
+
+
 # ---------------------------------------------------------------------------
 # torch conveniences (allocation + shape checks only)
 # ---------------------------------------------------------------------------
@@ -258,3 +276,34 @@ def decode_step(M, k, q, C_w, C_r, v, a, b, dims: SdmDims, o=None, widx_out=None
         o = torch.empty((B, H, dims.d_v), dtype=torch.float32, device=M.device)
     sdm_decode_step(M, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, dims, stream)
     return o
+
+
+def gates(a_raw, b_raw, A, dt_bias, dims: SdmDims, a=None, b=None, stream=None):
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    _expect(a_raw, (B, T, H), torch.float32, "a_raw")
+    _expect(b_raw, (B, T, H), torch.float32, "b_raw")
+    _expect(A, (H,), torch.float32, "A")
+    _expect(dt_bias, (H,), torch.float32, "dt_bias")
+    if a is None:
+        a = torch.empty((B, T, H), dtype=torch.float32, device=a_raw.device)
+    if b is None:
+        b = torch.empty((B, T, H), dtype=torch.float32, device=a_raw.device)
+    _expect(a, (B, T, H), torch.float32, "a")
+    _expect(b, (B, T, H), torch.float32, "b")
+    sdm_gates(a_raw, b_raw, A, dt_bias, dims, a, b, stream)
+    return a, b
+
+
+def output_norm_gate(o, g, gamma, eps: float, dims: SdmDims, y=None, stream=None):
+    import torch
+    shp = (dims.B, dims.T, dims.H, dims.d_v)
+    dt = _in_dtype(dims)
+    _expect(o, shp, torch.float32, "o")
+    _expect(g, shp, dt, "g")
+    _expect(gamma, (dims.d_v,), torch.float32, "gamma")
+    if y is None:
+        y = torch.empty(shp, dtype=dt, device=o.device)
+    _expect(y, shp, dt, "y")
+    sdm_output_norm_gate(o, g, gamma, eps, dims, y, stream)
+    return y

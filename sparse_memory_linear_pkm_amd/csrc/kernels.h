@@ -96,6 +96,26 @@ struct InitArgs {
     int64_t per_seq;  // H*N*d_v floats
 };
 
+struct GateArgs {
+    const float *a_raw, *b_raw;   // [B*T*H]
+    const float *A, *dt_bias;     // [H]
+    float *a, *b;                 // [B*T*H]
+    int64_t n;                    // B*T*H
+    int H;
+};
+
+struct NormArgs {
+    const float *o;       // [rows, d_v] fp32
+    const void *g;        // [rows, d_v] bf16 or fp32
+    const float *gamma;   // [d_v]
+    void *y;              // [rows, d_v] same dtype as g
+    int64_t rows;         // B*T*H
+    int d_v;              // a multiple of 32
+    float eps;
+};
+
+hipError_t launch_gates(const GateArgs &args, hipStream_t stream);
+hipError_t launch_out_norm_gate(const NormArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream);
 size_t address_smem_bytes(int n_sub, int k_prime);
 hipError_t launch_scan(const ScanArgs &args, bool bf16, void *workspace, size_t ws_bytes,

@@ -110,6 +110,7 @@ sdm_status sdm_state_init(float *M, const float *M0, const sdm_dims *d, sdm_stre
 {
     sdm_status st = check_memory_dims(d);
     if (st != SDM_OK) return st;
+    if (d->B == 0) return SDM_OK;
     if (!M || !M0) return fail(SDM_ERR_INVALID_ARG, "M and M0 must be non-NULL");
     if (!aligned(M, 16) || !aligned(M0, 16)) return fail(SDM_ERR_INVALID_ARG, "M and M0 must be 16-byte aligned");
     const int64_t per_seq = d->H * d->n_sub * d->n_sub * d->d_v;
@@ -126,6 +127,7 @@ sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const 
 {
     sdm_status st = check_method_dims(d, true);
     if (st != SDM_OK) return st;
+    if (d->B * d->T == 0) return SDM_OK;
     if (!k || !q || !C_w || !C_r || !widx || !wwt || !ridx || !rwt)
         return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
     const size_t al = d->in_dtype == SDM_BF16 ? 16 : 4;
@@ -178,6 +180,7 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
         return fail(SDM_ERR_INVALID_ARG, "W and R must not exceed N");
     if (d->W > kMaxList || d->R > kMaxList)
         return fail(SDM_ERR_UNSUPPORTED, "W and R must be <= %lld", (long long)kMaxList);
+    if (d->B * d->T == 0) return SDM_OK;
     if (!M || !widx || !wwt || !ridx || !rwt || !v || !a || !b || !o)
         return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
     if (!aligned(M, 16) || !aligned(o, 16)) return fail(SDM_ERR_INVALID_ARG, "M and o must be 16-byte aligned");
@@ -227,6 +230,7 @@ sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C
     sdm_status st = check_method_dims(d, false);
     if (st != SDM_OK) return st;
     if (d->T != 1) return fail(SDM_ERR_INVALID_ARG, "sdm_decode_step needs dims.T == 1");
+    if (d->B == 0) return SDM_OK;
     if (!M || !k || !q || !C_w || !C_r || !v || !a || !b || !o)
         return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
     const size_t al = d->in_dtype == SDM_BF16 ? 16 : 4;
@@ -250,6 +254,62 @@ sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C
     sdm::make_staircase(A.k_prime, A.R, A.stair[1]);
     hipError_t e = sdm::launch_decode(A, d->in_dtype == SDM_BF16, as_stream(stream));
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_decode_step launch");
+}
+
+sdm_status sdm_gates(const float *a_raw, const float *b_raw, const float *A, const float *dt_bias,
+                     const sdm_dims *d, float *a, float *b, sdm_stream_t stream)
+{
+    if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
+    if (d->reserved != 0) return fail(SDM_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->B < 0 || d->T < 0 || d->H < 1)
+        return fail(SDM_ERR_INVALID_ARG, "need B >= 0, T >= 0, H >= 1");
+    if (d->H > 0x7fffffff) return fail(SDM_ERR_UNSUPPORTED, "H too large");
+    if (d->B * d->T == 0) return SDM_OK;
+    if (!a_raw || !b_raw || !A || !dt_bias || !a || !b) return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(a_raw, 4) || !aligned(b_raw, 4) || !aligned(A, 4) || !aligned(dt_bias, 4) || !aligned(a, 4) ||
+        !aligned(b, 4))
+        return fail(SDM_ERR_INVALID_ARG, "gate arrays must be 4-byte aligned");
+    const int64_t n = d->B * d->T * d->H;
+    const size_t nb = sizeof(float) * (size_t)n, hb = sizeof(float) * (size_t)d->H;
+    // a may be a_raw and b may be b_raw (in place); any other overlap is an error
+    if (overlap(a, nb, b, nb) || overlap(a, nb, b_raw, nb) || overlap(b, nb, a_raw, nb) ||
+        (a != a_raw && overlap(a, nb, a_raw, nb)) || (b != b_raw && overlap(b, nb, b_raw, nb)))
+        return fail(SDM_ERR_INVALID_ARG, "a and b may only alias a_raw and b_raw exactly");
+    if (overlap(a, nb, A, hb) || overlap(a, nb, dt_bias, hb) || overlap(b, nb, A, hb) || overlap(b, nb, dt_bias, hb))
+        return fail(SDM_ERR_INVALID_ARG, "a or b overlaps A or dt_bias");
+    if (n == 0) return SDM_OK;
+    if ((n + 255) / 256 > 0x7fffffff) return fail(SDM_ERR_UNSUPPORTED, "B*T*H too large for one launch");
+    sdm::GateArgs G{a_raw, b_raw, A, dt_bias, a, b, n, (int)d->H};
+    hipError_t e = sdm::launch_gates(G, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_gates launch");
+}
+
+sdm_status sdm_output_norm_gate(const float *o, const void *g, const float *gamma, float eps, const sdm_dims *d,
+                                void *y, sdm_stream_t stream)
+{
+    if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
+    if (d->reserved != 0) return fail(SDM_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->B < 0 || d->T < 0 || d->H < 1 || d->d_v < 1)
+        return fail(SDM_ERR_INVALID_ARG, "need B >= 0, T >= 0, H >= 1, d_v >= 1");
+    if (d->in_dtype != SDM_F32 && d->in_dtype != SDM_BF16)
+        return fail(SDM_ERR_INVALID_ARG, "in_dtype must be SDM_F32 or SDM_BF16");
+    if (d->d_v % 32 != 0 || d->d_v > kMaxDv)
+        return fail(SDM_ERR_UNSUPPORTED, "d_v must be a multiple of 32 and <= %lld", (long long)kMaxDv);
+    if (!(eps >= 0.0f) || !(eps <= 3.4e38f)) return fail(SDM_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (d->B * d->T == 0) return SDM_OK;
+    if (!o || !g || !gamma || !y) return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t gal = d->in_dtype == SDM_BF16 ? 8 : 16;
+    if (!aligned(o, 16) || !aligned(gamma, 16) || !aligned(g, gal) || !aligned(y, gal))
+        return fail(SDM_ERR_INVALID_ARG, "o and gamma must be 16-byte aligned, g and y %zu-byte aligned", gal);
+    const int64_t rows = d->B * d->T * d->H;
+    const size_t ob = sizeof(float) * (size_t)(rows * d->d_v), gb = in_size(d) * (size_t)(rows * d->d_v);
+    if (overlap(y, gb, o, ob) || overlap(y, gb, g, gb) || overlap(y, gb, gamma, sizeof(float) * (size_t)d->d_v))
+        return fail(SDM_ERR_INVALID_ARG, "y overlaps an input");
+    if (rows == 0) return SDM_OK;
+    if ((rows + 31) / 32 > 0x7fffffff) return fail(SDM_ERR_UNSUPPORTED, "B*T*H too large for one launch");
+    sdm::NormArgs A{o, g, gamma, y, rows, (int)d->d_v, eps};
+    hipError_t e = sdm::launch_out_norm_gate(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_output_norm_gate launch");
 }
 
 }  // extern "C"

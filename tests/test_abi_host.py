@@ -133,3 +133,66 @@ def test_binding_raises_with_detail():
         sdm.sdm_pkm_address(None, FAKE, FAKE, FAKE, good_dims(), FAKE, FAKE, FAKE, FAKE, stream=0)
     assert ei.value.status == sdm.SDM_ERR_INVALID_ARG
     assert "NULL" in str(ei.value)
+
+
+def gates_call(dims, **ptrs):
+    p = dict(a_raw=FAKE, b_raw=FAKE + (1 << 30), A=FAKE + (2 << 30), dt=FAKE + (3 << 30), a=FAKE + (4 << 30),
+             b=FAKE + (5 << 30))
+    p.update(ptrs)
+    return sdm.sdm_gates(p["a_raw"], p["b_raw"], p["A"], p["dt"], dims, p["a"], p["b"], stream=0, check=False)
+
+
+def test_gates_rejects_bad_arguments():
+    assert gates_call(good_dims(H=0)) == sdm.SDM_ERR_INVALID_ARG
+    assert gates_call(good_dims(T=-1)) == sdm.SDM_ERR_INVALID_ARG
+    assert gates_call(good_dims(reserved=1)) == sdm.SDM_ERR_INVALID_ARG
+    assert gates_call(good_dims(), A=None) == sdm.SDM_ERR_INVALID_ARG
+    assert gates_call(good_dims(), a=FAKE + (4 << 30) + 2) == sdm.SDM_ERR_INVALID_ARG
+    # a may be a_raw exactly (in place), not a shifted view of it, and never b
+    assert gates_call(good_dims(), a=FAKE + 4) == sdm.SDM_ERR_INVALID_ARG
+    assert gates_call(good_dims(), b=FAKE + (4 << 30)) == sdm.SDM_ERR_INVALID_ARG
+    assert gates_call(good_dims(), a=FAKE + (1 << 30)) == sdm.SDM_ERR_INVALID_ARG   # a over b_raw
+    # nothing to do: validation passes and no kernel is launched
+    assert gates_call(good_dims(B=0)) == sdm.SDM_OK
+
+
+def norm_call(dims, eps=1e-5, **ptrs):
+    p = dict(o=FAKE, g=FAKE + (1 << 30), gamma=FAKE + (2 << 30), y=FAKE + (3 << 30))
+    p.update(ptrs)
+    return sdm.sdm_output_norm_gate(p["o"], p["g"], p["gamma"], eps, dims, p["y"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,eps,status", [
+    (dict(d_v=48), 1e-5, sdm.SDM_ERR_UNSUPPORTED),
+    (dict(d_v=2048), 1e-5, sdm.SDM_ERR_UNSUPPORTED),
+    (dict(in_dtype=3), 1e-5, sdm.SDM_ERR_INVALID_ARG),
+    (dict(H=0), 1e-5, sdm.SDM_ERR_INVALID_ARG),
+    (dict(), -1.0, sdm.SDM_ERR_INVALID_ARG),
+    (dict(), float("nan"), sdm.SDM_ERR_INVALID_ARG),
+    (dict(), float("inf"), sdm.SDM_ERR_INVALID_ARG),
+])
+def test_norm_gate_rejects_bad_dims(kw, eps, status):
+    assert norm_call(good_dims(**kw), eps) == status
+
+
+def test_norm_gate_rejects_null_misaligned_overlap():
+    assert norm_call(good_dims(), g=None) == sdm.SDM_ERR_INVALID_ARG
+    assert norm_call(good_dims(), o=FAKE + 8) == sdm.SDM_ERR_INVALID_ARG
+    assert norm_call(good_dims(), y=FAKE + (3 << 30) + 4) == sdm.SDM_ERR_INVALID_ARG
+    assert norm_call(good_dims(), y=FAKE + 64) == sdm.SDM_ERR_INVALID_ARG   # y inside o
+    assert norm_call(good_dims(B=0)) == sdm.SDM_OK
+
+
+def test_calls_without_work_accept_null_and_do_nothing():
+    # zero-sized work: valid dims, NULL buffers (what empty tensors give), nothing launched
+    assert sdm.sdm_state_init(None, None, good_dims(B=0), stream=0, check=False) == sdm.SDM_OK
+    assert addr(good_dims(T=0), k=None, q=None, widx=None) == sdm.SDM_OK
+    assert sdm.sdm_scan_forward(None, None, None, None, None, None, None, None, None, None, 0, good_dims(T=0),
+                                stream=0, check=False) == sdm.SDM_OK
+    assert sdm.sdm_decode_step(None, None, None, None, None, None, None, None, None, None, None,
+                               good_dims(B=0, T=1), stream=0, check=False) == sdm.SDM_OK
+    assert gates_call(good_dims(T=0), a_raw=None, a=None) == sdm.SDM_OK
+    assert norm_call(good_dims(B=0), o=None, y=None) == sdm.SDM_OK
+    # invalid dims are still rejected when there is no work
+    assert addr(good_dims(T=0, d_k=127)) == sdm.SDM_ERR_INVALID_ARG
+    assert norm_call(good_dims(T=0), eps=-1.0) == sdm.SDM_ERR_INVALID_ARG

@@ -438,3 +438,35 @@ def test_decode_matches_oracle_and_prefill(sdm, torch):
     np.testing.assert_array_equal(r_dec, to_host(ridx))
     np.testing.assert_array_equal(o_dec, to_host(o2))
     np.testing.assert_array_equal(M_dec, to_host(M2))
+
+
+def test_empty_inputs_touch_nothing(sdm, torch):
+    """No tokens (T = 0) or no sequences (B = 0): every call succeeds on the
+    empty tensors and leaves the state as it was, bit for bit."""
+    d = Dims(B=2, T=0, H=3, d_k=128, n_sub=16, d_v=32, k_prime=8, W=8, R=8)
+    note(f"empty inputs {d}")
+    T = torch
+    dims = gpu_dims(d)
+    M = T.randn((d.B, d.H, d.N, d.d_v), dtype=T.float32, device="cuda")
+    M_before = to_host(M).copy()
+    x = synth.make_inputs(d.replace(T=1), seed=3)
+    e = lambda *shape, dt=T.float32: T.empty(shape, dtype=dt, device="cuda")
+    k = e(d.B, 0, d.H, d.d_k, dt=T.bfloat16)
+    widx, wwt, ridx, rwt = sdm.pkm_address(k, k, to_dev(x["C_w"]), to_dev(x["C_r"]), dims)
+    assert widx.numel() == 0 and rwt.numel() == 0
+    o = sdm.scan_forward(M, widx, wwt, ridx, rwt, e(d.B, 0, d.H, d.d_v, dt=T.bfloat16), e(d.B, 0, d.H),
+                         e(d.B, 0, d.H), dims)
+    assert o.numel() == 0
+    a, b = sdm.gates(e(d.B, 0, d.H), e(d.B, 0, d.H), to_dev(np.ones(d.H, np.float32)),
+                     to_dev(np.zeros(d.H, np.float32)), dims)
+    y = sdm.output_norm_gate(o, e(d.B, 0, d.H, d.d_v, dt=T.bfloat16), to_dev(np.ones(d.d_v, np.float32)), 1e-5,
+                             dims)
+    d0 = d.replace(B=0, T=1)
+    dims0 = gpu_dims(d0)
+    M0 = to_dev(x["M0"])
+    sdm.state_init(M0, dims0, M=e(0, d.H, d.N, d.d_v))
+    sdm.decode_step(e(0, d.H, d.N, d.d_v), e(0, d.H, d.d_k, dt=T.bfloat16), e(0, d.H, d.d_k, dt=T.bfloat16),
+                    to_dev(x["C_w"]), to_dev(x["C_r"]), e(0, d.H, d.d_v, dt=T.bfloat16), e(0, d.H), e(0, d.H), dims0)
+    T.cuda.synchronize()
+    assert np.array_equal(to_host(M), M_before)
+    assert a.numel() == 0 and y.numel() == 0
