@@ -58,8 +58,9 @@ def _load():
         lib.orc_state_init.argtypes = [P, P, ctypes.POINTER(_Dims)]
         lib.orc_gates.argtypes = [P, P, P, P, ctypes.POINTER(_Dims), P, P]
         lib.orc_output_norm_gate.argtypes = [P, P, P, ctypes.c_double, ctypes.POINTER(_Dims), P]
+        lib.orc_gdn_dense.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(_Dims), I32]
         for f in (lib.orc_address, lib.orc_half_scores, lib.orc_slot_scores, lib.orc_scan,
-                  lib.orc_state_init, lib.orc_gates, lib.orc_output_norm_gate):
+                  lib.orc_state_init, lib.orc_gates, lib.orc_output_norm_gate, lib.orc_gdn_dense):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -226,3 +227,27 @@ def output_norm_gate(o, g, gamma, eps: float, d) -> np.ndarray:
     _check(lib.orc_output_norm_gate(_p(o), _p(g), _p(gamma), float(eps), ctypes.byref(dm), _p(y)),
            "orc_output_norm_gate")
     return y
+
+
+def gdn_dense(S, k, q, v, a, b, d, *, nthreads: Optional[int] = None) -> np.ndarray:
+    """The dense Gated DeltaNet recurrence, in place on S [B,H,d_k,d_v]
+    (float32, the state transposed: row j belongs to key dimension j).
+    k, q [B,T,H,d_k]; v [B,T,H,d_v] (input dtype); a, b [B,T,H].
+    Returns o [B,T,H,d_v] float32."""
+    lib = _load()
+    if S.dtype != np.float32 or not S.flags.c_contiguous:
+        raise TypeError("S must be a C-contiguous float32 array")
+    if S.shape != (d.B, d.H, d.d_k, d.d_v):
+        raise ValueError(f"S shape {S.shape} != {(d.B, d.H, d.d_k, d.d_v)}")
+    k, q, v = _in(k, d), _in(q, d), _in(v, d)
+    a = np.ascontiguousarray(a, np.float32)
+    b = np.ascontiguousarray(b, np.float32)
+    for name, arr, shp in (("k", k, (d.B, d.T, d.H, d.d_k)), ("q", q, (d.B, d.T, d.H, d.d_k)),
+                           ("v", v, (d.B, d.T, d.H, d.d_v)), ("a", a, (d.B, d.T, d.H)), ("b", b, (d.B, d.T, d.H))):
+        if arr.shape != shp:
+            raise ValueError(f"{name} shape {arr.shape} != {shp}")
+    o = np.empty((d.B, d.T, d.H, d.d_v), np.float32)
+    dm = _dims(d)
+    _check(lib.orc_gdn_dense(_p(S), _p(k), _p(q), _p(v), _p(a), _p(b), _p(o), ctypes.byref(dm),
+                             nthreads or default_threads()), "orc_gdn_dense")
+    return o

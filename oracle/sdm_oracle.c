@@ -382,3 +382,61 @@ int orc_output_norm_gate(const float *o, const void *g, const float *gamma, doub
     }
     return ORC_OK;
 }
+
+/* ---- the dense Gated DeltaNet recurrence (every slot selected) ----------- */
+/* [P] Sec. 2, Eq. 2 (Gated DeltaNet), the rule that Sec. 3.1 ("Connection to
+ * GDN") says SDM reduces to when every slot is selected with a dense key:
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
+ * with S_t in R^{d_v x d_k}.  Stored transposed, like the SDM memory with
+ * N = d_k slots: S [B,H,d_k,d_v], row j = the state's column for key
+ * dimension j.  Expanding the product, row j of the new state is
+ *     a S[j] + b k_j (v - a sum_l k_l S[l])
+ * (the prediction sum_l k_l S[l] is formed from the old state, before any
+ * row changes).  fp64 arithmetic, each stored state element and each output
+ * rounded once to fp32.
+ *   k, q [B,T,H,d_k] and v [B,T,H,d_v] (bf16 bits or fp32); a, b [B,T,H];
+ *   S [B,H,d_k,d_v] fp32 in/out; o [B,T,H,d_v] fp32. */
+int orc_gdn_dense(float *S, const void *k, const void *q, const void *v, const float *a, const float *b,
+                  float *o, const orc_dims *d, int nthreads)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->d_k < 1 || d->d_v < 1) return ORC_EINVAL;
+    const int64_t dk = d->d_k, dv = d->d_v, chains = d->B * d->H;
+    int err = ORC_OK;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)(2 * dv + 2 * dk));
+        if (!p) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t ch = 0; ch < chains; ++ch) {
+            if (!p || err) continue;
+            double *u = p + dv, *kk = u + dv, *qq = kk + dk;
+            const int64_t bb = ch / d->H, h = ch % d->H;
+            float *Sc = S + ch * dk * dv;
+            for (int64_t t = 0; t < d->T; ++t) {
+                const int64_t row = (bb * d->T + t) * d->H + h;
+                const double at = (double)a[row], bt = (double)b[row];
+                for (int64_t j = 0; j < dk; ++j) {
+                    kk[j] = load_in(k, d->in_bf16, row * dk + j);
+                    qq[j] = load_in(q, d->in_bf16, row * dk + j);
+                }
+                for (int64_t c = 0; c < dv; ++c) p[c] = 0.0;
+                for (int64_t j = 0; j < dk; ++j)
+                    for (int64_t c = 0; c < dv; ++c) p[c] += kk[j] * (double)Sc[j * dv + c];
+                for (int64_t c = 0; c < dv; ++c) u[c] = load_in(v, d->in_bf16, row * dv + c) - at * p[c];
+                for (int64_t j = 0; j < dk; ++j)
+                    for (int64_t c = 0; c < dv; ++c)
+                        Sc[j * dv + c] = (float)(at * (double)Sc[j * dv + c] + bt * kk[j] * u[c]);
+                for (int64_t c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < dk; ++j) acc += qq[j] * (double)Sc[j * dv + c];
+                    o[row * dv + c] = (float)acc;
+                }
+            }
+        }
+        free(p);
+    }
+    return err;
+}

@@ -29,6 +29,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = ["Dims", "PRESETS", "preset", "make_inputs", "make_layer_edge_inputs", "make_layer_edge_inputs_torch",
+           "make_gdn_inputs", "make_gdn_inputs_torch",
            "f32_to_bf16_bits",
            "bf16_bits_to_f32", "random_addressing"]
 
@@ -284,6 +285,52 @@ def make_layer_edge_inputs_torch(d: Dims, seed: int = 0, device: str = "cuda") -
     return dict(a_raw=draw(0, shp), b_raw=draw(1, shp), A=draw(2, (d.H,), "uniform") * 16.0,
                 dt_bias=draw(3, (d.H,), "uniform") * 4.65 - 6.9, o=draw(4, shp + (d.d_v,)) * 0.5,
                 g=draw(5, shp + (d.d_v,)).to(dt), gamma=draw(6, (d.d_v,)) * 0.1 + 1.0)
+
+
+def make_gdn_inputs(d: Dims, seed: int = 0) -> dict:
+    """Inputs of the dense Gated DeltaNet recurrence (numpy backend).
+
+      k, q : [B,T,H,d_k]   unit-norm directions (N(0,1) draws scaled to length 1,
+                           as Gated DeltaNet normalises its keys and queries),
+                           bf16 bits (or float32 when d.in_dtype == "f32")
+      v    : [B,T,H,d_v]   N(0,1), same encoding
+      a, b : [B,T,H]       float32, sigmoid(N(3,1)) and sigmoid(N(0,1)) as for SDM
+      S0   : [B,H,d_k,d_v] float32 initial state, N(0, 0.02) (variance)
+    """
+    names = ("k", "q", "v", "a", "b", "S0")
+    ss = np.random.SeedSequence([seed, 130363])
+    gs = {n: np.random.Generator(np.random.PCG64(s)) for n, s in zip(names, ss.spawn(len(names)))}
+    shp = (d.B, d.T, d.H)
+
+    def unit(g):
+        x = _normal(g, shp + (d.d_k,)).astype(np.float64)
+        x /= np.maximum(np.linalg.norm(x, axis=-1, keepdims=True), 1e-30)
+        return x.astype(np.float32)
+
+    enc = f32_to_bf16_bits if d.in_dtype == "bf16" else (lambda x: np.ascontiguousarray(x, np.float32))
+    return dict(k=enc(unit(gs["k"])), q=enc(unit(gs["q"])), v=enc(_normal(gs["v"], shp + (d.d_v,))),
+                a=_sigmoid(_normal(gs["a"], shp, mean=3.0)), b=_sigmoid(_normal(gs["b"], shp)),
+                S0=_normal(gs["S0"], (d.B, d.H, d.d_k, d.d_v), std=math.sqrt(0.02)))
+
+
+def make_gdn_inputs_torch(d: Dims, seed: int = 0, device: str = "cuda") -> dict:
+    """The distributions of make_gdn_inputs drawn on the GPU (torch generator)."""
+    import torch
+    gen = torch.Generator(device=device)
+    dt = torch.bfloat16 if d.in_dtype == "bf16" else torch.float32
+    shp = (d.B, d.T, d.H)
+
+    def normal(sub, shape):
+        gen.manual_seed(int(seed) * 1000003 + 200 + sub)
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit(sub):
+        x = normal(sub, shp + (d.d_k,))
+        return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+
+    return dict(k=unit(0).to(dt), q=unit(1).to(dt), v=normal(2, shp + (d.d_v,)).to(dt),
+                a=torch.sigmoid(normal(3, shp) + 3.0), b=torch.sigmoid(normal(4, shp)),
+                S0=normal(5, (d.B, d.H, d.d_k, d.d_v)) * math.sqrt(0.02))
 
 
 def random_addressing(d: Dims, seed: int = 0, *, hazard_slots: Optional[int] = None) -> dict:
