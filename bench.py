@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="small",
-                   choices=list(PREFILL_WORKLOADS) + ["decode"])
+                   choices=list(PREFILL_WORKLOADS) + ["decode", "gdn_1p4b"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle baseline (0 disables it)")
@@ -179,6 +179,84 @@ def layer_edges(sdm, synth, torch, d, dims, o, stream, seed, reps=20):
     return out
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (packed) peak, vendor figure
+
+
+def bench_gdn(args, sdm, synth, torch):
+    """The dense Gated DeltaNet recurrence at the 1.4B layer's shape (B, T, H,
+    d_k = d_v = 128, bf16 inputs): the rule the sparse memory reduces to with
+    every slot selected.  One step = reset the state from S0 + one
+    sdm_gdn_dense_forward over all B*T tokens."""
+    import oracle
+    base = synth.PRESETS["prefill_1p4b"].dims
+    d = base.replace(n_sub=8, k_prime=8, W=64, R=64)
+    x = synth.make_gdn_inputs_torch(d, args.seed)
+    dims = sdm.dims_from(d)
+    S = torch.empty_like(x["S0"])
+    o = torch.empty((d.B, d.T, d.H, d.d_v), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(timed):
+        S.copy_(x["S0"])
+        e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+        sdm.sdm_gdn_dense_forward(S, x["k"], x["q"], x["v"], x["a"], x["b"], o, dims, stream)
+        e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+        if timed:
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True); end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    k_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    th = d.B * d.T * d.H
+    flops = th * 6 * d.d_k * d.d_v          # k.s, the rank-1 update, q.s: 2 flops per state entry each
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    result = {
+        "metric": "dense Gated DeltaNet layer tokens/sec (the sparse memory with every slot selected)",
+        "value": d.B * d.T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": "gdn_1p4b", "B": d.B, "T": d.T, "H": d.H, "d_k": d.d_k, "d_v": d.d_v,
+                   "inputs": d.in_dtype, "state": "fp32",
+                   "step": "state reset from S0 + sdm_gdn_dense_forward over B*T tokens"},
+        "wall_s_timed_region": wall,
+        "kernels_ms": {"sdm_gdn_dense_forward": k_ms},
+        "roofline": {"kernel": "sdm_gdn_dense_kernel", "bound": "alu", "achieved": tflops,
+                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": None, "algorithmic_flops_per_launch": flops, "avg_launch_ms": k_ms},
+    }
+    if args.cpu_seconds > 0:
+        ds = d.replace(B=1, T=2048)
+        hx = synth.make_gdn_inputs(ds, args.seed)
+        threads = oracle.default_threads()
+        elapsed, reps = 0.0, 0
+        while elapsed < args.cpu_seconds or reps == 0:
+            S0 = hx["S0"].copy()
+            t0 = time.perf_counter()
+            oracle.gdn_dense(S0, hx["k"], hx["q"], hx["v"], hx["a"], hx["b"], ds, nthreads=threads)
+            elapsed += time.perf_counter() - t0
+            reps += 1
+            if reps >= 50:
+                break
+        result["cpu_baseline"] = {"value": reps * ds.T / elapsed, "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"1 sequence x {ds.T} tokens x {ds.H} heads; {reps} repetition(s), "
+                                            f"{elapsed:.1f} s"}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,6 +284,9 @@ def main():
         return
 
     name = args.workload
+    if name == "gdn_1p4b":
+        bench_gdn(args, sdm, synth, torch)
+        return
     d = synth.PRESETS[name].dims
     decode_mode = name == "decode"
     dx, host_x = device_inputs(name, d, args.seed)

@@ -187,6 +187,25 @@ sdm_status sdm_gates(const float *a_raw, const float *b_raw, const float *A, con
 sdm_status sdm_output_norm_gate(const float *o, const void *g, const float *gamma, float eps,
                                 const sdm_dims *dims, void *y, sdm_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * sdm_gdn_dense_forward -- the dense Gated DeltaNet recurrence, [P] Sec. 2
+ * Eq. 2, which [P] Sec. 3.1 ("Connection to GDN") states the sparse memory
+ * reduces to when every slot is selected with a dense key:
+ *   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t
+ * for every (b, h), tokens t = 0..T-1 in order, on S in place.  S is stored
+ * transposed, like the sparse memory with N = d_k slots:
+ *   S [B,H,d_k,d_v] fp32 in/out (row j for key dimension j);
+ *   k, q [B,T,H,d_k] and v [B,T,H,d_v] in_dtype (k, q 16-byte aligned);
+ *   a, b [B,T,H] fp32;  o [B,T,H,d_v] fp32 written.
+ * The same function as sdm_scan_forward with W = R = N = d_k, slot lists
+ * 0..N-1 and weights k_t (write) and q_t (read).  fp32 arithmetic; o and S
+ * must not overlap each other or the inputs.  Uses B, T, H, d_k (16, 32,
+ * 64, 128 or 256), d_v, in_dtype.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_gdn_dense_forward(float *S, const void *k, const void *q, const void *v,
+                                 const float *a, const float *b, float *o, const sdm_dims *dims,
+                                 sdm_stream_t stream);
+
 /* Static description of a status code. */
 const char *sdm_status_string(sdm_status status);
 

@@ -54,6 +54,7 @@ def load_library():
         "sdm_decode_step": [P, P, P, P, P, P, P, P, P, P, P, D, P],
         "sdm_gates": [P, P, P, P, D, P, P, P],
         "sdm_output_norm_gate": [P, P, P, ctypes.c_float, D, P, P],
+        "sdm_gdn_dense_forward": [P, P, P, P, P, P, P, D, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -183,6 +184,14 @@ def sdm_output_norm_gate(o, g, gamma, eps: float, dims: SdmDims, y, stream=None,
     return st
 
 
+def sdm_gdn_dense_forward(S, k, q, v, a, b, o, dims: SdmDims, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_gdn_dense_forward(_ptr(S), _ptr(k), _ptr(q), _ptr(v), _ptr(a), _ptr(b), _ptr(o),
+                                              ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_gdn_dense_forward")
+    return st
+
+
 # ---------------------------------------------------------------------------
 # torch conveniences (allocation + shape checks only)
 # ---------------------------------------------------------------------------
@@ -307,3 +316,20 @@ def output_norm_gate(o, g, gamma, eps: float, dims: SdmDims, y=None, stream=None
     _expect(y, shp, dt, "y")
     sdm_output_norm_gate(o, g, gamma, eps, dims, y, stream)
     return y
+
+
+def gdn_dense_forward(S, k, q, v, a, b, dims: SdmDims, o=None, stream=None):
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    dt = _in_dtype(dims)
+    _expect(S, (B, H, dims.d_k, dims.d_v), torch.float32, "S")
+    _expect(k, (B, T, H, dims.d_k), dt, "k")
+    _expect(q, (B, T, H, dims.d_k), dt, "q")
+    _expect(v, (B, T, H, dims.d_v), dt, "v")
+    _expect(a, (B, T, H), torch.float32, "a")
+    _expect(b, (B, T, H), torch.float32, "b")
+    if o is None:
+        o = torch.empty((B, T, H, dims.d_v), dtype=torch.float32, device=S.device)
+    _expect(o, (B, T, H, dims.d_v), torch.float32, "o")
+    sdm_gdn_dense_forward(S, k, q, v, a, b, o, dims, stream)
+    return o

@@ -114,6 +114,16 @@ struct NormArgs {
     float eps;
 };
 
+struct GdnArgs {
+    float *S;                   // [B,H,d_k,d_v] fp32, in/out
+    const void *k, *q, *v;      // [B,T,H,d_k], [B,T,H,d_k], [B,T,H,d_v]
+    const float *a, *b;         // [B,T,H]
+    float *o;                   // [B,T,H,d_v]
+    int64_t B, T;               // T >= 1
+    int H, d_k, d_v;            // d_k in {16, 32, 64, 128, 256}
+};
+
+hipError_t launch_gdn_dense(const GdnArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gates(const GateArgs &args, hipStream_t stream);
 hipError_t launch_out_norm_gate(const NormArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream);

@@ -312,4 +312,35 @@ sdm_status sdm_output_norm_gate(const float *o, const void *g, const float *gamm
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_output_norm_gate launch");
 }
 
+sdm_status sdm_gdn_dense_forward(float *S, const void *k, const void *q, const void *v, const float *a,
+                                 const float *b, float *o, const sdm_dims *d, sdm_stream_t stream)
+{
+    if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
+    if (d->reserved != 0) return fail(SDM_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->B < 0 || d->T < 0 || d->H < 1 || d->d_k < 1 || d->d_v < 1)
+        return fail(SDM_ERR_INVALID_ARG, "need B >= 0, T >= 0, H >= 1, d_k >= 1, d_v >= 1");
+    if (d->in_dtype != SDM_F32 && d->in_dtype != SDM_BF16)
+        return fail(SDM_ERR_INVALID_ARG, "in_dtype must be SDM_F32 or SDM_BF16");
+    if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128 && d->d_k != 256)
+        return fail(SDM_ERR_UNSUPPORTED, "d_k must be 16, 32, 64, 128 or 256 (got %lld)", (long long)d->d_k);
+    if (d->d_v > (1 << 20) || d->H > (1 << 20)) return fail(SDM_ERR_UNSUPPORTED, "H and d_v must be <= 2^20");
+    if (d->B * d->T == 0) return SDM_OK;
+    if (!S || !k || !q || !v || !a || !b || !o) return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(k, 16) || !aligned(q, 16) || !aligned(S, 4) || !aligned(o, 4) || !aligned(a, 4) || !aligned(b, 4) ||
+        !aligned(v, in_size(d)))
+        return fail(SDM_ERR_INVALID_ARG, "k and q must be 16-byte aligned, the other arrays element-aligned");
+    const int64_t rows = d->B * d->T * d->H;
+    const size_t sb = sizeof(float) * (size_t)(d->B * d->H * d->d_k * d->d_v);
+    const size_t ob = sizeof(float) * (size_t)(rows * d->d_v);
+    if (overlap(o, ob, S, sb)) return fail(SDM_ERR_INVALID_ARG, "o overlaps S");
+    if (overlap(S, sb, k, in_size(d) * (size_t)(rows * d->d_k)) || overlap(S, sb, q, in_size(d) * (size_t)(rows * d->d_k)) ||
+        overlap(S, sb, v, in_size(d) * (size_t)(rows * d->d_v)) || overlap(o, ob, k, in_size(d) * (size_t)(rows * d->d_k)) ||
+        overlap(o, ob, q, in_size(d) * (size_t)(rows * d->d_k)) || overlap(o, ob, v, in_size(d) * (size_t)(rows * d->d_v)))
+        return fail(SDM_ERR_INVALID_ARG, "S or o overlaps an input");
+    if (d->B * d->H * ((d->d_v + 15) / 16) > 0x7fffffff) return fail(SDM_ERR_UNSUPPORTED, "B*H*d_v too large");
+    sdm::GdnArgs A{S, k, q, v, a, b, o, d->B, d->T, (int)d->H, (int)d->d_k, (int)d->d_v};
+    hipError_t e = sdm::launch_gdn_dense(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_gdn_dense_forward launch");
+}
+
 }  // extern "C"

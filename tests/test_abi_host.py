@@ -196,3 +196,20 @@ def test_calls_without_work_accept_null_and_do_nothing():
     # invalid dims are still rejected when there is no work
     assert addr(good_dims(T=0, d_k=127)) == sdm.SDM_ERR_INVALID_ARG
     assert norm_call(good_dims(T=0), eps=-1.0) == sdm.SDM_ERR_INVALID_ARG
+
+
+def test_gdn_rejects_bad_arguments():
+    def call(dims, **ptrs):
+        p = dict(S=FAKE, k=FAKE + (1 << 30), q=FAKE + (2 << 30), v=FAKE + (3 << 30), a=FAKE + (4 << 30),
+                 b=FAKE + (5 << 30), o=FAKE + (6 << 30))
+        p.update(ptrs)
+        return sdm.sdm_gdn_dense_forward(p["S"], p["k"], p["q"], p["v"], p["a"], p["b"], p["o"], dims, stream=0,
+                                         check=False)
+    assert call(good_dims(d_k=48)) == sdm.SDM_ERR_UNSUPPORTED
+    assert call(good_dims(d_k=512)) == sdm.SDM_ERR_UNSUPPORTED
+    assert call(good_dims(H=0)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(in_dtype=5)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), k=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), q=FAKE + (2 << 30) + 8) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), o=FAKE + 4) == sdm.SDM_ERR_INVALID_ARG          # o over S
+    assert call(good_dims(T=0), S=None, k=None) == sdm.SDM_OK
