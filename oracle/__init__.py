@@ -59,8 +59,10 @@ def _load():
         lib.orc_gates.argtypes = [P, P, P, P, ctypes.POINTER(_Dims), P, P]
         lib.orc_output_norm_gate.argtypes = [P, P, P, ctypes.c_double, ctypes.POINTER(_Dims), P]
         lib.orc_gdn_dense.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(_Dims), I32]
+        lib.orc_scan_backward.argtypes = [P] * 15 + [ctypes.POINTER(_Dims), I32]
         for f in (lib.orc_address, lib.orc_half_scores, lib.orc_slot_scores, lib.orc_scan,
-                  lib.orc_state_init, lib.orc_gates, lib.orc_output_norm_gate, lib.orc_gdn_dense):
+                  lib.orc_state_init, lib.orc_gates, lib.orc_output_norm_gate, lib.orc_gdn_dense,
+                  lib.orc_scan_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -251,3 +253,31 @@ def gdn_dense(S, k, q, v, a, b, d, *, nthreads: Optional[int] = None) -> np.ndar
     _check(lib.orc_gdn_dense(_p(S), _p(k), _p(q), _p(v), _p(a), _p(b), _p(o), ctypes.byref(dm),
                              nthreads or default_threads()), "orc_gdn_dense")
     return o
+
+
+def scan_backward(M, widx, wwt, ridx, rwt, v, a, b, dout, d, dM_final=None, *, nthreads: Optional[int] = None):
+    """Gradients of the scan for dL/do = dout [B,T,H,d_v] and dL/dM_T =
+    dM_final (zeros when None).  M [B,H,N,d_v] is the state before the call
+    (not modified).  Returns a dict: dM (dL/dM before the call), dv, da, db,
+    dw [B,T,H,W], dr [B,T,H,R] (float32)."""
+    lib = _load()
+    M = np.ascontiguousarray(M, np.float32)
+    if M.shape != (d.B, d.H, d.N, d.d_v):
+        raise ValueError("M shape")
+    widx, ridx = (np.ascontiguousarray(x, np.int32) for x in (widx, ridx))
+    wwt, rwt, a, b = (np.ascontiguousarray(x, np.float32) for x in (wwt, rwt, a, b))
+    dout = np.ascontiguousarray(dout, np.float32)
+    v = _in(v, d)
+    if dout.shape != (d.B, d.T, d.H, d.d_v):
+        raise ValueError("dout shape")
+    dM = np.zeros_like(M) if dM_final is None else np.array(dM_final, np.float32, copy=True, order="C")
+    shp = (d.B, d.T, d.H)
+    out = dict(dM=dM, dv=np.empty(shp + (d.d_v,), np.float32), da=np.empty(shp, np.float32),
+               db=np.empty(shp, np.float32), dw=np.empty(shp + (d.W,), np.float32),
+               dr=np.empty(shp + (d.R,), np.float32))
+    dm = _dims(d)
+    _check(lib.orc_scan_backward(_p(M), _p(widx), _p(wwt), _p(ridx), _p(rwt), _p(v), _p(a), _p(b), _p(dout),
+                                 _p(out["dM"]), _p(out["dv"]), _p(out["da"]), _p(out["db"]), _p(out["dw"]),
+                                 _p(out["dr"]), ctypes.byref(dm), nthreads or default_threads()),
+           "orc_scan_backward")
+    return out

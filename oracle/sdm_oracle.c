@@ -440,3 +440,140 @@ int orc_gdn_dense(float *S, const void *k, const void *q, const void *v, const f
     }
     return err;
 }
+
+/* ---- gradients of the scan ---------------------------------------------- */
+/* Reverse-mode derivative of orc_scan for a loss L with given dL/do_t (dout)
+ * and dL/dM_T (dM on entry; zeros if the loss does not see the final state).
+ * [P] Sec. 3.1 steps 2-3 (Eq. 4) differentiated; the pages print no
+ * backward pass (its appendix is not among them), so this is the plain
+ * chain rule of the forward above, token by token in reverse:
+ *   forward:  X_j = M[s_j] (before),  p = sum_j w_j X_j,  u = v - a p,
+ *             M[s_j] = Y_j = a X_j + b w_j u,  Z_i = M[r_i] (after),
+ *             o = sum_i r_i Z_i
+ *   reverse, with G = dL/dM after the token:
+ *     dr_i = <do, Z_i>;  G[r_i] += r_i do
+ *     dY_j = G[s_j];  du = b sum_j w_j dY_j;  dv = du;  dp = -a du
+ *     da = sum_j <dY_j, X_j> - <p, du>;  db = sum_j w_j <dY_j, u>
+ *     dw_j = b <dY_j, u> + <dp, X_j>;  G[s_j] = a dY_j + w_j dp
+ *   and on exit G = dL/dM before the first token.
+ * The forward is re-run here (fp32 state, as orc_scan) to obtain X, p, u
+ * and Z; all gradient arithmetic is fp64, rounded once on output.
+ *   M [B,H,N,d_v] fp32: the state before the call (read only);
+ *   dM [B,H,N,d_v] fp32 in/out; dout [B,T,H,d_v] fp32;
+ *   dv [B,T,H,d_v], da, db [B,T,H], dw [B,T,H,W], dr [B,T,H,R] fp32 out. */
+int orc_scan_backward(const float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                      const float *rwt, const void *v, const float *a, const float *b, const float *dout,
+                      float *dM, float *dv, float *da, float *db, float *dw, float *dr, const orc_dims *d,
+                      int nthreads)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->n_sub < 1 || d->d_v < 1 || d->W < 1 || d->R < 1 ||
+        d->n_sub > 46340)
+        return ORC_EINVAL;
+    const int64_t N = d->n_sub * d->n_sub, dvv = d->d_v, W = d->W, R = d->R, T = d->T;
+    const int64_t chains = d->B * d->H;
+    int err = ORC_OK;
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        /* per chain: the forward state (fp32), the saved rows, G (fp64) */
+        float *Mc = (float *)malloc(sizeof(float) * (size_t)(N * dvv));
+        double *G = (double *)malloc(sizeof(double) * (size_t)(N * dvv));
+        float *X = (float *)malloc(sizeof(float) * (size_t)((T > 0 ? T : 1) * W * dvv));
+        float *Z = (float *)malloc(sizeof(float) * (size_t)((T > 0 ? T : 1) * R * dvv));
+        double *tmp = (double *)malloc(sizeof(double) * (size_t)(4 * dvv));
+        if (!Mc || !G || !X || !Z || !tmp) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t ch = 0; ch < chains; ++ch) {
+            if (!Mc || !G || !X || !Z || !tmp || err) continue;
+            const int64_t bb = ch / d->H, h = ch % d->H;
+            double *p = tmp, *u = tmp + dvv, *du = tmp + 2 * dvv, *dp = tmp + 3 * dvv;
+            memcpy(Mc, M + ch * N * dvv, sizeof(float) * (size_t)(N * dvv));
+            /* forward, saving the pre-write write rows and the post-write read rows */
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t row = (bb * T + t) * d->H + h;
+                const int32_t *wi = widx + row * W, *ri = ridx + row * R;
+                const float *ww = wwt + row * W;
+                for (int64_t j = 0; j < W; ++j) {
+                    if (wi[j] < 0 || wi[j] >= N) err = ORC_EINDEX;
+                    for (int64_t jj = 0; jj < j; ++jj)
+                        if (wi[jj] == wi[j]) err = ORC_EINDEX; /* write slots must be distinct */
+                }
+                for (int64_t j = 0; j < R; ++j)
+                    if (ri[j] < 0 || ri[j] >= N) err = ORC_EINDEX;
+                if (err) break;
+                const double at = (double)a[row], bt = (double)b[row];
+                for (int64_t c = 0; c < dvv; ++c) p[c] = 0.0;
+                for (int64_t j = 0; j < W; ++j) {
+                    memcpy(X + (t * W + j) * dvv, Mc + (int64_t)wi[j] * dvv, sizeof(float) * (size_t)dvv);
+                    for (int64_t c = 0; c < dvv; ++c) p[c] += (double)ww[j] * (double)Mc[(int64_t)wi[j] * dvv + c];
+                }
+                for (int64_t c = 0; c < dvv; ++c) u[c] = load_in(v, d->in_bf16, row * dvv + c) - at * p[c];
+                for (int64_t j = 0; j < W; ++j) {
+                    float *Mr = Mc + (int64_t)wi[j] * dvv;
+                    const double bw = bt * (double)ww[j];
+                    for (int64_t c = 0; c < dvv; ++c) Mr[c] = (float)(at * (double)Mr[c] + bw * u[c]);
+                }
+                for (int64_t i = 0; i < R; ++i)
+                    memcpy(Z + (t * R + i) * dvv, Mc + (int64_t)ri[i] * dvv, sizeof(float) * (size_t)dvv);
+            }
+            if (err) continue;
+            /* reverse */
+            for (int64_t e = 0; e < N * dvv; ++e) G[e] = (double)dM[ch * N * dvv + e];
+            for (int64_t t = T - 1; t >= 0; --t) {
+                const int64_t row = (bb * T + t) * d->H + h;
+                const int32_t *wi = widx + row * W, *ri = ridx + row * R;
+                const float *ww = wwt + row * W, *rw = rwt + row * R;
+                const float *dov = dout + row * dvv;
+                const double at = (double)a[row], bt = (double)b[row];
+                for (int64_t i = 0; i < R; ++i) {
+                    double s = 0.0;
+                    double *Gr = G + (int64_t)ri[i] * dvv;
+                    const float *Zi = Z + (t * R + i) * dvv;
+                    for (int64_t c = 0; c < dvv; ++c) {
+                        s += (double)dov[c] * (double)Zi[c];
+                        Gr[c] += (double)rw[i] * (double)dov[c];
+                    }
+                    dr[row * R + i] = (float)s;
+                }
+                for (int64_t c = 0; c < dvv; ++c) { p[c] = 0.0; du[c] = 0.0; }
+                for (int64_t j = 0; j < W; ++j) {
+                    const float *Xj = X + (t * W + j) * dvv;
+                    const double *Gw = G + (int64_t)wi[j] * dvv;
+                    for (int64_t c = 0; c < dvv; ++c) {
+                        p[c] += (double)ww[j] * (double)Xj[c];
+                        du[c] += (double)ww[j] * Gw[c];
+                    }
+                }
+                double sa = 0.0, sb = 0.0;
+                for (int64_t c = 0; c < dvv; ++c) {
+                    du[c] *= bt;
+                    u[c] = load_in(v, d->in_bf16, row * dvv + c) - at * p[c];
+                    dp[c] = -at * du[c];
+                    sa -= p[c] * du[c];
+                    dv[row * dvv + c] = (float)du[c];
+                }
+                for (int64_t j = 0; j < W; ++j) {
+                    const float *Xj = X + (t * W + j) * dvv;
+                    double *Gw = G + (int64_t)wi[j] * dvv;
+                    double yu = 0.0, px = 0.0, yx = 0.0;
+                    for (int64_t c = 0; c < dvv; ++c) {
+                        yu += Gw[c] * u[c];
+                        px += dp[c] * (double)Xj[c];
+                        yx += Gw[c] * (double)Xj[c];
+                        Gw[c] = at * Gw[c] + (double)ww[j] * dp[c];
+                    }
+                    dw[row * W + j] = (float)(bt * yu + px);
+                    sa += yx;
+                    sb += (double)ww[j] * yu;
+                }
+                da[row] = (float)sa;
+                db[row] = (float)sb;
+            }
+            for (int64_t e = 0; e < N * dvv; ++e) dM[ch * N * dvv + e] = (float)G[e];
+        }
+        free(Mc); free(G); free(X); free(Z); free(tmp);
+    }
+    return err;
+}
