@@ -138,6 +138,45 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
                             const sdm_dims *dims, sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * sdm_scan_forward_save -- sdm_scan_forward that also saves, for the
+ * backward pass, the rows each token used:
+ *   xsave [B,H,T,W,d_v] fp32: the write rows before the token's write;
+ *   zsave [B,H,T,R,d_v] fp32: the read rows after it (what o_t sums).
+ * Everything else as sdm_scan_forward (same results, bit for bit).  One
+ * (sequence, head) of xsave or zsave must stay below 2 GiB
+ * (SDM_ERR_UNSUPPORTED otherwise; split T into chunks).
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_scan_forward_save(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                 const float *rwt, const void *v, const float *a, const float *b,
+                                 float *o, float *xsave, float *zsave, void *workspace,
+                                 size_t workspace_bytes, const sdm_dims *dims, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * sdm_scan_backward -- reverse-mode gradients of sdm_scan_forward ([P]
+ * Sec. 3.1 steps 2-3, Eq. 4, differentiated; the pages print no backward
+ * pass).  For a loss L with dL/do_t = dout [B,T,H,d_v] fp32 and dL/dM after
+ * the call = dM on entry ([B,H,N,d_v] fp32; zeros if L does not see the
+ * final state), writes
+ *   dM  <- dL/dM before the call (in place),
+ *   dv [B,T,H,d_v], da, db [B,T,H], dw [B,T,H,W], dr [B,T,H,R]  (fp32),
+ * the gradients with respect to v, the gates and the write and read weights.
+ * xsave, zsave: from sdm_scan_forward_save of the same call.  Same slot
+ * lists, weights, v, a, b as the forward.  Per token, in reverse:
+ *   dr_i = <do, Z_i>;  G[r_i] += r_i do;  dY_j = G[s_j];  p = sum_j w_j X_j;
+ *   u = v - a p;  du = b sum_j w_j dY_j;  dv = du;  dp = -a du;
+ *   da = sum_j <dY_j, X_j> - <p, du>;  db = sum_j w_j <dY_j, u>;
+ *   dw_j = b <dY_j, u> + <dp, X_j>;  G[s_j] = a dY_j + w_j dp.
+ * fp32 arithmetic, every sum in a fixed order (deterministic).  Uses B, T,
+ * H, n_sub, d_v (<= 256), W, R, in_dtype.  Outputs must not overlap dM or
+ * each other.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                             const float *rwt, const void *v, const float *a, const float *b,
+                             const float *dout, const float *xsave, const float *zsave, float *dv,
+                             float *da, float *db, float *dw, float *dr, const sdm_dims *dims,
+                             sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * sdm_decode_step -- one new token for each of B sequences: the addressing of
  * sdm_pkm_address and one step of sdm_scan_forward fused in one launch
  * ([P] Sec. 3.1 steps 1-3 for T = 1).

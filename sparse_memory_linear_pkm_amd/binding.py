@@ -55,6 +55,8 @@ def load_library():
         "sdm_gates": [P, P, P, P, D, P, P, P],
         "sdm_output_norm_gate": [P, P, P, ctypes.c_float, D, P, P],
         "sdm_gdn_dense_forward": [P, P, P, P, P, P, P, D, P],
+        "sdm_scan_forward_save": [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
+        "sdm_scan_backward": [P] * 16 + [D, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -181,6 +183,26 @@ def sdm_output_norm_gate(o, g, gamma, eps: float, dims: SdmDims, y, stream=None,
                                              _ptr(y), _stream(stream))
     if check:
         _check(st, "sdm_output_norm_gate")
+    return st
+
+
+def sdm_scan_forward_save(M, widx, wwt, ridx, rwt, v, a, b, o, xsave, zsave, workspace, workspace_bytes: int,
+                          dims: SdmDims, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_scan_forward_save(_ptr(M), _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _ptr(v),
+                                              _ptr(a), _ptr(b), _ptr(o), _ptr(xsave), _ptr(zsave), _ptr(workspace),
+                                              int(workspace_bytes), ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_scan_forward_save")
+    return st
+
+
+def sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr, dims: SdmDims,
+                      stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_scan_backward(_ptr(dM), _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _ptr(v), _ptr(a),
+                                          _ptr(b), _ptr(dout), _ptr(xsave), _ptr(zsave), _ptr(dv), _ptr(da),
+                                          _ptr(db), _ptr(dw), _ptr(dr), ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_scan_backward")
     return st
 
 
@@ -333,3 +355,38 @@ def gdn_dense_forward(S, k, q, v, a, b, dims: SdmDims, o=None, stream=None):
     _expect(o, (B, T, H, dims.d_v), torch.float32, "o")
     sdm_gdn_dense_forward(S, k, q, v, a, b, o, dims, stream)
     return o
+
+
+def scan_forward_save(M, widx, wwt, ridx, rwt, v, a, b, dims: SdmDims, o=None, workspace=None, stream=None):
+    """scan_forward that also returns the saved rows (xsave, zsave) for scan_backward."""
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    dev = M.device
+    if o is None:
+        o = torch.empty((B, T, H, dims.d_v), dtype=torch.float32, device=dev)
+    xsave = torch.empty((B, H, T, dims.W, dims.d_v), dtype=torch.float32, device=dev)
+    zsave = torch.empty((B, H, T, dims.R, dims.d_v), dtype=torch.float32, device=dev)
+    need = sdm_scan_workspace_size(dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sdm_scan_forward_save(M, widx, wwt, ridx, rwt, v, a, b, o, xsave, zsave, workspace, ws_bytes, dims, stream)
+    return o, xsave, zsave
+
+
+def scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dims: SdmDims, stream=None):
+    """Gradients of the scan; dM is updated in place (dL/dM after -> before the
+    call).  Returns (dv, da, db, dw, dr)."""
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    dev = dM.device
+    _expect(dout, (B, T, H, dims.d_v), torch.float32, "dout")
+    _expect(xsave, (B, H, T, dims.W, dims.d_v), torch.float32, "xsave")
+    _expect(zsave, (B, H, T, dims.R, dims.d_v), torch.float32, "zsave")
+    dv = torch.empty((B, T, H, dims.d_v), dtype=torch.float32, device=dev)
+    da = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    db = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    dw = torch.empty((B, T, H, dims.W), dtype=torch.float32, device=dev)
+    dr = torch.empty((B, T, H, dims.R), dtype=torch.float32, device=dev)
+    sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr, dims, stream)
+    return dv, da, db, dw, dr

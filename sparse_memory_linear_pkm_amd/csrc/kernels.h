@@ -57,6 +57,10 @@ struct ScanArgs {
     float *o;
     int64_t B, T;
     int H, N, d_v, W, R;
+    // optional (both or neither): the rows each token used, for the backward
+    // pass: xsave [B,H,T,W,d_v] the write rows before the write, zsave
+    // [B,H,T,R,d_v] the read rows after it
+    float *xsave = nullptr, *zsave = nullptr;
 };
 
 
@@ -123,6 +127,20 @@ struct GdnArgs {
     int H, d_k, d_v;            // d_k in {16, 32, 64, 128, 256}
 };
 
+struct BwdArgs {
+    float *dM;                         // [B,H,N,d_v]: dL/dM after the call in, before it out
+    const int32_t *widx, *ridx;        // [B,T,H,W], [B,T,H,R]
+    const float *wwt, *rwt;
+    const void *v;                     // [B,T,H,d_v]
+    const float *a, *b;                // [B,T,H]
+    const float *dout;                 // [B,T,H,d_v]
+    const float *xsave, *zsave;        // [B,H,T,W,d_v], [B,H,T,R,d_v] from the forward
+    float *dv, *da, *db, *dw, *dr;     // [B,T,H,d_v], [B,T,H] x2, [B,T,H,W], [B,T,H,R]
+    int64_t B, T;
+    int H, N, d_v, W, R;               // d_v a multiple of 32, <= 256
+};
+
+hipError_t launch_scan_backward(const BwdArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gdn_dense(const GdnArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gates(const GateArgs &args, hipStream_t stream);
 hipError_t launch_out_norm_gate(const NormArgs &args, bool bf16, hipStream_t stream);

@@ -165,10 +165,37 @@ size_t sdm_scan_workspace_size(const sdm_dims *d)
                                      d->in_dtype == SDM_BF16);
 }
 
+static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                    const float *rwt, const void *v, const float *a, const float *b, float *o,
+                                    float *xsave, float *zsave, void *workspace, size_t workspace_bytes,
+                                    const sdm_dims *d, sdm_stream_t stream);
+
 sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
                             const float *rwt, const void *v, const float *a, const float *b,
                             float *o, void *workspace, size_t workspace_bytes, const sdm_dims *d,
                             sdm_stream_t stream)
+{
+    return scan_forward_impl(M, widx, wwt, ridx, rwt, v, a, b, o, nullptr, nullptr, workspace, workspace_bytes, d,
+                             stream);
+}
+
+sdm_status sdm_scan_forward_save(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                 const float *rwt, const void *v, const float *a, const float *b, float *o,
+                                 float *xsave, float *zsave, void *workspace, size_t workspace_bytes,
+                                 const sdm_dims *d, sdm_stream_t stream)
+{
+    if (d && d->B * d->T > 0 && (!xsave || !zsave))
+        return fail(SDM_ERR_INVALID_ARG, "xsave and zsave must be non-NULL");
+    if (!xsave || !zsave) return scan_forward_impl(M, widx, wwt, ridx, rwt, v, a, b, o, nullptr, nullptr, workspace,
+                                                   workspace_bytes, d, stream);
+    return scan_forward_impl(M, widx, wwt, ridx, rwt, v, a, b, o, xsave, zsave, workspace, workspace_bytes, d,
+                             stream);
+}
+
+static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                    const float *rwt, const void *v, const float *a, const float *b, float *o,
+                                    float *xsave, float *zsave, void *workspace, size_t workspace_bytes,
+                                    const sdm_dims *d, sdm_stream_t stream)
 {
     sdm_status st = check_memory_dims(d);
     if (st != SDM_OK) return st;
@@ -215,9 +242,20 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
             overlap(workspace, need, b, 4 * rows))
             return fail(SDM_ERR_INVALID_ARG, "workspace overlaps an input or output");
     }
+    if (xsave) {
+        if (!aligned(xsave, 16) || !aligned(zsave, 16)) return fail(SDM_ERR_INVALID_ARG, "xsave and zsave must be 16-byte aligned");
+        const uint64_t per = (uint64_t)d->T * (uint64_t)(d->W > d->R ? d->W : d->R) * (uint64_t)d->d_v * 4u;
+        if (per >= (1ull << 31))
+            return fail(SDM_ERR_UNSUPPORTED, "T too large to save: one (sequence, head) of xsave or zsave must stay below 2 GiB");
+        const size_t xb = sizeof(float) * (size_t)(rows * d->W * d->d_v), zb = sizeof(float) * (size_t)(rows * d->R * d->d_v);
+        if (overlap(xsave, xb, zsave, zb) || overlap(xsave, xb, M, msz) || overlap(zsave, zb, M, msz) ||
+            overlap(xsave, xb, o, osz) || overlap(zsave, zb, o, osz) || overlap(xsave, xb, workspace, need) ||
+            overlap(zsave, zb, workspace, need))
+            return fail(SDM_ERR_INVALID_ARG, "xsave or zsave overlaps another buffer");
+    }
     if (rows == 0) return SDM_OK;
     sdm::ScanArgs A{M, widx, wwt, ridx, rwt, v, a, b, o, d->B, d->T, (int)d->H, (int)N, (int)d->d_v,
-                    (int)d->W, (int)d->R};
+                    (int)d->W, (int)d->R, xsave, zsave};
     hipError_t e = sdm::launch_scan(A, d->in_dtype == SDM_BF16, workspace, workspace_bytes,
                                     as_stream(stream));
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan_forward launch");
@@ -341,6 +379,47 @@ sdm_status sdm_gdn_dense_forward(float *S, const void *k, const void *q, const v
     sdm::GdnArgs A{S, k, q, v, a, b, o, d->B, d->T, (int)d->H, (int)d->d_k, (int)d->d_v};
     hipError_t e = sdm::launch_gdn_dense(A, d->in_dtype == SDM_BF16, as_stream(stream));
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_gdn_dense_forward launch");
+}
+
+sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, const int32_t *ridx, const float *rwt,
+                             const void *v, const float *a, const float *b, const float *dout, const float *xsave,
+                             const float *zsave, float *dv, float *da, float *db, float *dw, float *dr,
+                             const sdm_dims *d, sdm_stream_t stream)
+{
+    sdm_status st = check_memory_dims(d);
+    if (st != SDM_OK) return st;
+    if (d->T < 0) return fail(SDM_ERR_INVALID_ARG, "T must be >= 0");
+    if (d->in_dtype != SDM_F32 && d->in_dtype != SDM_BF16)
+        return fail(SDM_ERR_INVALID_ARG, "in_dtype must be SDM_F32 or SDM_BF16");
+    if (d->W < 1 || d->R < 1) return fail(SDM_ERR_INVALID_ARG, "need W, R >= 1");
+    if (d->W > kMaxList || d->R > kMaxList)
+        return fail(SDM_ERR_UNSUPPORTED, "W and R must be <= %lld", (long long)kMaxList);
+    if (d->d_v > 256) return fail(SDM_ERR_UNSUPPORTED, "the backward scan needs d_v <= 256");
+    if (d->B * d->T == 0) return SDM_OK;
+    if (!dM || !widx || !wwt || !ridx || !rwt || !v || !a || !b || !dout || !xsave || !zsave || !dv || !da || !db ||
+        !dw || !dr)
+        return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(dM, 16) || !aligned(dout, 16) || !aligned(xsave, 16) || !aligned(zsave, 16) || !aligned(dv, 16) ||
+        !aligned(v, d->in_dtype == SDM_BF16 ? 8 : 16))
+        return fail(SDM_ERR_INVALID_ARG, "dM, dout, xsave, zsave and dv must be 16-byte aligned, v 8 (bf16) or 16");
+    if (!aligned(widx, 4) || !aligned(wwt, 4) || !aligned(ridx, 4) || !aligned(rwt, 4) || !aligned(a, 4) ||
+        !aligned(b, 4) || !aligned(da, 4) || !aligned(db, 4) || !aligned(dw, 4) || !aligned(dr, 4))
+        return fail(SDM_ERR_INVALID_ARG, "index, weight, gate and gradient arrays must be 4-byte aligned");
+    const int64_t N = d->n_sub * d->n_sub, rows = d->B * d->T * d->H;
+    const size_t msz = sizeof(float) * (size_t)(d->B * d->H * N * d->d_v);
+    const size_t vsz = sizeof(float) * (size_t)(rows * d->d_v);
+    const size_t outs[5] = {vsz, sizeof(float) * (size_t)rows, sizeof(float) * (size_t)rows,
+                            sizeof(float) * (size_t)(rows * d->W), sizeof(float) * (size_t)(rows * d->R)};
+    const void *optr[5] = {dv, da, db, dw, dr};
+    for (int i = 0; i < 5; ++i) {
+        if (overlap(optr[i], outs[i], dM, msz)) return fail(SDM_ERR_INVALID_ARG, "a gradient output overlaps dM");
+        for (int k = 0; k < i; ++k)
+            if (overlap(optr[i], outs[i], optr[k], outs[k])) return fail(SDM_ERR_INVALID_ARG, "gradient outputs overlap");
+    }
+    sdm::BwdArgs A{dM, widx, ridx, wwt, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr,
+                   d->B, d->T, (int)d->H, (int)N, (int)d->d_v, (int)d->W, (int)d->R};
+    hipError_t e = sdm::launch_scan_backward(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan_backward launch");
 }
 
 }  // extern "C"

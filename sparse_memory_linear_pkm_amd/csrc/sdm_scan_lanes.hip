@@ -127,7 +127,7 @@ __device__ __forceinline__ void xcd_decode(uint32_t id, uint32_t ngroups, uint32
 
 }  // namespace
 
-template <int Q, int D, int G, bool BF16>
+template <int Q, int D, int G, bool BF16, bool SAVE>
 __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, ScanStreams S)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
     constexpr int LQ = ilog2(Q), LK = ilog2(K);
     static_assert((1 << LQ) == Q, "Q is a power of two");
     constexpr int NTR = BF16 ? 1 : 2;            // 16-byte token records per chunk
-    constexpr int NVM = 6 + NTR;                 // vector-memory instructions per step (fixed)
+    constexpr int NVM = 6 + NTR + (SAVE ? 2 : 0);   // vector-memory instructions per step (fixed)
     static_assert((D - 1) * NVM <= 63, "pipeline deeper than the vmcnt range");
 
     static_assert(G == 2 || G == 4 || G == 8, "2, 4 or 8 waves per workgroup");
@@ -189,6 +189,13 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
     const uint32_t offO = (lane & (Q - 1)) == 0 ? (uint32_t)i * otok + colb : kOOB;
     float *obase = A.o + (size_t)(bb * T * H + h) * d_v;
     const uint32_t orec = (uint32_t)(K - 1) * otok + d_v * 4u;
+    // saved rows of this chain: [T][W or R][d_v] (sizes checked on the host)
+    const __amdgpu_buffer_rsrc_t Xrs =
+        SAVE ? make_rsrc(A.xsave + (size_t)ch * T * A.W * d_v, (uint32_t)((uint64_t)T * A.W * d_v * 4u))
+             : make_rsrc(A.o, 0u);
+    const __amdgpu_buffer_rsrc_t Zrs =
+        SAVE ? make_rsrc(A.zsave + (size_t)ch * T * A.R * d_v, (uint32_t)((uint64_t)T * A.R * d_v * 4u))
+             : make_rsrc(A.o, 0u);
 
     // register ring, slot = step % D
     uint4 lr[D];              // lane record of step s
@@ -301,6 +308,7 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
                 return lds_read16(lds_addr(&ring[rs][r][(wave + r) & (G - 1)]));
             };
             f32x4 o;
+            f32x4 sw = xw, sr = xr;   // the write row before, the read row after (saved)
             if (!intra) {
                 const f32x4 p = weighted_rows<Q>(wj, xw);
                 o = weighted_rows<Q>(rj, xr);
@@ -311,6 +319,7 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
                     if (hr && dr == 0) xr = own;
                     o = weighted_rows<Q>(rj, xr);
                 }
+                sr = xr;
             } else {
                 // Rounds: a token commits (writes its rows, takes its output)
                 // once every earlier token of the step it takes a row from has
@@ -338,7 +347,11 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
                     const f32x4 own = own_row(cr);
                     if (hr && dr == 0) yr = own;
                     const f32x4 o2 = weighted_rows<Q>(rj, yr);
-                    if (ready) ok = o2;
+                    if (ready) {
+                        ok = o2;
+                        sw = yw;
+                        sr = yr;
+                    }
                     const uint64_t rb = __builtin_amdgcn_ballot_w64(ready);
 #pragma unroll
                     for (int t = 0; t < K; ++t) done |= (uint32_t)((rb >> (t * Q)) & 1u) << t;
@@ -358,6 +371,14 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
                 const __amdgpu_buffer_rsrc_t Ors = make_rsrc(obase, orec);
                 __builtin_amdgcn_raw_buffer_store_b128(o, Ors, i < rem ? offO : kOOB, 0, 0);
                 obase += (size_t)K * H * d_v;
+                if constexpr (SAVE) {
+                    const int j = lane & (Q - 1);
+                    const uint32_t ut = (uint32_t)u;
+                    const uint32_t offx = (i < rem && j < A.W) ? ((ut * (uint32_t)A.W + j) * d_v) * 4u + colb : kOOB;
+                    const uint32_t offz = (i < rem && j < A.R) ? ((ut * (uint32_t)A.R + j) * d_v) * 4u + colb : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(sw, Xrs, offx, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(sr, Zrs, offz, 0, 0);
+                }
             }
             // ---- issue step + D (its gathers overwrite gath[s], read by
             // every wave before the barrier above) ----
@@ -375,7 +396,12 @@ template <int Q, int D, int G, bool BF16>
 static hipError_t launch_lanes(const ScanArgs &A, const ScanStreams &S, hipStream_t st)
 {
     const int64_t groups = A.B * A.H * (A.d_v / 4) / G;
-    hipLaunchKernelGGL((sdm_scan_lanes_kernel<Q, D, G, BF16>), dim3((unsigned)groups), dim3(64 * G), 0, st, A, S);
+    if (A.xsave)
+        hipLaunchKernelGGL((sdm_scan_lanes_kernel<Q, D, G, BF16, true>), dim3((unsigned)groups), dim3(64 * G), 0, st,
+                           A, S);
+    else
+        hipLaunchKernelGGL((sdm_scan_lanes_kernel<Q, D, G, BF16, false>), dim3((unsigned)groups), dim3(64 * G), 0,
+                           st, A, S);
     return hipGetLastError();
 }
 

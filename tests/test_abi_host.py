@@ -213,3 +213,26 @@ def test_gdn_rejects_bad_arguments():
     assert call(good_dims(), q=FAKE + (2 << 30) + 8) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(), o=FAKE + 4) == sdm.SDM_ERR_INVALID_ARG          # o over S
     assert call(good_dims(T=0), S=None, k=None) == sdm.SDM_OK
+
+
+def test_scan_backward_rejects_bad_arguments():
+    def call(dims, **ptrs):
+        names = ("dM", "widx", "wwt", "ridx", "rwt", "v", "a", "b", "dout", "xs", "zs", "dv", "da", "db", "dw", "dr")
+        p = {n: FAKE + (i << 30) for i, n in enumerate(names)}
+        p.update(ptrs)
+        return sdm.sdm_scan_backward(*(p[n] for n in names), dims, stream=0, check=False)
+    assert call(good_dims(d_v=512)) == sdm.SDM_ERR_UNSUPPORTED
+    assert call(good_dims(W=65, k_prime=16)) == sdm.SDM_ERR_UNSUPPORTED
+    assert call(good_dims(W=0)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), xs=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dv=FAKE + (11 << 30) + 4) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), da=FAKE + (11 << 30)) == sdm.SDM_ERR_INVALID_ARG   # da over dv
+    assert call(good_dims(T=0), dM=None) == sdm.SDM_OK
+
+
+def test_scan_forward_save_needs_both_buffers():
+    dims = good_dims()
+    args = [FAKE + (i << 30) for i in range(9)]
+    st = sdm.sdm_scan_forward_save(*args, None, FAKE + (10 << 30), FAKE + (11 << 30), 1 << 40, dims, stream=0,
+                                   check=False)
+    assert st == sdm.SDM_ERR_INVALID_ARG

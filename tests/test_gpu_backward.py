@@ -1,0 +1,111 @@
+"""GPU parity of the scan's gradients (sdm_scan_forward_save +
+sdm_scan_backward, through the C ABI) against the oracle's, and checks of
+the saved rows.
+
+Bar: every gradient (dM, dv, da, db, dw, dr) within 2e-3 x RMS of the
+oracle's, the scan's own bar; the forward with saving is bit-identical to
+the forward without.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sdm_synth as synth
+from sdm_synth import Dims
+
+from gpu_helpers import note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available()
+    return _t
+
+
+@pytest.fixture(scope="module")
+def sdm():
+    import sparse_memory_linear_pkm_amd as _s
+    _s.load_library()
+    return _s
+
+
+def close_rms(got, ref, what, bar=2e-3):
+    ref = ref.astype(np.float64)
+    scale = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 1.0
+    err = float(np.max(np.abs(got.astype(np.float64) - ref))) if ref.size else 0.0
+    note(f"{what}: max |err| / RMS = {err / max(scale, 1e-30):.2e}")
+    assert err <= bar * scale, f"{what}: max error {err:.3g} > {bar} x RMS {scale:.3g}"
+
+
+def run_case(sdm, torch, d, x, ad, seed):
+    dims = sdm.dims_from(d)
+    rng = np.random.default_rng(seed)
+    M0 = np.repeat(x["M0"][None], d.B, axis=0).copy()
+    dout = rng.normal(0, 1, (d.B, d.T, d.H, d.d_v)).astype(np.float32)
+    dMT = rng.normal(0, 1, M0.shape).astype(np.float32)
+    dev = {k: to_dev(v) for k, v in ad.items()}
+    M = to_dev(M0)
+    o, xs, zs = sdm.scan_forward_save(M, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]),
+                                      to_dev(x["a"]), to_dev(x["b"]), dims)
+    # the forward with saving gives the forward's results bit for bit
+    M2 = to_dev(M0)
+    o2 = sdm.scan_forward(M2, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]), to_dev(x["a"]),
+                          to_dev(x["b"]), dims)
+    dM = to_dev(dMT)
+    dv, da, db, dw, dr = sdm.scan_backward(dM, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]),
+                                           to_dev(x["a"]), to_dev(x["b"]), to_dev(dout), xs, zs, dims)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(o), to_host(o2)) and np.array_equal(to_host(M), to_host(M2))
+    # o is the read weights applied to the saved read rows
+    zh = to_host(zs)                                     # [B,H,T,R,d_v]
+    o_from_z = np.einsum("bthr,bhtrc->bthc", ad["rwt"].astype(np.float64), zh.astype(np.float64))
+    close_rms(to_host(o), o_from_z, "o from zsave", bar=1e-5)
+    g = oracle.scan_backward(M0, ad["widx"], ad["wwt"], ad["ridx"], ad["rwt"], x["v"], x["a"], x["b"], dout, d,
+                             dM_final=dMT)
+    for name, got in (("dM", dM), ("dv", dv), ("da", da), ("db", db), ("dw", dw), ("dr", dr)):
+        close_rms(to_host(got), g[name], name)
+
+
+CASES = {
+    "bf16_dv64_W16_hazards": (Dims(B=2, T=150, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=16, R=16), 40),
+    "f32_dv32_W8_R5": (Dims(B=3, T=97, H=1, d_k=32, n_sub=8, d_v=32, k_prime=8, W=8, R=5, in_dtype="f32"), 20),
+    "bf16_dv128_W32": (Dims(B=1, T=64, H=3, d_k=128, n_sub=32, d_v=128, k_prime=32, W=32, R=32), None),
+    "bf16_dv96_W4_R12": (Dims(B=2, T=33, H=2, d_k=128, n_sub=8, d_v=96, k_prime=8, W=4, R=12), 16),
+    "bf16_dv256_W64_R1": (Dims(B=1, T=20, H=2, d_k=128, n_sub=16, d_v=256, k_prime=16, W=64, R=1), 100),
+    "T1": (Dims(B=5, T=1, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=16, R=16), None),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_scan_backward_matches_oracle(sdm, torch, case):
+    d, pool = CASES[case]
+    note(f"scan backward {case} {d}")
+    x = synth.make_inputs(d, seed=17)
+    ad = synth.random_addressing(d, seed=17, hazard_slots=pool)
+    run_case(sdm, torch, d, x, ad, seed=3)
+
+
+def test_scan_backward_with_pkm_addressing(sdm, torch):
+    """Slot lists and weights from the GPU addressing of the small layer's
+    shape (T shortened)."""
+    d = synth.PRESETS["small"].dims.replace(B=2, T=300)
+    note(f"scan backward with PKM addressing {d}")
+    x = synth.make_inputs(d, seed=23)
+    widx, wwt, ridx, rwt = sdm.pkm_address(to_dev(x["k"]), to_dev(x["q"]), to_dev(x["C_w"]), to_dev(x["C_r"]),
+                                           sdm.dims_from(d))
+    torch.cuda.synchronize()
+    ad = dict(widx=to_host(widx), wwt=to_host(wwt), ridx=to_host(ridx), rwt=to_host(rwt))
+    run_case(sdm, torch, d, x, ad, seed=4)
+
+
+def test_scan_backward_full_size_small_layer(sdm, torch):
+    """The small layer at full size (B=4, T=4096, H=8, N=65,536, d_v=64),
+    random slot lists, every gradient element checked."""
+    d = synth.PRESETS["small"].dims
+    note(f"scan backward full size {d}")
+    x = synth.make_inputs(d, seed=29)
+    ad = synth.random_addressing(d, seed=29)
+    run_case(sdm, torch, d, x, ad, seed=5)

@@ -40,21 +40,21 @@ def lanes_asm(tmp_path_factory):
 
 
 def _kernels(asm):
-    # sdm_scan_lanes_kernel<Q, D, G, BF16>: mangled as ...ILi<Q>ELi<D>ELi<G>ELb<0|1>E...
-    pat = re.compile(r"^(_ZN3sdm21sdm_scan_lanes_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])E\w*):", re.M)
+    # sdm_scan_lanes_kernel<Q, D, G, BF16, SAVE>: mangled as ...ILi<Q>ELi<D>ELi<G>ELb<0|1>ELb<0|1>E...
+    pat = re.compile(r"^(_ZN3sdm21sdm_scan_lanes_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])ELb([01])E\w*):", re.M)
     for m in pat.finditer(asm):
         end = asm.index(".Lfunc_end", m.start())
-        yield int(m.group(3)), m.group(5) == "1", asm[m.start():end]
+        yield int(m.group(3)), m.group(5) == "1", m.group(6) == "1", asm[m.start():end]
 
 
 def test_scan_steady_state_waits(lanes_asm):
     found = 0
-    for D, bf16, body in _kernels(lanes_asm):
+    for D, bf16, save, body in _kernels(lanes_asm):
         found += 1
-        nvm = 6 + (1 if bf16 else 2)
+        nvm = 6 + (1 if bf16 else 2) + (2 if save else 0)
         waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", body)]
         tight = [w for w in waits if 0 < w < (D - 1) * nvm]
-        assert not tight, f"D={D} bf16={bf16}: waits below (D-1)*NVM = {(D - 1) * nvm}: {tight}"
+        assert not tight, f"D={D} bf16={bf16} save={save}: waits below (D-1)*NVM = {(D - 1) * nvm}: {tight}"
         # vmcnt(0) only in the prologue (twice) and after the loop (once)
-        assert waits.count(0) <= 3, f"D={D} bf16={bf16}: {waits.count(0)} full drains"
-    assert found >= 8
+        assert waits.count(0) <= 3, f"D={D} bf16={bf16} save={save}: {waits.count(0)} full drains"
+    assert found >= 16
