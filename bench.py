@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="small",
-                   choices=list(PREFILL_WORKLOADS) + ["decode", "gdn_1p4b"])
+                   choices=list(PREFILL_WORKLOADS) + ["decode", "gdn_1p4b", "train_small", "train_1p4b"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle baseline (0 disables it)")
@@ -257,6 +257,89 @@ def bench_gdn(args, sdm, synth, torch):
     print(json.dumps(result), flush=True)
 
 
+def bench_train(args, sdm, synth, torch, name):
+    """Forward with saving and the backward of the scan on a prefill layer
+    (small or 1.4B): one step = state init + PKM addressing + the scan with
+    its rows saved + the backward scan for a given dL/do (dL/dM_T = 0)."""
+    layer = {"train_small": "small", "train_1p4b": "prefill_1p4b"}[name]
+    d = synth.PRESETS[layer].dims
+    dx, _ = device_inputs(layer, d, args.seed)
+    dims = sdm.dims_from(d)
+    B, T, H, N = d.B, d.T, d.H, d.N
+    M = torch.empty((B, H, N, d.d_v), dtype=torch.float32, device="cuda")
+    dM = torch.empty_like(M)
+    widx = torch.empty((B, T, H, d.W), dtype=torch.int32, device="cuda")
+    wwt = torch.empty((B, T, H, d.W), dtype=torch.float32, device="cuda")
+    ridx = torch.empty((B, T, H, d.R), dtype=torch.int32, device="cuda")
+    rwt = torch.empty((B, T, H, d.R), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, T, H, d.d_v), dtype=torch.float32, device="cuda")
+    xs = torch.empty((B, H, T, d.d_v // 4, d.W, 4), dtype=torch.float32, device="cuda")
+    zs = torch.empty((B, H, T, d.d_v // 4, d.R, 4), dtype=torch.float32, device="cuda")
+    dout = torch.randn((B, T, H, d.d_v), dtype=torch.float32, device="cuda",
+                       generator=torch.Generator(device="cuda").manual_seed(args.seed + 1))
+    grads = [torch.empty((B, T, H, d.d_v), dtype=torch.float32, device="cuda"),
+             torch.empty((B, T, H), dtype=torch.float32, device="cuda"),
+             torch.empty((B, T, H), dtype=torch.float32, device="cuda"),
+             torch.empty((B, T, H, d.W), dtype=torch.float32, device="cuda"),
+             torch.empty((B, T, H, d.R), dtype=torch.float32, device="cuda")]
+    ws_bytes = sdm.sdm_scan_workspace_size(dims)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    timers = []
+
+    def step(timed):
+        E = lambda: torch.cuda.Event(enable_timing=timed)
+        ev = [E() for _ in range(5)]
+        ev[0].record(stream)
+        sdm.sdm_state_init(M, dx["M0"], dims, stream)
+        dM.zero_()
+        sdm.sdm_pkm_address(dx["k"], dx["q"], dx["C_w"], dx["C_r"], dims, widx, wwt, ridx, rwt, stream)
+        ev[1].record(stream)
+        sdm.sdm_scan_forward_save(M, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], o, xs, zs, ws, ws_bytes, dims,
+                                  stream)
+        ev[2].record(stream)
+        sdm.sdm_scan_backward(dM, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], dout, xs, zs, *grads, dims,
+                              stream)
+        ev[3].record(stream)
+        if timed:
+            timers.append(ev)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True); end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    avg = lambda a, b: sum(ev[a].elapsed_time(ev[b]) for ev in timers) / len(timers)
+    fwd_ms, bwd_ms = avg(1, 2), avg(2, 3)
+    th = B * T * H
+    bwd_bytes = th * 3 * (d.W + d.R) * d.d_v * 4   # G rows in and out, saved rows in
+    fwd_bytes = th * (2 * d.W + d.R + d.W + d.R) * d.d_v * 4   # the scan's rows plus the saved rows written
+    gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    result = {
+        "metric": "SDM layer training tokens/sec (addressing + scan forward with saved rows + scan backward)",
+        "value": B * T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": name, "B": B, "T": T, "H": H, "N": N, "d_v": d.d_v, "W": d.W, "R": d.R,
+                   "step": "state init + addressing + sdm_scan_forward_save + sdm_scan_backward"},
+        "wall_s_timed_region": wall,
+        "kernels_ms": {"init+address": avg(0, 1), "sdm_scan_forward_save": fwd_ms, "sdm_scan_backward": bwd_ms},
+        "roofline": {"kernel": "sdm_scan_backward_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": bwd_bytes, "avg_launch_ms": bwd_ms},
+        "forward_save": {"GB/s": fwd_bytes / (fwd_ms * 1e-3) / 1e9, "algorithmic_bytes_per_launch": fwd_bytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -286,6 +369,9 @@ def main():
     name = args.workload
     if name == "gdn_1p4b":
         bench_gdn(args, sdm, synth, torch)
+        return
+    if name.startswith("train_"):
+        bench_train(args, sdm, synth, torch, name)
         return
     d = synth.PRESETS[name].dims
     decode_mode = name == "decode"

@@ -140,8 +140,10 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
 /* ---------------------------------------------------------------------------
  * sdm_scan_forward_save -- sdm_scan_forward that also saves, for the
  * backward pass, the rows each token used:
- *   xsave [B,H,T,W,d_v] fp32: the write rows before the token's write;
- *   zsave [B,H,T,R,d_v] fp32: the read rows after it (what o_t sums).
+ *   xsave [B,H,T,d_v/4,W,4] fp32: the write rows before the token's write;
+ *   zsave [B,H,T,d_v/4,R,4] fp32: the read rows after it (what o_t sums);
+ *   both in 4-column chunks, the list positions of a chunk adjacent, so
+ *   that the lanes of one token store and load consecutive bytes.
  * Everything else as sdm_scan_forward (same results, bit for bit).  One
  * (sequence, head) of xsave or zsave must stay below 2 GiB
  * (SDM_ERR_UNSUPPORTED otherwise; split T into chunks).

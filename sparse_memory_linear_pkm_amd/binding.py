@@ -364,8 +364,8 @@ def scan_forward_save(M, widx, wwt, ridx, rwt, v, a, b, dims: SdmDims, o=None, w
     dev = M.device
     if o is None:
         o = torch.empty((B, T, H, dims.d_v), dtype=torch.float32, device=dev)
-    xsave = torch.empty((B, H, T, dims.W, dims.d_v), dtype=torch.float32, device=dev)
-    zsave = torch.empty((B, H, T, dims.R, dims.d_v), dtype=torch.float32, device=dev)
+    xsave = torch.empty((B, H, T, dims.d_v // 4, dims.W, 4), dtype=torch.float32, device=dev)
+    zsave = torch.empty((B, H, T, dims.d_v // 4, dims.R, 4), dtype=torch.float32, device=dev)
     need = sdm_scan_workspace_size(dims)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -381,8 +381,8 @@ def scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dims: S
     B, T, H = dims.B, dims.T, dims.H
     dev = dM.device
     _expect(dout, (B, T, H, dims.d_v), torch.float32, "dout")
-    _expect(xsave, (B, H, T, dims.W, dims.d_v), torch.float32, "xsave")
-    _expect(zsave, (B, H, T, dims.R, dims.d_v), torch.float32, "zsave")
+    _expect(xsave, (B, H, T, dims.d_v // 4, dims.W, 4), torch.float32, "xsave")
+    _expect(zsave, (B, H, T, dims.d_v // 4, dims.R, 4), torch.float32, "zsave")
     dv = torch.empty((B, T, H, dims.d_v), dtype=torch.float32, device=dev)
     da = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     db = torch.empty((B, T, H), dtype=torch.float32, device=dev)

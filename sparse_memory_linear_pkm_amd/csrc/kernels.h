@@ -58,8 +58,9 @@ struct ScanArgs {
     int64_t B, T;
     int H, N, d_v, W, R;
     // optional (both or neither): the rows each token used, for the backward
-    // pass: xsave [B,H,T,W,d_v] the write rows before the write, zsave
-    // [B,H,T,R,d_v] the read rows after it
+    // pass: xsave [B,H,T,d_v/4,W,4] the write rows before the write, zsave
+    // [B,H,T,d_v/4,R,4] the read rows after it (4-column chunks, the list
+    // positions of a chunk adjacent)
     float *xsave = nullptr, *zsave = nullptr;
 };
 
@@ -134,7 +135,7 @@ struct BwdArgs {
     const void *v;                     // [B,T,H,d_v]
     const float *a, *b;                // [B,T,H]
     const float *dout;                 // [B,T,H,d_v]
-    const float *xsave, *zsave;        // [B,H,T,W,d_v], [B,H,T,R,d_v] from the forward
+    const float *xsave, *zsave;        // [B,H,T,d_v/4,W,4], [B,H,T,d_v/4,R,4] from the forward
     float *dv, *da, *db, *dw, *dr;     // [B,T,H,d_v], [B,T,H] x2, [B,T,H,W], [B,T,H,R]
     int64_t B, T;
     int H, N, d_v, W, R;               // d_v a multiple of 32, <= 256

@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
     const uint32_t offO = (lane & (Q - 1)) == 0 ? (uint32_t)i * otok + colb : kOOB;
     float *obase = A.o + (size_t)(bb * T * H + h) * d_v;
     const uint32_t orec = (uint32_t)(K - 1) * otok + d_v * 4u;
-    // saved rows of this chain: [T][W or R][d_v] (sizes checked on the host)
+    // saved rows of this chain: [T][d_v/4][W or R][4] (sizes checked on the host)
     const __amdgpu_buffer_rsrc_t Xrs =
         SAVE ? make_rsrc(A.xsave + (size_t)ch * T * A.W * d_v, (uint32_t)((uint64_t)T * A.W * d_v * 4u))
              : make_rsrc(A.o, 0u);
@@ -374,8 +374,10 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
                 if constexpr (SAVE) {
                     const int j = lane & (Q - 1);
                     const uint32_t ut = (uint32_t)u;
-                    const uint32_t offx = (i < rem && j < A.W) ? ((ut * (uint32_t)A.W + j) * d_v) * 4u + colb : kOOB;
-                    const uint32_t offz = (i < rem && j < A.R) ? ((ut * (uint32_t)A.R + j) * d_v) * 4u + colb : kOOB;
+                    // [T][d_v/4][W or R][4]: the Q lanes of a token write consecutive 16-byte pieces
+                    const uint32_t tck = ut * nchunk + chunk;
+                    const uint32_t offx = (i < rem && j < A.W) ? (tck * (uint32_t)A.W + j) * 16u : kOOB;
+                    const uint32_t offz = (i < rem && j < A.R) ? (tck * (uint32_t)A.R + j) * 16u : kOOB;
                     __builtin_amdgcn_raw_buffer_store_b128(sw, Xrs, offx, 0, 0);
                     __builtin_amdgcn_raw_buffer_store_b128(sr, Zrs, offz, 0, 0);
                 }

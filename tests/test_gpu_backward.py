@@ -60,7 +60,8 @@ def run_case(sdm, torch, d, x, ad, seed):
     torch.cuda.synchronize()
     assert np.array_equal(to_host(o), to_host(o2)) and np.array_equal(to_host(M), to_host(M2))
     # o is the read weights applied to the saved read rows
-    zh = to_host(zs)                                     # [B,H,T,R,d_v]
+    zh = to_host(zs)                                     # [B,H,T,d_v/4,R,4]
+    zh = zh.transpose(0, 1, 2, 4, 3, 5).reshape(d.B, d.H, d.T, d.R, d.d_v)
     o_from_z = np.einsum("bthr,bhtrc->bthc", ad["rwt"].astype(np.float64), zh.astype(np.float64))
     close_rms(to_host(o), o_from_z, "o from zsave", bar=1e-5)
     g = oracle.scan_backward(M0, ad["widx"], ad["wwt"], ad["ridx"], ad["rwt"], x["v"], x["a"], x["b"], dout, d,
