@@ -10,7 +10,7 @@ import pytest
 import sdm_synth as synth
 from sdm_synth import Dims
 
-from gpu_helpers import note, to_host
+from gpu_helpers import note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -77,3 +77,73 @@ def test_graph_capture_replays_match_eager(sdm, torch):
         torch.cuda.synchronize()
         for name, t, r in zip(("M", "widx", "wwt", "ridx", "rwt", "o", "o1", "wo", "ro"), outs, ref):
             np.testing.assert_array_equal(to_host(t), r, err_msg=f"replay {rep}: {name}")
+
+
+def test_graph_capture_training_step_and_layer_edges(sdm, torch):
+    """The other entry points under capture: gates, the scan with its rows
+    saved, the backward scan, the output norm and gate, and the dense
+    recurrence; three replays, each bit-identical to the eager run."""
+    d = Dims(B=2, T=40, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=8, R=8)
+    note(f"graph capture, training step {d}")
+    x = synth.make_inputs(d, seed=31)
+    ad = synth.random_addressing(d, seed=31, hazard_slots=40)
+    e = synth.make_layer_edge_inputs(d, seed=31)
+    g = synth.make_gdn_inputs(d.replace(d_k=64), seed=31)
+    dims, gdims = sdm.dims_from(d), sdm.dims_from(d.replace(d_k=64))
+    T = torch
+    dev = {k: to_dev(v) for k, v in ad.items()}
+    M0 = to_dev(np.repeat(x["M0"][None], d.B, axis=0).copy())
+    M = T.empty_like(M0)
+    dM = T.empty_like(M0)
+    o = T.empty((d.B, d.T, d.H, d.d_v), dtype=T.float32, device="cuda")
+    xs = T.empty((d.B, d.H, d.T, d.d_v // 4, d.W, 4), dtype=T.float32, device="cuda")
+    zs = T.empty((d.B, d.H, d.T, d.d_v // 4, d.R, 4), dtype=T.float32, device="cuda")
+    dout = to_dev(np.random.default_rng(2).normal(0, 1, (d.B, d.T, d.H, d.d_v)).astype(np.float32))
+    grads = [T.empty((d.B, d.T, d.H, d.d_v), dtype=T.float32, device="cuda"),
+             T.empty((d.B, d.T, d.H), dtype=T.float32, device="cuda"),
+             T.empty((d.B, d.T, d.H), dtype=T.float32, device="cuda"),
+             T.empty((d.B, d.T, d.H, d.W), dtype=T.float32, device="cuda"),
+             T.empty((d.B, d.T, d.H, d.R), dtype=T.float32, device="cuda")]
+    a_g = T.empty((d.B, d.T, d.H), dtype=T.float32, device="cuda")
+    b_g = T.empty_like(a_g)
+    y = T.empty((d.B, d.T, d.H, d.d_v), dtype=T.bfloat16, device="cuda")
+    S0 = to_dev(g["S0"])
+    S = T.empty_like(S0)
+    og = T.empty((d.B, d.T, d.H, d.d_v), dtype=T.float32, device="cuda")
+    ws_bytes = sdm.sdm_scan_workspace_size(dims)
+    ws = T.empty(max(ws_bytes, 1), dtype=T.uint8, device="cuda")
+    inp = {k: to_dev(v) for k, v in e.items()}
+    gin = {k: to_dev(v) for k, v in g.items() if k != "S0"}
+    xv = to_dev(x["v"])
+
+    def step():
+        sdm.sdm_gates(inp["a_raw"], inp["b_raw"], inp["A"], inp["dt_bias"], dims, a_g, b_g)
+        M.copy_(M0)
+        dM.zero_()
+        sdm.sdm_scan_forward_save(M, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], xv, a_g, b_g, o, xs, zs, ws,
+                                  ws_bytes, dims)
+        sdm.sdm_scan_backward(dM, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], xv, a_g, b_g, dout, xs, zs,
+                              *grads, dims)
+        sdm.sdm_output_norm_gate(o, inp["g"], inp["gamma"], 1e-5, dims, y)
+        S.copy_(S0)
+        sdm.sdm_gdn_dense_forward(S, gin["k"], gin["q"], gin["v"], gin["a"], gin["b"], og, gdims)
+
+    outs = (a_g, b_g, M, dM, o, xs, zs, *grads, y, S, og)
+    step()
+    T.cuda.synchronize()
+    ref = [to_host(t).copy() for t in outs]
+    gr = T.cuda.CUDAGraph()
+    side = T.cuda.Stream()
+    side.wait_stream(T.cuda.current_stream())
+    with T.cuda.stream(side):
+        with T.cuda.graph(gr):
+            step()
+    T.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        T.cuda.synchronize()
+        gr.replay()
+        T.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(outs, ref)):
+            np.testing.assert_array_equal(to_host(t), r, err_msg=f"replay {rep}: output {i}")
