@@ -60,9 +60,10 @@ def _load():
         lib.orc_output_norm_gate.argtypes = [P, P, P, ctypes.c_double, ctypes.POINTER(_Dims), P]
         lib.orc_gdn_dense.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(_Dims), I32]
         lib.orc_scan_backward.argtypes = [P] * 15 + [ctypes.POINTER(_Dims), I32]
+        lib.orc_address_backward.argtypes = [P] * 10 + [ctypes.POINTER(_Dims), P, P, P, P]
         for f in (lib.orc_address, lib.orc_half_scores, lib.orc_slot_scores, lib.orc_scan,
                   lib.orc_state_init, lib.orc_gates, lib.orc_output_norm_gate, lib.orc_gdn_dense,
-                  lib.orc_scan_backward):
+                  lib.orc_scan_backward, lib.orc_address_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -281,3 +282,21 @@ def scan_backward(M, widx, wwt, ridx, rwt, v, a, b, dout, d, dM_final=None, *, n
                                  _p(out["dr"]), ctypes.byref(dm), nthreads or default_threads()),
            "orc_scan_backward")
     return out
+
+
+def address_backward(k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr, d):
+    """Gradients of the addressing with the selected slots held fixed, for
+    dL/dwwt = dw and dL/drwt = dr.  Returns (dk, dq, dC_w, dC_r), float32."""
+    lib = _load()
+    k, q, C_w, C_r = (_in(x, d) for x in (k, q, C_w, C_r))
+    widx, ridx = (np.ascontiguousarray(x, np.int32) for x in (widx, ridx))
+    wwt, rwt, dw, dr = (np.ascontiguousarray(x, np.float32) for x in (wwt, rwt, dw, dr))
+    dk = np.empty((d.B, d.T, d.H, d.d_k), np.float32)
+    dq = np.empty_like(dk)
+    dCw = np.empty((d.H, 2, d.n_sub, d.d_k // 2), np.float32)
+    dCr = np.empty_like(dCw)
+    dm = _dims(d)
+    _check(lib.orc_address_backward(_p(k), _p(q), _p(C_w), _p(C_r), _p(widx), _p(wwt), _p(ridx), _p(rwt), _p(dw),
+                                    _p(dr), ctypes.byref(dm), _p(dk), _p(dq), _p(dCw), _p(dCr)),
+           "orc_address_backward")
+    return dk, dq, dCw, dCr

@@ -577,3 +577,70 @@ int orc_scan_backward(const float *M, const int32_t *widx, const float *wwt, con
     }
     return err;
 }
+
+/* ---- gradients of the addressing ------------------------------------------ */
+/* Reverse-mode derivative of orc_address for given gradients of the weights
+ * (dw [B,T,H,W] for the write lists, dr [B,T,H,R] for the read lists), with
+ * the selected slots held fixed (the selection is piecewise constant).  The
+ * chain rule through [P] Sec. 4's softmax and Sec. 2's two-half scores:
+ *   weights = softmax(sc),  sc_j = s_0[i1_j] + s_1[i2_j]  (slot_j = i1_j n_sub + i2_j)
+ *   dsc_j  = wt_j (dwt_j - sum_k wt_k dwt_k)
+ *   s_c[u] = <x_c, C[h][c][u]>:  dx_c += dsc_j C[h][c][i_c j];  dC[h][c][i_c j] += dsc_j x_c
+ * for each kind (write: x = k with C_w; read: x = q with C_r).  fp64, each
+ * output rounded once.  dk, dq [B,T,H,d_k]; dCw, dCr [H,2,n_sub,d_k/2]
+ * (written; sums over every token). */
+int orc_address_backward(const void *k, const void *q, const void *C_w, const void *C_r, const int32_t *widx,
+                         const float *wwt, const int32_t *ridx, const float *rwt, const float *dw, const float *dr,
+                         const orc_dims *d, float *dk, float *dq, float *dCw, float *dCr)
+{
+    int err = check_dims(d);
+    if (err) return err;
+    const int64_t half = d->d_k / 2, ns = d->n_sub, N = ns * ns;
+    const int64_t rows = d->B * d->T * d->H;
+    const int64_t csz = d->H * 2 * ns * half;
+    double *acc = (double *)calloc((size_t)(2 * csz), sizeof(double));
+    double *dx = (double *)malloc(sizeof(double) * (size_t)d->d_k);
+    if (!acc || !dx) {
+        free(acc); free(dx);
+        return ORC_ENOMEM;
+    }
+    for (int kind = 0; kind < 2 && !err; ++kind) {
+        const void *X = kind ? q : k, *C = kind ? C_r : C_w;
+        const int32_t *idx = kind ? ridx : widx;
+        const float *wt = kind ? rwt : wwt, *dwt = kind ? dr : dw;
+        float *dX = kind ? dq : dk;
+        double *dC = acc + kind * csz;
+        const int64_t n = kind ? d->R : d->W;
+        for (int64_t r = 0; r < rows && !err; ++r) {
+            const int64_t h = r % d->H;
+            double g = 0.0;
+            for (int64_t j = 0; j < n; ++j) g += (double)wt[r * n + j] * (double)dwt[r * n + j];
+            for (int64_t e = 0; e < d->d_k; ++e) dx[e] = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                const int32_t s = idx[r * n + j];
+                if (s < 0 || s >= N) {
+                    err = ORC_EINDEX;
+                    break;
+                }
+                const double dsc = (double)wt[r * n + j] * ((double)dwt[r * n + j] - g);
+                const int64_t iu[2] = {s / ns, s % ns};
+                for (int c = 0; c < 2; ++c) {
+                    const int64_t cb = ((h * 2 + c) * ns + iu[c]) * half;
+                    for (int64_t e = 0; e < half; ++e) {
+                        dx[c * half + e] += dsc * load_in(C, d->in_bf16, cb + e);
+                        dC[cb + e] += dsc * load_in(X, d->in_bf16, r * d->d_k + c * half + e);
+                    }
+                }
+            }
+            for (int64_t e = 0; e < d->d_k; ++e) dX[r * d->d_k + e] = (float)dx[e];
+        }
+    }
+    if (!err)
+        for (int64_t e = 0; e < csz; ++e) {
+            dCw[e] = (float)acc[e];
+            dCr[e] = (float)acc[csz + e];
+        }
+    free(acc);
+    free(dx);
+    return err;
+}
