@@ -258,9 +258,10 @@ def bench_gdn(args, sdm, synth, torch):
 
 
 def bench_train(args, sdm, synth, torch, name):
-    """Forward with saving and the backward of the scan on a prefill layer
-    (small or 1.4B): one step = state init + PKM addressing + the scan with
-    its rows saved + the backward scan for a given dL/do (dL/dM_T = 0)."""
+    """Forward with saving and the backward on a prefill layer (small or
+    1.4B): one step = state init + PKM addressing + the scan with its rows
+    saved + the backward scan for a given dL/do (dL/dM_T = 0) + the
+    addressing's backward (into k, q and the shared codebook)."""
     layer = {"train_small": "small", "train_1p4b": "prefill_1p4b"}[name]
     d = synth.PRESETS[layer].dims
     dx, _ = device_inputs(layer, d, args.seed)
@@ -284,6 +285,11 @@ def bench_train(args, sdm, synth, torch, name):
              torch.empty((B, T, H, d.R), dtype=torch.float32, device="cuda")]
     ws_bytes = sdm.sdm_scan_workspace_size(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    aws_bytes = sdm.sdm_address_backward_workspace_size(dims)
+    aws = torch.empty(max(aws_bytes, 1), dtype=torch.uint8, device="cuda")
+    dk = torch.empty((B, T, H, d.d_k), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(dk)
+    dC = torch.empty((H, 2, d.n_sub, d.d_k // 2), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     timers = []
 
@@ -301,6 +307,10 @@ def bench_train(args, sdm, synth, torch, name):
         sdm.sdm_scan_backward(dM, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], dout, xs, zs, *grads, dims,
                               stream)
         ev[3].record(stream)
+        # the codebook is shared by both kinds: one gradient buffer receives both sums
+        sdm.sdm_address_backward(dx["k"], dx["q"], dx["C_w"], dx["C_r"], widx, wwt, ridx, rwt, grads[3], grads[4],
+                                 dims, dk, dq, dC, dC, aws, aws_bytes, stream)
+        ev[4].record(stream)
         if timed:
             timers.append(ev)
 
@@ -317,20 +327,23 @@ def bench_train(args, sdm, synth, torch, name):
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(end) / args.steps
     avg = lambda a, b: sum(ev[a].elapsed_time(ev[b]) for ev in timers) / len(timers)
-    fwd_ms, bwd_ms = avg(1, 2), avg(2, 3)
+    fwd_ms, bwd_ms, abwd_ms = avg(1, 2), avg(2, 3), avg(3, 4)
     th = B * T * H
     bwd_bytes = th * 3 * (d.W + d.R) * d.d_v * 4   # G rows in and out, saved rows in
     fwd_bytes = th * (2 * d.W + d.R + d.W + d.R) * d.d_v * 4   # the scan's rows plus the saved rows written
     gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
     result = {
-        "metric": "SDM layer training tokens/sec (addressing + scan forward with saved rows + scan backward)",
+        "metric": "SDM layer training tokens/sec (addressing + scan forward with saved rows + scan backward + "
+                  "addressing backward)",
         "value": B * T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": name, "B": B, "T": T, "H": H, "N": N, "d_v": d.d_v, "W": d.W, "R": d.R,
-                   "step": "state init + addressing + sdm_scan_forward_save + sdm_scan_backward"},
+                   "step": "state init + addressing + sdm_scan_forward_save + sdm_scan_backward + "
+                           "sdm_address_backward"},
         "wall_s_timed_region": wall,
-        "kernels_ms": {"init+address": avg(0, 1), "sdm_scan_forward_save": fwd_ms, "sdm_scan_backward": bwd_ms},
+        "kernels_ms": {"init+address": avg(0, 1), "sdm_scan_forward_save": fwd_ms, "sdm_scan_backward": bwd_ms,
+                       "sdm_address_backward": abwd_ms},
         "roofline": {"kernel": "sdm_scan_backward_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_launch": bwd_bytes, "avg_launch_ms": bwd_ms},

@@ -179,6 +179,34 @@ sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, c
                              sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * sdm_address_backward_workspace_size -- bytes of device workspace
+ * sdm_address_backward needs for these dims (0 on bad dims).  Host-only.
+ * ------------------------------------------------------------------------- */
+size_t sdm_address_backward_workspace_size(const sdm_dims *dims);
+
+/* ---------------------------------------------------------------------------
+ * sdm_address_backward -- gradients of sdm_pkm_address with the selected
+ * slots held fixed (the selection is piecewise constant): [P] Sec. 2 (slot
+ * score = the sum of the two half scores, each a dot product with a
+ * sub-key) and Sec. 4 (softmax over the selected scores), differentiated:
+ *   dsc_j = w_j (dw_j - sum_k w_k dw_k)
+ *   dx[half c] += dsc_j C[h][c][i_c],   dC[h][c][i_c] += dsc_j x[half c]
+ * with i_0 = slot / n_sub, i_1 = slot % n_sub, for the write lists (x = k,
+ * C = C_w, dw = dL/dwwt) and the read lists (x = q, C = C_r, dr = dL/drwt).
+ *   widx, wwt, ridx, rwt: the forward's lists and weights;
+ *   dk, dq [B,T,H,d_k] fp32 written;
+ *   dC_w, dC_r [H,2,n_sub,d_k/2] fp32 written (sums over every token); they
+ *   may be the same buffer (a shared codebook): it then receives the sum.
+ * workspace: at least sdm_address_backward_workspace_size(dims) bytes,
+ * 16-byte aligned.  fp32 arithmetic, every sum in a fixed order.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_address_backward(const void *k, const void *q, const void *C_w, const void *C_r,
+                                const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                const float *rwt, const float *dw, const float *dr,
+                                const sdm_dims *dims, float *dk, float *dq, float *dC_w, float *dC_r,
+                                void *workspace, size_t workspace_bytes, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * sdm_decode_step -- one new token for each of B sequences: the addressing of
  * sdm_pkm_address and one step of sdm_scan_forward fused in one launch
  * ([P] Sec. 3.1 steps 1-3 for T = 1).

@@ -11,10 +11,12 @@ from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_
                       sdm_state_init, sdm_pkm_address, sdm_scan_workspace_size, sdm_scan_forward,
                       sdm_decode_step, sdm_gates, sdm_output_norm_gate, sdm_gdn_dense_forward,
                       sdm_scan_forward_save, sdm_scan_backward, scan_forward_save, scan_backward,
+                      sdm_address_backward, sdm_address_backward_workspace_size, address_backward,
                       sdm_status_string,
                       sdm_last_error, sdm_version, state_init, pkm_address, scan_forward, decode_step,
                       gates, output_norm_gate, gdn_dense_forward)
 
 __all__ = [n for n in dir() if n.startswith(("sdm_", "SDM_", "Sdm")) or n in (
     "dims_from", "lib_path", "load_library", "state_init", "pkm_address", "scan_forward",
-    "decode_step", "gates", "output_norm_gate", "gdn_dense_forward", "scan_forward_save", "scan_backward")]
+    "decode_step", "gates", "output_norm_gate", "gdn_dense_forward", "scan_forward_save", "scan_backward",
+    "address_backward")]

@@ -57,6 +57,7 @@ def load_library():
         "sdm_gdn_dense_forward": [P, P, P, P, P, P, P, D, P],
         "sdm_scan_forward_save": [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
         "sdm_scan_backward": [P] * 16 + [D, P],
+        "sdm_address_backward": [P] * 10 + [D, P, P, P, P, P, ctypes.c_size_t, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -64,6 +65,8 @@ def load_library():
         f.restype = I32
     lib.sdm_scan_workspace_size.argtypes = [D]
     lib.sdm_scan_workspace_size.restype = ctypes.c_size_t
+    lib.sdm_address_backward_workspace_size.argtypes = [D]
+    lib.sdm_address_backward_workspace_size.restype = ctypes.c_size_t
     lib.sdm_status_string.argtypes = [I32]
     lib.sdm_status_string.restype = ctypes.c_char_p
     lib.sdm_last_error.argtypes = []
@@ -203,6 +206,21 @@ def sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv,
                                           _ptr(db), _ptr(dw), _ptr(dr), ctypes.byref(dims), _stream(stream))
     if check:
         _check(st, "sdm_scan_backward")
+    return st
+
+
+def sdm_address_backward_workspace_size(dims: SdmDims) -> int:
+    return int(load_library().sdm_address_backward_workspace_size(ctypes.byref(dims)))
+
+
+def sdm_address_backward(k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr, dims: SdmDims, dk, dq, dC_w, dC_r,
+                         workspace, workspace_bytes: int, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_address_backward(_ptr(k), _ptr(q), _ptr(C_w), _ptr(C_r), _ptr(widx), _ptr(wwt),
+                                             _ptr(ridx), _ptr(rwt), _ptr(dw), _ptr(dr), ctypes.byref(dims),
+                                             _ptr(dk), _ptr(dq), _ptr(dC_w), _ptr(dC_r), _ptr(workspace),
+                                             int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "sdm_address_backward")
     return st
 
 
@@ -390,3 +408,21 @@ def scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dims: S
     dr = torch.empty((B, T, H, dims.R), dtype=torch.float32, device=dev)
     sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr, dims, stream)
     return dv, da, db, dw, dr
+
+
+def address_backward(k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr, dims: SdmDims, shared_codebook_grad=False,
+                     stream=None):
+    """Gradients of the addressing (selection held fixed).  Returns (dk, dq,
+    dC_w, dC_r); with shared_codebook_grad one buffer receives both sums and
+    is returned twice."""
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    dev = k.device
+    dk = torch.empty((B, T, H, dims.d_k), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(dk)
+    dC_w = torch.empty((H, 2, dims.n_sub, dims.d_k // 2), dtype=torch.float32, device=dev)
+    dC_r = dC_w if shared_codebook_grad else torch.empty_like(dC_w)
+    need = sdm_address_backward_workspace_size(dims)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    sdm_address_backward(k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr, dims, dk, dq, dC_w, dC_r, ws, need, stream)
+    return dk, dq, dC_w, dC_r

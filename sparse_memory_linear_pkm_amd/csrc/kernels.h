@@ -141,6 +141,20 @@ struct BwdArgs {
     int H, N, d_v, W, R;               // d_v a multiple of 32, <= 256
 };
 
+struct AddrBwdArgs {
+    const void *k, *q, *C_w, *C_r;     // as for the addressing
+    const int32_t *widx, *ridx;        // [rows, W], [rows, R]
+    const float *wwt, *rwt;            // the forward's weights
+    const float *dw, *dr;              // dL/dwwt, dL/drwt
+    float *dk, *dq;                    // [rows, d_k]
+    float *dC_w, *dC_r;                // [H,2,n_sub,d_k/2]; may be the same buffer (summed)
+    int64_t rows;                      // B*T*H
+    int H, d_k, n_sub, W, R;
+};
+
+int address_bwd_parts(int64_t BT, int64_t H, int n_sub);
+size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int n_sub, int half);
+hipError_t launch_address_backward(const AddrBwdArgs &args, bool bf16, void *workspace, hipStream_t stream);
 hipError_t launch_scan_backward(const BwdArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gdn_dense(const GdnArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gates(const GateArgs &args, hipStream_t stream);

@@ -422,4 +422,49 @@ sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, c
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan_backward launch");
 }
 
+size_t sdm_address_backward_workspace_size(const sdm_dims *d)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->W < 1 || d->R < 1 || d->d_k < 2 || (d->d_k & 1) ||
+        d->n_sub < 1 || d->W > kMaxList || d->R > kMaxList || d->d_k > 512)
+        return 0;
+    return sdm::address_bwd_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->n_sub, (int)(d->d_k / 2));
+}
+
+sdm_status sdm_address_backward(const void *k, const void *q, const void *C_w, const void *C_r,
+                                const int32_t *widx, const float *wwt, const int32_t *ridx, const float *rwt,
+                                const float *dw, const float *dr, const sdm_dims *d, float *dk, float *dq,
+                                float *dC_w, float *dC_r, void *workspace, size_t workspace_bytes,
+                                sdm_stream_t stream)
+{
+    sdm_status st = check_method_dims(d, true);
+    if (st != SDM_OK) return st;
+    if (d->B * d->T == 0) return SDM_OK;
+    if (!k || !q || !C_w || !C_r || !widx || !wwt || !ridx || !rwt || !dw || !dr || !dk || !dq || !dC_w || !dC_r)
+        return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t ial = in_size(d);
+    if (!aligned(k, ial) || !aligned(q, ial) || !aligned(C_w, ial) || !aligned(C_r, ial) || !aligned(widx, 4) ||
+        !aligned(wwt, 4) || !aligned(ridx, 4) || !aligned(rwt, 4) || !aligned(dw, 4) || !aligned(dr, 4) ||
+        !aligned(dk, 4) || !aligned(dq, 4) || !aligned(dC_w, 4) || !aligned(dC_r, 4) || !aligned(workspace, 16))
+        return fail(SDM_ERR_INVALID_ARG, "misaligned argument");
+    const int64_t rows = d->B * d->T * d->H;
+    const size_t need = sdm::address_bwd_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->n_sub,
+                                                         (int)(d->d_k / 2));
+    if (!workspace || workspace_bytes < need)
+        return fail(SDM_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    const size_t xb = sizeof(float) * (size_t)(rows * d->d_k);
+    const size_t cb = sizeof(float) * (size_t)(d->H * 2 * d->n_sub * (d->d_k / 2));
+    const void *outs[4] = {dk, dq, dC_w, dC_r};
+    const size_t osz[4] = {xb, xb, cb, cb};
+    for (int i = 0; i < 4; ++i) {
+        if (overlap(outs[i], osz[i], workspace, need)) return fail(SDM_ERR_INVALID_ARG, "an output overlaps the workspace");
+        for (int j = 0; j < i; ++j)
+            if (!(i == 3 && j == 2 && dC_w == dC_r) && overlap(outs[i], osz[i], outs[j], osz[j]))
+                return fail(SDM_ERR_INVALID_ARG, "outputs overlap (only dC_w and dC_r may be the same buffer)");
+    }
+    sdm::AddrBwdArgs A{k, q, C_w, C_r, widx, ridx, wwt, rwt, dw, dr, dk, dq, dC_w, dC_r, rows, (int)d->H,
+                       (int)d->d_k, (int)d->n_sub, (int)d->W, (int)d->R};
+    hipError_t e = sdm::launch_address_backward(A, d->in_dtype == SDM_BF16, workspace, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_address_backward launch");
+}
+
 }  // extern "C"

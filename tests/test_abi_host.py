@@ -236,3 +236,21 @@ def test_scan_forward_save_needs_both_buffers():
     st = sdm.sdm_scan_forward_save(*args, None, FAKE + (10 << 30), FAKE + (11 << 30), 1 << 40, dims, stream=0,
                                    check=False)
     assert st == sdm.SDM_ERR_INVALID_ARG
+
+
+def test_address_backward_rejects_bad_arguments():
+    def call(dims, ws_bytes=1 << 40, **ptrs):
+        names = ("k", "q", "Cw", "Cr", "widx", "wwt", "ridx", "rwt", "dw", "dr")
+        p = {n: FAKE + (i << 30) for i, n in enumerate(names)}
+        outs = {"dk": FAKE + (10 << 30), "dq": FAKE + (11 << 30), "dCw": FAKE + (12 << 30), "dCr": FAKE + (13 << 30),
+                "ws": FAKE + (14 << 30)}
+        p.update(outs)
+        p.update(ptrs)
+        return sdm.sdm_address_backward(*(p[n] for n in names), dims, p["dk"], p["dq"], p["dCw"], p["dCr"], p["ws"],
+                                        ws_bytes, stream=0, check=False)
+    assert call(good_dims(d_k=127)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dk=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws_bytes=16) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dq=FAKE + (10 << 30) + 256) == sdm.SDM_ERR_INVALID_ARG    # dq inside dk
+    assert sdm.sdm_address_backward_workspace_size(good_dims()) > 0
+    assert call(good_dims(T=0), k=None) == sdm.SDM_OK

@@ -1,0 +1,90 @@
+"""GPU parity of the addressing gradients (sdm_address_backward, through
+the C ABI) against the oracle's, the selected slots held fixed.
+
+Bar: dk, dq and the codebook gradients within 2e-3 x RMS of the oracle's;
+a second run is bit-identical (every sum has a fixed order).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sdm_synth as synth
+from sdm_synth import Dims
+
+from gpu_helpers import note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    assert _t.cuda.is_available()
+    return _t
+
+
+@pytest.fixture(scope="module")
+def sdm():
+    import sparse_memory_linear_pkm_amd as _s
+    _s.load_library()
+    return _s
+
+
+def close_rms(got, ref, what, bar=2e-3):
+    ref = ref.astype(np.float64)
+    scale = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 1.0
+    err = float(np.max(np.abs(got.astype(np.float64) - ref))) if ref.size else 0.0
+    note(f"{what}: max |err| / RMS = {err / max(scale, 1e-30):.2e}")
+    assert err <= bar * scale, f"{what}: max error {err:.3g} > {bar} x RMS {scale:.3g}"
+
+
+def run_case(sdm, torch, d, seed, shared):
+    x = synth.make_inputs(d, seed=seed, separate_read_codebook=not shared)
+    dims = sdm.dims_from(d)
+    k, q, Cw, Cr = (to_dev(x[n]) for n in ("k", "q", "C_w", "C_r"))
+    if shared:
+        Cr = Cw
+    widx, wwt, ridx, rwt = sdm.pkm_address(k, q, Cw, Cr, dims)
+    rng = np.random.default_rng(seed)
+    dw = rng.normal(0, 1, (d.B, d.T, d.H, d.W)).astype(np.float32)
+    dr = rng.normal(0, 1, (d.B, d.T, d.H, d.R)).astype(np.float32)
+    out = sdm.address_backward(k, q, Cw, Cr, widx, wwt, ridx, rwt, to_dev(dw), to_dev(dr), dims,
+                               shared_codebook_grad=shared)
+    out2 = sdm.address_backward(k, q, Cw, Cr, widx, wwt, ridx, rwt, to_dev(dw), to_dev(dr), dims,
+                                shared_codebook_grad=shared)
+    torch.cuda.synchronize()
+    g = [to_host(t) for t in out]
+    for a, b in zip(g, (to_host(t) for t in out2)):
+        assert np.array_equal(a, b), "two runs differ"
+    hw, hr = to_host(widx), to_host(ridx)
+    ok, oq, oCw, oCr = oracle.address_backward(x["k"], x["q"], x["C_w"], x["C_r"] if not shared else x["C_w"], hw,
+                                               to_host(wwt), hr, to_host(rwt), dw, dr, d)
+    close_rms(g[0], ok, "dk")
+    close_rms(g[1], oq, "dq")
+    if shared:
+        close_rms(g[2], oCw.astype(np.float64) + oCr, "dC (shared)")
+    else:
+        close_rms(g[2], oCw, "dC_w")
+        close_rms(g[3], oCr, "dC_r")
+
+
+CASES = {
+    "bf16_small_shape": (Dims(B=2, T=100, H=3, d_k=128, n_sub=64, d_v=32, k_prime=16, W=16, R=16), False),
+    "bf16_shared": (Dims(B=2, T=77, H=2, d_k=128, n_sub=32, d_v=32, k_prime=8, W=8, R=12), True),
+    "f32_dk48": (Dims(B=1, T=50, H=2, d_k=48, n_sub=20, d_v=32, k_prime=6, W=5, R=3, in_dtype="f32"), False),
+    "bf16_two_ranges": (Dims(B=1, T=64, H=2, d_k=128, n_sub=300, d_v=32, k_prime=32, W=32, R=32), True),
+    "bf16_dk256": (Dims(B=1, T=40, H=1, d_k=256, n_sub=128, d_v=32, k_prime=64, W=64, R=1), False),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_address_backward_matches_oracle(sdm, torch, case):
+    d, shared = CASES[case]
+    note(f"address backward {case} {d}")
+    run_case(sdm, torch, d, seed=len(case), shared=shared)
+
+
+def test_address_backward_full_size_small_layer(sdm, torch):
+    d = synth.PRESETS["small"].dims
+    note(f"address backward full size {d}")
+    run_case(sdm, torch, d, seed=41, shared=True)
