@@ -61,9 +61,12 @@ def _load():
         lib.orc_gdn_dense.argtypes = [P, P, P, P, P, P, P, ctypes.POINTER(_Dims), I32]
         lib.orc_scan_backward.argtypes = [P] * 15 + [ctypes.POINTER(_Dims), I32]
         lib.orc_address_backward.argtypes = [P] * 10 + [ctypes.POINTER(_Dims), P, P, P, P]
+        lib.orc_gates_backward.argtypes = [P] * 6 + [ctypes.POINTER(_Dims), P, P, P, P]
+        lib.orc_output_norm_gate_backward.argtypes = [P, P, P, ctypes.c_double, P, ctypes.POINTER(_Dims), P, P, P]
         for f in (lib.orc_address, lib.orc_half_scores, lib.orc_slot_scores, lib.orc_scan,
                   lib.orc_state_init, lib.orc_gates, lib.orc_output_norm_gate, lib.orc_gdn_dense,
-                  lib.orc_scan_backward, lib.orc_address_backward):
+                  lib.orc_scan_backward, lib.orc_address_backward, lib.orc_gates_backward,
+                  lib.orc_output_norm_gate_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -300,3 +303,30 @@ def address_backward(k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr, d):
                                     _p(dr), ctypes.byref(dm), _p(dk), _p(dq), _p(dCw), _p(dCr)),
            "orc_address_backward")
     return dk, dq, dCw, dCr
+
+
+def gates_backward(a_raw, b_raw, A, dt_bias, da, db, d):
+    """Gradients of gates(): returns (da_raw, db_raw [B,T,H], dA, ddt_bias [H]), float32."""
+    lib = _load()
+    a_raw, b_raw, A, dt_bias, da, db = (np.ascontiguousarray(x, np.float32) for x in (a_raw, b_raw, A, dt_bias, da, db))
+    shp = (d.B, d.T, d.H)
+    out = (np.empty(shp, np.float32), np.empty(shp, np.float32), np.empty(d.H, np.float32), np.empty(d.H, np.float32))
+    dm = _dims(d)
+    _check(lib.orc_gates_backward(_p(a_raw), _p(b_raw), _p(A), _p(dt_bias), _p(da), _p(db), ctypes.byref(dm),
+                                  *(_p(x) for x in out)), "orc_gates_backward")
+    return out
+
+
+def output_norm_gate_backward(o, g, gamma, eps: float, dy, d):
+    """Gradients of output_norm_gate() for dL/dy = dy: returns (do, dg [B,T,H,d_v], dgamma [d_v]), float32."""
+    lib = _load()
+    o = np.ascontiguousarray(o, np.float32)
+    g = _in(g, d)
+    gamma = np.ascontiguousarray(gamma, np.float32)
+    dy = np.ascontiguousarray(dy, np.float32)
+    shp = (d.B, d.T, d.H, d.d_v)
+    out = (np.empty(shp, np.float32), np.empty(shp, np.float32), np.empty(d.d_v, np.float32))
+    dm = _dims(d)
+    _check(lib.orc_output_norm_gate_backward(_p(o), _p(g), _p(gamma), float(eps), _p(dy), ctypes.byref(dm),
+                                             *(_p(x) for x in out)), "orc_output_norm_gate_backward")
+    return out

@@ -644,3 +644,74 @@ int orc_address_backward(const void *k, const void *q, const void *C_w, const vo
     free(dx);
     return err;
 }
+
+/* ---- gradients of the gates and of the output norm and gate -------------- */
+/* Reverse mode of orc_gates: with z = a_raw + dt_bias[h], a = exp(-A sp(z)),
+ * sp' = sigmoid, b = sigmoid(b_raw):
+ *   da_raw = da * a * (-A[h]) * sigmoid(z);  ddt_bias[h] = sum of da_raw over (b, t)
+ *   dA[h] = sum over (b, t) of da * a * (-sp(z));  db_raw = db * b (1 - b)
+ * fp64, each output rounded once. */
+int orc_gates_backward(const float *a_raw, const float *b_raw, const float *A, const float *dt_bias, const float *da,
+                       const float *db, const orc_dims *d, float *da_raw, float *db_raw, float *dA, float *ddt)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1) return ORC_EINVAL;
+    double *acc = (double *)calloc((size_t)(2 * d->H), sizeof(double));
+    if (!acc) return ORC_ENOMEM;
+    const int64_t n = d->B * d->T * d->H;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t h = i % d->H;
+        const double z = (double)a_raw[i] + (double)dt_bias[h];
+        const double sp = softplus(z), sg = 1.0 / (1.0 + exp(-z));
+        const double a = exp(-(double)A[h] * sp);
+        const double g = (double)da[i] * a * (-(double)A[h]) * sg;
+        da_raw[i] = (float)g;
+        acc[d->H + h] += g;
+        acc[h] += (double)da[i] * a * (-sp);
+        const double b = 1.0 / (1.0 + exp(-(double)b_raw[i]));
+        db_raw[i] = (float)((double)db[i] * b * (1.0 - b));
+    }
+    for (int64_t h = 0; h < d->H; ++h) {
+        dA[h] = (float)acc[h];
+        ddt[h] = (float)acc[d->H + h];
+    }
+    free(acc);
+    return ORC_OK;
+}
+
+/* Reverse mode of orc_output_norm_gate, per row with inv = (mean o^2 + eps)^-1/2,
+ * n = o inv, s = sigmoid(g), q = dy gamma g s:
+ *   do = inv (q - n <q, n> / d_v);  dg = dy gamma n s (1 + g (1 - s));
+ *   dgamma = sum over rows of dy n g s.
+ * fp64; do, dg [B,T,H,d_v] and dgamma [d_v] rounded once to fp32. */
+int orc_output_norm_gate_backward(const float *o, const void *g, const float *gamma, double eps, const float *dy,
+                                  const orc_dims *d, float *dout, float *dg, float *dgamma)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->d_v < 1 || !(eps >= 0.0)) return ORC_EINVAL;
+    const int64_t rows = d->B * d->T * d->H, dv = d->d_v;
+    double *acc = (double *)calloc((size_t)dv, sizeof(double));
+    double *q = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!acc || !q) {
+        free(acc); free(q);
+        return ORC_ENOMEM;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int64_t c = 0; c < dv; ++c) ss += (double)o[r * dv + c] * (double)o[r * dv + c];
+        const double inv = 1.0 / sqrt(ss / (double)dv + eps);
+        double qn = 0.0;
+        for (int64_t c = 0; c < dv; ++c) {
+            const double gc = load_in(g, d->in_bf16, r * dv + c), s = 1.0 / (1.0 + exp(-gc));
+            const double n = (double)o[r * dv + c] * inv, y = (double)dy[r * dv + c];
+            q[c] = y * (double)gamma[c] * gc * s;
+            qn += q[c] * n;
+            dg[r * dv + c] = (float)(y * (double)gamma[c] * n * s * (1.0 + gc * (1.0 - s)));
+            acc[c] += y * n * gc * s;
+        }
+        for (int64_t c = 0; c < dv; ++c)
+            dout[r * dv + c] = (float)(inv * (q[c] - (double)o[r * dv + c] * inv * qn / (double)dv));
+    }
+    for (int64_t c = 0; c < dv; ++c) dgamma[c] = (float)acc[c];
+    free(acc);
+    free(q);
+    return ORC_OK;
+}

@@ -142,3 +142,66 @@ def test_norm_gate_rows_independent():
     yp = oracle.output_norm_gate(o.reshape(10, 8)[perm].reshape(1, 5, 2, 8),
                                  g.reshape(10, 8)[perm].reshape(1, 5, 2, 8), gamma, 1e-6, d)
     assert np.array_equal(yp.reshape(10, 8), y.reshape(10, 8)[perm])
+
+
+# ---------------------------------------------------------------------------
+# gradients of the gates and of the output norm and gate: central differences
+# of the forward definitions written here in numpy (fp64)
+# ---------------------------------------------------------------------------
+def _gates64(a_raw, b_raw, A, dt):
+    z = a_raw + dt[None, None, :]
+    return np.exp(-A[None, None, :] * np.logaddexp(0.0, z)), scipy.special.expit(b_raw)
+
+
+def test_gates_gradients_match_central_differences():
+    d = dims(B=2, T=7, H=3)
+    rng = np.random.default_rng(21)
+    a_raw = rng.normal(0, 2, (2, 7, 3)).astype(np.float32)
+    b_raw = rng.normal(0, 2, (2, 7, 3)).astype(np.float32)
+    A = rng.uniform(0.5, 4, 3).astype(np.float32)
+    dt = rng.normal(-1, 1, 3).astype(np.float32)
+    da = rng.normal(0, 1, (2, 7, 3)).astype(np.float32)
+    db = rng.normal(0, 1, (2, 7, 3)).astype(np.float32)
+    g = oracle.gates_backward(a_raw, b_raw, A, dt, da, db, d)
+    base = dict(a_raw=a_raw.astype(np.float64), b_raw=b_raw.astype(np.float64), A=A.astype(np.float64),
+                dt=dt.astype(np.float64))
+
+    def loss(**over):
+        y = {k: over.get(k, v) for k, v in base.items()}
+        a, b = _gates64(y["a_raw"], y["b_raw"], y["A"], y["dt"])
+        return float(np.sum(da * a) + np.sum(db * b))
+
+    for name, gr in zip(("a_raw", "b_raw", "A", "dt"), g):
+        delta = rng.normal(0, 1, base[name].shape)
+        h = 1e-6
+        fd = (loss(**{name: base[name] + h * delta}) - loss(**{name: base[name] - h * delta})) / (2 * h)
+        an = float(np.sum(gr.astype(np.float64) * delta))
+        assert abs(fd - an) <= 1e-6 * (abs(fd) + np.sqrt(np.sum(gr.astype(np.float64) ** 2))), (name, fd, an)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_norm_gate_gradients_match_central_differences(in_dtype):
+    d = dims(B=2, T=5, H=2, d_v=16, in_dtype=in_dtype)
+    rng = np.random.default_rng(22)
+    o = rng.normal(0, 0.5, (2, 5, 2, 16)).astype(np.float32)
+    g32 = rng.normal(0, 1.5, (2, 5, 2, 16)).astype(np.float32)
+    g = synth.f32_to_bf16_bits(g32) if in_dtype == "bf16" else g32
+    gdec = (synth.bf16_bits_to_f32(g) if in_dtype == "bf16" else g32).astype(np.float64)
+    gamma = rng.normal(1, 0.3, 16).astype(np.float32)
+    dy = rng.normal(0, 1, (2, 5, 2, 16)).astype(np.float32)
+    eps = 1e-3
+    do, dg, dgamma = oracle.output_norm_gate_backward(o, g, gamma, eps, dy, d)
+    base = dict(o=o.astype(np.float64), g=gdec, gamma=gamma.astype(np.float64))
+
+    def loss(**over):
+        y = {k: over.get(k, v) for k, v in base.items()}
+        ref = (F.rms_norm(torch.from_numpy(y["o"]), (16,), torch.from_numpy(y["gamma"]), eps) *
+               F.silu(torch.from_numpy(y["g"]))).numpy()
+        return float(np.sum(dy * ref))
+
+    for name, gr in (("o", do), ("g", dg), ("gamma", dgamma)):
+        delta = rng.normal(0, 1, base[name].shape)
+        h = 1e-6
+        fd = (loss(**{name: base[name] + h * delta}) - loss(**{name: base[name] - h * delta})) / (2 * h)
+        an = float(np.sum(gr.astype(np.float64) * delta))
+        assert abs(fd - an) <= 1e-6 * (abs(fd) + np.sqrt(np.sum(gr.astype(np.float64) ** 2))), (name, fd, an)
