@@ -650,7 +650,8 @@ int orc_address_backward(const void *k, const void *q, const void *C_w, const vo
  * sp' = sigmoid, b = sigmoid(b_raw):
  *   da_raw = da * a * (-A[h]) * sigmoid(z);  ddt_bias[h] = sum of da_raw over (b, t)
  *   dA[h] = sum over (b, t) of da * a * (-sp(z));  db_raw = db * b (1 - b)
- * fp64, each output rounded once. */
+ * fp64, each output rounded once.  1 - sigmoid(x) is taken as sigmoid(-x), the
+ * same number without the cancellation that loses it when x is large. */
 int orc_gates_backward(const float *a_raw, const float *b_raw, const float *A, const float *dt_bias, const float *da,
                        const float *db, const orc_dims *d, float *da_raw, float *db_raw, float *dA, float *ddt)
 {
@@ -667,8 +668,8 @@ int orc_gates_backward(const float *a_raw, const float *b_raw, const float *A, c
         da_raw[i] = (float)g;
         acc[d->H + h] += g;
         acc[h] += (double)da[i] * a * (-sp);
-        const double b = 1.0 / (1.0 + exp(-(double)b_raw[i]));
-        db_raw[i] = (float)((double)db[i] * b * (1.0 - b));
+        const double b = 1.0 / (1.0 + exp(-(double)b_raw[i])), nb = 1.0 / (1.0 + exp((double)b_raw[i]));
+        db_raw[i] = (float)((double)db[i] * b * nb);
     }
     for (int64_t h = 0; h < d->H; ++h) {
         dA[h] = (float)acc[h];
@@ -700,11 +701,12 @@ int orc_output_norm_gate_backward(const float *o, const void *g, const float *ga
         const double inv = 1.0 / sqrt(ss / (double)dv + eps);
         double qn = 0.0;
         for (int64_t c = 0; c < dv; ++c) {
-            const double gc = load_in(g, d->in_bf16, r * dv + c), s = 1.0 / (1.0 + exp(-gc));
+            const double gc = load_in(g, d->in_bf16, r * dv + c), s = 1.0 / (1.0 + exp(-gc)),
+                         ns = 1.0 / (1.0 + exp(gc));   /* 1 - s */
             const double n = (double)o[r * dv + c] * inv, y = (double)dy[r * dv + c];
             q[c] = y * (double)gamma[c] * gc * s;
             qn += q[c] * n;
-            dg[r * dv + c] = (float)(y * (double)gamma[c] * n * s * (1.0 + gc * (1.0 - s)));
+            dg[r * dv + c] = (float)(y * (double)gamma[c] * n * s * (1.0 + gc * ns));
             acc[c] += y * n * gc * s;
         }
         for (int64_t c = 0; c < dv; ++c)

@@ -205,3 +205,19 @@ def test_norm_gate_gradients_match_central_differences(in_dtype):
         fd = (loss(**{name: base[name] + h * delta}) - loss(**{name: base[name] - h * delta})) / (2 * h)
         an = float(np.sum(gr.astype(np.float64) * delta))
         assert abs(fd - an) <= 1e-6 * (abs(fd) + np.sqrt(np.sum(gr.astype(np.float64) ** 2))), (name, fd, an)
+
+
+def test_gates_gradient_tails():
+    """Far in the sigmoid's tails its derivative is e^-|x| to within a
+    relative 2 e^-|x| (the leading term of e^-|x| / (1 + e^-|x|)^2), so
+    db_raw for db = 1 must be that exponential, not a difference of two
+    numbers near 1 rounded to 0."""
+    xs = np.array([40.0, -40.0, 60.0, -60.0, 100.0, -100.0], np.float32)
+    d = dims(B=1, T=6, H=1)
+    z = np.zeros((1, 6, 1), np.float32)
+    _, db_raw, _, _ = oracle.gates_backward(z, xs.reshape(1, 6, 1), np.ones(1, np.float32),
+                                            np.zeros(1, np.float32), z, np.ones((1, 6, 1), np.float32), d)
+    want = np.exp(-np.abs(xs.astype(np.float64)))
+    got = db_raw.reshape(-1).astype(np.float64)
+    ulp = np.spacing(want.astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - want) <= ulp), (got, want)
