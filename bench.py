@@ -13,8 +13,8 @@ Prints one JSON line: whole-step tokens/s, the roofline of the dominant
 kernel (the scan; HBM-bound) measured with HIP events on the launch stream,
 a per-kernel breakdown, and the CPU oracle timed on the host as a baseline.
 After the timed region it also times the steps either side of the path (the
-gates, and the read-out's norm and output gate) on the same layer, reported
-under "layer_edges" and not counted in the step.
+gates, and the read-out's norm and output gate, and the backward of both)
+on the same layer, reported under "layer_edges" and not counted in the step.
 """
 from __future__ import annotations
 
@@ -143,38 +143,60 @@ def cpu_baseline(name, d, host_x, seed, min_seconds):
 
 def layer_edges(sdm, synth, torch, d, dims, o, stream, seed, reps=20):
     """The steps either side of the path, timed after the timed region (they
-    are not part of the step): the gates from their pre-activations, and the
-    norm and output gate of the scan's read-out o.  Per-launch time from HIP
-    events on the launch stream, against the HBM peak."""
+    are not part of the step): the gates from their pre-activations, the norm
+    and output gate of the scan's read-out o, and the backward of both for
+    given upstream gradients.  Per-launch time from HIP events on the launch
+    stream, against the HBM peak."""
     x = synth.make_layer_edge_inputs_torch(d, seed)
     a = torch.empty_like(x["a_raw"])
     b = torch.empty_like(x["b_raw"])
     y = torch.empty(o.shape, dtype=x["g"].dtype, device="cuda")
-
-    def once():
-        sdm.sdm_gates(x["a_raw"], x["b_raw"], x["A"], x["dt_bias"], dims, a, b, stream)
-        sdm.sdm_output_norm_gate(o, x["g"], x["gamma"], 1e-5, dims, y, stream)
-
-    once()
+    gen = torch.Generator(device="cuda").manual_seed(seed + 3)
+    da = torch.randn(a.shape, generator=gen, dtype=torch.float32, device="cuda")
+    db = torch.randn(a.shape, generator=gen, dtype=torch.float32, device="cuda")
+    dy = torch.randn(o.shape, generator=gen, dtype=torch.float32, device="cuda")
+    da_raw, db_raw = torch.empty_like(a), torch.empty_like(b)
+    dA, ddt = torch.empty_like(x["A"]), torch.empty_like(x["A"])
+    do, dg, dgamma = torch.empty_like(o), torch.empty_like(o), torch.empty_like(x["gamma"])
+    nws_bytes = sdm.sdm_output_norm_gate_backward_workspace_size(dims)
+    nws = torch.empty(max(nws_bytes, 1), dtype=torch.uint8, device="cuda")
+    gws_bytes = sdm.sdm_gates_backward_workspace_size(dims)
+    gws = torch.empty(max(gws_bytes, 1), dtype=torch.uint8, device="cuda")
+    calls = [
+        ("sdm_gates", lambda: sdm.sdm_gates(x["a_raw"], x["b_raw"], x["A"], x["dt_bias"], dims, a, b, stream)),
+        ("sdm_output_norm_gate", lambda: sdm.sdm_output_norm_gate(o, x["g"], x["gamma"], 1e-5, dims, y, stream)),
+        ("sdm_gates_backward", lambda: sdm.sdm_gates_backward(x["a_raw"], x["b_raw"], x["A"], x["dt_bias"], da, db,
+                                                               dims, da_raw, db_raw, dA, ddt, gws, gws_bytes,
+                                                               stream)),
+        ("sdm_output_norm_gate_backward", lambda: sdm.sdm_output_norm_gate_backward(
+            o, x["g"], x["gamma"], 1e-5, dy, dims, do, dg, dgamma, nws, nws_bytes, stream)),
+    ]
+    for _, f in calls:
+        f()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * reps)]
+    nc = len(calls)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range((nc + 1) * reps)]
     for r in range(reps):
-        ev[3 * r].record(stream)
-        sdm.sdm_gates(x["a_raw"], x["b_raw"], x["A"], x["dt_bias"], dims, a, b, stream)
-        ev[3 * r + 1].record(stream)
-        sdm.sdm_output_norm_gate(o, x["g"], x["gamma"], 1e-5, dims, y, stream)
-        ev[3 * r + 2].record(stream)
+        ev[(nc + 1) * r].record(stream)
+        for c, (_, f) in enumerate(calls):
+            f()
+            ev[(nc + 1) * r + c + 1].record(stream)
     torch.cuda.synchronize()
-    g_ms = sum(ev[3 * r].elapsed_time(ev[3 * r + 1]) for r in range(reps)) / reps
-    n_ms = sum(ev[3 * r + 1].elapsed_time(ev[3 * r + 2]) for r in range(reps)) / reps
+    ms = [sum(ev[(nc + 1) * r + c].elapsed_time(ev[(nc + 1) * r + c + 1]) for r in range(reps)) / reps
+          for c in range(nc)]
     th = d.B * d.T * d.H
     esz = 2 if d.in_dtype == "bf16" else 4
-    g_bytes = th * 16 + d.H * 8                       # a_raw, b_raw read; a, b written
-    n_bytes = th * d.d_v * (4 + 2 * esz) + d.d_v * 4   # o, g read; y written
+    nbytes = {
+        "sdm_gates": th * 16 + d.H * 8,                                     # a_raw, b_raw read; a, b written
+        "sdm_output_norm_gate": th * d.d_v * (4 + 2 * esz) + d.d_v * 4,     # o, g read; y written
+        "sdm_gates_backward": th * 24,   # a_raw, b_raw, da, db read; da_raw, db_raw written
+        "sdm_output_norm_gate_backward": th * d.d_v * (4 + esz + 4 + 8) + d.d_v * 4,   # o, g, dy read; do, dg written
+    }
     out = {}
-    for name, ms, nb in (("sdm_gates", g_ms, g_bytes), ("sdm_output_norm_gate", n_ms, n_bytes)):
-        gbs = nb / (ms * 1e-3) / 1e9
-        out[name] = {"bound": "hbm", "ms": ms, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    for (name, _), t in zip(calls, ms):
+        nb = nbytes[name]
+        gbs = nb / (t * 1e-3) / 1e9
+        out[name] = {"bound": "hbm", "ms": t, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nb}
     return out
 
@@ -258,59 +280,80 @@ def bench_gdn(args, sdm, synth, torch):
 
 
 def bench_train(args, sdm, synth, torch, name):
-    """Forward with saving and the backward on a prefill layer (small or
-    1.4B): one step = state init + PKM addressing + the scan with its rows
-    saved + the backward scan for a given dL/do (dL/dM_T = 0) + the
-    addressing's backward (into k, q and the shared codebook)."""
+    """Forward with saving and the backward of a whole prefill layer between
+    its projections (small or 1.4B).  One step = state init + the gates from
+    their pre-activations + PKM addressing + the scan with its rows saved +
+    the output norm and gate; then, for a given dL/dy (dL/dM_T = 0), the
+    norm's backward + the backward scan + the addressing's backward (into k,
+    q and the shared codebook) + the gates' backward."""
     layer = {"train_small": "small", "train_1p4b": "prefill_1p4b"}[name]
     d = synth.PRESETS[layer].dims
     dx, _ = device_inputs(layer, d, args.seed)
+    ex = synth.make_layer_edge_inputs_torch(d, seed=args.seed + 7)
     dims = sdm.dims_from(d)
     B, T, H, N = d.B, d.T, d.H, d.N
-    M = torch.empty((B, H, N, d.d_v), dtype=torch.float32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    M = torch.empty((B, H, N, d.d_v), **f32)
     dM = torch.empty_like(M)
     widx = torch.empty((B, T, H, d.W), dtype=torch.int32, device="cuda")
-    wwt = torch.empty((B, T, H, d.W), dtype=torch.float32, device="cuda")
+    wwt = torch.empty((B, T, H, d.W), **f32)
     ridx = torch.empty((B, T, H, d.R), dtype=torch.int32, device="cuda")
-    rwt = torch.empty((B, T, H, d.R), dtype=torch.float32, device="cuda")
-    o = torch.empty((B, T, H, d.d_v), dtype=torch.float32, device="cuda")
-    xs = torch.empty((B, H, T, d.d_v // 4, d.W, 4), dtype=torch.float32, device="cuda")
-    zs = torch.empty((B, H, T, d.d_v // 4, d.R, 4), dtype=torch.float32, device="cuda")
-    dout = torch.randn((B, T, H, d.d_v), dtype=torch.float32, device="cuda",
-                       generator=torch.Generator(device="cuda").manual_seed(args.seed + 1))
-    grads = [torch.empty((B, T, H, d.d_v), dtype=torch.float32, device="cuda"),
-             torch.empty((B, T, H), dtype=torch.float32, device="cuda"),
-             torch.empty((B, T, H), dtype=torch.float32, device="cuda"),
-             torch.empty((B, T, H, d.W), dtype=torch.float32, device="cuda"),
-             torch.empty((B, T, H, d.R), dtype=torch.float32, device="cuda")]
+    rwt = torch.empty((B, T, H, d.R), **f32)
+    a = torch.empty((B, T, H), **f32)
+    b = torch.empty((B, T, H), **f32)
+    o = torch.empty((B, T, H, d.d_v), **f32)
+    y = torch.empty((B, T, H, d.d_v), dtype=ex["g"].dtype, device="cuda")
+    xs = torch.empty((B, H, T, d.d_v // 4, d.W, 4), **f32)
+    zs = torch.empty((B, H, T, d.d_v // 4, d.R, 4), **f32)
+    dy = torch.randn((B, T, H, d.d_v), generator=torch.Generator(device="cuda").manual_seed(args.seed + 1), **f32)
+    do = torch.empty((B, T, H, d.d_v), **f32)
+    dg = torch.empty_like(do)
+    dgamma = torch.empty(d.d_v, **f32)
+    grads = [torch.empty((B, T, H, d.d_v), **f32), torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32),
+             torch.empty((B, T, H, d.W), **f32), torch.empty((B, T, H, d.R), **f32)]
+    da_raw, db_raw = torch.empty((B, T, H), **f32), torch.empty((B, T, H), **f32)
+    dA, ddt = torch.empty(H, **f32), torch.empty(H, **f32)
     ws_bytes = sdm.sdm_scan_workspace_size(dims)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     aws_bytes = sdm.sdm_address_backward_workspace_size(dims)
     aws = torch.empty(max(aws_bytes, 1), dtype=torch.uint8, device="cuda")
-    dk = torch.empty((B, T, H, d.d_k), dtype=torch.float32, device="cuda")
+    nws_bytes = sdm.sdm_output_norm_gate_backward_workspace_size(dims)
+    nws = torch.empty(max(nws_bytes, 1), dtype=torch.uint8, device="cuda")
+    gws_bytes = sdm.sdm_gates_backward_workspace_size(dims)
+    gws = torch.empty(max(gws_bytes, 1), dtype=torch.uint8, device="cuda")
+    dk = torch.empty((B, T, H, d.d_k), **f32)
     dq = torch.empty_like(dk)
-    dC = torch.empty((H, 2, d.n_sub, d.d_k // 2), dtype=torch.float32, device="cuda")
+    dC = torch.empty((H, 2, d.n_sub, d.d_k // 2), **f32)
     stream = torch.cuda.current_stream()
+    eps = 1e-5
+    names = ["init+gates+address", "sdm_scan_forward_save", "sdm_output_norm_gate",
+             "sdm_output_norm_gate_backward", "sdm_scan_backward", "sdm_address_backward", "sdm_gates_backward"]
     timers = []
 
     def step(timed):
-        E = lambda: torch.cuda.Event(enable_timing=timed)
-        ev = [E() for _ in range(5)]
+        ev = [torch.cuda.Event(enable_timing=timed) for _ in range(len(names) + 1)]
         ev[0].record(stream)
         sdm.sdm_state_init(M, dx["M0"], dims, stream)
         dM.zero_()
+        sdm.sdm_gates(ex["a_raw"], ex["b_raw"], ex["A"], ex["dt_bias"], dims, a, b, stream)
         sdm.sdm_pkm_address(dx["k"], dx["q"], dx["C_w"], dx["C_r"], dims, widx, wwt, ridx, rwt, stream)
         ev[1].record(stream)
-        sdm.sdm_scan_forward_save(M, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], o, xs, zs, ws, ws_bytes, dims,
-                                  stream)
+        sdm.sdm_scan_forward_save(M, widx, wwt, ridx, rwt, dx["v"], a, b, o, xs, zs, ws, ws_bytes, dims, stream)
         ev[2].record(stream)
-        sdm.sdm_scan_backward(dM, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], dout, xs, zs, *grads, dims,
-                              stream)
+        sdm.sdm_output_norm_gate(o, ex["g"], ex["gamma"], eps, dims, y, stream)
         ev[3].record(stream)
+        sdm.sdm_output_norm_gate_backward(o, ex["g"], ex["gamma"], eps, dy, dims, do, dg, dgamma, nws, nws_bytes,
+                                          stream)
+        ev[4].record(stream)
+        sdm.sdm_scan_backward(dM, widx, wwt, ridx, rwt, dx["v"], a, b, do, xs, zs, *grads, dims, stream)
+        ev[5].record(stream)
         # the codebook is shared by both kinds: one gradient buffer receives both sums
         sdm.sdm_address_backward(dx["k"], dx["q"], dx["C_w"], dx["C_r"], widx, wwt, ridx, rwt, grads[3], grads[4],
                                  dims, dk, dq, dC, dC, aws, aws_bytes, stream)
-        ev[4].record(stream)
+        ev[6].record(stream)
+        sdm.sdm_gates_backward(ex["a_raw"], ex["b_raw"], ex["A"], ex["dt_bias"], grads[1], grads[2], dims, da_raw,
+                               db_raw, dA, ddt, gws, gws_bytes, stream)
+        ev[7].record(stream)
         if timed:
             timers.append(ev)
 
@@ -326,28 +369,32 @@ def bench_train(args, sdm, synth, torch, name):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(end) / args.steps
-    avg = lambda a, b: sum(ev[a].elapsed_time(ev[b]) for ev in timers) / len(timers)
-    fwd_ms, bwd_ms, abwd_ms = avg(1, 2), avg(2, 3), avg(3, 4)
+    kms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in timers) / len(timers) for i, n in enumerate(names)}
+    fwd_ms, bwd_ms = kms["sdm_scan_forward_save"], kms["sdm_scan_backward"]
     th = B * T * H
     bwd_bytes = th * 3 * (d.W + d.R) * d.d_v * 4   # G rows in and out, saved rows in
     fwd_bytes = th * (2 * d.W + d.R + d.W + d.R) * d.d_v * 4   # the scan's rows plus the saved rows written
+    # norm backward: o, g, dy read, do and dg written
+    nbwd_bytes = th * d.d_v * (4 + (2 if d.in_dtype == "bf16" else 4) + 4 + 4 + 4)
     gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
     result = {
-        "metric": "SDM layer training tokens/sec (addressing + scan forward with saved rows + scan backward + "
-                  "addressing backward)",
+        "metric": "SDM layer training tokens/sec (gates + addressing + scan forward with saved rows + output norm "
+                  "and gate, and the backward of each)",
         "value": B * T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
         "config": {"workload": name, "B": B, "T": T, "H": H, "N": N, "d_v": d.d_v, "W": d.W, "R": d.R,
-                   "step": "state init + addressing + sdm_scan_forward_save + sdm_scan_backward + "
-                           "sdm_address_backward"},
+                   "step": "state init + sdm_gates + addressing + sdm_scan_forward_save + sdm_output_norm_gate + "
+                           "sdm_output_norm_gate_backward + sdm_scan_backward + sdm_address_backward + "
+                           "sdm_gates_backward"},
         "wall_s_timed_region": wall,
-        "kernels_ms": {"init+address": avg(0, 1), "sdm_scan_forward_save": fwd_ms, "sdm_scan_backward": bwd_ms,
-                       "sdm_address_backward": abwd_ms},
+        "kernels_ms": kms,
         "roofline": {"kernel": "sdm_scan_backward_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_launch": bwd_bytes, "avg_launch_ms": bwd_ms},
         "forward_save": {"GB/s": fwd_bytes / (fwd_ms * 1e-3) / 1e9, "algorithmic_bytes_per_launch": fwd_bytes},
+        "norm_backward": {"GB/s": nbwd_bytes / (kms["sdm_output_norm_gate_backward"] * 1e-3) / 1e9,
+                          "algorithmic_bytes_per_launch": nbwd_bytes},
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)

@@ -257,6 +257,55 @@ sdm_status sdm_output_norm_gate(const float *o, const void *g, const float *gamm
                                 const sdm_dims *dims, void *y, sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * sdm_gates_backward -- reverse mode of sdm_gates (the chain rule through
+ * the same formulas): given da = dL/da and db = dL/db [B,T,H] fp32,
+ *   da_raw = da * a * (-A[h]) * sigmoid(a_raw + dt_bias[h])
+ *   db_raw = db * b * (1 - b)
+ *   dA[h]       = sum over (b,t) of da * a * (-softplus(a_raw + dt_bias[h]))
+ *   ddt_bias[h] = sum over (b,t) of da_raw
+ *   a_raw, b_raw, A, dt_bias: the forward's inputs;
+ *   da_raw, db_raw [B,T,H] fp32 written;  dA, ddt_bias [H] fp32 written.
+ * workspace: at least sdm_gates_backward_workspace_size(dims) bytes, 4-byte
+ * aligned.  fp32 arithmetic; the per-head sums use a fixed order (the same
+ * bits on every run).  No output may overlap an input, another output or
+ * the workspace (SDM_ERR_INVALID_ARG).  Uses B, T, H of dims.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_gates_backward(const float *a_raw, const float *b_raw, const float *A,
+                              const float *dt_bias, const float *da, const float *db,
+                              const sdm_dims *dims, float *da_raw, float *db_raw, float *dA,
+                              float *ddt_bias, void *workspace, size_t workspace_bytes,
+                              sdm_stream_t stream);
+
+/* Workspace bytes of sdm_gates_backward for these dims (at most 4 KiB per
+ * head: per-part sums of dA and ddt_bias); 0 for invalid dims or no work. */
+size_t sdm_gates_backward_workspace_size(const sdm_dims *dims);
+
+/* Workspace bytes of sdm_output_norm_gate_backward for these dims (at most
+ * 4 MiB: 1024 partial rows of d_v floats); 0 for invalid dims. */
+size_t sdm_output_norm_gate_backward_workspace_size(const sdm_dims *dims);
+
+/* ---------------------------------------------------------------------------
+ * sdm_output_norm_gate_backward -- reverse mode of sdm_output_norm_gate.
+ * With n = o / sqrt(mean(o^2) + eps) per row, s = sigmoid(g) and
+ * q = dy * gamma * g * s:
+ *   dout   = (q - n * <q, n> / d_v) / sqrt(mean(o^2) + eps)
+ *   dg     = dy * gamma * n * s * (1 + g * (1 - s))
+ *   dgamma = sum over the rows of dy * n * g * s
+ *   o, g, gamma, eps: the forward's inputs (same layout and alignment);
+ *   dy [B,T,H,d_v] fp32 (dL/dy), 16-byte aligned;
+ *   dout, dg [B,T,H,d_v] fp32 written, 16-byte aligned;  dgamma [d_v] fp32.
+ * workspace: at least sdm_output_norm_gate_backward_workspace_size(dims)
+ * bytes, 16-byte aligned.  fp32 arithmetic; dgamma is summed in a fixed
+ * order.  No output may overlap an input, another output or the workspace
+ * (SDM_ERR_INVALID_ARG).  Uses B, T, H, d_v (a multiple of 32, <= 1024),
+ * in_dtype.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_output_norm_gate_backward(const float *o, const void *g, const float *gamma,
+                                         float eps, const float *dy, const sdm_dims *dims,
+                                         float *dout, float *dg, float *dgamma, void *workspace,
+                                         size_t workspace_bytes, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * sdm_gdn_dense_forward -- the dense Gated DeltaNet recurrence, [P] Sec. 2
  * Eq. 2, which [P] Sec. 3.1 ("Connection to GDN") states the sparse memory
  * reduces to when every slot is selected with a dense key:

@@ -28,7 +28,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-__all__ = ["Dims", "PRESETS", "preset", "make_inputs", "make_layer_edge_inputs", "make_layer_edge_inputs_torch",
+__all__ = ["Dims", "PRESETS", "preset", "make_inputs", "make_layer_edge_inputs", "make_layer_edge_grads", "make_layer_edge_inputs_torch",
            "make_gdn_inputs", "make_gdn_inputs_torch",
            "f32_to_bf16_bits",
            "bf16_bits_to_f32", "random_addressing"]
@@ -267,6 +267,19 @@ def make_layer_edge_inputs(d: Dims, seed: int = 0) -> dict:
                 o=_normal(gs["o"], shp + (d.d_v,), std=0.5),
                 g=f32_to_bf16_bits(g) if d.in_dtype == "bf16" else g,
                 gamma=_normal(gs["gamma"], (d.d_v,), std=0.1, mean=1.0))
+
+
+def make_layer_edge_grads(d: Dims, seed: int = 0) -> dict:
+    """Upstream gradients for the backward of the steps either side of the
+    path (numpy backend), all float32 N(0, 1):
+      da, db : [B,T,H]      dL/da and dL/db (what the scan's backward gives)
+      dy     : [B,T,H,d_v]  dL/dy (what the head-mixing projection's backward gives)
+    """
+    names = ("da", "db", "dy")
+    ss = np.random.SeedSequence([seed, 611953])
+    gs = {n: np.random.Generator(np.random.PCG64(s)) for n, s in zip(names, ss.spawn(len(names)))}
+    shp = (d.B, d.T, d.H)
+    return dict(da=_normal(gs["da"], shp), db=_normal(gs["db"], shp), dy=_normal(gs["dy"], shp + (d.d_v,)))
 
 
 def make_layer_edge_inputs_torch(d: Dims, seed: int = 0, device: str = "cuda") -> dict:

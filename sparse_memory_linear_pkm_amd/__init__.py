@@ -12,6 +12,8 @@ from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_
                       sdm_decode_step, sdm_gates, sdm_output_norm_gate, sdm_gdn_dense_forward,
                       sdm_scan_forward_save, sdm_scan_backward, scan_forward_save, scan_backward,
                       sdm_address_backward, sdm_address_backward_workspace_size, address_backward,
+                      sdm_gates_backward, sdm_gates_backward_workspace_size, sdm_output_norm_gate_backward,
+                      sdm_output_norm_gate_backward_workspace_size, gates_backward, output_norm_gate_backward,
                       sdm_status_string,
                       sdm_last_error, sdm_version, state_init, pkm_address, scan_forward, decode_step,
                       gates, output_norm_gate, gdn_dense_forward)
@@ -19,4 +21,4 @@ from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_
 __all__ = [n for n in dir() if n.startswith(("sdm_", "SDM_", "Sdm")) or n in (
     "dims_from", "lib_path", "load_library", "state_init", "pkm_address", "scan_forward",
     "decode_step", "gates", "output_norm_gate", "gdn_dense_forward", "scan_forward_save", "scan_backward",
-    "address_backward")]
+    "address_backward", "gates_backward", "output_norm_gate_backward")]

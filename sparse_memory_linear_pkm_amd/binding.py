@@ -58,6 +58,8 @@ def load_library():
         "sdm_scan_forward_save": [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
         "sdm_scan_backward": [P] * 16 + [D, P],
         "sdm_address_backward": [P] * 10 + [D, P, P, P, P, P, ctypes.c_size_t, P],
+        "sdm_gates_backward": [P] * 6 + [D, P, P, P, P, P, ctypes.c_size_t, P],
+        "sdm_output_norm_gate_backward": [P, P, P, ctypes.c_float, P, D, P, P, P, P, ctypes.c_size_t, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -67,6 +69,10 @@ def load_library():
     lib.sdm_scan_workspace_size.restype = ctypes.c_size_t
     lib.sdm_address_backward_workspace_size.argtypes = [D]
     lib.sdm_address_backward_workspace_size.restype = ctypes.c_size_t
+    lib.sdm_gates_backward_workspace_size.argtypes = [D]
+    lib.sdm_gates_backward_workspace_size.restype = ctypes.c_size_t
+    lib.sdm_output_norm_gate_backward_workspace_size.argtypes = [D]
+    lib.sdm_output_norm_gate_backward_workspace_size.restype = ctypes.c_size_t
     lib.sdm_status_string.argtypes = [I32]
     lib.sdm_status_string.restype = ctypes.c_char_p
     lib.sdm_last_error.argtypes = []
@@ -186,6 +192,34 @@ def sdm_output_norm_gate(o, g, gamma, eps: float, dims: SdmDims, y, stream=None,
                                              _ptr(y), _stream(stream))
     if check:
         _check(st, "sdm_output_norm_gate")
+    return st
+
+
+def sdm_gates_backward_workspace_size(dims: SdmDims) -> int:
+    return int(load_library().sdm_gates_backward_workspace_size(ctypes.byref(dims)))
+
+
+def sdm_gates_backward(a_raw, b_raw, A, dt_bias, da, db, dims: SdmDims, da_raw, db_raw, dA, ddt_bias, workspace,
+                       workspace_bytes: int, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_gates_backward(_ptr(a_raw), _ptr(b_raw), _ptr(A), _ptr(dt_bias), _ptr(da), _ptr(db),
+                                           ctypes.byref(dims), _ptr(da_raw), _ptr(db_raw), _ptr(dA),
+                                           _ptr(ddt_bias), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "sdm_gates_backward")
+    return st
+
+
+def sdm_output_norm_gate_backward_workspace_size(dims: SdmDims) -> int:
+    return int(load_library().sdm_output_norm_gate_backward_workspace_size(ctypes.byref(dims)))
+
+
+def sdm_output_norm_gate_backward(o, g, gamma, eps: float, dy, dims: SdmDims, dout, dg, dgamma, workspace,
+                                  workspace_bytes: int, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_output_norm_gate_backward(_ptr(o), _ptr(g), _ptr(gamma), float(eps), _ptr(dy),
+                                                      ctypes.byref(dims), _ptr(dout), _ptr(dg), _ptr(dgamma),
+                                                      _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "sdm_output_norm_gate_backward")
     return st
 
 
@@ -426,3 +460,44 @@ def address_backward(k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr, dims: SdmDims
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     sdm_address_backward(k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr, dims, dk, dq, dC_w, dC_r, ws, need, stream)
     return dk, dq, dC_w, dC_r
+
+
+def gates_backward(a_raw, b_raw, A, dt_bias, da, db, dims: SdmDims, workspace=None, stream=None):
+    """Gradients of gates(): returns (da_raw, db_raw [B,T,H], dA, ddt_bias [H])."""
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    for name, x, shp in (("a_raw", a_raw, (B, T, H)), ("b_raw", b_raw, (B, T, H)), ("A", A, (H,)),
+                         ("dt_bias", dt_bias, (H,)), ("da", da, (B, T, H)), ("db", db, (B, T, H))):
+        _expect(x, shp, torch.float32, name)
+    dev = a_raw.device
+    da_raw = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    db_raw = torch.empty_like(da_raw)
+    dA = torch.empty(H, dtype=torch.float32, device=dev)
+    ddt = torch.empty_like(dA)
+    need = sdm_gates_backward_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    sdm_gates_backward(a_raw, b_raw, A, dt_bias, da, db, dims, da_raw, db_raw, dA, ddt, workspace, ws_bytes, stream)
+    return da_raw, db_raw, dA, ddt
+
+
+def output_norm_gate_backward(o, g, gamma, eps: float, dy, dims: SdmDims, workspace=None, stream=None):
+    """Gradients of output_norm_gate() for dL/dy = dy: returns (do, dg
+    [B,T,H,d_v], dgamma [d_v]), all float32."""
+    import torch
+    shp = (dims.B, dims.T, dims.H, dims.d_v)
+    _expect(o, shp, torch.float32, "o")
+    _expect(g, shp, _in_dtype(dims), "g")
+    _expect(gamma, (dims.d_v,), torch.float32, "gamma")
+    _expect(dy, shp, torch.float32, "dy")
+    dev = o.device
+    dout = torch.empty(shp, dtype=torch.float32, device=dev)
+    dg = torch.empty_like(dout)
+    dgamma = torch.empty(dims.d_v, dtype=torch.float32, device=dev)
+    need = sdm_output_norm_gate_backward_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    sdm_output_norm_gate_backward(o, g, gamma, eps, dy, dims, dout, dg, dgamma, workspace, ws_bytes, stream)
+    return dout, dg, dgamma

@@ -157,6 +157,38 @@ size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R
 hipError_t launch_address_backward(const AddrBwdArgs &args, bool bf16, void *workspace, hipStream_t stream);
 hipError_t launch_scan_backward(const BwdArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gdn_dense(const GdnArgs &args, bool bf16, hipStream_t stream);
+struct GateBwdArgs {
+    const float *a_raw, *b_raw, *A, *dt_bias, *da, *db;
+    float *da_raw, *db_raw, *dA, *ddt;
+    float *part;                  // workspace [2][parts][H]: per-part sums of dA, ddt_bias
+    int64_t n;                    // B*T*H
+    int64_t H;
+};
+
+// grid of the gates' backward (see gates_bwd_layout)
+struct GateBwdLayout {
+    int hp, hblocks, parts;
+    int64_t chunk;                // tokens per part
+};
+constexpr int kGateBwdParts = 512;
+GateBwdLayout gates_bwd_layout(int64_t bt, int64_t H);
+
+struct NormBwdArgs {
+    const float *o;
+    const void *g;
+    const float *gamma, *dy;
+    float *dout, *dg, *dgamma;
+    float *part;                  // workspace [norm_bwd_blocks(rows)][d_v]
+    int64_t rows;
+    int d_v;
+    float eps;
+};
+
+// workgroups (and dgamma partial rows) of the norm's backward
+constexpr int kNormBwdBlocks = 1024;
+int norm_bwd_blocks(int64_t rows);
+hipError_t launch_gates_backward(const GateBwdArgs &args, hipStream_t stream);
+hipError_t launch_out_norm_gate_backward(const NormBwdArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gates(const GateArgs &args, hipStream_t stream);
 hipError_t launch_out_norm_gate(const NormArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream);

@@ -350,6 +350,106 @@ sdm_status sdm_output_norm_gate(const float *o, const void *g, const float *gamm
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_output_norm_gate launch");
 }
 
+size_t sdm_gates_backward_workspace_size(const sdm_dims *d)
+{
+    if (!d || d->reserved != 0 || d->B < 0 || d->T < 0 || d->H < 1 || d->H > 0x7fffffff) return 0;
+    const sdm::GateBwdLayout L = sdm::gates_bwd_layout(d->B * d->T, d->H);
+    return d->B * d->T == 0 ? 0 : sizeof(float) * 2 * (size_t)L.parts * (size_t)d->H;
+}
+
+sdm_status sdm_gates_backward(const float *a_raw, const float *b_raw, const float *A, const float *dt_bias,
+                              const float *da, const float *db, const sdm_dims *d, float *da_raw, float *db_raw,
+                              float *dA, float *ddt_bias, void *workspace, size_t workspace_bytes,
+                              sdm_stream_t stream)
+{
+    if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
+    if (d->reserved != 0) return fail(SDM_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->B < 0 || d->T < 0 || d->H < 1)
+        return fail(SDM_ERR_INVALID_ARG, "need B >= 0, T >= 0, H >= 1");
+    if (d->H > 0x7fffffff) return fail(SDM_ERR_UNSUPPORTED, "H too large");
+    if (d->B * d->T == 0) return SDM_OK;
+    const void *ins[6] = {a_raw, b_raw, A, dt_bias, da, db};
+    void *outs[5] = {da_raw, db_raw, dA, ddt_bias, workspace};
+    for (const void *p : ins)
+        if (!p || !aligned(p, 4)) return fail(SDM_ERR_INVALID_ARG, "NULL or misaligned input");
+    for (const void *p : outs)
+        if (!p || !aligned(p, 4)) return fail(SDM_ERR_INVALID_ARG, "NULL or misaligned output or workspace");
+    const size_t need = sdm_gates_backward_workspace_size(d);
+    if (workspace_bytes < need)
+        return fail(SDM_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    const int64_t n = d->B * d->T * d->H;
+    const size_t nb = sizeof(float) * (size_t)n, hb = sizeof(float) * (size_t)d->H;
+    const size_t isz[6] = {nb, nb, hb, hb, nb, nb}, osz[5] = {nb, nb, hb, hb, need};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], osz[i], ins[j], isz[j])) return fail(SDM_ERR_INVALID_ARG, "an output overlaps an input");
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], osz[i], outs[j], osz[j]))
+                return fail(SDM_ERR_INVALID_ARG, "outputs (or the workspace) overlap");
+    }
+    sdm::GateBwdArgs G{a_raw, b_raw, A, dt_bias, da, db, da_raw, db_raw, dA, ddt_bias,
+                       static_cast<float *>(workspace), n, d->H};
+    hipError_t e = sdm::launch_gates_backward(G, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_gates_backward launch");
+}
+
+static bool norm_dims_ok(const sdm_dims *d)
+{
+    return d && d->reserved == 0 && d->B >= 0 && d->T >= 0 && d->H >= 1 && d->d_v >= 1 && d->d_v % 32 == 0 &&
+           d->d_v <= kMaxDv && (d->in_dtype == SDM_F32 || d->in_dtype == SDM_BF16);
+}
+
+size_t sdm_output_norm_gate_backward_workspace_size(const sdm_dims *d)
+{
+    if (!norm_dims_ok(d)) return 0;
+    const int64_t rows = d->B * d->T * d->H;
+    return sizeof(float) * (size_t)sdm::norm_bwd_blocks(rows) * (size_t)d->d_v;
+}
+
+sdm_status sdm_output_norm_gate_backward(const float *o, const void *g, const float *gamma, float eps,
+                                         const float *dy, const sdm_dims *d, float *dout, float *dg,
+                                         float *dgamma, void *workspace, size_t workspace_bytes,
+                                         sdm_stream_t stream)
+{
+    if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
+    if (d->reserved != 0) return fail(SDM_ERR_INVALID_ARG, "dims.reserved must be 0");
+    if (d->B < 0 || d->T < 0 || d->H < 1 || d->d_v < 1)
+        return fail(SDM_ERR_INVALID_ARG, "need B >= 0, T >= 0, H >= 1, d_v >= 1");
+    if (d->in_dtype != SDM_F32 && d->in_dtype != SDM_BF16)
+        return fail(SDM_ERR_INVALID_ARG, "in_dtype must be SDM_F32 or SDM_BF16");
+    if (d->d_v % 32 != 0 || d->d_v > kMaxDv)
+        return fail(SDM_ERR_UNSUPPORTED, "d_v must be a multiple of 32 and <= %lld", (long long)kMaxDv);
+    if (!(eps >= 0.0f) || !(eps <= 3.4e38f)) return fail(SDM_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (d->B * d->T == 0) return SDM_OK;
+    if (!o || !g || !gamma || !dy || !dout || !dg || !dgamma || !workspace)
+        return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    const size_t gal = d->in_dtype == SDM_BF16 ? 8 : 16;
+    if (!aligned(o, 16) || !aligned(gamma, 16) || !aligned(g, gal) || !aligned(dy, 16) || !aligned(dout, 16) ||
+        !aligned(dg, 16) || !aligned(dgamma, 4) || !aligned(workspace, 16))
+        return fail(SDM_ERR_INVALID_ARG, "o, gamma, dy, dout, dg and the workspace must be 16-byte aligned, g %zu-byte",
+                    gal);
+    const int64_t rows = d->B * d->T * d->H;
+    const size_t need = sdm_output_norm_gate_backward_workspace_size(d);
+    if (workspace_bytes < need)
+        return fail(SDM_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+    const size_t ob = sizeof(float) * (size_t)(rows * d->d_v), gb = in_size(d) * (size_t)(rows * d->d_v);
+    const size_t vb = sizeof(float) * (size_t)d->d_v;
+    const void *ins[4] = {o, g, gamma, dy};
+    const size_t isz[4] = {ob, gb, vb, ob};
+    const void *outs[4] = {dout, dg, dgamma, workspace};
+    const size_t osz[4] = {ob, ob, vb, need};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlap(outs[i], osz[i], ins[j], isz[j])) return fail(SDM_ERR_INVALID_ARG, "an output overlaps an input");
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], osz[i], outs[j], osz[j]))
+                return fail(SDM_ERR_INVALID_ARG, "outputs (or the workspace) overlap");
+    }
+    sdm::NormBwdArgs A{o, g, gamma, dy, dout, dg, dgamma, static_cast<float *>(workspace), rows, (int)d->d_v, eps};
+    hipError_t e = sdm::launch_out_norm_gate_backward(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_output_norm_gate_backward launch");
+}
+
 sdm_status sdm_gdn_dense_forward(float *S, const void *k, const void *q, const void *v, const float *a,
                                  const float *b, float *o, const sdm_dims *d, sdm_stream_t stream)
 {

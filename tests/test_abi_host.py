@@ -254,3 +254,52 @@ def test_address_backward_rejects_bad_arguments():
     assert call(good_dims(), dq=FAKE + (10 << 30) + 256) == sdm.SDM_ERR_INVALID_ARG    # dq inside dk
     assert sdm.sdm_address_backward_workspace_size(good_dims()) > 0
     assert call(good_dims(T=0), k=None) == sdm.SDM_OK
+
+
+def test_gates_backward_rejects_bad_arguments():
+    def call(dims, ws_bytes=1 << 40, **ptrs):
+        names = ("a_raw", "b_raw", "A", "dt", "da", "db", "da_raw", "db_raw", "dA", "ddt", "ws")
+        p = {n: FAKE + (i << 30) for i, n in enumerate(names)}
+        p.update(ptrs)
+        return sdm.sdm_gates_backward(*(p[n] for n in names[:6]), dims, *(p[n] for n in names[6:]), ws_bytes,
+                                      stream=0, check=False)
+    assert call(good_dims(H=0)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(reserved=1)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), da=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dA=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), db_raw=FAKE + (7 << 30) + 2) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), da_raw=FAKE + (4 << 30)) == sdm.SDM_ERR_INVALID_ARG      # in place over da
+    assert call(good_dims(), ddt=FAKE + (8 << 30) + 4) == sdm.SDM_ERR_INVALID_ARG     # ddt over dA
+    assert call(good_dims(), ws=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws_bytes=4) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws=FAKE + (6 << 30) + 64) == sdm.SDM_ERR_INVALID_ARG    # workspace inside da_raw
+    assert call(good_dims(T=0), a_raw=None, dA=None, ws=None) == sdm.SDM_OK
+    # per head, two sums for each part of the tokens
+    assert sdm.sdm_gates_backward_workspace_size(good_dims(B=2, T=8, H=2)) == 2 * 1 * 2 * 4
+    assert sdm.sdm_gates_backward_workspace_size(good_dims(B=8, T=8192, H=16)) == 2 * 512 * 16 * 4
+    assert sdm.sdm_gates_backward_workspace_size(good_dims(T=0)) == 0
+
+
+def test_norm_gate_backward_rejects_bad_arguments():
+    def call(dims, eps=1e-5, ws_bytes=1 << 40, **ptrs):
+        names = ("o", "g", "gamma", "dy", "dout", "dg", "dgamma", "ws")
+        p = {n: FAKE + (i << 30) for i, n in enumerate(names)}
+        p.update(ptrs)
+        return sdm.sdm_output_norm_gate_backward(p["o"], p["g"], p["gamma"], eps, p["dy"], dims, p["dout"], p["dg"],
+                                                 p["dgamma"], p["ws"], ws_bytes, stream=0, check=False)
+    assert call(good_dims(d_v=48)) == sdm.SDM_ERR_UNSUPPORTED
+    assert call(good_dims(d_v=2048)) == sdm.SDM_ERR_UNSUPPORTED
+    assert call(good_dims(in_dtype=3)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), eps=float("nan")) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dy=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws_bytes=16) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dout=FAKE + (4 << 30) + 8) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dg=FAKE + (3 << 30)) == sdm.SDM_ERR_INVALID_ARG           # dg over dy
+    assert call(good_dims(), ws=FAKE + (4 << 30) + 256) == sdm.SDM_ERR_INVALID_ARG     # workspace inside dout
+    assert call(good_dims(B=0), o=None, ws=None) == sdm.SDM_OK
+    # one partial row of d_v floats per workgroup, at most 1024 workgroups
+    assert sdm.sdm_output_norm_gate_backward_workspace_size(good_dims(B=2, T=8, H=2)) == 4 * 64
+    big = good_dims(B=4, T=4096, H=16, d_v=128)
+    assert sdm.sdm_output_norm_gate_backward_workspace_size(big) == 4 * 1024 * 128
+    assert sdm.sdm_output_norm_gate_backward_workspace_size(good_dims(d_v=48)) == 0

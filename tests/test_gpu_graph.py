@@ -81,8 +81,9 @@ def test_graph_capture_replays_match_eager(sdm, torch):
 
 def test_graph_capture_training_step_and_layer_edges(sdm, torch):
     """The other entry points under capture: gates, the scan with its rows
-    saved, the backward scan, the output norm and gate, and the dense
-    recurrence; three replays, each bit-identical to the eager run."""
+    saved, the backward scan, the output norm and gate, the backward of the
+    norm and of the gates, and the dense recurrence; three replays, each
+    bit-identical to the eager run."""
     d = Dims(B=2, T=40, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=8, R=8)
     note(f"graph capture, training step {d}")
     x = synth.make_inputs(d, seed=31)
@@ -115,6 +116,14 @@ def test_graph_capture_training_step_and_layer_edges(sdm, torch):
     inp = {k: to_dev(v) for k, v in e.items()}
     gin = {k: to_dev(v) for k, v in g.items() if k != "S0"}
     xv = to_dev(x["v"])
+    do_n, dg_n = T.empty_like(o), T.empty_like(o)
+    dgamma = T.empty(d.d_v, dtype=T.float32, device="cuda")
+    gb = [T.empty((d.B, d.T, d.H), dtype=T.float32, device="cuda") for _ in range(2)]
+    gb += [T.empty(d.H, dtype=T.float32, device="cuda") for _ in range(2)]
+    nws_bytes = sdm.sdm_output_norm_gate_backward_workspace_size(dims)
+    nws = T.empty(max(nws_bytes, 1), dtype=T.uint8, device="cuda")
+    gws_bytes = sdm.sdm_gates_backward_workspace_size(dims)
+    gws = T.empty(max(gws_bytes, 1), dtype=T.uint8, device="cuda")
 
     def step():
         sdm.sdm_gates(inp["a_raw"], inp["b_raw"], inp["A"], inp["dt_bias"], dims, a_g, b_g)
@@ -125,10 +134,14 @@ def test_graph_capture_training_step_and_layer_edges(sdm, torch):
         sdm.sdm_scan_backward(dM, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], xv, a_g, b_g, dout, xs, zs,
                               *grads, dims)
         sdm.sdm_output_norm_gate(o, inp["g"], inp["gamma"], 1e-5, dims, y)
+        sdm.sdm_output_norm_gate_backward(o, inp["g"], inp["gamma"], 1e-5, dout, dims, do_n, dg_n, dgamma, nws,
+                                          nws_bytes)
+        sdm.sdm_gates_backward(inp["a_raw"], inp["b_raw"], inp["A"], inp["dt_bias"], grads[1], grads[2], dims,
+                               *gb, gws, gws_bytes)
         S.copy_(S0)
         sdm.sdm_gdn_dense_forward(S, gin["k"], gin["q"], gin["v"], gin["a"], gin["b"], og, gdims)
 
-    outs = (a_g, b_g, M, dM, o, xs, zs, *grads, y, S, og)
+    outs = (a_g, b_g, M, dM, o, xs, zs, *grads, y, do_n, dg_n, dgamma, *gb, S, og)
     step()
     T.cuda.synchronize()
     ref = [to_host(t).copy() for t in outs]
