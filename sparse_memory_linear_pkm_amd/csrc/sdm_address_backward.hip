@@ -8,16 +8,19 @@
 //     dC[h][c][i_c(j)] += dsc_j x_c          (summed over every token)
 // for each kind (write: x = k against C_w, read: x = q against C_r).
 //
-// Three launches, every sum in a fixed order (deterministic):
+// Every sum has a fixed order (deterministic), and nothing uses floating-
+// point atomics:
 //   1. one wave per (token-head, kind): the softmax backward (dsc, kept in
 //      the workspace) and dx, summed over the list in order;
-//   2. one wave per (kind, head, half, range of 8 sub-keys, part of the
-//      tokens): the wave's lanes scan 64 list entries at a time for those
-//      that select a sub-key of its range, and adds dsc * x for each, in
-//      token and list order, into the 8 rows held in registers (each lane
-//      owns columns); the part's rows go to the workspace;
-//   3. the parts summed in order (and the two kinds together when the
-//      caller passes one codebook-gradient buffer for both).
+//   2. the codebook gradient: the list entries of each (kind, head, half)
+//      are put in order of the sub-key they select by a stable counting
+//      sort (integer counts per chunk of entries, their prefix sums, then a
+//      scatter that keeps token-then-list order within a sub-key), as
+//      (row, dsc) pairs, entries of one token that select the same sub-key
+//      combined into one;
+//   3. one wave per (head, half, sub-key) [and kind, unless one buffer takes
+//      both kinds' sums] walks its sorted entries and adds dsc * x for each
+//      into registers (each lane owns columns): every entry is read once.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -25,8 +28,7 @@ namespace sdm {
 
 namespace {
 
-constexpr int kAbRows = 8;                 // sub-key rows per wave, in registers
-constexpr int64_t kAbWaves = 16384;        // target number of waves for the codebook gradient
+constexpr int64_t kAbChunk = 4096;         // list entries per chunk of the counting sort
 
 template <bool BF16>
 __device__ __forceinline__ float ld_in(const void *p, int64_t e)
@@ -37,27 +39,64 @@ __device__ __forceinline__ float ld_in(const void *p, int64_t e)
         return static_cast<const float *>(p)[e];
 }
 
-}  // namespace
-
-// token parts: enough waves to fill the chip, at least one token per part
-int address_bwd_parts(int64_t BT, int64_t H, int n_sub)
+// lanes whose key equals this lane's: one ballot per key bit
+__device__ __forceinline__ uint64_t same_key(int key, int key_bits)
 {
-    const int64_t units = 2 * H * 2 * ((n_sub + kAbRows - 1) / kAbRows);
-    int64_t p = (kAbWaves + units - 1) / units;
-    if (p > BT) p = BT;
-    return (int)(p < 1 ? 1 : p);
+    uint64_t eq = ~0ull;
+    for (int b = 0; b < key_bits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t ones = __builtin_amdgcn_ballot_w64(bit);
+        eq &= bit ? ones : ~ones;
+    }
+    return eq;
 }
 
-size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int n_sub, int half)
+// sum of v over the lanes of mask g, in lane order (each lane its own g)
+__device__ __forceinline__ float sum_in_lane_order(float v, uint64_t g)
 {
-    const int P = address_bwd_parts(B * T, H, n_sub);
-    const size_t dsc = sizeof(float) * (size_t)(B * T * H * (W + R));
-    const size_t parts = sizeof(float) * (size_t)(2 * H * 2 * P) * (size_t)n_sub * half;
-    return ((dsc + 255) & ~(size_t)255) + parts;
+    float s = 0.f;
+    for (int l = 0; l < kWave; ++l) {
+        const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+        s += ((g >> l) & 1) ? x : 0.f;
+    }
+    return s;
+}
+
+}  // namespace
+
+// Workspace layout (each piece starting on a 256-byte boundary):
+//   dsc     [rows][W] then [rows][R] fp32 (kind 0 then kind 1)
+//   cnt     per kind k, [H][2][nch_k][n_sub] int32: entries of each chunk
+//           per sub-key, then (in place) their offset within the sub-key
+//   start   [2][H][2][n_sub + 1] int32: where each sub-key's entries begin
+//   sorted  per kind k, [H][2][B*T*n_k] (row, dsc) pairs
+// where n_0 = W, n_1 = R and nch_k = ceil(B*T*n_k / kAbChunk).
+AddrBwdLayout address_bwd_layout(int64_t BT, int64_t H, int W, int R, int n_sub)
+{
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    AddrBwdLayout L;
+    L.nch[0] = (BT * W + kAbChunk - 1) / kAbChunk;
+    L.nch[1] = (BT * R + kAbChunk - 1) / kAbChunk;
+    const int64_t rows = BT * H;
+    L.off_cnt = up(sizeof(float) * (size_t)(rows * (W + R)));
+    L.cnt1 = (size_t)(H * 2 * L.nch[0] * n_sub);
+    L.off_start = L.off_cnt + up(sizeof(int32_t) * (L.cnt1 + (size_t)(H * 2 * L.nch[1] * n_sub)));
+    L.off_sorted = L.off_start + up(sizeof(int32_t) * (size_t)(2 * H * 2 * (n_sub + 1)));
+    L.sorted1 = (size_t)(H * 2 * BT * W);
+    L.bytes = L.off_sorted + up(sizeof(int2) * (L.sorted1 + (size_t)(H * 2 * BT * R)));
+    return L;
+}
+
+size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int n_sub, int)
+{
+    return address_bwd_layout(B * T, H, W, R, n_sub).bytes;
 }
 
 // 1. softmax backward and dx: one wave per (row, kind); lanes over the list
-// for dsc, over the features for dx
+// for dsc, over the features for dx.  Each lane first turns its entry's
+// slot into the element offsets of its two sub-key rows (the divisions by
+// n_sub once per entry, in parallel), so that the loop over entries only
+// reads them back (readlane) and loads.
 template <bool BF16, int NM>
 __global__ void __launch_bounds__(256) sdm_address_bwd_dx_kernel(AddrBwdArgs A, float *dsc_ws)
 {
@@ -80,35 +119,40 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_dx_kernel(AddrBwdArgs A, 
     const float w = lane < n ? wl : 0.f, g = lane < n ? gl : 0.f;
     const float mean = wave_sum_f32(w * g);
     const float ds = w * (g - mean);
-    const int32_t s = lane < n ? sl : 0;
     if (lane < n) dsc_ws[(kind ? rows * A.W : 0) + r * n + lane] = ds;
-    // NM = ceil(d_k / 64) features per lane
+    // entries past the list and slots outside the memory add exactly nothing
+    const bool ok = lane < n && sl >= 0 && sl < ns * ns;
+    const float dsl = ok ? ds : 0.f;
+    const int32_t s = ok ? sl : 0;
+    // element offsets (in the codebook) of this entry's rows of half 0 and half 1
+    const int32_t off0 = ((h * 2 + 0) * ns + s / ns) * half;
+    const int32_t off1 = ((h * 2 + 1) * ns + s % ns) * half - half;
+    // feature e of a lane: e < half reads half 0 at e, else half 1 at e - half
+    int32_t fe[NM];
+    bool h1[NM], live[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const int e = lane + kWave * m;
+        live[m] = e < A.d_k;
+        h1[m] = e >= half;
+        fe[m] = live[m] ? e : half;   // a valid element of half 1 for dead features
+        h1[m] = live[m] ? h1[m] : true;
+    }
     float acc[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[m] = 0.f;
-    // eight list entries at a time, their codebook loads issued together;
-    // entries past the list (dsc 0, slot 0) and slots outside the memory
-    // (dsc forced to 0) add exactly nothing
+    // eight list entries at a time, their codebook loads issued together
     constexpr int kJ = 8;
     for (int j0 = 0; j0 < n; j0 += kJ) {
         float cv[kJ][NM], dj[kJ];
 #pragma unroll
         for (int jj = 0; jj < kJ; ++jj) {
             const int j = min(j0 + jj, kWave - 1);
-            int32_t sj = __builtin_amdgcn_readlane(s, j);
-            dj[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ds), j));
-            const bool ok = j0 + jj < n && sj >= 0 && sj < ns * ns;
-            dj[jj] = ok ? dj[jj] : 0.f;
-            sj = ok ? sj : 0;
-            const int64_t row0 = ((int64_t)(h * 2 + 0) * ns + sj / ns) * half;
-            const int64_t row1 = ((int64_t)(h * 2 + 1) * ns + sj % ns) * half;
+            const int32_t o0 = __builtin_amdgcn_readlane(off0, j);
+            const int32_t o1 = __builtin_amdgcn_readlane(off1, j);
+            dj[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dsl), j));
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                const int e = lane + kWave * m;
-                const int ec = e < A.d_k ? e : 0;
-                const float cl = ld_in<BF16>(C, ec < half ? row0 + ec : row1 + (ec - half));
-                cv[jj][m] = e < A.d_k ? cl : 0.f;
-            }
+            for (int m = 0; m < NM; ++m) cv[jj][m] = ld_in<BF16>(C, (h1[m] ? o1 : o0) + fe[m]);
         }
 #pragma unroll
         for (int jj = 0; jj < kJ; ++jj)
@@ -117,158 +161,337 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_dx_kernel(AddrBwdArgs A, 
     }
     float *dx = (kind ? A.dq : A.dk) + r * A.d_k;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        const int e = lane + kWave * m;
-        if (e < A.d_k) dx[e] = acc[m];
-    }
+    for (int m = 0; m < NM; ++m)
+        if (live[m]) dx[lane + kWave * m] = acc[m];
 }
 
-// 2. codebook-gradient parts: one wave per (kind, head, half, range of
-// kAbRows sub-keys, token part); HM = ceil(half / 64) columns per lane
-template <bool BF16, int HM>
-__global__ void __launch_bounds__(256) sdm_address_bwd_dc_kernel(AddrBwdArgs A, const float *dsc_ws, float *parts,
-                                                                 int P)
+namespace {
+
+// the pieces of the workspace for one launch
+struct AbWs {
+    float *dsc;
+    int32_t *cnt, *start;
+    int2 *sorted;
+    int64_t nch[2];
+    size_t cnt1, sorted1;
+};
+
+// which (kind, head, chunk) a workgroup of the count and scatter passes takes
+__device__ __forceinline__ void chunk_unit(const AddrBwdArgs &A, const AbWs &S, int &kind, int &h, int64_t &ch)
 {
-    const int half = A.d_k / 2, ns = A.n_sub, N = ns * ns;
-    const int nrg = (ns + kAbRows - 1) / kAbRows;
-    const int64_t units = (int64_t)2 * A.H * 2 * nrg * P;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-    if (unit >= units) return;                  // whole waves
-    int64_t id = unit;
-    const int part = (int)(id % P); id /= P;
-    const int rg = (int)(id % nrg); id /= nrg;
-    const int c = (int)(id % 2); id /= 2;
-    const int h = (int)(id % A.H); id /= A.H;
-    const int kind = (int)id;
-    const int lane = lane_id();
-    const int u0 = rg * kAbRows;
-    const int n = kind ? A.R : A.W;
-    const int64_t bt_all = A.rows / A.H;
-    const int64_t per = (bt_all + P - 1) / P;
-    const int64_t bt0 = min(bt_all, (int64_t)part * per), bt1 = min(bt_all, bt0 + per);
-    const int32_t *idx = kind ? A.ridx : A.widx;
-    const float *dsc = dsc_ws + (kind ? A.rows * A.W : 0);
-    const void *X = kind ? A.q : A.k;
-    float acc[kAbRows][HM];
-#pragma unroll
-    for (int rr = 0; rr < kAbRows; ++rr)
-#pragma unroll
-        for (int m = 0; m < HM; ++m) acc[rr][m] = 0.f;
-    const int64_t f1 = bt1 * n;
-    for (int64_t f0 = bt0 * n; f0 < f1; f0 += kWave) {
-        // 64 list entries, one per lane, in token-then-list order
-        const int64_t f = f0 + lane < f1 ? f0 + lane : f0;
-        const int64_t bt = f / n;
-        const int j = (int)(f - bt * n);
-        const int64_t r = bt * A.H + h;
-        const int32_t sl = idx[r * n + j];
-        const float dl = dsc[r * n + j];
-        const bool ok = f0 + lane < f1 && sl >= 0 && sl < N;
-        const int u = ok ? (c ? sl % ns : sl / ns) - u0 : -1;
-        uint64_t hit = __builtin_amdgcn_ballot_w64(ok && u >= 0 && u < kAbRows);
-        while (hit) {
-            // up to four hits at a time: their input rows are loaded together
-            int kk[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                kk[q] = hit ? __builtin_ctzll(hit) : -1;
-                hit &= hit ? hit - 1 : 0;
-            }
-            float xv[4][HM], dq[4];
-            int uq[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int k = kk[q] < 0 ? kk[0] : kk[q];
-                const int64_t rk = (int64_t)__builtin_amdgcn_readlane((int)(r & 0x7fffffff), k) |
-                                   ((int64_t)__builtin_amdgcn_readlane((int)(r >> 31), k) << 31);
-                dq[q] = kk[q] < 0 ? 0.f : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dl), k));
-                uq[q] = __builtin_amdgcn_readlane(u, k);
-#pragma unroll
-                for (int m = 0; m < HM; ++m) {
-                    const int e = lane + kWave * m;
-                    const float xl = ld_in<BF16>(X, rk * A.d_k + c * half + (e < half ? e : 0));
-                    xv[q][m] = e < half ? xl : 0.f;
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int rr = 0; rr < kAbRows; ++rr)
-#pragma unroll
-                    for (int m = 0; m < HM; ++m) {
-                        const float t = __builtin_fmaf(dq[q], xv[q][m], acc[rr][m]);
-                        acc[rr][m] = uq[q] == rr ? t : acc[rr][m];
-                    }
-        }
-    }
-    float *out = parts + ((((size_t)kind * A.H + h) * 2 + c) * P + part) * (size_t)ns * half;
-#pragma unroll
-    for (int rr = 0; rr < kAbRows; ++rr)
-#pragma unroll
-        for (int m = 0; m < HM; ++m) {
-            const int e = lane + kWave * m;
-            if (u0 + rr < ns && e < half) out[(size_t)(u0 + rr) * half + e] = acc[rr][m];
-        }
+    int64_t id = blockIdx.x;
+    kind = id >= (int64_t)A.H * S.nch[0] ? 1 : 0;
+    if (kind) id -= (int64_t)A.H * S.nch[0];
+    h = (int)(id / S.nch[kind]);
+    ch = id - (int64_t)h * S.nch[kind];
 }
 
-// 3. the parts summed in order, into dC_w and dC_r (or one buffer for both)
-__global__ void __launch_bounds__(256) sdm_address_bwd_reduce_kernel(AddrBwdArgs A, const float *parts, int P)
+__device__ __forceinline__ int32_t *cnt_row(const AddrBwdArgs &A, const AbWs &S, int kind, int h, int c, int64_t ch)
+{
+    return S.cnt + (kind ? S.cnt1 : 0) + ((int64_t)(h * 2 + c) * S.nch[kind] + ch) * A.n_sub;
+}
+
+}  // namespace
+
+// The sort's entries: within each group of 64 consecutive list entries (in
+// token-then-list order), those of one token that select the same sub-key
+// of a half are combined into one entry (their dsc summed in list order),
+// placed where the first of them is.  lanes of the token of this lane:
+__device__ __forceinline__ uint64_t same_row(int64_t bt, int64_t fb, int n)
+{
+    const int64_t lo = bt * n - fb, hi = lo + n;   // the token's entries, relative to the group
+    const uint64_t upto = hi >= kWave ? ~0ull : ((1ull << hi) - 1ull);
+    const uint64_t from = lo <= 0 ? ~0ull : ~((1ull << lo) - 1ull);
+    return upto & from;
+}
+
+// 2a. entries per sub-key in each chunk of kAbChunk list entries (integer
+// counts: the order of the LDS atomics does not matter); four waves, each
+// taking every fourth group of 64 entries
+__global__ void __launch_bounds__(256) sdm_address_bwd_count_kernel(AddrBwdArgs A, AbWs S, int key_bits)
+{
+    extern __shared__ int32_t hist[];   // [2][n_sub]
+    int kind, h;
+    int64_t ch;
+    chunk_unit(A, S, kind, h, ch);
+    const int ns = A.n_sub, n = kind ? A.R : A.W;
+    const int32_t N = ns * ns;
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    for (int i = threadIdx.x; i < 2 * ns; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    const int64_t total = A.rows / A.H * n;
+    const int64_t f0 = ch * kAbChunk, f1 = min(total, f0 + kAbChunk);
+    const int32_t *idx = kind ? A.ridx : A.widx;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t fb = f0 + wv * kWave; fb < f1; fb += 4 * kWave) {
+        const bool in = fb + lane < f1;
+        const int64_t f = in ? fb + lane : fb;
+        const int64_t bt = f / n;
+        const int32_t sl = idx[(bt * A.H + h) * n + (f - bt * n)];
+        const bool ok = in && sl >= 0 && sl < N;
+        const uint64_t valid = __builtin_amdgcn_ballot_w64(ok) & same_row(bt, fb, n);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int key = ok ? (c ? sl % ns : sl / ns) : 0;
+            const uint64_t grp = same_key(key, key_bits) & valid;
+            if (ok && (grp & below) == 0) atomicAdd(&hist[c * ns + key], 1);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * ns; i += blockDim.x) cnt_row(A, S, kind, h, i / ns, ch)[i % ns] = hist[i];
+}
+
+// 2b. per (kind, head, half) and sub-key: the counts of the chunks turned in
+// place into their exclusive prefix sums (the chunk's offset within the
+// sub-key), and the sub-key's total; one thread per sub-key
+__global__ void __launch_bounds__(256) sdm_address_bwd_chunk_prefix_kernel(AddrBwdArgs A, AbWs S)
+{
+    const int seg = blockIdx.y;   // (kind * H + h) * 2 + c
+    const int kind = seg / (2 * A.H), h = (seg / 2) % A.H, c = seg % 2;
+    const int u = blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= A.n_sub) return;
+    int32_t *col = cnt_row(A, S, kind, h, c, 0) + u;
+    const int64_t nch = S.nch[kind];
+    int32_t run = 0;
+    int64_t k = 0;
+    for (; k + 8 <= nch; k += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = col[(k + i) * A.n_sub];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            col[(k + i) * A.n_sub] = run;
+            run += v[i];
+        }
+    }
+    for (; k < nch; ++k) {
+        const int32_t v = col[k * A.n_sub];
+        col[k * A.n_sub] = run;
+        run += v;
+    }
+    S.start[(int64_t)seg * (A.n_sub + 1) + u] = run;   // the total, until 2c
+}
+
+// 2c. per (kind, head, half): exclusive prefix over the sub-keys' totals, in
+// place, and the grand total after them
+__global__ void __launch_bounds__(256) sdm_address_bwd_key_prefix_kernel(AddrBwdArgs A, AbWs S)
+{
+    __shared__ int32_t part[256];
+    int32_t *st = S.start + (int64_t)blockIdx.x * (A.n_sub + 1);
+    const int ns = A.n_sub;
+    const int per = (ns + 255) / 256;
+    const int b0 = min(ns, (int)threadIdx.x * per), b1 = min(ns, b0 + per);
+    int32_t sum = 0;
+    for (int u = b0; u < b1; ++u) sum += st[u];
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    // inclusive scan of the 256 partial sums (Hillis-Steele)
+    for (int d = 1; d < 256; d <<= 1) {
+        const int32_t add = (int)threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+        __syncthreads();
+        part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int32_t run = part[threadIdx.x] - sum;
+    for (int u = b0; u < b1; ++u) {
+        const int32_t v = st[u];
+        st[u] = run;
+        run += v;
+    }
+    if (threadIdx.x == 255) st[ns] = part[255];
+}
+
+// 2d. stable scatter: one wave per (kind, head, chunk) walks its entries 64
+// at a time in token-then-list order (the next 64 loaded while the current
+// ones are placed); the combined entries that select the same sub-key find
+// each other with one ballot per key bit and take consecutive places after
+// the sub-key's running offset (in LDS), in lane order.  A combined entry's
+// dsc is its first member's plus the others' in lane order, read from LDS.
+__global__ void __launch_bounds__(64) sdm_address_bwd_scatter_kernel(AddrBwdArgs A, AbWs S, int key_bits)
+{
+    extern __shared__ int32_t ctr[];   // [2][n_sub]
+    __shared__ float dsl[kWave];
+    int kind, h;
+    int64_t ch;
+    chunk_unit(A, S, kind, h, ch);
+    const int ns = A.n_sub, n = kind ? A.R : A.W;
+    const int32_t N = ns * ns;
+    const int lane = lane_id();
+    for (int c = 0; c < 2; ++c) {
+        const int32_t *cr = cnt_row(A, S, kind, h, c, ch);
+        const int32_t *st = S.start + (int64_t)((kind * A.H + h) * 2 + c) * (ns + 1);
+        for (int u = lane; u < ns; u += kWave) ctr[c * ns + u] = st[u] + cr[u];
+    }
+    __syncthreads();
+    const int64_t BT = A.rows / A.H, total = BT * n;
+    const int64_t f0 = ch * kAbChunk, f1 = min(total, f0 + kAbChunk);
+    const int32_t *idx = kind ? A.ridx : A.widx;
+    const float *dsc = S.dsc + (kind ? A.rows * A.W : 0);
+    int2 *out[2];
+    for (int c = 0; c < 2; ++c) out[c] = S.sorted + (kind ? S.sorted1 : 0) + (int64_t)(h * 2 + c) * total;
+    const uint64_t below = (1ull << lane) - 1ull;
+    // the list entry of this lane in the group of 64 starting at fb (a valid
+    // entry past the end)
+    auto entry = [&](int64_t fb) {
+        const int64_t f = fb + lane < f1 ? fb + lane : f0;
+        const int64_t bt = f / n;
+        return (bt * A.H + h) * n + (f - bt * n);
+    };
+    int64_t e = entry(f0);
+    int32_t sl = idx[e];
+    float ds = dsc[e];
+    for (int64_t fb = f0; fb < f1; fb += kWave) {
+        const int64_t en = entry(fb + kWave);
+        const int32_t sln = idx[en];
+        const float dsn = dsc[en];
+        const bool ok = fb + lane < f1 && sl >= 0 && sl < N;
+        const int64_t bt = e / ((int64_t)A.H * n);
+        const uint64_t valid = __builtin_amdgcn_ballot_w64(ok) & same_row(bt, fb, n);
+        const int32_t row = (int32_t)(e / n);
+        dsl[lane] = ds;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int key = ok ? (c ? sl % ns : sl / ns) : 0;
+            const uint64_t eq = same_key(key, key_bits);
+            const uint64_t grp = eq & valid;
+            const bool lead = ok && (grp & below) == 0;
+            float gs = ds;
+            uint64_t rest = lead ? grp & ~(below | (1ull << lane)) : 0ull;
+            while (rest) {
+                gs += dsl[__builtin_ctzll(rest)];
+                rest &= rest - 1;
+            }
+            const uint64_t peers = eq & __builtin_amdgcn_ballot_w64(lead);   // this step's entries of the key
+            const int rank = __builtin_popcountll(peers & below);
+            const int base = ctr[c * ns + key];
+            if (lead) {
+                out[c][base + rank] = make_int2(row, __float_as_int(gs));
+                if (rank == 0) ctr[c * ns + key] = base + __builtin_popcountll(peers);
+            }
+        }
+        e = en;
+        sl = sln;
+        ds = dsn;
+    }
+}
+
+// 3. one wave per (head, half, sub-key) and kind (or both kinds in order
+// when one buffer takes both sums): the sorted entries 64 at a time, their
+// input rows loaded eight at a time, dsc * x added in order; HM =
+// ceil(half / 64) columns per lane
+template <bool BF16, int HM>
+__global__ void __launch_bounds__(256) sdm_address_bwd_accum_kernel(AddrBwdArgs A, AbWs S)
 {
     const int half = A.d_k / 2, ns = A.n_sub;
-    const int64_t per_hc = (int64_t)ns * half;
-    const int64_t per_kind = (int64_t)A.H * 2 * per_hc;   // elements of one codebook gradient
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool shared = A.dC_w == A.dC_r;
-    if (i >= (shared ? 1 : 2) * per_kind) return;
-    const int kind0 = shared ? 0 : (int)(i / per_kind);
-    const int64_t e = shared ? i : i - kind0 * per_kind;
-    const int64_t hc = e / per_hc, w = e - hc * per_hc;    // (h, c) and the element within
-    float s = 0.f;
+    const int64_t per_kind = (int64_t)A.H * 2 * ns;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (unit >= (shared ? 1 : 2) * per_kind) return;   // whole waves
+    const int kind0 = (int)(unit / per_kind);
+    const int64_t hcu = unit - kind0 * per_kind;        // (h * 2 + c) * ns + u
+    const int hc = (int)(hcu / ns), u = (int)(hcu - (int64_t)hc * ns), c = hc % 2;
+    const int lane = lane_id();
+    const int64_t BT = A.rows / A.H;
+    float acc[HM];
+#pragma unroll
+    for (int m = 0; m < HM; ++m) acc[m] = 0.f;
     for (int kind = kind0; kind <= (shared ? 1 : kind0); ++kind) {
-        const float *p0 = parts + ((size_t)kind * A.H * 2 + hc) * P * per_hc + w;
-        for (int p = 0; p < P; ++p) s += p0[(size_t)p * per_hc];
+        const int n = kind ? A.R : A.W;
+        const int32_t *st = S.start + (int64_t)(kind * A.H * 2 + hc) * (ns + 1);
+        const int2 *ent = S.sorted + (kind ? S.sorted1 : 0) + (int64_t)hc * BT * n;
+        const void *X = kind ? A.q : A.k;
+        const int32_t s0 = st[u], s1 = st[u + 1];
+        for (int32_t e0 = s0; e0 < s1; e0 += kWave) {
+            const int cnt = min(kWave, s1 - e0);
+            const int2 me = ent[lane < cnt ? e0 + lane : e0];
+            for (int q0 = 0; q0 < cnt; q0 += 8) {
+                float xv[8][HM], dq[8];
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int q = min(q0 + qq, kWave - 1);
+                    const int32_t r = __builtin_amdgcn_readlane(me.x, q);
+                    const float d = __int_as_float(__builtin_amdgcn_readlane(me.y, q));
+                    dq[qq] = q0 + qq < cnt ? d : 0.f;
+#pragma unroll
+                    for (int m = 0; m < HM; ++m) {
+                        const int e = lane + kWave * m;
+                        const float xl = ld_in<BF16>(X, (int64_t)r * A.d_k + c * half + (e < half ? e : 0));
+                        xv[qq][m] = e < half ? xl : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq)
+#pragma unroll
+                    for (int m = 0; m < HM; ++m) acc[m] = __builtin_fmaf(dq[qq], xv[qq][m], acc[m]);
+            }
+        }
     }
-    (kind0 ? A.dC_r : A.dC_w)[e] = s;
+    float *out = (kind0 ? A.dC_r : A.dC_w) + hcu * half;
+#pragma unroll
+    for (int m = 0; m < HM; ++m) {
+        const int e = lane + kWave * m;
+        if (e < half) out[e] = acc[m];
+    }
 }
 
 hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hipStream_t stream)
 {
     if (A.rows == 0) return hipSuccess;
-    const int half = A.d_k / 2;
-    const int P = address_bwd_parts(A.rows / A.H, A.H, A.n_sub);
-    float *dsc = static_cast<float *>(ws);
-    const size_t dsc_bytes = sizeof(float) * (size_t)(A.rows * (A.W + A.R));
-    float *parts = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + ((dsc_bytes + 255) & ~(size_t)255));
+    const int half = A.d_k / 2, ns = A.n_sub;
+    const int64_t BT = A.rows / A.H;
+    const AddrBwdLayout L = address_bwd_layout(BT, A.H, A.W, A.R, ns);
+    unsigned char *base = static_cast<unsigned char *>(ws);
+    AbWs S;
+    S.dsc = reinterpret_cast<float *>(base);
+    S.cnt = reinterpret_cast<int32_t *>(base + L.off_cnt);
+    S.start = reinterpret_cast<int32_t *>(base + L.off_start);
+    S.sorted = reinterpret_cast<int2 *>(base + L.off_sorted);
+    S.nch[0] = L.nch[0];
+    S.nch[1] = L.nch[1];
+    S.cnt1 = L.cnt1;
+    S.sorted1 = L.sorted1;
+    int key_bits = 0;
+    while ((1 << key_bits) < ns) ++key_bits;
     const int64_t b1 = (2 * A.rows + 3) / 4;
-    const int64_t units = 2 * (int64_t)A.H * 2 * ((A.n_sub + kAbRows - 1) / kAbRows) * P;
-    const int64_t b2 = (units + 3) / 4;
-    const int64_t per_kind = (int64_t)A.H * 2 * A.n_sub * half;
-    const int64_t b3 = ((A.dC_w == A.dC_r ? 1 : 2) * per_kind + 255) / 256;
+    const int64_t chunks = (int64_t)A.H * (L.nch[0] + L.nch[1]);
+    const int segs = 2 * A.H * 2;
+    const bool shared = A.dC_w == A.dC_r;
+    const int64_t b4 = ((shared ? 1 : 2) * (int64_t)A.H * 2 * ns + 3) / 4;
+    const size_t hist_bytes = sizeof(int32_t) * 2 * (size_t)ns;
     const int nm = (A.d_k + kWave - 1) / kWave, hm = (half + kWave - 1) / kWave;
 #define SDM_AB_DX(BF, M)                                                                                      \
-    hipLaunchKernelGGL((sdm_address_bwd_dx_kernel<BF, M>), dim3((unsigned)b1), dim3(256), 0, stream, A, dsc)
-#define SDM_AB_DC(BF, M)                                                                                      \
-    hipLaunchKernelGGL((sdm_address_bwd_dc_kernel<BF, M>), dim3((unsigned)b2), dim3(256), 0, stream, A, dsc, parts, P)
+    hipLaunchKernelGGL((sdm_address_bwd_dx_kernel<BF, M>), dim3((unsigned)b1), dim3(256), 0, stream, A, S.dsc)
+#define SDM_AB_ACC(BF, M)                                                                                     \
+    hipLaunchKernelGGL((sdm_address_bwd_accum_kernel<BF, M>), dim3((unsigned)b4), dim3(256), 0, stream, A, S)
     if (bf16) {
         if (nm <= 1) SDM_AB_DX(true, 1);
         else if (nm <= 2) SDM_AB_DX(true, 2);
         else if (nm <= 4) SDM_AB_DX(true, 4);
         else SDM_AB_DX(true, 8);
-        if (hm <= 1) SDM_AB_DC(true, 1);
-        else if (hm <= 2) SDM_AB_DC(true, 2);
-        else SDM_AB_DC(true, 4);
     } else {
         if (nm <= 1) SDM_AB_DX(false, 1);
         else if (nm <= 2) SDM_AB_DX(false, 2);
         else if (nm <= 4) SDM_AB_DX(false, 4);
         else SDM_AB_DX(false, 8);
-        if (hm <= 1) SDM_AB_DC(false, 1);
-        else if (hm <= 2) SDM_AB_DC(false, 2);
-        else SDM_AB_DC(false, 4);
+    }
+    hipLaunchKernelGGL(sdm_address_bwd_count_kernel, dim3((unsigned)chunks), dim3(256), hist_bytes, stream, A, S,
+                       key_bits);
+    hipLaunchKernelGGL(sdm_address_bwd_chunk_prefix_kernel, dim3((unsigned)((ns + 255) / 256), (unsigned)segs), dim3(256),
+                       0, stream, A, S);
+    hipLaunchKernelGGL(sdm_address_bwd_key_prefix_kernel, dim3((unsigned)segs), dim3(256), 0, stream, A, S);
+    hipLaunchKernelGGL(sdm_address_bwd_scatter_kernel, dim3((unsigned)chunks), dim3(kWave), hist_bytes, stream, A, S,
+                       key_bits);
+    if (bf16) {
+        if (hm <= 1) SDM_AB_ACC(true, 1);
+        else if (hm <= 2) SDM_AB_ACC(true, 2);
+        else SDM_AB_ACC(true, 4);
+    } else {
+        if (hm <= 1) SDM_AB_ACC(false, 1);
+        else if (hm <= 2) SDM_AB_ACC(false, 2);
+        else SDM_AB_ACC(false, 4);
     }
 #undef SDM_AB_DX
-#undef SDM_AB_DC
-    hipLaunchKernelGGL(sdm_address_bwd_reduce_kernel, dim3((unsigned)b3), dim3(256), 0, stream, A, parts, P);
+#undef SDM_AB_ACC
     return hipGetLastError();
 }
 

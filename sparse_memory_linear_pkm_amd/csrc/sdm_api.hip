@@ -547,6 +547,10 @@ sdm_status sdm_address_backward(const void *k, const void *q, const void *C_w, c
         !aligned(dk, 4) || !aligned(dq, 4) || !aligned(dC_w, 4) || !aligned(dC_r, 4) || !aligned(workspace, 16))
         return fail(SDM_ERR_INVALID_ARG, "misaligned argument");
     const int64_t rows = d->B * d->T * d->H;
+    // token-head rows and the list entries of one (kind, head) are indexed with int32
+    if (rows > 0x7fffffff || d->B * d->T * (d->W > d->R ? d->W : d->R) > 0x7fffffff ||
+        d->H * d->n_sub * d->d_k > 0x7fffffff)
+        return fail(SDM_ERR_UNSUPPORTED, "B*T*H, B*T*max(W, R) and the codebook size must be < 2^31");
     const size_t need = sdm::address_bwd_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->n_sub,
                                                          (int)(d->d_k / 2));
     if (!workspace || workspace_bytes < need)
