@@ -29,6 +29,7 @@ namespace sdm {
 namespace {
 
 constexpr int64_t kAbChunk = 4096;         // list entries per chunk of the counting sort
+constexpr int64_t kAbDxRows = 8;           // token-head rows per wave of the dx pass
 
 template <bool BF16>
 __device__ __forceinline__ float ld_in(const void *p, int64_t e)
@@ -92,41 +93,31 @@ size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R
     return address_bwd_layout(B * T, H, W, R, n_sub).bytes;
 }
 
-// 1. softmax backward and dx: one wave per (row, kind); lanes over the list
-// for dsc, over the features for dx.  Each lane first turns its entry's
-// slot into the element offsets of its two sub-key rows (the divisions by
-// n_sub once per entry, in parallel), so that the loop over entries only
-// reads them back (readlane) and loads.
-template <bool BF16, int NM>
+// 1. softmax backward and dx: one wave per kAbDxRows consecutive rows of one
+// kind (the next row's list loaded while the current one is processed);
+// lanes over the list for dsc, over the features for dx.  Each lane first
+// turns its entry's slot into the element offsets of its two sub-key rows
+// (the divisions by n_sub once per entry, in parallel), so that the loop
+// over entries only reads them back (readlane) and loads.
+template <bool BF16, int NM, int KJ>
 __global__ void __launch_bounds__(256) sdm_address_bwd_dx_kernel(AddrBwdArgs A, float *dsc_ws)
 {
     const int64_t rows = A.rows;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-    if (gw >= 2 * rows) return;                 // whole waves
-    const int kind = (int)(gw / rows);
-    const int64_t r = gw - (int64_t)kind * rows;
+    const int64_t wpk = (rows + kAbDxRows - 1) / kAbDxRows;   // waves per kind
+    // the wave's index, uniform (so that the codebook's buffer resource is scalar)
+    const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    if (gw >= 2 * wpk) return;                 // whole waves
+    const int kind = (int)(gw / wpk);
+    const int64_t r0 = (gw - (int64_t)kind * wpk) * kAbDxRows;
+    const int64_t r1 = min(rows, r0 + kAbDxRows);
     const int lane = lane_id();
     const int n = kind ? A.R : A.W;
-    const int32_t *idx = (kind ? A.ridx : A.widx) + r * n;
-    const float *wt = (kind ? A.rwt : A.wwt) + r * n;
-    const float *dwt = (kind ? A.dr : A.dw) + r * n;
+    const int32_t *idx = kind ? A.ridx : A.widx;
+    const float *wt = kind ? A.rwt : A.wwt;
+    const float *dwt = kind ? A.dr : A.dw;
     const void *C = kind ? A.C_r : A.C_w;
-    const int h = (int)(r % A.H);
     const int ns = A.n_sub, half = A.d_k / 2;
     const int jl = lane < n ? lane : 0;   // unconditional loads, masked after
-    const float wl = wt[jl], gl = dwt[jl];
-    const int32_t sl = idx[jl];
-    const float w = lane < n ? wl : 0.f, g = lane < n ? gl : 0.f;
-    const float mean = wave_sum_f32(w * g);
-    const float ds = w * (g - mean);
-    if (lane < n) dsc_ws[(kind ? rows * A.W : 0) + r * n + lane] = ds;
-    // entries past the list and slots outside the memory add exactly nothing
-    const bool ok = lane < n && sl >= 0 && sl < ns * ns;
-    const float dsl = ok ? ds : 0.f;
-    const int32_t s = ok ? sl : 0;
-    // element offsets (in the codebook) of this entry's rows of half 0 and half 1
-    const int32_t off0 = ((h * 2 + 0) * ns + s / ns) * half;
-    const int32_t off1 = ((h * 2 + 1) * ns + s % ns) * half - half;
     // feature e of a lane: e < half reads half 0 at e, else half 1 at e - half
     int32_t fe[NM];
     bool h1[NM], live[NM];
@@ -134,35 +125,67 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_dx_kernel(AddrBwdArgs A, 
     for (int m = 0; m < NM; ++m) {
         const int e = lane + kWave * m;
         live[m] = e < A.d_k;
-        h1[m] = e >= half;
+        h1[m] = live[m] ? e >= half : true;
         fe[m] = live[m] ? e : half;   // a valid element of half 1 for dead features
-        h1[m] = live[m] ? h1[m] : true;
     }
-    float acc[NM];
+    float wl = wt[r0 * n + jl], gl = dwt[r0 * n + jl];
+    int32_t sl = idx[r0 * n + jl];
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t rn = r + 1 < r1 ? r + 1 : r;
+        const float wn = wt[rn * n + jl], gn = dwt[rn * n + jl];
+        const int32_t sn = idx[rn * n + jl];
+        const int h = (int)(r % A.H);
+        const float w = lane < n ? wl : 0.f, g = lane < n ? gl : 0.f;
+        const float mean = wave_sum_f32(w * g);
+        const float ds = w * (g - mean);
+        if (lane < n) dsc_ws[(kind ? rows * A.W : 0) + r * n + lane] = ds;
+        // entries past the list and slots outside the memory add exactly nothing
+        const bool ok = lane < n && sl >= 0 && sl < ns * ns;
+        const float dsl = ok ? ds : 0.f;
+        const int32_t s = ok ? sl : 0;
+        // byte offsets (in the head's codebook) of this entry's rows of half 0
+        // and half 1, the latter less half a row so that feature e adds e
+        constexpr int esz = BF16 ? 2 : 4;
+        const int32_t off0 = (s / ns) * half * esz;
+        const int32_t off1 = ((ns + s % ns) * half - half) * esz;
+        const __amdgpu_buffer_rsrc_t Crs = make_rsrc(static_cast<const unsigned char *>(C) +
+                                                         (int64_t)h * 2 * ns * half * esz,
+                                                     (uint32_t)(2 * ns * half * esz));
+        float acc[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) acc[m] = 0.f;
-    // eight list entries at a time, their codebook loads issued together
-    constexpr int kJ = 8;
-    for (int j0 = 0; j0 < n; j0 += kJ) {
-        float cv[kJ][NM], dj[kJ];
+        for (int m = 0; m < NM; ++m) acc[m] = 0.f;
+        // KJ list entries at a time, their codebook loads issued together
+        constexpr int kJ = KJ;
+        for (int j0 = 0; j0 < n; j0 += kJ) {
+            float cv[kJ][NM], dj[kJ];
 #pragma unroll
-        for (int jj = 0; jj < kJ; ++jj) {
-            const int j = min(j0 + jj, kWave - 1);
-            const int32_t o0 = __builtin_amdgcn_readlane(off0, j);
-            const int32_t o1 = __builtin_amdgcn_readlane(off1, j);
-            dj[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dsl), j));
+            for (int jj = 0; jj < kJ; ++jj) {
+                const int j = min(j0 + jj, kWave - 1);
+                const int32_t o0 = __builtin_amdgcn_readlane(off0, j);
+                const int32_t o1 = __builtin_amdgcn_readlane(off1, j);
+                dj[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dsl), j));
 #pragma unroll
-            for (int m = 0; m < NM; ++m) cv[jj][m] = ld_in<BF16>(C, (h1[m] ? o1 : o0) + fe[m]);
+                for (int m = 0; m < NM; ++m) {
+                    const uint32_t off = (uint32_t)((h1[m] ? o1 : o0) + fe[m] * esz);
+                    if constexpr (BF16)
+                        cv[jj][m] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(Crs, off, 0, 0) << 16);
+                    else
+                        cv[jj][m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Crs, off, 0, 0));
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < kJ; ++jj)
+#pragma unroll
+                for (int m = 0; m < NM; ++m) acc[m] = __builtin_fmaf(dj[jj], cv[jj][m], acc[m]);
         }
+        float *dx = (kind ? A.dq : A.dk) + r * A.d_k;
 #pragma unroll
-        for (int jj = 0; jj < kJ; ++jj)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) acc[m] = __builtin_fmaf(dj[jj], cv[jj][m], acc[m]);
+        for (int m = 0; m < NM; ++m)
+            if (live[m]) dx[lane + kWave * m] = acc[m];
+        wl = wn;
+        gl = gn;
+        sl = sn;
     }
-    float *dx = (kind ? A.dq : A.dk) + r * A.d_k;
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-        if (live[m]) dx[lane + kWave * m] = acc[m];
 }
 
 namespace {
@@ -385,7 +408,7 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_accum_kernel(AddrBwdArgs 
     const int half = A.d_k / 2, ns = A.n_sub;
     const bool shared = A.dC_w == A.dC_r;
     const int64_t per_kind = (int64_t)A.H * 2 * ns;
-    const int64_t unit = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     if (unit >= (shared ? 1 : 2) * per_kind) return;   // whole waves
     const int kind0 = (int)(unit / per_kind);
     const int64_t hcu = unit - kind0 * per_kind;        // (h * 2 + c) * ns + u
@@ -452,15 +475,25 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
     S.sorted1 = L.sorted1;
     int key_bits = 0;
     while ((1 << key_bits) < ns) ++key_bits;
-    const int64_t b1 = (2 * A.rows + 3) / 4;
+    const int64_t b1 = (2 * ((A.rows + kAbDxRows - 1) / kAbDxRows) + 3) / 4;
     const int64_t chunks = (int64_t)A.H * (L.nch[0] + L.nch[1]);
     const int segs = 2 * A.H * 2;
     const bool shared = A.dC_w == A.dC_r;
     const int64_t b4 = ((shared ? 1 : 2) * (int64_t)A.H * 2 * ns + 3) / 4;
     const size_t hist_bytes = sizeof(int32_t) * 2 * (size_t)ns;
     const int nm = (A.d_k + kWave - 1) / kWave, hm = (half + kWave - 1) / kWave;
+    // list entries whose codebook loads are issued together: 8, or 16 for
+    // longer lists (32 measured slower on the 1.4B layer: fewer waves fit)
+    const int maxn = A.W > A.R ? A.W : A.R;
 #define SDM_AB_DX(BF, M)                                                                                      \
-    hipLaunchKernelGGL((sdm_address_bwd_dx_kernel<BF, M>), dim3((unsigned)b1), dim3(256), 0, stream, A, S.dsc)
+    do {                                                                                                      \
+        if (maxn <= 8)                                                                                        \
+            hipLaunchKernelGGL((sdm_address_bwd_dx_kernel<BF, M, 8>), dim3((unsigned)b1), dim3(256), 0, stream, A, \
+                               S.dsc);                                                                        \
+        else                                                                                                  \
+            hipLaunchKernelGGL((sdm_address_bwd_dx_kernel<BF, M, 16>), dim3((unsigned)b1), dim3(256), 0, stream, \
+                               A, S.dsc);                                                                     \
+    } while (0)
 #define SDM_AB_ACC(BF, M)                                                                                     \
     hipLaunchKernelGGL((sdm_address_bwd_accum_kernel<BF, M>), dim3((unsigned)b4), dim3(256), 0, stream, A, S)
     if (bf16) {
