@@ -269,9 +269,10 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_count_kernel(AddrBwdArgs 
 // sub-key), and the sub-key's total; one thread per sub-key
 __global__ void __launch_bounds__(256) sdm_address_bwd_chunk_prefix_kernel(AddrBwdArgs A, AbWs S)
 {
-    const int seg = blockIdx.y;   // (kind * H + h) * 2 + c
+    const int nbb = (A.n_sub + 255) / 256;      // workgroups per segment
+    const int seg = blockIdx.x / nbb;           // (kind * H + h) * 2 + c
     const int kind = seg / (2 * A.H), h = (seg / 2) % A.H, c = seg % 2;
-    const int u = blockIdx.x * blockDim.x + threadIdx.x;
+    const int u = (blockIdx.x - seg * nbb) * blockDim.x + threadIdx.x;
     if (u >= A.n_sub) return;
     int32_t *col = cnt_row(A, S, kind, h, c, 0) + u;
     const int64_t nch = S.nch[kind];
@@ -509,8 +510,8 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
     }
     hipLaunchKernelGGL(sdm_address_bwd_count_kernel, dim3((unsigned)chunks), dim3(256), hist_bytes, stream, A, S,
                        key_bits);
-    hipLaunchKernelGGL(sdm_address_bwd_chunk_prefix_kernel, dim3((unsigned)((ns + 255) / 256), (unsigned)segs), dim3(256),
-                       0, stream, A, S);
+    hipLaunchKernelGGL(sdm_address_bwd_chunk_prefix_kernel, dim3((unsigned)(((ns + 255) / 256) * segs)), dim3(256), 0,
+                       stream, A, S);
     hipLaunchKernelGGL(sdm_address_bwd_key_prefix_kernel, dim3((unsigned)segs), dim3(256), 0, stream, A, S);
     hipLaunchKernelGGL(sdm_address_bwd_scatter_kernel, dim3((unsigned)chunks), dim3(kWave), hist_bytes, stream, A, S,
                        key_bits);

@@ -82,8 +82,8 @@ def test_graph_capture_replays_match_eager(sdm, torch):
 def test_graph_capture_training_step_and_layer_edges(sdm, torch):
     """The other entry points under capture: gates, the scan with its rows
     saved, the backward scan, the output norm and gate, the backward of the
-    norm and of the gates, and the dense recurrence; three replays, each
-    bit-identical to the eager run."""
+    norm and of the gates, the addressing's backward, and the dense
+    recurrence; three replays, each bit-identical to the eager run."""
     d = Dims(B=2, T=40, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=8, R=8)
     note(f"graph capture, training step {d}")
     x = synth.make_inputs(d, seed=31)
@@ -124,6 +124,12 @@ def test_graph_capture_training_step_and_layer_edges(sdm, torch):
     nws = T.empty(max(nws_bytes, 1), dtype=T.uint8, device="cuda")
     gws_bytes = sdm.sdm_gates_backward_workspace_size(dims)
     gws = T.empty(max(gws_bytes, 1), dtype=T.uint8, device="cuda")
+    aws_bytes = sdm.sdm_address_backward_workspace_size(dims)
+    aws = T.empty(max(aws_bytes, 1), dtype=T.uint8, device="cuda")
+    kx, qx, Cw = to_dev(x["k"]), to_dev(x["q"]), to_dev(x["C_w"])
+    dk = T.empty((d.B, d.T, d.H, d.d_k), dtype=T.float32, device="cuda")
+    dq = T.empty_like(dk)
+    dC = T.empty((d.H, 2, d.n_sub, d.d_k // 2), dtype=T.float32, device="cuda")
 
     def step():
         sdm.sdm_gates(inp["a_raw"], inp["b_raw"], inp["A"], inp["dt_bias"], dims, a_g, b_g)
@@ -138,10 +144,12 @@ def test_graph_capture_training_step_and_layer_edges(sdm, torch):
                                           nws_bytes)
         sdm.sdm_gates_backward(inp["a_raw"], inp["b_raw"], inp["A"], inp["dt_bias"], grads[1], grads[2], dims,
                                *gb, gws, gws_bytes)
+        sdm.sdm_address_backward(kx, qx, Cw, Cw, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], grads[3], grads[4],
+                                 dims, dk, dq, dC, dC, aws, aws_bytes)
         S.copy_(S0)
         sdm.sdm_gdn_dense_forward(S, gin["k"], gin["q"], gin["v"], gin["a"], gin["b"], og, gdims)
 
-    outs = (a_g, b_g, M, dM, o, xs, zs, *grads, y, do_n, dg_n, dgamma, *gb, S, og)
+    outs = (a_g, b_g, M, dM, o, xs, zs, *grads, y, do_n, dg_n, dgamma, *gb, dk, dq, dC, S, og)
     step()
     T.cuda.synchronize()
     ref = [to_host(t).copy() for t in outs]
