@@ -201,6 +201,45 @@ def layer_edges(sdm, synth, torch, d, dims, o, stream, seed, reps=20):
     return out
 
 
+def decode_batches(sdm, torch, dx, per, M, o, dims1, d, nsteps, stream):
+    """After the timed region: one batch of `nsteps` decode steps from the
+    learned initial state, two ways.  Plain: sdm_state_init copies M0 into
+    every sequence (B x |M0| bytes), then the steps.  Copy-on-write: the
+    bitmap is cleared, then sdm_decode_step_cow reads every row a sequence
+    has not written from M0.  Times from HIP events on the launch stream;
+    the state buffer M is reused."""
+    touched = torch.empty(sdm.sdm_cow_bitmap_bytes(dims1) // 4, dtype=torch.int32, device="cuda")
+    ev = {n: torch.cuda.Event(enable_timing=True) for n in ("p0", "p1", "p2", "c0", "c1", "c2")}
+
+    def steps(cow):
+        for t in range(nsteps):
+            args = (per["k"][t], per["q"][t], dx["C_w"], dx["C_r"], per["v"][t], per["a"][t], per["b"][t], o,
+                    None, None, dims1, stream)
+            if cow:
+                sdm.sdm_decode_step_cow(M, dx["M0"], touched, *args)
+            else:
+                sdm.sdm_decode_step(M, *args)
+
+    ev["p0"].record(stream)
+    sdm.sdm_state_init(M, dx["M0"], dims1, stream)
+    ev["p1"].record(stream)
+    steps(False)
+    ev["p2"].record(stream)
+    ev["c0"].record(stream)
+    sdm.sdm_cow_reset(touched, dims1, stream)
+    ev["c1"].record(stream)
+    steps(True)
+    ev["c2"].record(stream)
+    torch.cuda.synchronize()
+    el = lambda a, b: ev[a].elapsed_time(ev[b])
+    return {"steps": nsteps,
+            "plain": {"state_init_ms": el("p0", "p1"), "steps_ms": el("p1", "p2"), "batch_ms": el("p0", "p2")},
+            "copy_on_write": {"bitmap_reset_ms": el("c0", "c1"), "steps_ms": el("c1", "c2"),
+                              "batch_ms": el("c0", "c2"), "bitmap_bytes": touched.numel() * 4},
+            "batch_tokens_per_s_plain": d.B * nsteps / (el("p0", "p2") * 1e-3),
+            "batch_tokens_per_s_cow": d.B * nsteps / (el("c0", "c2") * 1e-3)}
+
+
 FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (packed) peak, vendor figure
 
 
@@ -553,6 +592,7 @@ def main():
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                               "traffic": None, "algorithmic_bytes_per_launch": bytes_per_launch,
                               "avg_launch_ms": dec_ms}
+        result["copy_on_write"] = decode_batches(sdm, torch, dx, per, M, o, dims1, d, nsteps, stream)
     else:
         spans = {"sdm_state_init": ("init0", "init1"), "sdm_pkm_address": ("start", "addr1"),
                  "sdm_scan_forward": ("scan0", "scan1"), "sdm_decode_step": ("scan1", "dec1")}

@@ -222,6 +222,43 @@ sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C
                            sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Copy-on-write state for decode ([P] Sec. 3.1 "Learned Initial State": every
+ * sequence starts from the shared M0).  Instead of copying M0 into every
+ * sequence (sdm_state_init: B x |M0| bytes written), each (b, h) keeps a
+ * bitmap of the slots it has written; a row whose bit is clear is read from
+ * M0.  A decode step touches at most W rows per (b, h), so after a few
+ * thousand steps most of a large memory is still M0's.
+ *   touched [B][H][ceil(N/32)] uint32 (bit s % 32 of word s / 32: slot s of
+ *   that (b, h) has been written and lives in M).  Bytes:
+ *   sdm_cow_bitmap_bytes(dims).
+ * ------------------------------------------------------------------------- */
+size_t sdm_cow_bitmap_bytes(const sdm_dims *dims);
+
+/* sdm_cow_reset -- every sequence starts from M0: clears the bitmap (a fill
+ * kernel, safe under graph capture).  Uses B, H, n_sub of dims. */
+sdm_status sdm_cow_reset(uint32_t *touched, const sdm_dims *dims, sdm_stream_t stream);
+
+/* sdm_decode_step_cow -- sdm_decode_step on a copy-on-write state: the rows
+ * it gathers are taken from M where their bit is set and from M0 [H,N,d_v]
+ * otherwise; the rows it writes go to M and get their bit set.  M needs no
+ * initialisation.  Outputs and the rows written are bit-identical to
+ * sdm_state_init followed by sdm_decode_step.  M0, M, the bitmap and o must
+ * not overlap (SDM_ERR_INVALID_ARG); other arguments as sdm_decode_step.
+ * Calls that overlap on one bitmap race. */
+sdm_status sdm_decode_step_cow(float *M, const float *M0, uint32_t *touched, const void *k,
+                               const void *q, const void *C_w, const void *C_r, const void *v,
+                               const float *a, const float *b, float *o, int32_t *widx_out,
+                               int32_t *ridx_out, const sdm_dims *dims, sdm_stream_t stream);
+
+/* sdm_cow_materialize -- turns a copy-on-write state into a plain one: every
+ * row whose bit is clear takes M0's values, then every bit is set (so further
+ * copy-on-write steps read M only).  After it, M is exactly the state that
+ * sdm_state_init and the same plain steps would have produced.  Uses B, H,
+ * n_sub, d_v of dims. */
+sdm_status sdm_cow_materialize(float *M, const float *M0, uint32_t *touched, const sdm_dims *dims,
+                               sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * sdm_gates -- the scan's gates from their pre-activations: [P] Sec. 3.1
  * step 2 (per-head forget gate a_t with a learnable decay A, input gate
  * b_t) with the Gated DeltaNet parameterisation that [P] Sec. 4 initialises

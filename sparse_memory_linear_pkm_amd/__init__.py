@@ -9,7 +9,8 @@ is no fallback implementation.
 from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP, SDM_F32,
                       SDM_BF16, SdmDims, SdmError, dims_from, lib_path, load_library,
                       sdm_state_init, sdm_pkm_address, sdm_scan_workspace_size, sdm_scan_forward,
-                      sdm_decode_step, sdm_gates, sdm_output_norm_gate, sdm_gdn_dense_forward,
+                      sdm_decode_step, sdm_cow_bitmap_bytes, sdm_cow_reset, sdm_decode_step_cow,
+                      sdm_cow_materialize, sdm_gates, sdm_output_norm_gate, sdm_gdn_dense_forward,
                       sdm_scan_forward_save, sdm_scan_backward, scan_forward_save, scan_backward,
                       sdm_address_backward, sdm_address_backward_workspace_size, address_backward,
                       sdm_gates_backward, sdm_gates_backward_workspace_size, sdm_output_norm_gate_backward,

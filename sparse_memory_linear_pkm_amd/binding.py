@@ -59,12 +59,17 @@ def load_library():
         "sdm_scan_backward": [P] * 16 + [D, P],
         "sdm_address_backward": [P] * 10 + [D, P, P, P, P, P, ctypes.c_size_t, P],
         "sdm_gates_backward": [P] * 6 + [D, P, P, P, P, P, ctypes.c_size_t, P],
+        "sdm_cow_reset": [P, D, P],
+        "sdm_decode_step_cow": [P] * 13 + [D, P],
+        "sdm_cow_materialize": [P, P, P, D, P],
         "sdm_output_norm_gate_backward": [P, P, P, ctypes.c_float, P, D, P, P, P, P, ctypes.c_size_t, P],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = I32
+    lib.sdm_cow_bitmap_bytes.argtypes = [D]
+    lib.sdm_cow_bitmap_bytes.restype = ctypes.c_size_t
     lib.sdm_scan_workspace_size.argtypes = [D]
     lib.sdm_scan_workspace_size.restype = ctypes.c_size_t
     lib.sdm_address_backward_workspace_size.argtypes = [D]
@@ -176,6 +181,34 @@ def sdm_decode_step(M, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, dims: Sdm
                                         ctypes.byref(dims), _stream(stream))
     if check:
         _check(st, "sdm_decode_step")
+    return st
+
+
+def sdm_cow_bitmap_bytes(dims: SdmDims) -> int:
+    return int(load_library().sdm_cow_bitmap_bytes(ctypes.byref(dims)))
+
+
+def sdm_cow_reset(touched, dims: SdmDims, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_cow_reset(_ptr(touched), ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_cow_reset")
+    return st
+
+
+def sdm_decode_step_cow(M, M0, touched, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, dims: SdmDims, stream=None,
+                        *, check: bool = True) -> int:
+    st = load_library().sdm_decode_step_cow(_ptr(M), _ptr(M0), _ptr(touched), _ptr(k), _ptr(q), _ptr(C_w), _ptr(C_r),
+                                            _ptr(v), _ptr(a), _ptr(b), _ptr(o), _ptr(widx_out), _ptr(ridx_out),
+                                            ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_decode_step_cow")
+    return st
+
+
+def sdm_cow_materialize(M, M0, touched, dims: SdmDims, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_cow_materialize(_ptr(M), _ptr(M0), _ptr(touched), ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_cow_materialize")
     return st
 
 

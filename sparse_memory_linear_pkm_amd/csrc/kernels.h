@@ -90,9 +90,22 @@ struct DecodeArgs {
     const float *a, *b;
     float *o;
     int32_t *widx_out, *ridx_out;
+    // copy-on-write state: rows of (b, h) whose bit in touched is clear are
+    // read from M0 [H,N,d_v] instead of M (nullptr: M holds every row)
+    const float *M0;
+    uint32_t *touched;    // [B][H][ceil(N / 32)]
     int B, H, d_k, n_sub, d_v, k_prime, W, R, N;
     Staircase stair[2];   // merge candidates for (k', W) and (k', R)
 };
+
+struct CowArgs {
+    float *M;
+    const float *M0;
+    uint32_t *touched;
+    int64_t B, H, N, d_v;
+};
+hipError_t launch_cow_reset(const CowArgs &A, hipStream_t stream);
+hipError_t launch_cow_materialize(const CowArgs &A, hipStream_t stream);
 
 struct InitArgs {
     float *M;

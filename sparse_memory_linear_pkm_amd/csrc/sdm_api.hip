@@ -261,9 +261,77 @@ static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan_forward launch");
 }
 
+static sdm_status decode_impl(float *M, const float *M0, uint32_t *touched, const void *k, const void *q,
+                              const void *C_w, const void *C_r, const void *v, const float *a, const float *b,
+                              float *o, int32_t *widx_out, int32_t *ridx_out, const sdm_dims *d, sdm_stream_t stream);
+
 sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C_w, const void *C_r,
                            const void *v, const float *a, const float *b, float *o, int32_t *widx_out,
                            int32_t *ridx_out, const sdm_dims *d, sdm_stream_t stream)
+{
+    return decode_impl(M, nullptr, nullptr, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, d, stream);
+}
+
+size_t sdm_cow_bitmap_bytes(const sdm_dims *d)
+{
+    if (!d || d->B < 0 || d->H < 1 || d->n_sub < 1 || d->n_sub > 46340) return 0;
+    return sizeof(uint32_t) * (size_t)(d->B * d->H) * (size_t)((d->n_sub * d->n_sub + 31) / 32);
+}
+
+// checks shared by the copy-on-write calls: M0, the bitmap, and their overlaps with M
+static sdm_status check_cow(float *M, const float *M0, const uint32_t *touched, const sdm_dims *d)
+{
+    if (!M || !M0 || !touched) return fail(SDM_ERR_INVALID_ARG, "NULL pointer argument");
+    if (!aligned(M, 16) || !aligned(M0, 16) || !aligned(touched, 4))
+        return fail(SDM_ERR_INVALID_ARG, "M and M0 must be 16-byte aligned, the bitmap 4-byte aligned");
+    const int64_t N = d->n_sub * d->n_sub;
+    const size_t msz = sizeof(float) * (size_t)(d->B * d->H * N * d->d_v);
+    const size_t m0sz = sizeof(float) * (size_t)(d->H * N * d->d_v);
+    const size_t tsz = sdm_cow_bitmap_bytes(d);
+    if (overlap(M, msz, M0, m0sz) || overlap(touched, tsz, M, msz) || overlap(touched, tsz, M0, m0sz))
+        return fail(SDM_ERR_INVALID_ARG, "M, M0 and the bitmap must not overlap");
+    return SDM_OK;
+}
+
+sdm_status sdm_cow_reset(uint32_t *touched, const sdm_dims *d, sdm_stream_t stream)
+{
+    if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
+    if (d->B < 0 || d->H < 1 || d->n_sub < 1) return fail(SDM_ERR_INVALID_ARG, "need B >= 0, H >= 1, n_sub >= 1");
+    if (d->n_sub > 46340) return fail(SDM_ERR_INVALID_ARG, "n_sub^2 must fit in int32");
+    if (d->B == 0) return SDM_OK;
+    if (!touched || !aligned(touched, 4)) return fail(SDM_ERR_INVALID_ARG, "NULL or misaligned bitmap");
+    sdm::CowArgs A{nullptr, nullptr, touched, d->B, d->H, d->n_sub * d->n_sub, d->d_v};
+    hipError_t e = sdm::launch_cow_reset(A, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_cow_reset launch");
+}
+
+sdm_status sdm_cow_materialize(float *M, const float *M0, uint32_t *touched, const sdm_dims *d,
+                               sdm_stream_t stream)
+{
+    sdm_status st = check_memory_dims(d);
+    if (st != SDM_OK) return st;
+    if (d->B == 0) return SDM_OK;
+    st = check_cow(M, M0, touched, d);
+    if (st != SDM_OK) return st;
+    sdm::CowArgs A{M, M0, touched, d->B, d->H, d->n_sub * d->n_sub, d->d_v};
+    hipError_t e = sdm::launch_cow_materialize(A, as_stream(stream));
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_cow_materialize launch");
+}
+
+sdm_status sdm_decode_step_cow(float *M, const float *M0, uint32_t *touched, const void *k, const void *q,
+                               const void *C_w, const void *C_r, const void *v, const float *a, const float *b,
+                               float *o, int32_t *widx_out, int32_t *ridx_out, const sdm_dims *d,
+                               sdm_stream_t stream)
+{
+    if (d && d->B > 0) {
+        if (!M0 || !touched) return fail(SDM_ERR_INVALID_ARG, "M0 and the bitmap must be non-NULL");
+    }
+    return decode_impl(M, M0, touched, k, q, C_w, C_r, v, a, b, o, widx_out, ridx_out, d, stream);
+}
+
+static sdm_status decode_impl(float *M, const float *M0, uint32_t *touched, const void *k, const void *q,
+                              const void *C_w, const void *C_r, const void *v, const float *a, const float *b,
+                              float *o, int32_t *widx_out, int32_t *ridx_out, const sdm_dims *d, sdm_stream_t stream)
 {
     sdm_status st = check_method_dims(d, false);
     if (st != SDM_OK) return st;
@@ -283,9 +351,18 @@ sdm_status sdm_decode_step(float *M, const void *k, const void *q, const void *C
     if (overlap(o, sizeof(float) * d->B * d->H * d->d_v, M, msz)) return fail(SDM_ERR_INVALID_ARG, "o overlaps M");
     if (d->B * d->H > 0x7fffffff) return fail(SDM_ERR_UNSUPPORTED, "B*H too large");
     if (d->B == 0) return SDM_OK;
+    if (touched) {
+        const sdm_status cs = check_cow(M, M0, touched, d);
+        if (cs != SDM_OK) return cs;
+        const size_t tsz = sdm_cow_bitmap_bytes(d);
+        const size_t osz = sizeof(float) * (size_t)(d->B * d->H * d->d_v);
+        if (overlap(touched, tsz, o, osz) || overlap(M0, sizeof(float) * (size_t)(d->H * N * d->d_v), o, osz))
+            return fail(SDM_ERR_INVALID_ARG, "o overlaps M0 or the bitmap");
+    }
     sdm::DecodeArgs A{};
     A.M = M; A.k = k; A.q = q; A.C_w = C_w; A.C_r = C_r; A.v = v; A.a = a; A.b = b; A.o = o;
     A.widx_out = widx_out; A.ridx_out = ridx_out;
+    A.M0 = M0; A.touched = touched;
     A.B = (int)d->B; A.H = (int)d->H; A.d_k = (int)d->d_k; A.n_sub = (int)d->n_sub;
     A.d_v = (int)d->d_v; A.k_prime = (int)d->k_prime; A.W = (int)d->W; A.R = (int)d->R; A.N = (int)N;
     sdm::make_staircase(A.k_prime, A.W, A.stair[0]);

@@ -28,7 +28,7 @@ constexpr int kDecWaves = 16;
 
 struct DecodeLds {
     // byte offsets into dynamic LDS
-    size_t S, L, scratch, stair, lidx, lwt, mpos, total;
+    size_t S, L, scratch, stair, lidx, lwt, mpos, lbit, total;
 };
 
 __host__ __device__ inline DecodeLds decode_lds_layout(int n_sub, int kp, int ts)
@@ -41,7 +41,8 @@ __host__ __device__ inline DecodeLds decode_lds_layout(int n_sub, int kp, int ts
     o.lidx = o.stair + sizeof(uint16_t) * 2 * kMaxStair;              // int32 [2][ts][64]
     o.lwt = o.lidx + sizeof(int32_t) * 2 * (size_t)ts * kWave;        // float [2][ts][64]
     o.mpos = o.lwt + sizeof(float) * 2 * (size_t)ts * kWave;          // int32 [ts][64]
-    o.total = o.mpos + sizeof(int32_t) * (size_t)ts * kWave;
+    o.lbit = o.mpos + sizeof(int32_t) * (size_t)ts * kWave;           // int32 [2][ts][64] (copy-on-write)
+    o.total = o.lbit + sizeof(int32_t) * 2 * (size_t)ts * kWave;
     return o;
 }
 
@@ -135,7 +136,12 @@ __device__ __forceinline__ void score_batched(const uint16_t *const (&x)[NKIND],
     }
 }
 
-template <int Q, bool BF16>
+// COW: the state is copy-on-write over M0 (A.touched): the merge waves look
+// up the bit of each selected slot (in LDS for phase D), each gathered row
+// is then loaded from M where the sequence has written it and from M0
+// elsewhere, and the rows the step writes are marked once every bit has been
+// read (after the barrier before phase D).
+template <int Q, bool BF16, bool COW>
 __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A, int TS)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -155,6 +161,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
     int32_t *lidx = reinterpret_cast<int32_t *>(smem + lay.lidx);       // [kind][row][64]
     float *lwt = reinterpret_cast<float *>(smem + lay.lwt);             // [kind][row][64]
     int32_t *mpos = reinterpret_cast<int32_t *>(smem + lay.mpos);       // [row][64]
+    int32_t *lbit = reinterpret_cast<int32_t *>(smem + lay.lbit);       // [kind][row][64]
+    const size_t wpb = ((size_t)A.N + 31) / 32;   // bitmap words per (b, h)
 
     // A. scores: list l = kind * 2 + c; row r of the tile = sequence b0 + r
     // (rows past the live ones are scored as zero vectors)
@@ -218,6 +226,14 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
         merge_softmax<1>(L0, L1, kp, n_sub, n, stair + kind * kMaxStair, A.stair[kind].count, wscr, slot, wt);
         lidx[(kind * TS + r) * kWave + lane] = lane < n ? slot[0] : -1;
         lwt[(kind * TS + r) * kWave + lane] = lane < n ? wt[0] : 0.f;
+        if constexpr (COW) {
+            // whether the sequence has written the slot before this step (a
+            // valid word for idle lanes and rows past the live ones)
+            const int rr = r < nb ? r : 0;
+            const uint32_t s = (uint32_t)(lane < n ? slot[0] : 0);
+            const uint32_t word = A.touched[((size_t)(b0 + rr) * A.H + h) * wpb + (s >> 5)];
+            lbit[(kind * TS + r) * kWave + lane] = (int32_t)((word >> (s & 31)) & 1u);
+        }
         int32_t *out = kind ? A.ridx_out : A.widx_out;
         if (out && r < nb && lane < n) out[((size_t)(b0 + r) * A.H + h) * n + lane] = slot[0];
     }
@@ -249,6 +265,15 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
     // PB passes of a wave at a time, all their loads issued first; one row
     // (sequence) per pass, so the buffer resources are uniform
     constexpr int PB = 4;
+    if constexpr (COW) {
+        // every bit this step reads was taken before the last barrier: mark
+        // the rows the step writes
+        for (int r = wave; r < nb; r += kDecWaves) {
+            const int s = lidx[r * kWave + lane];
+            if (lane < A.W && s >= 0 && s < A.N)
+                atomicOr(A.touched + ((size_t)(b0 + r) * A.H + h) * wpb + ((uint32_t)s >> 5), 1u << (s & 31));
+        }
+    }
     for (int p0 = wave; p0 < npass; p0 += kDecWaves * PB) {
         f32x4 xw[PB], xr[PB], v4[PB];
         int mm[PB];
@@ -266,8 +291,22 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
             mm[t] = mpos[r * kWave + j];
             const uint32_t offw = (live && j < A.W) ? (uint32_t)sw * d_v * 4u + col4 : kOOB;
             const uint32_t offr = (live && j < A.R && mm[t] < 0) ? (uint32_t)sr * d_v * 4u + col4 : kOOB;
-            xw[t] = __builtin_amdgcn_raw_buffer_load_b128(Mrs, offw, 0, 0);
-            xr[t] = __builtin_amdgcn_raw_buffer_load_b128(Mrs, offr, 0, 0);
+            if constexpr (COW) {
+                // each row from M if the sequence has written it, else from M0
+                // (the other load is out of range: no memory access, zeros)
+                const __amdgpu_buffer_rsrc_t M0rs =
+                    make_rsrc(A.M0 + (size_t)h * A.N * d_v, (uint32_t)((uint64_t)A.N * d_v * 4u));
+                const bool bwt = lbit[r * kWave + j] != 0, brd = lbit[(TS + r) * kWave + j] != 0;
+                const f32x4 wm = __builtin_amdgcn_raw_buffer_load_b128(Mrs, bwt ? offw : kOOB, 0, 0);
+                const f32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(M0rs, bwt ? kOOB : offw, 0, 0);
+                const f32x4 rm = __builtin_amdgcn_raw_buffer_load_b128(Mrs, brd ? offr : kOOB, 0, 0);
+                const f32x4 r0 = __builtin_amdgcn_raw_buffer_load_b128(M0rs, brd ? kOOB : offr, 0, 0);
+                xw[t] = bwt ? wm : w0;
+                xr[t] = brd ? rm : r0;
+            } else {
+                xw[t] = __builtin_amdgcn_raw_buffer_load_b128(Mrs, offw, 0, 0);
+                xr[t] = __builtin_amdgcn_raw_buffer_load_b128(Mrs, offr, 0, 0);
+            }
             const __amdgpu_buffer_rsrc_t Vrs =
                 make_rsrc(static_cast<const unsigned char *>(A.v) + bh * d_v * esz, d_v * (uint32_t)esz);
             if constexpr (BF16) {
@@ -293,6 +332,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
             const float wj = lwt[r * kWave + j], rj = lwt[(TS + r) * kWave + j];
             const uint32_t offw = (live && j < A.W) ? (uint32_t)sw * d_v * 4u + col4 : kOOB;
             const float at = A.a[bh], bt = A.b[bh];
+
             const f32x4 p = weighted_rows<Q>(wj, xw[t]);
             const f32x4 nm = written_row(xw[t], at, bt * wj, v4[t], p);
             __builtin_amdgcn_raw_buffer_store_b128(nm, Mrs, offw, 0, 0);
@@ -303,6 +343,65 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
             __builtin_amdgcn_raw_buffer_store_b128(o, Ors, (live && j == 0) ? col4 : kOOB, 0, 0);
         }
     }
+}
+
+// copy-on-write state: clear every sequence's bitmap (no row written yet)
+__global__ void __launch_bounds__(256) sdm_cow_reset_kernel(CowArgs A)
+{
+    const int64_t n = A.B * A.H * ((A.N + 31) / 32);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        A.touched[i] = 0u;
+}
+
+// copy-on-write state made plain: the rows not yet written take M0's values
+// (one 16-byte chunk per thread)
+__global__ void __launch_bounds__(256) sdm_cow_materialize_kernel(CowArgs A)
+{
+    const int64_t cpr = A.d_v / 4;                      // chunks per row
+    const int64_t n = A.B * A.H * A.N * cpr;
+    const int64_t wpb = (A.N + 31) / 32;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = i / cpr, c = i - row * cpr;     // row of [B*H][N]
+        const int64_t bh = row / A.N, slot = row - bh * A.N;
+        const uint32_t word = A.touched[bh * wpb + (slot >> 5)];
+        if (((word >> (slot & 31)) & 1u) == 0u) {
+            const int64_t h = bh % A.H;
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(A.M0 + (h * A.N + slot) * A.d_v + c * 4);
+            *reinterpret_cast<f32x4 *>(A.M + row * A.d_v + c * 4) = x;
+        }
+    }
+}
+
+// ... and then every row marked as written
+__global__ void __launch_bounds__(256) sdm_cow_mark_all_kernel(CowArgs A)
+{
+    const int64_t n = A.B * A.H * ((A.N + 31) / 32);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        A.touched[i] = ~0u;
+}
+
+static unsigned grid_for(int64_t n)
+{
+    const int64_t b = (n + 255) / 256;
+    return (unsigned)(b < 1 ? 1 : b > (1 << 20) ? (1 << 20) : b);
+}
+
+hipError_t launch_cow_reset(const CowArgs &A, hipStream_t stream)
+{
+    const int64_t n = A.B * A.H * ((A.N + 31) / 32);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(sdm_cow_reset_kernel, dim3(grid_for(n)), dim3(256), 0, stream, A);
+    return hipGetLastError();
+}
+
+hipError_t launch_cow_materialize(const CowArgs &A, hipStream_t stream)
+{
+    const int64_t n = A.B * A.H * A.N * (A.d_v / 4);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(sdm_cow_materialize_kernel, dim3(grid_for(n)), dim3(256), 0, stream, A);
+    hipLaunchKernelGGL(sdm_cow_mark_all_kernel, dim3(grid_for(A.B * A.H * ((A.N + 31) / 32))), dim3(256), 0, stream,
+                       A);
+    return hipGetLastError();
 }
 
 // Sequences per workgroup: the most (up to 4) whose LDS fits and that still
@@ -326,15 +425,21 @@ static hipError_t launch_decode_q(const DecodeArgs &A, bool bf16, hipStream_t st
     if (ts == 0) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)A.H * ((A.B + ts - 1) / ts);
     const size_t smem = decode_lds_layout(A.n_sub, A.k_prime, ts).total;
-    const void *fn = bf16 ? (const void *)sdm_decode_kernel<Q, true> : (const void *)sdm_decode_kernel<Q, false>;
+    const bool cow = A.touched != nullptr;
+    const void *fn = bf16 ? (cow ? (const void *)sdm_decode_kernel<Q, true, true> : (const void *)sdm_decode_kernel<Q, true, false>)
+                          : (cow ? (const void *)sdm_decode_kernel<Q, false, true> : (const void *)sdm_decode_kernel<Q, false, false>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    if (bf16)
-        hipLaunchKernelGGL((sdm_decode_kernel<Q, true>), dim3((unsigned)blocks), dim3(64 * kDecWaves), smem, stream,
-                           A, ts);
-    else
-        hipLaunchKernelGGL((sdm_decode_kernel<Q, false>), dim3((unsigned)blocks), dim3(64 * kDecWaves), smem,
-                           stream, A, ts);
+#define SDM_DEC_LAUNCH(BF, CW) \
+    hipLaunchKernelGGL((sdm_decode_kernel<Q, BF, CW>), dim3((unsigned)blocks), dim3(64 * kDecWaves), smem, stream, A, ts)
+    if (bf16) {
+        if (cow) SDM_DEC_LAUNCH(true, true);
+        else SDM_DEC_LAUNCH(true, false);
+    } else {
+        if (cow) SDM_DEC_LAUNCH(false, true);
+        else SDM_DEC_LAUNCH(false, false);
+    }
+#undef SDM_DEC_LAUNCH
     return hipGetLastError();
 }
 

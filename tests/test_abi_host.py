@@ -303,3 +303,26 @@ def test_norm_gate_backward_rejects_bad_arguments():
     big = good_dims(B=4, T=4096, H=16, d_v=128)
     assert sdm.sdm_output_norm_gate_backward_workspace_size(big) == 4 * 1024 * 128
     assert sdm.sdm_output_norm_gate_backward_workspace_size(good_dims(d_v=48)) == 0
+
+
+def test_cow_calls_reject_bad_arguments():
+    d = good_dims(T=1)
+    nb = sdm.sdm_cow_bitmap_bytes(d)
+    assert nb == 4 * d.B * d.H * ((d.n_sub * d.n_sub + 31) // 32)
+    assert sdm.sdm_cow_bitmap_bytes(good_dims(H=0)) == 0
+    assert sdm.sdm_cow_reset(None, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
+    assert sdm.sdm_cow_reset(FAKE + 2, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
+    assert sdm.sdm_cow_reset(None, good_dims(B=0, T=1), stream=0, check=False) == sdm.SDM_OK
+    M, M0, tb = FAKE, FAKE + (1 << 36), FAKE + (2 << 36)
+    assert sdm.sdm_cow_materialize(M, None, tb, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
+    assert sdm.sdm_cow_materialize(M, M + 64, tb, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG   # M0 in M
+    assert sdm.sdm_cow_materialize(M, M0, M0 + 16, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG  # bitmap in M0
+    assert sdm.sdm_cow_materialize(M, M0 + 8, tb, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG   # misaligned
+    ins = [FAKE + ((3 + i) << 36) for i in range(8)]   # k, q, C_w, C_r, v, a, b, o
+    step = lambda M_, M0_, tb_, dims=d: sdm.sdm_decode_step_cow(M_, M0_, tb_, *ins, None, None, dims, stream=0,
+                                                                check=False)
+    assert step(M, None, tb) == sdm.SDM_ERR_INVALID_ARG
+    assert step(M, M0, None) == sdm.SDM_ERR_INVALID_ARG
+    assert step(M, M0, ins[7]) == sdm.SDM_ERR_INVALID_ARG                       # bitmap over o
+    assert step(M, M0, tb, dims=good_dims(T=2)) == sdm.SDM_ERR_INVALID_ARG     # T must be 1
+    assert step(None, None, None, dims=good_dims(B=0, T=1)) == sdm.SDM_OK
