@@ -168,3 +168,50 @@ def test_graph_capture_training_step_and_layer_edges(sdm, torch):
         T.cuda.synchronize()
         for i, (t, r) in enumerate(zip(outs, ref)):
             np.testing.assert_array_equal(to_host(t), r, err_msg=f"replay {rep}: output {i}")
+
+
+def test_graph_capture_copy_on_write_decode(sdm, torch):
+    """A batch of copy-on-write decode steps under capture: bitmap reset,
+    four steps, materialize; three replays (with the state and bitmap
+    overwritten in between), each bit-identical to the eager run."""
+    d = Dims(B=3, T=4, H=2, d_k=128, n_sub=32, d_v=64, k_prime=8, W=8, R=6)
+    note(f"graph capture, copy-on-write decode {d}")
+    x = synth.make_inputs_torch(d, seed=22)
+    dims1 = sdm.dims_from(d.replace(T=1))
+    T = torch
+    M = T.empty((d.B, d.H, d.N, d.d_v), dtype=T.float32, device="cuda")
+    touched = T.empty(sdm.sdm_cow_bitmap_bytes(dims1) // 4, dtype=T.int32, device="cuda")
+    per = [{k: x[k][:, t].contiguous() for k in ("k", "q", "v", "a", "b")} for t in range(d.T)]
+    o1 = [T.empty((d.B, d.H, d.d_v), dtype=T.float32, device="cuda") for _ in range(d.T)]
+    wo = [T.empty((d.B, d.H, d.W), dtype=T.int32, device="cuda") for _ in range(d.T)]
+
+    def step():
+        sdm.sdm_cow_reset(touched, dims1)
+        for t in range(d.T):
+            p = per[t]
+            sdm.sdm_decode_step_cow(M, x["M0"], touched, p["k"], p["q"], x["C_w"], x["C_r"], p["v"], p["a"], p["b"],
+                                    o1[t], wo[t], None, dims1)
+        sdm.sdm_cow_materialize(M, x["M0"], touched, dims1)
+
+    outs = (M, touched, *o1, *wo)
+    M.fill_(float("nan"))
+    step()
+    T.cuda.synchronize()
+    ref = [to_host(t).copy() for t in outs]
+    g = T.cuda.CUDAGraph()
+    side = T.cuda.Stream()
+    side.wait_stream(T.cuda.current_stream())
+    with T.cuda.stream(side):
+        with T.cuda.graph(g):
+            step()
+    T.cuda.synchronize()
+    for rep in range(3):
+        M.fill_(float("nan"))
+        touched.fill_(-1)
+        for t in o1 + wo:
+            t.zero_()
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        for i, (t, r) in enumerate(zip(outs, ref)):
+            np.testing.assert_array_equal(to_host(t), r, err_msg=f"replay {rep}: output {i}")
