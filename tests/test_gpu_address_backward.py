@@ -38,8 +38,15 @@ def close_rms(got, ref, what, bar=2e-3):
     assert err <= bar * scale, f"{what}: max error {err:.3g} > {bar} x RMS {scale:.3g}"
 
 
-def run_case(sdm, torch, d, seed, shared):
-    x = synth.make_inputs(d, seed=seed, separate_read_codebook=not shared)
+def run_case(sdm, torch, d, seed, shared, hot=0):
+    """hot > 0: the first `hot` sub-keys of every half get 8x the norm, so
+    most tokens select them (a few very large buckets in the sort)."""
+    x = synth.make_inputs(d, seed=seed, separate_read_codebook=not shared, m0=False)
+    if hot:
+        for name in ("C_w", "C_r"):
+            C = synth.bf16_bits_to_f32(x[name]) if d.in_dtype == "bf16" else x[name].copy()
+            C[:, :, :hot] *= 8.0
+            x[name] = synth.f32_to_bf16_bits(C) if d.in_dtype == "bf16" else C
     dims = sdm.dims_from(d)
     k, q, Cw, Cr = (to_dev(x[n]) for n in ("k", "q", "C_w", "C_r"))
     if shared:
@@ -82,6 +89,22 @@ def test_address_backward_matches_oracle(sdm, torch, case):
     d, shared = CASES[case]
     note(f"address backward {case} {d}")
     run_case(sdm, torch, d, seed=len(case), shared=shared)
+
+
+@pytest.mark.parametrize("shared", [True, False], ids=["shared", "separate"])
+def test_address_backward_hot_subkeys(sdm, torch, shared):
+    d = Dims(B=2, T=600, H=2, d_k=128, n_sub=64, d_v=32, k_prime=16, W=16, R=16)
+    note(f"address backward hot sub-keys {d}")
+    run_case(sdm, torch, d, seed=9, shared=shared, hot=3)
+
+
+def test_address_backward_full_size_1p4b(sdm, torch):
+    """The 1.4B training shape at full size (B=8, T=8192, H=16, n_sub=512,
+    W=R=32, one codebook for both kinds, as the training bench runs it):
+    every element of dk, dq and the codebook gradient."""
+    d = synth.PRESETS["prefill_1p4b"].dims
+    note(f"address backward full size {d}")
+    run_case(sdm, torch, d, seed=43, shared=True)
 
 
 def test_address_backward_full_size_small_layer(sdm, torch):

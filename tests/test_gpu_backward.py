@@ -110,3 +110,35 @@ def test_scan_backward_full_size_small_layer(sdm, torch):
     x = synth.make_inputs(d, seed=29)
     ad = synth.random_addressing(d, seed=29)
     run_case(sdm, torch, d, x, ad, seed=5)
+
+
+def test_scan_backward_full_size_1p4b_sampled(sdm, torch):
+    """The 1.4B training shape at full size (B=8, T=8192, H=16, N=262,144,
+    d_v=128, W=R=32) in the training bench's launch configuration: slot
+    lists from the GPU addressing, the forward with saving, the backward for
+    a random dL/do with dL/dM_T = 0.  Two sampled chains (sequence, head),
+    every gradient of each, against the oracle run on that chain alone
+    (chains do not interact)."""
+    T = torch
+    d = synth.PRESETS["prefill_1p4b"].dims
+    note(f"scan backward full size 1.4B, sampled chains {d}")
+    x = synth.make_inputs_torch(d, seed=31)
+    dims = sdm.dims_from(d)
+    widx, wwt, ridx, rwt = sdm.pkm_address(x["k"], x["q"], x["C_w"], x["C_r"], dims)
+    M = sdm.state_init(x["M0"], dims)
+    o, xs, zs = sdm.scan_forward_save(M, widx, wwt, ridx, rwt, x["v"], x["a"], x["b"], dims)
+    del M, o
+    dout = T.randn((d.B, d.T, d.H, d.d_v), generator=T.Generator(device="cuda").manual_seed(7), device="cuda")
+    dM = T.zeros((d.B, d.H, d.N, d.d_v), dtype=T.float32, device="cuda")
+    dv, da, db, dw, dr = sdm.scan_backward(dM, widx, wwt, ridx, rwt, x["v"], x["a"], x["b"], dout, xs, zs, dims)
+    T.cuda.synchronize()
+    del xs, zs
+    d1 = d.replace(B=1, H=1)
+    for b, h in ((0, 0), (d.B - 1, d.H - 1)):
+        note(f"chain b={b} h={h}")
+        sl = lambda t: to_host(t[b:b + 1, :, h:h + 1].contiguous())
+        g = oracle.scan_backward(to_host(x["M0"][h:h + 1]).reshape(1, 1, d.N, d.d_v), sl(widx), sl(wwt), sl(ridx),
+                                 sl(rwt), sl(x["v"]), sl(x["a"]), sl(x["b"]), sl(dout), d1)
+        close_rms(to_host(dM[b:b + 1, h:h + 1]), g["dM"], f"dM[{b},{h}]")
+        for name, got in (("dv", dv), ("da", da), ("db", db), ("dw", dw), ("dr", dr)):
+            close_rms(sl(got), g[name], f"{name}[{b},{h}]")
