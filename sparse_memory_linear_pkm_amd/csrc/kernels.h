@@ -168,10 +168,12 @@ struct AddrBwdArgs {
 // the addressing backward's workspace (see address_bwd_layout)
 struct AddrBwdLayout {
     int64_t nch[2];               // chunks of list entries per (kind, head, half)
-    size_t off_cnt, off_start, off_sorted, bytes;   // byte offsets, total size
+    int64_t maxp;                 // pieces of the sums pass per (kind, head, half), at most
+    int half;
+    size_t off_cnt, off_start, off_sorted, off_pstart, off_pmap, off_part, bytes;   // byte offsets, total size
     size_t cnt1, sorted1;         // elements of kind 0's counts and sorted entries
 };
-AddrBwdLayout address_bwd_layout(int64_t BT, int64_t H, int W, int R, int n_sub);
+AddrBwdLayout address_bwd_layout(int64_t BT, int64_t H, int W, int R, int n_sub, int half);
 size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int n_sub, int half);
 hipError_t launch_address_backward(const AddrBwdArgs &args, bool bf16, void *workspace, hipStream_t stream);
 hipError_t launch_scan_backward(const BwdArgs &args, bool bf16, hipStream_t stream);

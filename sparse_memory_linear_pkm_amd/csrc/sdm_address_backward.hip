@@ -18,9 +18,12 @@
 //      scatter that keeps token-then-list order within a sub-key), as
 //      (row, dsc) pairs, entries of one token that select the same sub-key
 //      combined into one;
-//   3. one wave per (head, half, sub-key) [and kind, unless one buffer takes
-//      both kinds' sums] walks its sorted entries and adds dsc * x for each
-//      into registers (each lane owns columns): every entry is read once.
+//   3. each sub-key's sorted entries are cut into pieces of at most
+//      kAbPiece (so that a sub-key most tokens select does not serialise
+//      one wave); one wave per piece adds dsc * x for its entries in order
+//      into registers (each lane owns columns), every entry read once; then
+//      one wave per (head, half, sub-key) [and kind, unless one buffer takes
+//      both kinds' sums] adds its pieces in order.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,6 +33,7 @@ namespace {
 
 constexpr int64_t kAbChunk = 4096;         // list entries per chunk of the counting sort
 constexpr int64_t kAbDxRows = 8;           // token-head rows per wave of the dx pass
+constexpr int kAbPiece = 2048;             // sorted entries per wave of the sums pass at most
 
 template <bool BF16>
 __device__ __forceinline__ float ld_in(const void *p, int64_t e)
@@ -71,11 +75,15 @@ __device__ __forceinline__ float sum_in_lane_order(float v, uint64_t g)
 //           per sub-key, then (in place) their offset within the sub-key
 //   start   [2][H][2][n_sub + 1] int32: where each sub-key's entries begin
 //   sorted  per kind k, [H][2][B*T*n_k] (row, dsc) pairs
+//   pstart  [2][H][2][n_sub + 1] int32: each sub-key's first piece
+//   pmap    [2][H][2][maxp] int32: the sub-key of each piece
+//   part    [2][H][2][maxp][d_k / 2] fp32: each piece's sums
 // where n_0 = W, n_1 = R and nch_k = ceil(B*T*n_k / kAbChunk).
-AddrBwdLayout address_bwd_layout(int64_t BT, int64_t H, int W, int R, int n_sub)
+AddrBwdLayout address_bwd_layout(int64_t BT, int64_t H, int W, int R, int n_sub, int half)
 {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     AddrBwdLayout L;
+    L.half = half;
     L.nch[0] = (BT * W + kAbChunk - 1) / kAbChunk;
     L.nch[1] = (BT * R + kAbChunk - 1) / kAbChunk;
     const int64_t rows = BT * H;
@@ -84,13 +92,20 @@ AddrBwdLayout address_bwd_layout(int64_t BT, int64_t H, int W, int R, int n_sub)
     L.off_start = L.off_cnt + up(sizeof(int32_t) * (L.cnt1 + (size_t)(H * 2 * L.nch[1] * n_sub)));
     L.off_sorted = L.off_start + up(sizeof(int32_t) * (size_t)(2 * H * 2 * (n_sub + 1)));
     L.sorted1 = (size_t)(H * 2 * BT * W);
-    L.bytes = L.off_sorted + up(sizeof(int2) * (L.sorted1 + (size_t)(H * 2 * BT * R)));
+    const int64_t segs = 2 * H * 2;
+    // pieces of at most kAbPiece entries per (kind, head, half): at most
+    // entries / kAbPiece + n_sub (one partial piece per sub-key)
+    L.maxp = (BT * (W > R ? W : R) + kAbPiece - 1) / kAbPiece + n_sub;
+    L.off_pstart = L.off_sorted + up(sizeof(int2) * (L.sorted1 + (size_t)(H * 2 * BT * R)));
+    L.off_pmap = L.off_pstart + up(sizeof(int32_t) * (size_t)(segs * (n_sub + 1)));
+    L.off_part = L.off_pmap + up(sizeof(int32_t) * (size_t)(segs * L.maxp));
+    L.bytes = L.off_part + up(sizeof(float) * (size_t)(segs * L.maxp) * (size_t)half);
     return L;
 }
 
-size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int n_sub, int)
+size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int n_sub, int half)
 {
-    return address_bwd_layout(B * T, H, W, R, n_sub).bytes;
+    return address_bwd_layout(B * T, H, W, R, n_sub, half).bytes;
 }
 
 // 1. softmax backward and dx: one wave per kAbDxRows consecutive rows of one
@@ -195,8 +210,11 @@ struct AbWs {
     float *dsc;
     int32_t *cnt, *start;
     int2 *sorted;
+    int32_t *pstart, *pmap;   // [seg][n_sub + 1] first piece of each sub-key; [seg][maxp] sub-key of each piece
+    float *part;              // [seg][maxp][half] each piece's sums
     int64_t nch[2];
     size_t cnt1, sorted1;
+    int64_t maxp;
 };
 
 // which (kind, head, chunk) a workgroup of the count and scatter passes takes
@@ -317,12 +335,35 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_key_prefix_kernel(AddrBwd
         __syncthreads();
     }
     int32_t run = part[threadIdx.x] - sum;
+    const int32_t total = part[255];
+    // the sub-keys' pieces of at most kAbPiece entries (empty sub-keys have none)
+    int32_t np = 0;
+    for (int u = b0; u < b1; ++u) np += (st[u] + kAbPiece - 1) / kAbPiece;
+    __syncthreads();   // every thread has read its scan results before part is reused
+    part[threadIdx.x] = np;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int32_t add = (int)threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+        __syncthreads();
+        part[threadIdx.x] += add;
+        __syncthreads();
+    }
+    int32_t prun = part[threadIdx.x] - np;
+    int32_t *ps = S.pstart + (int64_t)blockIdx.x * (ns + 1);
+    int32_t *pm = S.pmap + (int64_t)blockIdx.x * S.maxp;
     for (int u = b0; u < b1; ++u) {
         const int32_t v = st[u];
+        const int32_t pu = (v + kAbPiece - 1) / kAbPiece;
         st[u] = run;
+        ps[u] = prun;
+        for (int i = 0; i < pu; ++i) pm[prun + i] = u;
         run += v;
+        prun += pu;
     }
-    if (threadIdx.x == 255) st[ns] = part[255];
+    if (threadIdx.x == 255) {
+        st[ns] = total;
+        ps[ns] = part[255];
+    }
 }
 
 // 2d. stable scatter: one wave per (kind, head, chunk) walks its entries 64
@@ -399,12 +440,68 @@ __global__ void __launch_bounds__(64) sdm_address_bwd_scatter_kernel(AddrBwdArgs
     }
 }
 
-// 3. one wave per (head, half, sub-key) and kind (or both kinds in order
-// when one buffer takes both sums): the sorted entries 64 at a time, their
-// input rows loaded eight at a time, dsc * x added in order; HM =
-// ceil(half / 64) columns per lane
+// 3a. one wave per piece (at most kAbPiece consecutive sorted entries of one
+// sub-key of one (kind, head, half)): dsc * x summed in order into registers
+// (each lane owns columns), the entries 64 at a time with their input rows
+// loaded eight at a time; HM = ceil(half / 64) columns per lane
 template <bool BF16, int HM>
 __global__ void __launch_bounds__(256) sdm_address_bwd_accum_kernel(AddrBwdArgs A, AbWs S)
+{
+    const int half = A.d_k / 2, ns = A.n_sub;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int64_t seg = unit / S.maxp, lp = unit - seg * S.maxp;
+    if (seg >= 2 * A.H * 2) return;                     // whole waves
+    const int32_t *ps = S.pstart + seg * (ns + 1);
+    if (lp >= ps[ns]) return;
+    const int u = S.pmap[seg * S.maxp + lp];
+    const int kind = (int)(seg / (2 * A.H)), hc = (int)(seg - (int64_t)kind * 2 * A.H), c = hc % 2;
+    const int lane = lane_id();
+    const int64_t BT = A.rows / A.H;
+    const int n = kind ? A.R : A.W;
+    const int32_t *st = S.start + seg * (ns + 1);
+    const int2 *ent = S.sorted + (kind ? S.sorted1 : 0) + (int64_t)hc * BT * n;
+    const void *X = kind ? A.q : A.k;
+    const int32_t s0 = st[u] + (int32_t)(lp - ps[u]) * kAbPiece;
+    const int32_t s1 = min(s0 + kAbPiece, st[u + 1]);
+    float acc[HM];
+#pragma unroll
+    for (int m = 0; m < HM; ++m) acc[m] = 0.f;
+    for (int32_t e0 = s0; e0 < s1; e0 += kWave) {
+        const int cnt = min(kWave, s1 - e0);
+        const int2 me = ent[lane < cnt ? e0 + lane : e0];
+        for (int q0 = 0; q0 < cnt; q0 += 8) {
+            float xv[8][HM], dq[8];
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) {
+                const int q = min(q0 + qq, kWave - 1);
+                const int32_t r = __builtin_amdgcn_readlane(me.x, q);
+                const float d = __int_as_float(__builtin_amdgcn_readlane(me.y, q));
+                dq[qq] = q0 + qq < cnt ? d : 0.f;
+#pragma unroll
+                for (int m = 0; m < HM; ++m) {
+                    const int e = lane + kWave * m;
+                    const float xl = ld_in<BF16>(X, (int64_t)r * A.d_k + c * half + (e < half ? e : 0));
+                    xv[qq][m] = e < half ? xl : 0.f;
+                }
+            }
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq)
+#pragma unroll
+                for (int m = 0; m < HM; ++m) acc[m] = __builtin_fmaf(dq[qq], xv[qq][m], acc[m]);
+        }
+    }
+    float *out = S.part + (seg * S.maxp + lp) * half;
+#pragma unroll
+    for (int m = 0; m < HM; ++m) {
+        const int e = lane + kWave * m;
+        if (e < half) out[e] = acc[m];
+    }
+}
+
+// 3b. one wave per (head, half, sub-key) and kind (or both kinds in order
+// when one buffer takes both sums): the sub-key's pieces added in order
+template <int HM>
+__global__ void __launch_bounds__(256) sdm_address_bwd_pieces_kernel(AddrBwdArgs A, AbWs S)
 {
     const int half = A.d_k / 2, ns = A.n_sub;
     const bool shared = A.dC_w == A.dC_r;
@@ -413,40 +510,22 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_accum_kernel(AddrBwdArgs 
     if (unit >= (shared ? 1 : 2) * per_kind) return;   // whole waves
     const int kind0 = (int)(unit / per_kind);
     const int64_t hcu = unit - kind0 * per_kind;        // (h * 2 + c) * ns + u
-    const int hc = (int)(hcu / ns), u = (int)(hcu - (int64_t)hc * ns), c = hc % 2;
+    const int hc = (int)(hcu / ns), u = (int)(hcu - (int64_t)hc * ns);
     const int lane = lane_id();
-    const int64_t BT = A.rows / A.H;
     float acc[HM];
 #pragma unroll
     for (int m = 0; m < HM; ++m) acc[m] = 0.f;
     for (int kind = kind0; kind <= (shared ? 1 : kind0); ++kind) {
-        const int n = kind ? A.R : A.W;
-        const int32_t *st = S.start + (int64_t)(kind * A.H * 2 + hc) * (ns + 1);
-        const int2 *ent = S.sorted + (kind ? S.sorted1 : 0) + (int64_t)hc * BT * n;
-        const void *X = kind ? A.q : A.k;
-        const int32_t s0 = st[u], s1 = st[u + 1];
-        for (int32_t e0 = s0; e0 < s1; e0 += kWave) {
-            const int cnt = min(kWave, s1 - e0);
-            const int2 me = ent[lane < cnt ? e0 + lane : e0];
-            for (int q0 = 0; q0 < cnt; q0 += 8) {
-                float xv[8][HM], dq[8];
+        const int64_t seg = (int64_t)kind * 2 * A.H + hc;
+        const int32_t *ps = S.pstart + seg * (ns + 1);
+        const int32_t p0 = ps[u], p1 = ps[u + 1];
+        for (int32_t p = p0; p < p1; ++p) {
+            const float *pr = S.part + (seg * S.maxp + p) * half;
 #pragma unroll
-                for (int qq = 0; qq < 8; ++qq) {
-                    const int q = min(q0 + qq, kWave - 1);
-                    const int32_t r = __builtin_amdgcn_readlane(me.x, q);
-                    const float d = __int_as_float(__builtin_amdgcn_readlane(me.y, q));
-                    dq[qq] = q0 + qq < cnt ? d : 0.f;
-#pragma unroll
-                    for (int m = 0; m < HM; ++m) {
-                        const int e = lane + kWave * m;
-                        const float xl = ld_in<BF16>(X, (int64_t)r * A.d_k + c * half + (e < half ? e : 0));
-                        xv[qq][m] = e < half ? xl : 0.f;
-                    }
-                }
-#pragma unroll
-                for (int qq = 0; qq < 8; ++qq)
-#pragma unroll
-                    for (int m = 0; m < HM; ++m) acc[m] = __builtin_fmaf(dq[qq], xv[qq][m], acc[m]);
+            for (int m = 0; m < HM; ++m) {
+                const int e = lane + kWave * m;
+                const float v = pr[e < half ? e : 0];
+                acc[m] += e < half ? v : 0.f;
             }
         }
     }
@@ -463,13 +542,17 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
     if (A.rows == 0) return hipSuccess;
     const int half = A.d_k / 2, ns = A.n_sub;
     const int64_t BT = A.rows / A.H;
-    const AddrBwdLayout L = address_bwd_layout(BT, A.H, A.W, A.R, ns);
+    const AddrBwdLayout L = address_bwd_layout(BT, A.H, A.W, A.R, ns, half);
     unsigned char *base = static_cast<unsigned char *>(ws);
     AbWs S;
     S.dsc = reinterpret_cast<float *>(base);
     S.cnt = reinterpret_cast<int32_t *>(base + L.off_cnt);
     S.start = reinterpret_cast<int32_t *>(base + L.off_start);
     S.sorted = reinterpret_cast<int2 *>(base + L.off_sorted);
+    S.pstart = reinterpret_cast<int32_t *>(base + L.off_pstart);
+    S.pmap = reinterpret_cast<int32_t *>(base + L.off_pmap);
+    S.part = reinterpret_cast<float *>(base + L.off_part);
+    S.maxp = L.maxp;
     S.nch[0] = L.nch[0];
     S.nch[1] = L.nch[1];
     S.cnt1 = L.cnt1;
@@ -480,7 +563,8 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
     const int64_t chunks = (int64_t)A.H * (L.nch[0] + L.nch[1]);
     const int segs = 2 * A.H * 2;
     const bool shared = A.dC_w == A.dC_r;
-    const int64_t b4 = ((shared ? 1 : 2) * (int64_t)A.H * 2 * ns + 3) / 4;
+    const int64_t b4 = (segs * L.maxp + 3) / 4;
+    const int64_t b5 = ((shared ? 1 : 2) * (int64_t)A.H * 2 * ns + 3) / 4;
     const size_t hist_bytes = sizeof(int32_t) * 2 * (size_t)ns;
     const int nm = (A.d_k + kWave - 1) / kWave, hm = (half + kWave - 1) / kWave;
     // list entries whose codebook loads are issued together: 8, or 16 for
@@ -524,6 +608,12 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
         else if (hm <= 2) SDM_AB_ACC(false, 2);
         else SDM_AB_ACC(false, 4);
     }
+    if (hm <= 1)
+        hipLaunchKernelGGL(sdm_address_bwd_pieces_kernel<1>, dim3((unsigned)b5), dim3(256), 0, stream, A, S);
+    else if (hm <= 2)
+        hipLaunchKernelGGL(sdm_address_bwd_pieces_kernel<2>, dim3((unsigned)b5), dim3(256), 0, stream, A, S);
+    else
+        hipLaunchKernelGGL(sdm_address_bwd_pieces_kernel<4>, dim3((unsigned)b5), dim3(256), 0, stream, A, S);
 #undef SDM_AB_DX
 #undef SDM_AB_ACC
     return hipGetLastError();
