@@ -181,3 +181,34 @@ def test_cow_decode_layer_shape(sdm, torch):
         for h in range(d.H):
             rows = T.unique(w[b, :, h])
             assert T.equal(Mc[b, h, rows], Mp[b, h, rows])
+
+
+@pytest.mark.parametrize("B", [64, 127], ids=["TS2", "TS4_ragged"])
+def test_decode_tiled_sequences(sdm, torch, B):
+    """Enough sequences that a decode workgroup takes 2 (B = 64) or 4
+    (B = 127, the last tile partly filled) of them, H = 8: the plain decode
+    reproduces the prefill of the same tokens bit for bit, and the
+    copy-on-write decode the plain one."""
+    T = torch
+    d = Dims(B=B, T=3, H=8, d_k=128, n_sub=16, d_v=32, k_prime=8, W=8, R=8)
+    note(f"decode with tiled sequences {d}")
+    x = synth.make_inputs(d, seed=45)
+    dx = {k: to_dev(v) for k, v in x.items()}
+    plain, Mp, _ = run_steps(sdm, T, d, dx, False, range(d.T))
+    cow, Mc, tb = run_steps(sdm, T, d, dx, True, range(d.T))
+    dims = sdm.dims_from(d)
+    widx, wwt, ridx, rwt = sdm.pkm_address(dx["k"], dx["q"], dx["C_w"], dx["C_r"], dims)
+    M2 = sdm.state_init(dx["M0"], dims)
+    o2 = sdm.scan_forward(M2, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], dims)
+    T.cuda.synchronize()
+    hp, hc = host_outs(plain), host_outs(cow)
+    np.testing.assert_array_equal(np.stack([s[0] for s in hp], 1), to_host(o2))
+    np.testing.assert_array_equal(np.stack([s[1] for s in hp], 1), to_host(widx))
+    np.testing.assert_array_equal(np.stack([s[2] for s in hp], 1), to_host(ridx))
+    np.testing.assert_array_equal(to_host(Mp), to_host(M2))
+    for t in range(d.T):
+        for i in range(3):
+            np.testing.assert_array_equal(hc[t][i], hp[t][i], err_msg=f"step {t} output {i}")
+    sdm.sdm_cow_materialize(Mc, dx["M0"], tb, sdm.dims_from(d.replace(T=1)))
+    T.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(Mc), to_host(Mp))
