@@ -212,3 +212,31 @@ def test_decode_tiled_sequences(sdm, torch, B):
     sdm.sdm_cow_materialize(Mc, dx["M0"], tb, sdm.dims_from(d.replace(T=1)))
     T.cuda.synchronize()
     np.testing.assert_array_equal(to_host(Mc), to_host(Mp))
+
+
+@pytest.mark.parametrize("d_k,shared", [(64, False), (128, False), (256, True), (256, False)],
+                         ids=["dk64_separate", "dk128_separate", "dk256_shared", "dk256_separate"])
+def test_decode_scoring_routes(sdm, torch, d_k, shared):
+    """The decode step's other scoring routes (separate read codebook: one
+    kind at a time; d_k = 256: the generic tile): plain decode against the
+    prefill of the same tokens and copy-on-write against plain, bit for bit."""
+    T = torch
+    d = Dims(B=3, T=3, H=2, d_k=d_k, n_sub=16, d_v=64, k_prime=8, W=8, R=6)
+    note(f"decode scoring route d_k={d_k} shared={shared} {d}")
+    x = synth.make_inputs(d, seed=46, separate_read_codebook=not shared)
+    dx = {k: to_dev(v) for k, v in x.items()}
+    plain, Mp, _ = run_steps(sdm, T, d, dx, False, range(d.T))
+    cow, Mc, tb = run_steps(sdm, T, d, dx, True, range(d.T))
+    dims = sdm.dims_from(d)
+    widx, wwt, ridx, rwt = sdm.pkm_address(dx["k"], dx["q"], dx["C_w"], dx["C_r"], dims)
+    M2 = sdm.state_init(dx["M0"], dims)
+    o2 = sdm.scan_forward(M2, widx, wwt, ridx, rwt, dx["v"], dx["a"], dx["b"], dims)
+    T.cuda.synchronize()
+    hp, hc = host_outs(plain), host_outs(cow)
+    np.testing.assert_array_equal(np.stack([s[1] for s in hp], 1), to_host(widx))
+    np.testing.assert_array_equal(np.stack([s[2] for s in hp], 1), to_host(ridx))
+    np.testing.assert_array_equal(np.stack([s[0] for s in hp], 1), to_host(o2))
+    np.testing.assert_array_equal(to_host(Mp), to_host(M2))
+    for t in range(d.T):
+        for i in range(3):
+            np.testing.assert_array_equal(hc[t][i], hp[t][i], err_msg=f"step {t} output {i}")
