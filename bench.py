@@ -53,18 +53,24 @@ def parse():
     return p.parse_args()
 
 
-def scan_source_hash() -> str:
+# sources of the scan's backward (its counter summaries carry their hash)
+BACKWARD_SOURCES = ("sdm_scan_backward.hip", "scan_lanes.h", "device_common.h", "kernels.h")
+
+
+def scan_source_hash(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "sparse_memory_linear_pkm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per scan launch from the committed counter summary, if it was
-    taken on the current scan kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"sdm_scan_{workload}_hbm_traffic.txt")
+def measured_traffic(workload: str, backward: bool = False):
+    """HBM bytes per launch of the scan (or of the scan's backward) from the
+    committed counter summary, if it was taken on the current kernel
+    source; else None."""
+    stem = "sdm_scan_backward" if backward else "sdm_scan"
+    path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -72,7 +78,8 @@ def measured_traffic(workload: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("scan_source_sha256_16") != scan_source_hash():
+    key = "backward_source_sha256_16" if backward else "scan_source_sha256_16"
+    if kv.get(key) != scan_source_hash(BACKWARD_SOURCES if backward else KERNEL_SOURCES):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -429,7 +436,7 @@ def bench_train(args, sdm, synth, torch, name):
         "wall_s_timed_region": wall,
         "kernels_ms": kms,
         "roofline": {"kernel": "sdm_scan_backward_kernel", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(name, backward=True),
                      "algorithmic_bytes_per_launch": bwd_bytes, "avg_launch_ms": bwd_ms},
         "forward_save": {"GB/s": fwd_bytes / (fwd_ms * 1e-3) / 1e9, "algorithmic_bytes_per_launch": fwd_bytes},
         "norm_backward": {"GB/s": nbwd_bytes / (kms["sdm_output_norm_gate_backward"] * 1e-3) / 1e9,
