@@ -449,9 +449,9 @@ def bench_train(args, sdm, synth, torch, name):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every (sequence, head) chain is independent; see the sharding notes in DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (every (sequence, head) chain is "
+              "independent, so heads or sequences would shard with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
