@@ -218,8 +218,9 @@ __global__ void __launch_bounds__(1024) sdm_scan_backward_rows_kernel(BwdArgs A)
         k.ww = A.wwt[row * W + jwc];
         k.a = A.a[row];
         k.b = A.b[row];
-        k.z = ld4(Z + ((tt * nchunk + c) * R + jrc) * 4);
-        k.x = ld4(X + ((tt * nchunk + c) * W + jwc) * 4);
+        // the saved rows are read once: non-temporal loads
+        k.z = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Z + ((tt * nchunk + c) * R + jrc) * 4));
+        k.x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(X + ((tt * nchunk + c) * W + jwc) * 4));
         k.dov = ld4(A.dout + row * d_v + col);
         if constexpr (BF16) {
             const uint2 r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(A.v) + row * d_v + col);

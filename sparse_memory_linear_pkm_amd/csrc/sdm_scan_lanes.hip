@@ -378,8 +378,9 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
                     const uint32_t tck = ut * nchunk + chunk;
                     const uint32_t offx = (i < rem && j < A.W) ? (tck * (uint32_t)A.W + j) * 16u : kOOB;
                     const uint32_t offz = (i < rem && j < A.R) ? (tck * (uint32_t)A.R + j) * 16u : kOOB;
-                    __builtin_amdgcn_raw_buffer_store_b128(sw, Xrs, offx, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(sr, Zrs, offz, 0, 0);
+                    // read once, by the backward, much later: non-temporal (cache policy nt)
+                    __builtin_amdgcn_raw_buffer_store_b128(sw, Xrs, offx, 0, 2);
+                    __builtin_amdgcn_raw_buffer_store_b128(sr, Zrs, offz, 0, 2);
                 }
             }
             // ---- issue step + D (its gathers overwrite gath[s], read by
