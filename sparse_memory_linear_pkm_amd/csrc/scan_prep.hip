@@ -29,10 +29,13 @@
 //   gofs[chain][t][j]:          byte offsets of write row j and read row j in
 //                               the (b, h) memory plus 2^30 (0: no row), so a
 //                               zero read past the end maps to an offset at
-//                               or beyond 2^31, outside every memory; bit 31
-//                               of the write offset set: the write is
-//                               superseded (not stored).  The lane record
-//                               repeats the write offset without that bit.
+//                               or beyond 2^31, outside every memory (one
+//                               memory is at most 2 GiB, so offset + 2^30
+//                               stays below 2^32); bit 0 of the write offset
+//                               set: the write is superseded (not stored).
+//                               Row offsets are multiples of d_v * 4 >= 128,
+//                               so bit 0 is free.  The lane record repeats
+//                               the write offset without that bit.
 //   tok[chain][t][c], c < d_v/4: {a_t, v_t[4c .. 4c+3], b_t} as one 16-byte
 //                               record (bf16 v: 2 words) or two (fp32 v:
 //                               {a_t, b_t, 0, 0}, then the 4 values)
@@ -173,7 +176,7 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
                 const int64_t last = (t / A.K) * A.K + look;   // <= t + look
                 const int hi = (int)((last < tend - 1 ? last : tend - 1) - tlo);
                 gw = (uint32_t)ws[u] * rowb + kRowBias;
-                if (hi > ul && latest(ws[u], ul + 1, hi) >= 0) gw |= 0x80000000u;
+                if (hi > ul && latest(ws[u], ul + 1, hi) >= 0) gw |= 1u;
             }
             if (j < R) {
                 const int v = latest(rs[u], lo, ul);
@@ -182,7 +185,7 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
             }
             const int64_t s = (ch * A.T + t) * Q + j;
             A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(wv[u]), __float_as_uint(rv[u]),
-                                      gw & 0x7FFFFFFFu);
+                                      gw & ~1u);
             A.st.gofs[s] = make_uint2(gw, gr);
         }
     }

@@ -222,15 +222,15 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_lanes_kernel(ScanArgs A, Scan
     // this wave's share of the gathers of a step (rows RPW*w .. RPW*w+RPW-1 of
     // the write and of the read rows, whole segments) into gath[sl], from the
     // row offsets in go[sl]; a zero offset record lands at or beyond 2^31
-    // (bit 31 of a write-row offset marks a write superseded within the next
-    // D - 1 steps: its store offset lands past the range and is dropped)
+    // (bit 0 of a write-row offset marks a write superseded within the next
+    // D - 1 steps: its store goes to kOOB, past the range, and is dropped)
     auto gathers = [&](int sl) __attribute__((always_inline)) {
-        ofw[sl] = go[sl].x - kRowBias + segb + cg * 16u;
+        const uint32_t ofg = (go[sl].x & ~1u) - kRowBias + segb + cg * 16u;
+        ofw[sl] = (go[sl].x & 1u) ? kOOB : ofg;
         // formed here, so that the row offset register is free for the next
         // load into the same ring slot (a copy at the loop edge would wait
         // for that load)
         asm volatile("" : "+v"(ofw[sl]));
-        const uint32_t ofg = (go[sl].x & 0x7FFFFFFFu) - kRowBias + segb + cg * 16u;
         const uint32_t ofr = go[sl].y - kRowBias + segb + cg * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             Mrs, (__attribute__((address_space(3))) void *)&gath[sl][0][wave * RPW][0], 16, ofg, 0, 0, 0);
