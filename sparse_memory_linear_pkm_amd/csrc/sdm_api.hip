@@ -593,6 +593,18 @@ sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, c
         for (int k = 0; k < i; ++k)
             if (overlap(optr[i], outs[i], optr[k], outs[k])) return fail(SDM_ERR_INVALID_ARG, "gradient outputs overlap");
     }
+    // dM and the gradient outputs are written while the inputs are read
+    const size_t lw = 4 * (size_t)(rows * d->W), lr = 4 * (size_t)(rows * d->R);
+    const void *iptr[10] = {widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave};
+    const size_t isz[10] = {lw, lw, lr, lr, in_size(d) * (size_t)(rows * d->d_v), 4 * (size_t)rows,
+                            4 * (size_t)rows, vsz, 4 * (size_t)(rows * d->W * d->d_v),
+                            4 * (size_t)(rows * d->R * d->d_v)};
+    for (int j = 0; j < 10; ++j) {
+        if (overlap(dM, msz, iptr[j], isz[j])) return fail(SDM_ERR_INVALID_ARG, "dM overlaps an input");
+        for (int i = 0; i < 5; ++i)
+            if (overlap(optr[i], outs[i], iptr[j], isz[j]))
+                return fail(SDM_ERR_INVALID_ARG, "a gradient output overlaps an input");
+    }
     sdm::BwdArgs A{dM, widx, ridx, wwt, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr,
                    d->B, d->T, (int)d->H, (int)N, (int)d->d_v, (int)d->W, (int)d->R};
     hipError_t e = sdm::launch_scan_backward(A, d->in_dtype == SDM_BF16, as_stream(stream));
@@ -641,6 +653,16 @@ sdm_status sdm_address_backward(const void *k, const void *q, const void *C_w, c
         for (int j = 0; j < i; ++j)
             if (!(i == 3 && j == 2 && dC_w == dC_r) && overlap(outs[i], osz[i], outs[j], osz[j]))
                 return fail(SDM_ERR_INVALID_ARG, "outputs overlap (only dC_w and dC_r may be the same buffer)");
+    }
+    // the outputs and the workspace are written while the inputs are read
+    const size_t ib = ial * (size_t)(rows * d->d_k), icb = ial * (size_t)(d->H * 2 * d->n_sub * (d->d_k / 2));
+    const size_t lw = 4 * (size_t)(rows * d->W), lr = 4 * (size_t)(rows * d->R);
+    const void *ins[10] = {k, q, C_w, C_r, widx, wwt, ridx, rwt, dw, dr};
+    const size_t isz[10] = {ib, ib, icb, icb, lw, lw, lr, lr, lw, lr};
+    for (int j = 0; j < 10; ++j) {
+        if (overlap(workspace, need, ins[j], isz[j])) return fail(SDM_ERR_INVALID_ARG, "the workspace overlaps an input");
+        for (int i = 0; i < 4; ++i)
+            if (overlap(outs[i], osz[i], ins[j], isz[j])) return fail(SDM_ERR_INVALID_ARG, "an output overlaps an input");
     }
     sdm::AddrBwdArgs A{k, q, C_w, C_r, widx, ridx, wwt, rwt, dw, dr, dk, dq, dC_w, dC_r, rows, (int)d->H,
                        (int)d->d_k, (int)d->n_sub, (int)d->W, (int)d->R};

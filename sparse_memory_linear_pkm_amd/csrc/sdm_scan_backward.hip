@@ -242,10 +242,32 @@ __global__ void __launch_bounds__(1024) sdm_scan_backward_rows_kernel(BwdArgs A)
         else
             v4 = (f32x4){__uint_as_float(k.v[0]), __uint_as_float(k.v[1]), __uint_as_float(k.v[2]),
                          __uint_as_float(k.v[3])};
-        // the read row: its output's gradient, then into G
-        const uint32_t roff = goff(jr, k.ri);
-        const f32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(Grs, roff, 0, 0);
-        const float rw = jr ? k.rw : 0.f;
+        // the read row: its output's gradient, then into G.  A slot listed
+        // at several read positions of the token is updated once, by its
+        // first position, with the sum of those positions' weights in list
+        // order (two lanes storing to one address in one instruction would
+        // lose a term).  The lists of all chunks are the same, so lane s
+        // holds position s.
+        const uint32_t roff0 = goff(jr, k.ri);
+        const f32x4 gv = __builtin_amdgcn_raw_buffer_load_b128(Grs, roff0, 0, 0);
+        uint64_t later = 0;   // lanes whose slot is also at an earlier position
+#pragma unroll
+        for (int s = 0; s + 1 < Q; ++s) {
+            if (s + 1 >= R) break;   // uniform
+            const int32_t ss = __builtin_amdgcn_readlane(k.ri, s);
+            later |= __builtin_amdgcn_ballot_w64(jr && j > s && k.ri == ss);
+        }
+        float rw = jr ? k.rw : 0.f;
+        if (later != 0) {   // uniform, and rare: repeated read slots
+            float sum = 0.f;
+            for (int s = 0; s < R; ++s) {
+                const int32_t ss = __builtin_amdgcn_readlane(k.ri, s);
+                const float ws = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(k.rw), s));
+                if (k.ri == ss) sum += ws;
+            }
+            rw = jr ? sum : 0.f;
+        }
+        const uint32_t roff = ((later >> lane) & 1u) ? kOOB : roff0;
         __builtin_amdgcn_raw_buffer_store_b128(
             (f32x4){__builtin_fmaf(rw, dov.x, gv.x), __builtin_fmaf(rw, dov.y, gv.y), __builtin_fmaf(rw, dov.z, gv.z),
                     __builtin_fmaf(rw, dov.w, gv.w)},

@@ -227,6 +227,10 @@ def test_scan_backward_rejects_bad_arguments():
     assert call(good_dims(), xs=None) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(), dv=FAKE + (11 << 30) + 4) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(), da=FAKE + (11 << 30)) == sdm.SDM_ERR_INVALID_ARG   # da over dv
+    # outputs over inputs: dv over v, dw over the saved write rows, dM over dout
+    assert call(good_dims(), dv=FAKE + (5 << 30)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dw=FAKE + (9 << 30) + 64) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dM=FAKE + (8 << 30)) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(T=0), dM=None) == sdm.SDM_OK
 
 
@@ -252,6 +256,10 @@ def test_address_backward_rejects_bad_arguments():
     assert call(good_dims(), dk=None) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(), ws_bytes=16) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(), dq=FAKE + (10 << 30) + 256) == sdm.SDM_ERR_INVALID_ARG    # dq inside dk
+    # outputs or workspace over inputs: dk over k, the workspace over C_w, dC_w over dw
+    assert call(good_dims(), dk=FAKE) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws=FAKE + (2 << 30) + 16) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dCw=FAKE + (8 << 30)) == sdm.SDM_ERR_INVALID_ARG
     assert sdm.sdm_address_backward_workspace_size(good_dims()) > 0
     assert call(good_dims(T=0), k=None) == sdm.SDM_OK
 
