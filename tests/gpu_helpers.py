@@ -57,6 +57,44 @@ def compare_slot_lists(gpu_idx: np.ndarray, orc_idx: np.ndarray, x: np.ndarray, 
     return rows_differ, int(diff.sum())
 
 
+def list_weights(x: np.ndarray, C: np.ndarray, d, idx: np.ndarray, rows=None) -> np.ndarray:
+    """The oracle's weights for given slot lists: the softmax, in fp64, of the
+    oracle's fp32 slot scores of each list (what the oracle would return had
+    it selected these slots).  idx [..., n] holds the lists of the flat
+    token-head rows `rows` (default: every row of x, in order)."""
+    n = idx.shape[-1]
+    flat = np.ascontiguousarray(idx).reshape(-1, n)
+    if rows is None:
+        rows = np.arange(flat.shape[0])
+    rows = np.asarray(rows, np.int64)
+    if flat.shape[0] == 0:
+        return np.zeros(idx.shape, np.float32)
+    s = oracle.slot_scores(x, C, d, np.repeat(rows, n), flat.ravel()).reshape(-1, n).astype(np.float64)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).astype(np.float32).reshape(idx.shape)
+
+
+def replay_weights(gpu_idx: np.ndarray, orc_idx: np.ndarray, orc_wt: np.ndarray, x: np.ndarray, C: np.ndarray,
+                   d) -> np.ndarray:
+    """Weights of the GPU's own lists as the oracle defines them: the oracle's
+    weights where the lists agree, the oracle's softmax over the GPU list's
+    slot scores where a near-tie selected other slots."""
+    n = gpu_idx.shape[-1]
+    g = gpu_idx.reshape(-1, n)
+    w = np.array(orc_wt, np.float32).reshape(-1, n)
+    differ = np.nonzero((g != orc_idx.reshape(-1, n)).any(axis=1))[0]
+    if differ.size:
+        w[differ] = list_weights(x, C, d, g[differ], rows=differ)
+    return w.reshape(gpu_idx.shape)
+
+
+def check_weights(gpu_idx, gpu_wt, orc_idx, orc_wt, x, C, d, atol: float = 1e-6):
+    """GPU weights within atol of the oracle's weights for the GPU's lists, on
+    every row (near-tie rows included)."""
+    ref = replay_weights(gpu_idx, orc_idx, orc_wt, x, C, d)
+    np.testing.assert_allclose(gpu_wt, ref, rtol=0, atol=atol)
+
+
 def rms(x: np.ndarray) -> float:
     return float(np.sqrt(np.mean(np.asarray(x, np.float64) ** 2)))
 

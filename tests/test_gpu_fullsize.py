@@ -17,7 +17,7 @@ import pytest
 import oracle
 import sdm_synth as synth
 
-from gpu_helpers import assert_close_rms, compare_slot_lists, note, to_host
+from gpu_helpers import assert_close_rms, check_weights, compare_slot_lists, note, replay_weights, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -53,10 +53,9 @@ def _sample_address(sdm, torch, x, d, gpu_lists, tsel):
     rr, _ = compare_slot_lists(gr, orr, hx["q"], hx["C_r"], ds)
     rows = rw.size
     assert rw.sum() <= 0.01 * rows + 1 and rr.sum() <= 0.01 * rows + 1
-    same_w = ~rw.reshape(gww.shape[:-1])
-    same_r = ~rr.reshape(grw.shape[:-1])
-    np.testing.assert_allclose(gww[same_w], oww[same_w], rtol=0, atol=1e-6)
-    np.testing.assert_allclose(grw[same_r], orw[same_r], rtol=0, atol=1e-6)
+    # every row's weights, near-tie rows against the oracle's softmax over the GPU's own list
+    check_weights(gw, gww, ow, oww, hx["k"], hx["C_w"], ds)
+    check_weights(gr, grw, orr, orw, hx["q"], hx["C_r"], ds)
 
 
 def _replay_chain(x, d, lists, M_gpu, o_gpu, b, h, T):
@@ -129,7 +128,8 @@ def test_fullsize_long_context_prefix(sdm, torch):
 
 def test_fullsize_decode_layer(sdm, torch):
     """16 decode steps of all 32 x 8 chains of the decode layer (N = 2^20
-    slots per head, 137 GB of state); two chains are replayed by the oracle."""
+    slots per head, 137 GB of state); eight chains are replayed by the oracle
+    on the decode step's own slot lists."""
     p = synth.PRESETS["decode"]
     d = p.dims.replace(T=16)
     note(f"full-size decode {d}")
@@ -147,7 +147,9 @@ def test_fullsize_decode_layer(sdm, torch):
         wl.append(wo)
         rl.append(ro)
     torch.cuda.synchronize()
-    for b, h in ((0, 0), (d.B - 1, d.H - 1)):
+    rng = np.random.default_rng(6)
+    chains = [(0, 0), (d.B - 1, d.H - 1)] + [(int(rng.integers(d.B)), int(rng.integers(d.H))) for _ in range(6)]
+    for b, h in chains:
         dc = d.replace(B=1, H=1)
         sl = lambda k: np.ascontiguousarray(to_host(x[k][b:b + 1, :, h:h + 1]))
         hx = {k: sl(k) for k in ("k", "q", "v", "a", "b")}
@@ -158,12 +160,18 @@ def test_fullsize_decode_layer(sdm, torch):
         gr = np.stack([to_host(r[b, h]) for r in rl])[None, :, None]
         compare_slot_lists(gw, ow, hx["k"], hx["C_w"], dc)
         compare_slot_lists(gr, orr, hx["q"], hx["C_r"], dc)
-        if np.array_equal(gw, ow) and np.array_equal(gr, orr):
-            M1 = np.ascontiguousarray(to_host(x["M0"][h])[None, None])
-            o_ref = oracle.scan(M1, ow, oww, orr, orw, hx["v"], hx["a"], hx["b"], dc)
-            o_dec = np.stack([to_host(o[b, h]) for o in outs])
-            assert_close_rms(o_dec, o_ref[0, :, 0], what=f"decode o ({b},{h})")
-            rows = np.unique(ow.ravel())
-            assert_close_rms(to_host(M[b, h])[rows], M1[0, 0][rows], what=f"decode M ({b},{h})")
+        # the oracle scan replayed on the GPU's own lists (near-tie swaps included)
+        ww = replay_weights(gw, ow, oww, hx["k"], hx["C_w"], dc)
+        rw = replay_weights(gr, orr, orw, hx["q"], hx["C_r"], dc)
+        M1 = np.ascontiguousarray(to_host(x["M0"][h])[None, None])
+        o_ref = oracle.scan(M1, gw, ww, gr, rw, hx["v"], hx["a"], hx["b"], dc)
+        o_dec = np.stack([to_host(o[b, h]) for o in outs])
+        assert_close_rms(o_dec, o_ref[0, :, 0], what=f"decode o ({b},{h})")
+        rows = np.unique(gw.ravel())
+        Mg = to_host(M[b, h])
+        assert_close_rms(Mg[rows], M1[0, 0][rows], what=f"decode M ({b},{h})")
+        sample = rng.choice(d.N, size=4096, replace=False)
+        sample = sample[~np.isin(sample, rows)]
+        np.testing.assert_array_equal(Mg[sample], to_host(x["M0"][h])[sample])
     del x, M, outs
     _free(torch)

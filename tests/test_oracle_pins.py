@@ -171,6 +171,38 @@ def test_half_scores_match_fp64_matmul():
     np.testing.assert_array_equal(hs[..., 1, :], ref1)
 
 
+@pytest.mark.parametrize("in_dtype,sep", [("bf16", False), ("bf16", True), ("f32", True)])
+def test_slot_scores_equal_brute_force(in_dtype, sep):
+    """oracle.slot_scores (the near-tie classifier of the GPU parity tests)
+    equals the brute-force fp32 score s1[i1] + s2[i2] of the named slot, with
+    i1 = slot // n_sub taken from the first half of the key and
+    i2 = slot % n_sub from the second ([P] Sec. 2, product keys), for random
+    token-head rows of several heads, both codebooks and both input dtypes.
+    n_sub is not a power of two and the rows span heads, so a swapped split,
+    a transposed codebook or a wrong head fails."""
+    d = Dims(B=2, T=7, H=3, d_k=64 if in_dtype == "bf16" else 24, n_sub=37, d_v=8, k_prime=5, W=3, R=2,
+             in_dtype=in_dtype)
+    x = synth.make_inputs(d, seed=17, m0=False, separate_read_codebook=sep)
+    g = np.random.default_rng(23)
+    n = 400
+    rows = g.integers(0, d.B * d.T * d.H, n)
+    slots = g.integers(0, d.N, n).astype(np.int32)
+    for xk, ck in (("k", "C_w"), ("q", "C_r")):
+        xf = x[xk].reshape(d.B * d.T * d.H, d.d_k)
+        got = oracle.slot_scores(x[xk], x[ck], d, rows, slots)
+        full = [brute_scores(xf[r], x[ck][r % d.H], d) for r in rows]
+        want = np.array([f[s] for f, s in zip(full, slots)], np.float32)
+        np.testing.assert_array_equal(got, want)
+        # the pin is sensitive to the slot split: the swapped split gives other scores
+        i1, i2 = slots // d.n_sub, slots % d.n_sub
+        swapped = np.array([f[b * d.n_sub + a] for f, a, b in zip(full, i1, i2)], np.float32)
+        assert np.mean(swapped != want) > 0.9
+    if sep:
+        # the two codebooks give different scores for the same input
+        assert np.mean(oracle.slot_scores(x["k"], x["C_w"], d, rows, slots)
+                       != oracle.slot_scores(x["k"], x["C_r"], d, rows, slots)) > 0.9
+
+
 def test_softmax_weights():
     d = dims(B=2, T=20, H=2, d_k=16, n_sub=9, k_prime=6, W=6, R=1)
     x = synth.make_inputs(d, seed=4)
