@@ -168,9 +168,12 @@ sdm_status sdm_scan_forward_save(float *M, const int32_t *widx, const float *wwt
  *   u = v - a p;  du = b sum_j w_j dY_j;  dv = du;  dp = -a du;
  *   da = sum_j <dY_j, X_j> - <p, du>;  db = sum_j w_j <dY_j, u>;
  *   dw_j = b <dY_j, u> + <dp, X_j>;  G[s_j] = a dY_j + w_j dp.
- * fp32 arithmetic, every sum in a fixed order (deterministic).  Uses B, T,
- * H, n_sub, d_v (<= 256), W, R, in_dtype.  Outputs must not overlap dM or
- * each other.
+ * A read slot may appear at several positions of one token: each position
+ * adds its r_i do to G (the positions are merged, their weights summed in
+ * list order).  Write slots of one token must be distinct, as in the
+ * forward.  fp32 arithmetic, every sum in a fixed order (deterministic).
+ * Uses B, T, H, n_sub, d_v (<= 256), W, R, in_dtype.  dM and the outputs
+ * must not overlap each other or any input (SDM_ERR_INVALID_ARG).
  * ------------------------------------------------------------------------- */
 sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, const int32_t *ridx,
                              const float *rwt, const void *v, const float *a, const float *b,
@@ -198,7 +201,9 @@ size_t sdm_address_backward_workspace_size(const sdm_dims *dims);
  *   dC_w, dC_r [H,2,n_sub,d_k/2] fp32 written (sums over every token); they
  *   may be the same buffer (a shared codebook): it then receives the sum.
  * workspace: at least sdm_address_backward_workspace_size(dims) bytes,
- * 16-byte aligned.  fp32 arithmetic, every sum in a fixed order.
+ * 16-byte aligned.  fp32 arithmetic, every sum in a fixed order.  The
+ * outputs and the workspace must not overlap each other (except dC_w ==
+ * dC_r) or any input (SDM_ERR_INVALID_ARG).
  * ------------------------------------------------------------------------- */
 sdm_status sdm_address_backward(const void *k, const void *q, const void *C_w, const void *C_r,
                                 const int32_t *widx, const float *wwt, const int32_t *ridx,

@@ -89,6 +89,26 @@ def test_scan_backward_matches_oracle(sdm, torch, case):
     run_case(sdm, torch, d, x, ad, seed=3)
 
 
+def test_scan_backward_repeated_read_slots(sdm, torch):
+    """A read slot listed at several positions of one token (allowed: only
+    write slots must be distinct) adds every position's r_i do into G; the
+    lane-per-position backward merges such positions.  Every third token
+    repeats position 1 at positions 3 and 7, every fifth repeats position 0
+    at the last position; the slots come from a small pool, so the repeated
+    rows are also written and read by nearby tokens."""
+    for d in (Dims(B=2, T=120, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=16, R=16),
+              Dims(B=1, T=90, H=3, d_k=128, n_sub=32, d_v=128, k_prime=32, W=32, R=32)):
+        note(f"scan backward repeated read slots {d}")
+        x = synth.make_inputs(d, seed=29)
+        ad = synth.random_addressing(d, seed=29, hazard_slots=60)
+        r = ad["ridx"]
+        r[:, 0::3, :, 3] = r[:, 0::3, :, 1]
+        r[:, 0::3, :, 7] = r[:, 0::3, :, 1]
+        r[:, 0::5, :, d.R - 1] = r[:, 0::5, :, 0]
+        assert any(len(set(r[b, t, h])) < d.R for b in range(d.B) for t in range(d.T) for h in range(d.H))
+        run_case(sdm, torch, d, x, ad, seed=5)
+
+
 def test_scan_backward_with_pkm_addressing(sdm, torch):
     """Slot lists and weights from the GPU addressing of the small layer's
     shape (T shortened)."""
