@@ -138,6 +138,28 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
                             const sdm_dims *dims, sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * sdm_scan_forward_noalloc -- sdm_scan_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): same arguments without the
+ * workspace, same kernels and results, bit for bit.  The preparation
+ * streams live in a static scratch array of SDM_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) that each GPU the library runs on holds until the process ends;
+ * its device address is looked up once per device, on the first call with
+ * that device current.  The call allocates nothing (no hipMalloc, no
+ * hipFree).  Dims with sdm_scan_workspace_size(dims) above
+ * SDM_NOALLOC_SCRATCH_BYTES give SDM_ERR_UNSUPPORTED before anything is
+ * launched (split T or B, or use sdm_scan_forward).  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must not be issued; calls in order
+ * on one stream are safe.  Nothing needs clearing between calls (the scan
+ * reads only scratch bytes its preparation pass wrote in the same call).
+ * ------------------------------------------------------------------------- */
+#define SDM_NOALLOC_SCRATCH_BYTES ((size_t)134217728)
+sdm_status sdm_scan_forward_noalloc(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                    const float *rwt, const void *v, const float *a, const float *b,
+                                    float *o, const sdm_dims *dims, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * sdm_scan_forward_save -- sdm_scan_forward that also saves, for the
  * backward pass, the rows each token used:
  *   xsave [B,H,T,d_v/4,W,4] fp32: the write rows before the token's write;

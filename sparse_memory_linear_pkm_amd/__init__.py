@@ -7,11 +7,12 @@ If the library has not been built, the first call raises ImportError; there
 is no fallback implementation.
 """
 from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP, SDM_F32,
-                      SDM_BF16, SdmDims, SdmError, dims_from, lib_path, load_library,
+                      SDM_BF16, SDM_NOALLOC_SCRATCH_BYTES, SdmDims, SdmError, dims_from, lib_path, load_library,
                       sdm_state_init, sdm_pkm_address, sdm_scan_workspace_size, sdm_scan_forward,
                       sdm_decode_step, sdm_cow_bitmap_bytes, sdm_cow_reset, sdm_decode_step_cow,
                       sdm_cow_materialize, sdm_gates, sdm_output_norm_gate, sdm_gdn_dense_forward,
                       sdm_scan_forward_save, sdm_scan_backward, scan_forward_save, scan_backward,
+                      sdm_scan_forward_noalloc, scan_forward_noalloc,
                       sdm_address_backward, sdm_address_backward_workspace_size, address_backward,
                       sdm_gates_backward, sdm_gates_backward_workspace_size, sdm_output_norm_gate_backward,
                       sdm_output_norm_gate_backward_workspace_size, gates_backward, output_norm_gate_backward,
@@ -22,4 +23,4 @@ from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_
 __all__ = [n for n in dir() if n.startswith(("sdm_", "SDM_", "Sdm")) or n in (
     "dims_from", "lib_path", "load_library", "state_init", "pkm_address", "scan_forward",
     "decode_step", "gates", "output_norm_gate", "gdn_dense_forward", "scan_forward_save", "scan_backward",
-    "address_backward", "gates_backward", "output_norm_gate_backward")]
+    "address_backward", "gates_backward", "output_norm_gate_backward", "scan_forward_noalloc")]

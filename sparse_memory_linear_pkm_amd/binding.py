@@ -16,6 +16,7 @@ _LIB_NAME = "libsdm.so"
 
 SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP = 0, -1, -2, -3
 SDM_F32, SDM_BF16 = 0, 1
+SDM_NOALLOC_SCRATCH_BYTES = 134217728   # static scratch of sdm_scan_forward_noalloc (include/sdm.h)
 
 
 class SdmError(RuntimeError):
@@ -56,6 +57,7 @@ def load_library():
         "sdm_output_norm_gate": [P, P, P, ctypes.c_float, D, P, P],
         "sdm_gdn_dense_forward": [P, P, P, P, P, P, P, D, P],
         "sdm_scan_forward_save": [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
+        "sdm_scan_forward_noalloc": [P, P, P, P, P, P, P, P, P, D, P],
         "sdm_scan_backward": [P] * 16 + [D, P],
         "sdm_address_backward": [P] * 10 + [D, P, P, P, P, P, ctypes.c_size_t, P],
         "sdm_gates_backward": [P] * 6 + [D, P, P, P, P, P, ctypes.c_size_t, P],
@@ -171,6 +173,15 @@ def sdm_scan_forward(M, widx, wwt, ridx, rwt, v, a, b, o, workspace, workspace_b
                                          int(workspace_bytes), ctypes.byref(dims), _stream(stream))
     if check:
         _check(st, "sdm_scan_forward")
+    return st
+
+
+def sdm_scan_forward_noalloc(M, widx, wwt, ridx, rwt, v, a, b, o, dims: SdmDims, stream=None, *,
+                             check: bool = True) -> int:
+    st = load_library().sdm_scan_forward_noalloc(_ptr(M), _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _ptr(v),
+                                                 _ptr(a), _ptr(b), _ptr(o), ctypes.byref(dims), _stream(stream))
+    if check:
+        _check(st, "sdm_scan_forward_noalloc")
     return st
 
 
@@ -371,6 +382,27 @@ def scan_forward(M, widx, wwt, ridx, rwt, v, a, b, dims: SdmDims, o=None, worksp
         workspace = torch.empty(need, dtype=torch.uint8, device=M.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sdm_scan_forward(M, widx, wwt, ridx, rwt, v, a, b, o, workspace, ws_bytes, dims, stream)
+    return o
+
+
+def scan_forward_noalloc(M, widx, wwt, ridx, rwt, v, a, b, dims: SdmDims, o=None, stream=None):
+    """scan_forward through the allocation-free entry point (the library's
+    static scratch instead of a workspace); o is allocated here if None."""
+    import torch
+    B, T, H = dims.B, dims.T, dims.H
+    N = dims.n_sub * dims.n_sub
+    _expect(M, (B, H, N, dims.d_v), torch.float32, "M")
+    _expect(widx, (B, T, H, dims.W), torch.int32, "widx")
+    _expect(wwt, (B, T, H, dims.W), torch.float32, "wwt")
+    _expect(ridx, (B, T, H, dims.R), torch.int32, "ridx")
+    _expect(rwt, (B, T, H, dims.R), torch.float32, "rwt")
+    _expect(v, (B, T, H, dims.d_v), _in_dtype(dims), "v")
+    _expect(a, (B, T, H), torch.float32, "a")
+    _expect(b, (B, T, H), torch.float32, "b")
+    if o is None:
+        o = torch.empty((B, T, H, dims.d_v), dtype=torch.float32, device=M.device)
+    _expect(o, (B, T, H, dims.d_v), torch.float32, "o")
+    sdm_scan_forward_noalloc(M, widx, wwt, ridx, rwt, v, a, b, o, dims, stream)
     return o
 
 

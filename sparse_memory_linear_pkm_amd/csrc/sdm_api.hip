@@ -8,9 +8,17 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
+
+// Scratch of sdm_scan_forward_noalloc: the scan's preparation streams live
+// here instead of in a caller workspace.  Each GPU the library runs on holds
+// its own copy (SDM_NOALLOC_SCRATCH_BYTES) until the process ends.  In host
+// code the name is only a host-side stand-in: kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SDM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -168,7 +176,7 @@ size_t sdm_scan_workspace_size(const sdm_dims *d)
 static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
                                     const float *rwt, const void *v, const float *a, const float *b, float *o,
                                     float *xsave, float *zsave, void *workspace, size_t workspace_bytes,
-                                    const sdm_dims *d, sdm_stream_t stream);
+                                    const sdm_dims *d, sdm_stream_t stream, bool noalloc = false);
 
 sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
                             const float *rwt, const void *v, const float *a, const float *b,
@@ -177,6 +185,13 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
 {
     return scan_forward_impl(M, widx, wwt, ridx, rwt, v, a, b, o, nullptr, nullptr, workspace, workspace_bytes, d,
                              stream);
+}
+
+sdm_status sdm_scan_forward_noalloc(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                    const float *rwt, const void *v, const float *a, const float *b, float *o,
+                                    const sdm_dims *d, sdm_stream_t stream)
+{
+    return scan_forward_impl(M, widx, wwt, ridx, rwt, v, a, b, o, nullptr, nullptr, nullptr, 0, d, stream, true);
 }
 
 sdm_status sdm_scan_forward_save(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
@@ -192,10 +207,34 @@ sdm_status sdm_scan_forward_save(float *M, const int32_t *widx, const float *wwt
                              stream);
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; later calls reuse it.
+static sdm_status scratch_address(void **out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SDM_ERR_UNSUPPORTED, "device ordinal %d beyond the %d the static scratch tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(SDM_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return SDM_OK;
+}
+
 static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
                                     const float *rwt, const void *v, const float *a, const float *b, float *o,
                                     float *xsave, float *zsave, void *workspace, size_t workspace_bytes,
-                                    const sdm_dims *d, sdm_stream_t stream)
+                                    const sdm_dims *d, sdm_stream_t stream, bool noalloc)
 {
     sdm_status st = check_memory_dims(d);
     if (st != SDM_OK) return st;
@@ -230,6 +269,18 @@ static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *
         return fail(SDM_ERR_UNSUPPORTED, "T too large: one (sequence, head) stream of the scan must stay below 2 GiB");
     const size_t need = sdm::scan_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v,
                                                   d->in_dtype == SDM_BF16);
+    if (noalloc) {
+        if (need > (size_t)SDM_NOALLOC_SCRATCH_BYTES)
+            return fail(SDM_ERR_UNSUPPORTED,
+                        "sdm_scan_forward_noalloc: these dims need %zu bytes of scratch, the static scratch holds "
+                        "%zu (split T or B, or call sdm_scan_forward with a workspace)",
+                        need, (size_t)SDM_NOALLOC_SCRATCH_BYTES);
+        // every byte the scan reads from the scratch is written first by its
+        // preparation pass in the same call, so nothing needs clearing
+        sdm_status sst = scratch_address(&workspace);
+        if (sst != SDM_OK) return sst;
+        workspace_bytes = (size_t)SDM_NOALLOC_SCRATCH_BYTES;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(SDM_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
     if (need > 0 && !aligned(workspace, 16)) return fail(SDM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");

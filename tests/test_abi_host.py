@@ -234,6 +234,19 @@ def test_scan_backward_rejects_bad_arguments():
     assert call(good_dims(T=0), dM=None) == sdm.SDM_OK
 
 
+def test_scan_noalloc_rejects_beyond_scratch_on_the_host():
+    """The allocation-free scan refuses dims whose preparation streams exceed
+    its static scratch before touching the device, and a call without work
+    succeeds on NULL buffers."""
+    big = good_dims(B=4, T=4096, H=16, d_v=128, W=32, R=32, k_prime=16)
+    assert sdm.sdm_scan_workspace_size(big) > sdm.SDM_NOALLOC_SCRATCH_BYTES
+    args = [FAKE + (i << 30) for i in range(9)]
+    assert sdm.sdm_scan_forward_noalloc(*args, big, stream=0, check=False) == sdm.SDM_ERR_UNSUPPORTED
+    assert "scratch" in sdm.sdm_last_error()
+    assert sdm.sdm_scan_forward_noalloc(*args, good_dims(W=0), stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
+    assert sdm.sdm_scan_forward_noalloc(*([None] * 9), good_dims(T=0), stream=0, check=False) == sdm.SDM_OK
+
+
 def test_scan_forward_save_needs_both_buffers():
     dims = good_dims()
     args = [FAKE + (i << 30) for i in range(9)]
