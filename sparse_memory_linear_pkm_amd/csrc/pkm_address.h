@@ -31,12 +31,14 @@ constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimensio
 //   NB: sub-key tiles whose codebook loads a wave issues together (a
 //      latency-bound caller with few waves wants many in flight; the result
 //      does not depend on NB).
+//   sst: row stride of S in elements (0: n_sub).
 template <bool BF16, int NB = 1, int NK = 0>
 __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_stride, int nrows,
                                                 int srows,
                                                 const void *Cc /* [n_sub, half] of (h, c) */,
-                                                int c, int half, int n_sub, uint32_t *S)
+                                                int c, int half, int n_sub, uint32_t *S, int sst = 0)
 {
+    if (sst == 0) sst = n_sub;
     const int tid = threadIdx.x;
     const int nthreads = blockDim.x;
     if constexpr (BF16) {
@@ -90,7 +92,7 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int row = 4 * kg + e;
-                        if (row < srows) S[row * n_sub + u] = score_bits(acc[t][e]);
+                        if (row < srows) S[row * sst + u] = score_bits(acc[t][e]);
                     }
                 }
             }
@@ -106,7 +108,7 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
                 const float *cr = Cf + (int64_t)u * half;
                 for (int d = 0; d < half; ++d) acc = __builtin_fmaf(xr[d], cr[d], acc);
             }
-            S[e] = score_bits(acc);
+            S[row * sst + u] = score_bits(acc);
         }
     }
 }
@@ -127,14 +129,16 @@ __device__ __forceinline__ void load_staircase(const Staircase &st, uint16_t *st
 // Top-k' of NR rows of half scores, one wave.  Row r's n_sub score bits are
 // at S + rows[r] * n_sub; lane j < k' of keys[r] receives the j-th best
 // (score desc, sub-key asc).
+// sst: row stride of S in elements (0: n_sub).
 template <int NR>
 __device__ __forceinline__ void half_topk(const uint32_t *S, const int (&rows)[NR], int n_sub, int kp,
-                                          uint64_t *scratch, uint64_t (&keys)[NR])
+                                          uint64_t *scratch, uint64_t (&keys)[NR], int sst = 0)
 {
+    if (sst == 0) sst = n_sub;
     int ib = 1;   // bits of a sub-key index
     while ((1 << ib) < n_sub) ++ib;
     wave_topn<NR>(n_sub, kp,
-                  [&](int r, int p) { return ((uint64_t)S[rows[r] * n_sub + p] << 32) | (uint32_t)~p; },
+                  [&](int r, int p) { return ((uint64_t)S[rows[r] * sst + p] << 32) | (uint32_t)~p; },
                   scratch, keys, ib);
 }
 

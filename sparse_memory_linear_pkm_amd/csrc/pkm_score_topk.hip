@@ -8,36 +8,46 @@
 // and one kind (write: k against C_w, read: q against C_r):
 //   1. for each half c: the [16 x d_k/2] x [d_k/2 x n_sub] score tile on bf16
 //      MFMA (fp32 accumulation) into LDS;
-//   2. each wave takes 4 of the 16 rows together: exact top-k' of the half;
+//   2. each wave takes 4 of the 16 rows, one per 16-lane group: exact top-k'
+//      of the half (pkm_select16.h);
 //   3. each wave: exact top-n of the outer-sum candidates of its 4 rows
 //      (staircase-pruned, with an exact fallback), softmax, store slots and
 //      weights.
-// The N slot scores are never materialised.
+// Rows whose fast selection cannot vouch for its order (tied key prefixes,
+// more than 64 survivors, a tie at the staircase border) are redone by the
+// one-row routines of pkm_address.h.  The N slot scores are never
+// materialised.
 //
 // Work placement: consecutive workgroup ids are spread over the 8 XCDs, so
 // the id is decoded such that the workgroups of one (head, kind) -- which
 // all read the same codebook -- land on the same XCD and share its L2.
 #include "kernels.h"
 #include "pkm_address.h"
+#include "pkm_select16.h"
 
 namespace sdm {
 
 constexpr int kAddrWaves = 4;
-constexpr int kRowsPerWave = kTileRows / kAddrWaves;
 constexpr int kXcds = 8;
 
 struct AddrLds {
     // byte offsets into dynamic LDS
-    size_t S, L, scratch, stair, total;
+    size_t S, L, buf, cnt, scratch, stair, total;
+    int sst;   // row stride of S in elements
 };
 
 __host__ __device__ inline AddrLds addr_lds_layout(int n_sub, int kp)
 {
     AddrLds o;
-    o.S = 0;                                                   // float [16][n_sub]
-    o.L = o.S + sizeof(float) * kTileRows * (size_t)n_sub;     // HalfEntry [2][16][kp]
-    o.scratch = o.L + sizeof(HalfEntry) * 2 * kTileRows * (size_t)kp;  // u64 [4][4][64]
-    o.stair = o.scratch + sizeof(uint64_t) * kAddrWaves * kRowsPerWave * kWave;
+    // rows padded with zeros to a multiple of 64 candidates, plus 4 elements
+    // so that consecutive rows start in different LDS banks
+    o.sst = ((n_sub + 63) / 64) * 64 + 4;
+    o.S = 0;                                                      // uint32 [16][sst]
+    o.L = o.S + sizeof(uint32_t) * kTileRows * (size_t)o.sst;     // HalfEntry [2][16][kp]
+    o.buf = o.L + sizeof(HalfEntry) * 2 * kTileRows * (size_t)kp; // uint32 [16][64] survivors
+    o.cnt = o.buf + sizeof(uint32_t) * kTileRows * 64;            // uint32 [16]
+    o.scratch = o.cnt + sizeof(uint32_t) * kTileRows;             // uint64 [4][64] (one-row routines)
+    o.stair = o.scratch + sizeof(uint64_t) * kAddrWaves * kWave;
     o.total = o.stair + sizeof(uint16_t) * kMaxStair;
     return o;
 }
@@ -74,11 +84,15 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
     const int n_sub = args.n_sub, kp = args.k_prime, half = args.d_k / 2, n = K.n_out;
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
+    const int g = lane >> 4, c16 = lane & (kGroupLanes - 1);
 
     const AddrLds lay = addr_lds_layout(n_sub, kp);
+    const int sst = lay.sst;
     uint32_t *S = reinterpret_cast<uint32_t *>(smem + lay.S);
     HalfEntry *L = reinterpret_cast<HalfEntry *>(smem + lay.L);
-    uint64_t *wscr = reinterpret_cast<uint64_t *>(smem + lay.scratch) + wave * kRowsPerWave * kWave;
+    uint32_t *buf = reinterpret_cast<uint32_t *>(smem + lay.buf);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + lay.cnt);
+    uint64_t *wscr = reinterpret_cast<uint64_t *>(smem + lay.scratch) + wave * kWave;
     uint16_t *stair = reinterpret_cast<uint16_t *>(smem + lay.stair);
 
     const size_t esz = BF16 ? 2 : 4;
@@ -90,45 +104,72 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
 
     load_staircase(K.stair, stair);   // ordered before use by the barriers below
     const int nstair = K.stair.count;
+    // the padding of every score row past n_sub holds score bits 0 (below
+    // every real score; the scoring never writes it); counters start at 0
+    {
+        const int padw = sst - n_sub;
+        for (int e = threadIdx.x; e < kTileRows * padw; e += blockDim.x)
+            S[(e / padw) * sst + n_sub + e % padw] = 0u;
+        if (threadIdx.x < kTileRows) cnt[threadIdx.x] = 0u;
+    }
 
-    int rows[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) rows[i] = wave + i * kAddrWaves;
+    // rows of this wave: wave + 4 g for lane group g
+    const int row_g = wave + kAddrWaves * g;
+    const RowBuf rb{buf + wave * kAddrWaves * 64, cnt + wave * kAddrWaves};
 
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         score_half_tile<BF16, 1, NK>(xb, row_stride, nrows, kTileRows,
-                              Cb + (int64_t)c * n_sub * half * esz, c, half, n_sub, S);
+                                     Cb + (int64_t)c * n_sub * half * esz, c, half, n_sub, S, sst);
         __syncthreads();
-        uint64_t keys[kRowsPerWave];
-        half_topk<kRowsPerWave>(S, rows, n_sub, kp, wscr, keys);
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) {
-            if (lane < kp) {
-                HalfEntry e;
-                e.score = __float_as_uint(key_score(keys[i]));
-                e.index = key_index(keys[i]);
-                L[(c * kTileRows + rows[i]) * kp + lane] = e;
+        const bool bad = half_topk16(S, sst, row_g, n_sub, kp, rb, L + (c * kTileRows + row_g) * kp);
+        // rows the fast path could not vouch for: the exact one-row routine
+        const uint64_t bb = __ballot(bad);
+        for (int gg = 0; gg < kAddrWaves; ++gg) {
+            if ((bb >> (16 * gg)) & 0xFFFFull) {
+                const int rows1[1] = {wave + kAddrWaves * gg};
+                uint64_t keys[1];
+                half_topk<1>(S, rows1, n_sub, kp, wscr, keys, sst);
+                if (lane < kp) {
+                    HalfEntry e;
+                    e.score = __float_as_uint(key_score(keys[0]));
+                    e.index = key_index(keys[0]);
+                    L[(c * kTileRows + rows1[0]) * kp + lane] = e;
+                }
+                wave_lds_sync();
             }
         }
         __syncthreads();
     }
 
-    const HalfEntry *L0[kRowsPerWave], *L1[kRowsPerWave];
+    int slot[4];
+    float wt[4];
+    const bool bad = merge16(L + row_g * kp, L + (kTileRows + row_g) * kp, kp, n_sub, n, stair, nstair, rb, slot, wt);
+    if (!bad && row_g < nrows) {
+        const int64_t gr = (bt0 + row_g) * args.H + h;
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        L0[i] = L + rows[i] * kp;
-        L1[i] = L + (kTileRows + rows[i]) * kp;
+        for (int r = 0; r < 4; ++r) {
+            const int j = 4 * c16 + r;
+            if (j < n) {
+                K.idx[gr * n + j] = slot[r];
+                K.wt[gr * n + j] = wt[r];
+            }
+        }
     }
-    int slot[kRowsPerWave];
-    float wt[kRowsPerWave];
-    merge_softmax<kRowsPerWave>(L0, L1, kp, n_sub, n, stair, nstair, wscr, slot, wt);
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        if (rows[i] < nrows && lane < n) {
-            const int64_t g = (bt0 + rows[i]) * args.H + h;
-            K.idx[g * n + lane] = slot[i];
-            K.wt[g * n + lane] = wt[i];
+    const uint64_t bb = __ballot(bad);
+    for (int gg = 0; gg < kAddrWaves; ++gg) {
+        if ((bb >> (16 * gg)) & 0xFFFFull) {
+            const int r1 = wave + kAddrWaves * gg;
+            const HalfEntry *L0[1] = {L + r1 * kp}, *L1[1] = {L + (kTileRows + r1) * kp};
+            int s1[1];
+            float w1[1];
+            merge_softmax<1>(L0, L1, kp, n_sub, n, stair, nstair, wscr, s1, w1);
+            if (r1 < nrows && lane < n) {
+                const int64_t gr = (bt0 + r1) * args.H + h;
+                K.idx[gr * n + lane] = s1[0];
+                K.wt[gr * n + lane] = w1[0];
+            }
+            wave_lds_sync();
         }
     }
 }

@@ -1,0 +1,401 @@
+// pkm_select16.h -- the prefill addressing's selections, four token rows per
+// wave, sixteen lanes per row.
+//
+// "Sparse Delta Memory: Scaling the State of Linear RNNs through Sparsity",
+// Sec. 2 (Product-Key Memories: top-k' of each half, then the best slots of
+// the k' x k' outer sum) and Sec. 4 (softmax over the selected scores).
+//
+// Every selection here is exact: the result is the top of the list in the
+// total order (score descending, index ascending), the same lists the
+// one-row routines of pkm_address.h produce (and the decode step uses), and
+// the weights are computed with the same operations in the same order, so
+// the prefill and the decode step give bit-identical slots and weights.
+//
+// Layout: lane l of a wave serves row group g = l / 16 (one token row) as
+// lane c = l % 16 of that group.  A list of up to 64 values of a row lives
+// in the group's 16 lanes x 4 registers (element i = 4c + r), so the
+// compare-exchanges of a sort are register pairs inside a lane or lane pairs
+// inside a 16-lane DPP row (quad_perm, row_ror, row_mirror, bank-masked
+// row_shl/row_shr); the four rows of a wave never exchange data.
+//
+// Selection of the n best of a row's candidates (n <= 64):
+//   1. group maxima: every lane folds its candidates into 4 running maxima
+//      (64 per row); tau = the n-th largest of them, found by sorting the 64.
+//      At least n candidates reach tau (one per group maximum above it), so
+//      the n best all do;
+//   2. the candidates that reach tau (typically 1.1-1.4 n) are compacted into
+//      a per-row LDS buffer (a per-lane bit mask, one LDS atomic per lane to
+//      reserve space, then the set bits);
+//   3. the survivors are sorted as 32-bit keys: the score bits above tau,
+//      shifted right just enough to leave room for the index in the low
+//      bits.  Where the shift drops bits, two different scores can share a
+//      key prefix; the sorted list is then checked pair by pair against the
+//      full (score, index) order.  A row with a misordered pair, or with more
+//      than 64 survivors, is redone by the one-row exact routine.
+#pragma once
+
+#include "device_common.h"
+#include "pkm_address.h"
+
+namespace sdm {
+
+constexpr int kGroupLanes = 16;
+
+// x of lane (c ^ M) of the same 16-lane row, M in {1, 2, 3, 4, 7, 8, 15}.
+template <int M>
+__device__ __forceinline__ uint32_t row_xor(uint32_t x)
+{
+    const int xi = (int)x;
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    } else if constexpr (M == 3) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x1B, 0xF, 0xF, false);    // quad_perm [3,2,1,0]
+    } else if constexpr (M == 4) {
+        // banks 0 and 2 (lanes 0-3, 8-11) read 4 lanes up, banks 1 and 3 read 4 lanes down
+        const int up = __builtin_amdgcn_update_dpp(xi, xi, 0x104, 0xF, 0x5, false);    // row_shl:4
+        return (uint32_t)__builtin_amdgcn_update_dpp(up, xi, 0x114, 0xF, 0xA, false);  // row_shr:4
+    } else if constexpr (M == 7) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    } else if constexpr (M == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, false);   // row_ror:8
+    } else {
+        static_assert(M == 15, "lane distance within a row");
+        return (uint32_t)__builtin_amdgcn_mov_dpp(xi, 0x140, 0xF, 0xF, false);   // row_mirror
+    }
+}
+
+// One compare-exchange stage of the list x (element i = 4c + r): i and
+// i ^ M are compared and the lower index keeps the larger value.
+template <int M>
+__device__ __forceinline__ void cmpx_stage(uint32_t (&x)[4])
+{
+    constexpr int HB = M >= 32 ? 32 : M >= 16 ? 16 : M >= 8 ? 8 : M >= 4 ? 4 : M >= 2 ? 2 : 1;   // highest bit of M
+    constexpr int LM = M >> 2, RM = M & 3;
+    if constexpr (LM == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if ((r & HB) == 0) {
+                const uint32_t a = x[r], b = x[r ^ RM];
+                x[r] = a > b ? a : b;
+                x[r ^ RM] = a > b ? b : a;
+            }
+        }
+    } else {
+        const bool lower = (lane_id() & (HB >> 2)) == 0;
+        uint32_t y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = row_xor<LM>(x[r ^ RM]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t hi = x[r] > y[r] ? x[r] : y[r], lo = x[r] > y[r] ? y[r] : x[r];
+            x[r] = lower ? hi : lo;
+        }
+    }
+}
+
+// Sorts each 16-lane row's 64 values (lanes x 4 registers) descending: a
+// bitonic network whose merges start with a flip (i against i ^ (K - 1)),
+// so that every comparator points the same way.
+__device__ __forceinline__ void sort64_desc(uint32_t (&x)[4])
+{
+    cmpx_stage<1>(x);
+    cmpx_stage<3>(x); cmpx_stage<1>(x);
+    cmpx_stage<7>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+    cmpx_stage<15>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+    cmpx_stage<31>(x); cmpx_stage<8>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+    cmpx_stage<63>(x); cmpx_stage<16>(x); cmpx_stage<8>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+}
+
+// The element of rank j (uniform) of a sorted row list, in every lane of the row.
+__device__ __forceinline__ uint32_t rank_value(const uint32_t (&x)[4], int j)
+{
+    const int r = j & 3;
+    const uint32_t v = r == 0 ? x[0] : r == 1 ? x[1] : r == 2 ? x[2] : x[3];
+    const int src = (lane_id() & ~(kGroupLanes - 1)) + (j >> 2);
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)v);
+}
+
+// The next element of the sorted row list (rank 4c + r + 1); lane 15's last
+// register receives 0.
+__device__ __forceinline__ void next_in_list(const uint32_t (&x)[4], uint32_t (&nx)[4])
+{
+    nx[0] = x[1];
+    nx[1] = x[2];
+    nx[2] = x[3];
+    nx[3] = (uint32_t)__builtin_amdgcn_mov_dpp((int)x[0], 0x101, 0xF, 0xF, true);   // row_shl:1, lane 15 gets 0
+}
+
+__device__ __forceinline__ uint32_t group_max16(uint32_t x)
+{
+    uint32_t y;
+    y = row_xor<1>(x); x = x > y ? x : y;
+    y = row_xor<2>(x); x = x > y ? x : y;
+    y = row_xor<4>(x); x = x > y ? x : y;
+    y = row_xor<8>(x); x = x > y ? x : y;
+    return x;
+}
+
+// Shift that fits (score bits - tau) >> sh, plus one, below 2^(32 - ib).
+__device__ __forceinline__ uint32_t key_shift(uint32_t span, int ib)
+{
+    const int lim = 31 - ib;   // (span >> sh) < 2^lim
+    const int bl = span ? 32 - __clz((int)span) : 0;
+    return bl > lim ? (uint32_t)(bl - lim) : 0u;
+}
+
+// m = (m << 1) | (x >= t): one compare into VCC and one add with carry.
+__device__ __forceinline__ void push_ge(uint32_t &m, uint32_t x, uint32_t t)
+{
+    asm volatile("v_cmp_ge_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(m) : "v"(x), "v"(t) : "vcc");
+}
+
+// Per-row survivor buffers of a wave: 4 rows x 64 entries, 4 counters.
+struct RowBuf {
+    uint32_t *buf;   // [4][64]
+    uint32_t *cnt;   // [4]
+};
+
+// Compacts the candidates of this lane whose bit is set in mask[] into the
+// row's buffer (the order of the entries is not fixed; every use sorts
+// them).  pos_of(q) maps mask bit q to the stored value.  Returns the row's
+// survivor count (all lanes of the row).  The counter is zero on entry; the
+// caller re-zeroes it after use.
+template <int NMW, class PosOf>
+__device__ __forceinline__ uint32_t compact_row(const uint32_t (&mask)[NMW], RowBuf rb, PosOf pos_of)
+{
+    const int g = lane_id() >> 4;
+    uint32_t n = 0;
+#pragma unroll
+    for (int w = 0; w < NMW; ++w) n += __popc(mask[w]);
+    uint32_t pos = n ? atomicAdd(&rb.cnt[g], n) : 0u;
+#pragma unroll
+    for (int w = 0; w < NMW; ++w) {
+        uint32_t m = mask[w];
+        while (m) {
+            const int b = __ffs((int)m) - 1;
+            m &= m - 1u;
+            if (pos < 64u) rb.buf[g * 64 + pos] = pos_of(32 * w + b);
+            ++pos;
+        }
+    }
+    wave_lds_sync();
+    return rb.cnt[g];
+}
+
+// Raw fp32 bits of order-preserving score bits (inverse of score_bits).
+__device__ __forceinline__ uint32_t raw_of_score_bits(uint32_t u)
+{
+    return (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+}
+
+// Top-k' of one half for the 4 rows of this wave (row of lane group g =
+// row_g): S holds the row's score bits at S + row_g * sst, zero from n_sub
+// up to the next multiple of 64.  Lane j < k' of the row's list is written
+// to Lrow[j] (best first).  Returns true if this lane's row must be redone
+// by the exact one-row routine.
+__device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_g, int n_sub, int kp, RowBuf rb,
+                                            HalfEntry *Lrow)
+{
+    const int c = lane_id() & (kGroupLanes - 1);
+    const uint32_t *Sr = S + (size_t)row_g * sst;
+    const int nch = (n_sub + 63) >> 6;   // 64 candidates of a row per chunk, 4 per lane
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < nch; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(Sr + 64 * i + 4 * c);
+        m[0] = v.x > m[0] ? v.x : m[0];
+        m[1] = v.y > m[1] ? v.y : m[1];
+        m[2] = v.z > m[2] ? v.z : m[2];
+        m[3] = v.w > m[3] ? v.w : m[3];
+    }
+    sort64_desc(m);
+    const uint32_t tau = rank_value(m, kp - 1);
+    const uint32_t top = rank_value(m, 0);
+    // candidates reaching tau: word w holds chunks 8w .. 8w + 7, candidate
+    // (chunk i, k) at bit 31 - (4 (i - 8w) + k) (shifted in from the right
+    // in order, then left-aligned)
+    uint32_t mask[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (8 * w < nch) {   // uniform
+            uint32_t mw = 0u;
+#pragma unroll
+            for (int k8 = 0; k8 < 8; ++k8) {
+                const int i = 8 * w + k8;
+                if (i < nch) {   // uniform
+                    const uint4 v = *reinterpret_cast<const uint4 *>(Sr + 64 * i + 4 * c);
+                    push_ge(mw, v.x, tau);
+                    push_ge(mw, v.y, tau);
+                    push_ge(mw, v.z, tau);
+                    push_ge(mw, v.w, tau);
+                }
+            }
+            const int pushed = 4 * min(8, nch - 8 * w);
+            mask[w] = pushed < 32 ? mw << (32 - pushed) : mw;
+        }
+    }
+    const uint32_t total = compact_row<4>(mask, rb, [&](int q) {
+        const int e = 32 * (q >> 5) + 31 - (q & 31);   // candidate number 4i + k
+        return (uint32_t)(64 * (e >> 2) + 4 * c + (e & 3));
+    });
+    const int g = lane_id() >> 4;
+    int ib = 1;   // bits of a sub-key index
+    while ((1 << ib) < n_sub) ++ib;
+    const uint32_t imask = (1u << ib) - 1u;
+    const uint32_t sh = key_shift(top - tau, ib);
+    uint32_t key[4];
+    const uint4 e = *reinterpret_cast<const uint4 *>(rb.buf + g * 64 + 4 * c);
+    const uint32_t ent[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t j = (uint32_t)(4 * c + r);
+        const uint32_t p = j < total ? ent[r] : 0u;
+        const uint32_t s = Sr[p];
+        key[r] = j < total ? ((((s - tau) >> sh) + 1u) << ib) | (imask - p) : 0u;
+    }
+    wave_lds_sync();
+    if (c == 0) rb.cnt[g] = 0u;   // buffer free for the next selection
+    sort64_desc(key);
+    // full scores of the sorted list, and the check of neighbouring pairs
+    // whose shifted scores tie
+    uint32_t p[4], s[4], nk[4], ns[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        p[r] = imask - (key[r] & imask);
+        s[r] = key[r] ? Sr[p[r]] : 0u;
+    }
+    next_in_list(key, nk);
+    next_in_list(s, ns);
+    // every neighbouring pair of survivors in the full order (a misordered
+    // pair anywhere in a run of tied prefixes could reach the top k')
+    bool bad = total > 64u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool tie = nk[r] && (key[r] >> ib) == (nk[r] >> ib);
+        bad = bad || (tie && s[r] < ns[r]);
+    }
+    // one lane's verdict for the whole row
+    const uint64_t bb = __ballot(bad);
+    const bool row_bad = ((bb >> (16 * g)) & 0xFFFFull) != 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int j = 4 * c + r;
+        if (!row_bad && j < kp) {
+            HalfEntry he;
+            he.score = raw_of_score_bits(s[r]);
+            he.index = p[r];
+            Lrow[j] = he;
+        }
+    }
+    return row_bad;
+}
+
+// Merge of the two half lists of the 4 rows of this wave into the best n
+// slots and their softmax weights.  L0, L1: this lane's row's k' entries of
+// half 0 and half 1.  On success lane (c, r) holds rank 4c + r: slot[r],
+// wt[r] (ranks >= n hold weight 0).  Returns true if this lane's row must
+// be redone by the exact one-row routine (merge_softmax<1>).
+__device__ __forceinline__ bool merge16(const HalfEntry *L0, const HalfEntry *L1, int kp, int n_sub, int n,
+                                        const uint16_t *stair, int nstair, RowBuf rb, int (&slot)[4],
+                                        float (&wt)[4])
+{
+    constexpr int kMaxPer = (kMaxStair + kGroupLanes - 1) / kGroupLanes;   // staircase entries per lane
+    const int c = lane_id() & (kGroupLanes - 1);
+    const int g = lane_id() >> 4;
+    uint32_t sb[kMaxPer];
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+        const int sp = c + kGroupLanes * i;
+        uint32_t v = 0u;
+        if (sp < nstair) {
+            const uint32_t ab = stair[sp];
+            const float sum = __uint_as_float(L0[ab >> 8].score) + __uint_as_float(L1[ab & 0xff].score);
+            v = score_bits(sum);
+        }
+        sb[i] = v;
+        m[i & 3] = v > m[i & 3] ? v : m[i & 3];
+    }
+    sort64_desc(m);
+    const uint32_t tau = rank_value(m, n - 1);
+    const uint32_t top = rank_value(m, 0);
+    uint32_t mask[1] = {0u};
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) mask[0] |= (sb[i] >= tau && sb[i] != 0u) ? 1u << i : 0u;
+    const uint32_t total = compact_row<1>(mask, rb, [&](int q) { return (uint32_t)(c + kGroupLanes * q); });
+    constexpr int ib = 9;   // staircase positions < 512
+    constexpr uint32_t imask = (1u << ib) - 1u;
+    const uint32_t sh = key_shift(top - tau, ib);
+    uint32_t key[4];
+    const uint4 e = *reinterpret_cast<const uint4 *>(rb.buf + g * 64 + 4 * c);
+    const uint32_t ent[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t j = (uint32_t)(4 * c + r);
+        const uint32_t sp = j < total ? ent[r] : 0u;
+        const uint32_t ab = stair[sp];
+        const uint32_t s = score_bits(__uint_as_float(L0[ab >> 8].score) + __uint_as_float(L1[ab & 0xff].score));
+        key[r] = j < total ? ((((s - tau) >> sh) + 1u) << ib) | (imask - sp) : 0u;
+    }
+    wave_lds_sync();
+    if (c == 0) rb.cnt[g] = 0u;
+    sort64_desc(key);
+    uint32_t s[4], sl[4], nk[4], ns[4], nsl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t sp = imask - (key[r] & imask);
+        const uint32_t ab = key[r] ? stair[sp] : 0u;
+        const HalfEntry a = L0[ab >> 8], b = L1[ab & 0xff];
+        s[r] = key[r] ? score_bits(__uint_as_float(a.score) + __uint_as_float(b.score)) : 0u;
+        sl[r] = a.index * (uint32_t)n_sub + b.index;
+    }
+    next_in_list(key, nk);
+    next_in_list(s, ns);
+    next_in_list(sl, nsl);
+    bool bad = total > 64u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        // every neighbouring pair of survivors in (score desc, slot asc) order
+        const bool ordered = s[r] > ns[r] || (s[r] == ns[r] && sl[r] < nsl[r]);
+        bad = bad || (nk[r] != 0u && !ordered);
+    }
+    // the staircase holds the top n unless a pair just outside it reaches
+    // the n-th score: (a, n / (a + 1)) bounds every pair outside
+    uint32_t fb = 0u;
+    for (int a = c; a < kp; a += kGroupLanes) {
+        const int b0 = n / (a + 1);
+        if (b0 < kp) {
+            const uint32_t v = score_bits(__uint_as_float(L0[a].score) + __uint_as_float(L1[b0].score));
+            fb = v > fb ? v : fb;
+        }
+    }
+    fb = group_max16(fb);
+    const uint32_t nth = rank_value(s, n - 1);
+    bad = bad || !(nth > fb);
+    const uint64_t bb = __ballot(bad);
+    const bool row_bad = ((bb >> (16 * g)) & 0xFFFFull) != 0;
+    // softmax over the n best, the sums in the order of wave_sum_f32 over
+    // ranks (pairs of neighbouring ranks first), so the weights match the
+    // one-row routine's bit for bit
+    const float smax = key_score((uint64_t)rank_value(s, 0) << 32);
+    float ex[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int j = 4 * c + r;
+        ex[r] = j < n ? __expf(key_score((uint64_t)s[r] << 32) - smax) : 0.f;
+    }
+    float z = (ex[0] + ex[1]) + (ex[2] + ex[3]);
+    z += __uint_as_float(row_xor<1>(__float_as_uint(z)));
+    z += __uint_as_float(row_xor<2>(__float_as_uint(z)));
+    z += __uint_as_float(row_xor<4>(__float_as_uint(z)));
+    z += __uint_as_float(row_xor<8>(__float_as_uint(z)));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        wt[r] = __fdividef(ex[r], z);
+        slot[r] = (int)sl[r];
+    }
+    return row_bad;
+}
+
+}  // namespace sdm
