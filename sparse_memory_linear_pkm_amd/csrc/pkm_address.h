@@ -32,7 +32,11 @@ constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimensio
 //      latency-bound caller with few waves wants many in flight; the result
 //      does not depend on NB).
 //   sst: row stride of S in elements (0: n_sub).
-template <bool BF16, int NB = 1, int NK = 0>
+//   RAW: store the raw fp32 bits instead of score_bits (for callers that
+//        compare the stored scores as floats).
+//   FULL: n_sub is a multiple of 16 * NB, so every sub-key tile a wave takes
+//        is whole and no lane needs the bounds check.
+template <bool BF16, int NB = 1, int NK = 0, bool RAW = false, bool FULL = false>
 __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_stride, int nrows,
                                                 int srows,
                                                 const void *Cc /* [n_sub, half] of (h, c) */,
@@ -76,9 +80,13 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
 #pragma unroll
                     for (int t = 0; t < NB; ++t) {
                         const int u = (st0 + t) * 16 + r;   // sub-key (B column) of this lane
-                        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)min(u, n_sub - 1) * half +
-                                                                          kk * 32 + kg * 8);
-                        bv[t] = u < n_sub ? b : zero;
+                        if constexpr (FULL) {
+                            bv[t] = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)u * half + kk * 32 + kg * 8);
+                        } else {
+                            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)min(u, n_sub - 1) * half +
+                                                                              kk * 32 + kg * 8);
+                            bv[t] = u < n_sub ? b : zero;
+                        }
                     }
 #pragma unroll
                     for (int t = 0; t < NB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], bv[t], acc[t], 0, 0, 0);
@@ -88,11 +96,11 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
 #pragma unroll
             for (int t = 0; t < NB; ++t) {
                 const int u = (st0 + t) * 16 + r;
-                if (u < n_sub) {
+                if (FULL || u < n_sub) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int row = 4 * kg + e;
-                        if (row < srows) S[row * sst + u] = score_bits(acc[t][e]);
+                        if (row < srows) S[row * sst + u] = RAW ? __float_as_uint(acc[t][e]) : score_bits(acc[t][e]);
                     }
                 }
             }
@@ -108,7 +116,7 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
                 const float *cr = Cf + (int64_t)u * half;
                 for (int d = 0; d < half; ++d) acc = __builtin_fmaf(xr[d], cr[d], acc);
             }
-            S[row * sst + u] = score_bits(acc);
+            S[row * sst + u] = RAW ? __float_as_uint(acc) : score_bits(acc);
         }
     }
 }
@@ -129,8 +137,9 @@ __device__ __forceinline__ void load_staircase(const Staircase &st, uint16_t *st
 // Top-k' of NR rows of half scores, one wave.  Row r's n_sub score bits are
 // at S + rows[r] * n_sub; lane j < k' of keys[r] receives the j-th best
 // (score desc, sub-key asc).
-// sst: row stride of S in elements (0: n_sub).
-template <int NR>
+// sst: row stride of S in elements (0: n_sub).  RAW: S holds raw fp32 bits
+// (converted to score_bits on the fly).
+template <int NR, bool RAW = false>
 __device__ __forceinline__ void half_topk(const uint32_t *S, const int (&rows)[NR], int n_sub, int kp,
                                           uint64_t *scratch, uint64_t (&keys)[NR], int sst = 0)
 {
@@ -138,7 +147,10 @@ __device__ __forceinline__ void half_topk(const uint32_t *S, const int (&rows)[N
     int ib = 1;   // bits of a sub-key index
     while ((1 << ib) < n_sub) ++ib;
     wave_topn<NR>(n_sub, kp,
-                  [&](int r, int p) { return ((uint64_t)S[rows[r] * sst + p] << 32) | (uint32_t)~p; },
+                  [&](int r, int p) {
+                      const uint32_t v = S[rows[r] * sst + p];
+                      return ((uint64_t)(RAW ? score_bits(__uint_as_float(v)) : v) << 32) | (uint32_t)~p;
+                  },
                   scratch, keys, ib);
 }
 

@@ -32,7 +32,7 @@ constexpr int kXcds = 8;
 
 struct AddrLds {
     // byte offsets into dynamic LDS
-    size_t S, L, buf, cnt, scratch, stair, total;
+    size_t S, L, buf, scratch, stair, total;
     int sst;   // row stride of S in elements
 };
 
@@ -45,15 +45,18 @@ __host__ __device__ inline AddrLds addr_lds_layout(int n_sub, int kp)
     o.S = 0;                                                      // uint32 [16][sst]
     o.L = o.S + sizeof(uint32_t) * kTileRows * (size_t)o.sst;     // HalfEntry [2][16][kp]
     o.buf = o.L + sizeof(HalfEntry) * 2 * kTileRows * (size_t)kp; // uint32 [16][64] survivors
-    o.cnt = o.buf + sizeof(uint32_t) * kTileRows * 64;            // uint32 [16]
-    o.scratch = o.cnt + sizeof(uint32_t) * kTileRows;             // uint64 [4][64] (one-row routines)
+    o.scratch = o.buf + sizeof(uint32_t) * kTileRows * 64;        // uint64 [4][64] (one-row routines)
     o.stair = o.scratch + sizeof(uint64_t) * kAddrWaves * kWave;
     o.total = o.stair + sizeof(uint16_t) * kMaxStair;
     return o;
 }
 
-// NK: compile-time k-steps of the scoring tile (d_k = 64 * NK), 0 = any d_k
-template <bool BF16, int NK>
+// Codebook loads a wave issues together in the scoring (sub-key tiles).
+constexpr int kScoreNB = 4;
+
+// NK: compile-time k-steps of the scoring tile (d_k = 64 * NK), 0 = any d_k.
+// FULL: n_sub is a multiple of 16 * kScoreNB (no bounds checks in the scoring).
+template <bool BF16, int NK, bool FULL>
 __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, int ntiles)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -91,7 +94,6 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
     uint32_t *S = reinterpret_cast<uint32_t *>(smem + lay.S);
     HalfEntry *L = reinterpret_cast<HalfEntry *>(smem + lay.L);
     uint32_t *buf = reinterpret_cast<uint32_t *>(smem + lay.buf);
-    uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + lay.cnt);
     uint64_t *wscr = reinterpret_cast<uint64_t *>(smem + lay.scratch) + wave * kWave;
     uint16_t *stair = reinterpret_cast<uint16_t *>(smem + lay.stair);
 
@@ -104,23 +106,23 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
 
     load_staircase(K.stair, stair);   // ordered before use by the barriers below
     const int nstair = K.stair.count;
-    // the padding of every score row past n_sub holds score bits 0 (below
-    // every real score; the scoring never writes it); counters start at 0
+    // the padding of every score row past n_sub holds -inf (below every real
+    // score; the scoring never writes it)
     {
         const int padw = sst - n_sub;
         for (int e = threadIdx.x; e < kTileRows * padw; e += blockDim.x)
-            S[(e / padw) * sst + n_sub + e % padw] = 0u;
-        if (threadIdx.x < kTileRows) cnt[threadIdx.x] = 0u;
+            S[(e / padw) * sst + n_sub + e % padw] = 0xFF800000u;
     }
 
     // rows of this wave: wave + 4 g for lane group g
     const int row_g = wave + kAddrWaves * g;
-    const RowBuf rb{buf + wave * kAddrWaves * 64, cnt + wave * kAddrWaves};
+    const RowBuf rb{buf + wave * kAddrWaves * 64};
 
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        score_half_tile<BF16, 1, NK>(xb, row_stride, nrows, kTileRows,
-                                     Cb + (int64_t)c * n_sub * half * esz, c, half, n_sub, S, sst);
+        score_half_tile<BF16, kScoreNB, NK, true, FULL>(xb, row_stride, nrows, kTileRows,
+                                                       Cb + (int64_t)c * n_sub * half * esz, c, half, n_sub, S,
+                                                       sst);
         __syncthreads();
         const bool bad = half_topk16(S, sst, row_g, n_sub, kp, rb, L + (c * kTileRows + row_g) * kp);
         // rows the fast path could not vouch for: the exact one-row routine
@@ -129,7 +131,7 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
             if ((bb >> (16 * gg)) & 0xFFFFull) {
                 const int rows1[1] = {wave + kAddrWaves * gg};
                 uint64_t keys[1];
-                half_topk<1>(S, rows1, n_sub, kp, wscr, keys, sst);
+                half_topk<1, true>(S, rows1, n_sub, kp, wscr, keys, sst);
                 if (lane < kp) {
                     HalfEntry e;
                     e.score = __float_as_uint(key_score(keys[0]));
@@ -190,12 +192,13 @@ hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t st
         return hipSuccess;
     };
     hipError_t e;
+    const bool full = args.n_sub % (16 * kScoreNB) == 0;
     if (!bf16)
-        e = launch(pkm_score_topk_kernel<false, 0>);
+        e = launch(pkm_score_topk_kernel<false, 0, false>);
     else if (args.d_k == 128)
-        e = launch(pkm_score_topk_kernel<true, 2>);
+        e = full ? launch(pkm_score_topk_kernel<true, 2, true>) : launch(pkm_score_topk_kernel<true, 2, false>);
     else
-        e = launch(pkm_score_topk_kernel<true, 0>);
+        e = full ? launch(pkm_score_topk_kernel<true, 0, true>) : launch(pkm_score_topk_kernel<true, 0, false>);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

@@ -108,13 +108,35 @@ __device__ __forceinline__ void sort64_desc(uint32_t (&x)[4])
     cmpx_stage<63>(x); cmpx_stage<16>(x); cmpx_stage<8>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
 }
 
+// The value lane 16 g + c0 (c0 uniform) holds, in every lane of row group g
+// (four readlanes and a select: no LDS round trip).
+__device__ __forceinline__ uint32_t row_lane_value(uint32_t v, int c0)
+{
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_readlane((int)v, c0);
+    const uint32_t v1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16 + c0);
+    const uint32_t v2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32 + c0);
+    const uint32_t v3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48 + c0);
+    const int g = lane_id() >> 4;
+    return g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+}
+
 // The element of rank j (uniform) of a sorted row list, in every lane of the row.
 __device__ __forceinline__ uint32_t rank_value(const uint32_t (&x)[4], int j)
 {
     const int r = j & 3;
     const uint32_t v = r == 0 ? x[0] : r == 1 ? x[1] : r == 2 ? x[2] : x[3];
-    const int src = (lane_id() & ~(kGroupLanes - 1)) + (j >> 2);
-    return (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)v);
+    return row_lane_value(v, j >> 2);
+}
+
+// Inclusive prefix sum over the 16 lanes of each row group (DPP row_shr with
+// zero fill).
+__device__ __forceinline__ uint32_t row_inclusive_sum(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    return x;
 }
 
 // The next element of the sorted row list (rank 4c + r + 1); lane 15's last
@@ -137,6 +159,12 @@ __device__ __forceinline__ uint32_t group_max16(uint32_t x)
     return x;
 }
 
+// Raw fp32 bits of order-preserving score bits (inverse of score_bits).
+__device__ __forceinline__ uint32_t raw_of_score_bits(uint32_t u)
+{
+    return (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+}
+
 // Shift that fits (score bits - tau) >> sh, plus one, below 2^(32 - ib).
 __device__ __forceinline__ uint32_t key_shift(uint32_t span, int ib)
 {
@@ -145,23 +173,22 @@ __device__ __forceinline__ uint32_t key_shift(uint32_t span, int ib)
     return bl > lim ? (uint32_t)(bl - lim) : 0u;
 }
 
-// m = (m << 1) | (x >= t): one compare into VCC and one add with carry.
-__device__ __forceinline__ void push_ge(uint32_t &m, uint32_t x, uint32_t t)
+// m = (m << 1) | (x >= t) for fp32 x, t (-0 equals +0; no NaNs): one
+// compare into VCC and one add with carry.
+__device__ __forceinline__ void push_ge_f32(uint32_t &m, float x, float t)
 {
-    asm volatile("v_cmp_ge_u32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(m) : "v"(x), "v"(t) : "vcc");
+    asm volatile("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(m) : "v"(x), "v"(t) : "vcc");
 }
 
-// Per-row survivor buffers of a wave: 4 rows x 64 entries, 4 counters.
+// Per-row survivor buffers of a wave: 4 rows x 64 entries.
 struct RowBuf {
     uint32_t *buf;   // [4][64]
-    uint32_t *cnt;   // [4]
 };
 
 // Compacts the candidates of this lane whose bit is set in mask[] into the
-// row's buffer (the order of the entries is not fixed; every use sorts
-// them).  pos_of(q) maps mask bit q to the stored value.  Returns the row's
-// survivor count (all lanes of the row).  The counter is zero on entry; the
-// caller re-zeroes it after use.
+// row's buffer, lanes in order (a prefix sum of the lanes' counts over the
+// row group).  pos_of(q) maps mask bit q to the stored value.  Returns the
+// row's survivor count (all lanes of the row); entries past 64 are dropped.
 template <int NMW, class PosOf>
 __device__ __forceinline__ uint32_t compact_row(const uint32_t (&mask)[NMW], RowBuf rb, PosOf pos_of)
 {
@@ -169,7 +196,8 @@ __device__ __forceinline__ uint32_t compact_row(const uint32_t (&mask)[NMW], Row
     uint32_t n = 0;
 #pragma unroll
     for (int w = 0; w < NMW; ++w) n += __popc(mask[w]);
-    uint32_t pos = n ? atomicAdd(&rb.cnt[g], n) : 0u;
+    const uint32_t incl = row_inclusive_sum(n);
+    uint32_t pos = incl - n;
 #pragma unroll
     for (int w = 0; w < NMW; ++w) {
         uint32_t m = mask[w];
@@ -181,37 +209,38 @@ __device__ __forceinline__ uint32_t compact_row(const uint32_t (&mask)[NMW], Row
         }
     }
     wave_lds_sync();
-    return rb.cnt[g];
-}
-
-// Raw fp32 bits of order-preserving score bits (inverse of score_bits).
-__device__ __forceinline__ uint32_t raw_of_score_bits(uint32_t u)
-{
-    return (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+    return row_lane_value(incl, 15);
 }
 
 // Top-k' of one half for the 4 rows of this wave (row of lane group g =
-// row_g): S holds the row's score bits at S + row_g * sst, zero from n_sub
-// up to the next multiple of 64.  Lane j < k' of the row's list is written
-// to Lrow[j] (best first).  Returns true if this lane's row must be redone
-// by the exact one-row routine.
+// row_g): S holds the row's raw fp32 scores at S + row_g * sst, -inf from
+// n_sub up to the next multiple of 64.  Lane j < k' of the row's list is
+// written to Lrow[j] (best first).  Returns true if this lane's row must be
+// redone by the exact one-row routine.  Scores are compared as floats while
+// scanning (the same order as score_bits for finite values) and as
+// score_bits in the sorts.
 __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_g, int n_sub, int kp, RowBuf rb,
                                             HalfEntry *Lrow)
 {
     const int c = lane_id() & (kGroupLanes - 1);
     const uint32_t *Sr = S + (size_t)row_g * sst;
     const int nch = (n_sub + 63) >> 6;   // 64 candidates of a row per chunk, 4 per lane
-    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    float mf[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     for (int i = 0; i < nch; ++i) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(Sr + 64 * i + 4 * c);
-        m[0] = v.x > m[0] ? v.x : m[0];
-        m[1] = v.y > m[1] ? v.y : m[1];
-        m[2] = v.z > m[2] ? v.z : m[2];
-        m[3] = v.w > m[3] ? v.w : m[3];
+        const float4 v = *reinterpret_cast<const float4 *>(Sr + 64 * i + 4 * c);
+        mf[0] = fmaxf(mf[0], v.x);
+        mf[1] = fmaxf(mf[1], v.y);
+        mf[2] = fmaxf(mf[2], v.z);
+        mf[3] = fmaxf(mf[3], v.w);
     }
+    // an all-padding group (-inf) maps below every finite score
+    uint32_t m[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = score_bits(mf[r]);
     sort64_desc(m);
     const uint32_t tau = rank_value(m, kp - 1);
     const uint32_t top = rank_value(m, 0);
+    const float tauf = __uint_as_float(raw_of_score_bits(tau));
     // candidates reaching tau: word w holds chunks 8w .. 8w + 7, candidate
     // (chunk i, k) at bit 31 - (4 (i - 8w) + k) (shifted in from the right
     // in order, then left-aligned)
@@ -224,11 +253,11 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
             for (int k8 = 0; k8 < 8; ++k8) {
                 const int i = 8 * w + k8;
                 if (i < nch) {   // uniform
-                    const uint4 v = *reinterpret_cast<const uint4 *>(Sr + 64 * i + 4 * c);
-                    push_ge(mw, v.x, tau);
-                    push_ge(mw, v.y, tau);
-                    push_ge(mw, v.z, tau);
-                    push_ge(mw, v.w, tau);
+                    const float4 v = *reinterpret_cast<const float4 *>(Sr + 64 * i + 4 * c);
+                    push_ge_f32(mw, v.x, tauf);
+                    push_ge_f32(mw, v.y, tauf);
+                    push_ge_f32(mw, v.z, tauf);
+                    push_ge_f32(mw, v.w, tauf);
                 }
             }
             const int pushed = 4 * min(8, nch - 8 * w);
@@ -251,11 +280,10 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
     for (int r = 0; r < 4; ++r) {
         const uint32_t j = (uint32_t)(4 * c + r);
         const uint32_t p = j < total ? ent[r] : 0u;
-        const uint32_t s = Sr[p];
+        const uint32_t s = score_bits(__uint_as_float(Sr[p]));
         key[r] = j < total ? ((((s - tau) >> sh) + 1u) << ib) | (imask - p) : 0u;
     }
-    wave_lds_sync();
-    if (c == 0) rb.cnt[g] = 0u;   // buffer free for the next selection
+    wave_lds_sync();   // the buffer is free for the next selection
     sort64_desc(key);
     // full scores of the sorted list, and the check of neighbouring pairs
     // whose shifted scores tie
@@ -263,7 +291,7 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         p[r] = imask - (key[r] & imask);
-        s[r] = key[r] ? Sr[p[r]] : 0u;
+        s[r] = key[r] ? score_bits(__uint_as_float(Sr[p[r]])) : 0u;
     }
     next_in_list(key, nk);
     next_in_list(s, ns);
@@ -339,7 +367,6 @@ __device__ __forceinline__ bool merge16(const HalfEntry *L0, const HalfEntry *L1
         key[r] = j < total ? ((((s - tau) >> sh) + 1u) << ib) | (imask - sp) : 0u;
     }
     wave_lds_sync();
-    if (c == 0) rb.cnt[g] = 0u;
     sort64_desc(key);
     uint32_t s[4], sl[4], nk[4], ns[4], nsl[4];
 #pragma unroll
