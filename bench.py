@@ -46,7 +46,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="long_context",
-                   choices=list(PREFILL_WORKLOADS) + ["decode", "gdn_1p4b", "train_small", "train_1p4b"])
+                   choices=list(PREFILL_WORKLOADS) + ["decode", "gdn_1p4b", "train_small", "train_1p4b",
+                                                      "row_traffic"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle baseline (0 disables it)")
@@ -455,6 +456,56 @@ def bench_train(args, sdm, synth, torch, name):
     print(json.dumps(result), flush=True)
 
 
+def bench_row_traffic(args, torch):
+    """What the MI355X delivers for the scan's memory-access pattern: the
+    random row-segment gathers (write rows and read rows) and the stores of
+    the write rows, in the scan's instruction form and workgroup layout, with
+    no arithmetic and no dependence between steps (libsdm_bench.so).  Run on
+    the long-context layer's table (16 chains of 2^20 rows of 512 bytes) with
+    the segment sizes the scan can use (32, 64, 128 bytes: 2, 4, 8 waves per
+    workgroup), and with the same bytes split over 4x the chains (4x the
+    workgroups) at 32 bytes.  Bytes per workgroup and step: 64 rows x 3 x
+    segment."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_memory_linear_pkm_amd", "libsdm_bench.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m sparse_memory_linear_pkm_amd.build`")
+    lib = ctypes.CDLL(path)
+    fn = lib.sdm_bench_row_traffic
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                   ctypes.c_uint32, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    row_bytes = 512
+    M = torch.zeros(16 * (1 << 20) * row_bytes // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    configs = [(16, 20, 32), (16, 20, 64), (16, 20, 128), (64, 18, 32), (256, 16, 32)]
+    steps = max(1024, args.steps * 1024)
+    out = []
+    for chains, lg, seg in configs:
+        wgs = chains * row_bytes // seg
+        nbytes = wgs * steps * 64 * 3 * seg
+        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, 1024, 1, stream.cuda_stream)
+        assert rc == 0, rc
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, steps, 7, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert rc == 0, rc
+        ms = e0.elapsed_time(e1)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append({"chains": chains, "rows_per_chain": 1 << lg, "segment_bytes": seg, "workgroups": wgs,
+                    "waves": wgs * seg // 16, "steps": steps, "bytes": nbytes, "ms": ms, "GB/s": gbs,
+                    "frac_of_hbm_peak": gbs / HBM_PEAK_GBS})
+    print(json.dumps({"metric": "scan access-pattern bandwidth (random row-segment gathers and stores, no arithmetic)",
+                      "unit": "GB/s", "n_gpus": 1, "peak": HBM_PEAK_GBS, "data": "synthetic",
+                      "config": {"workload": "row_traffic", "row_bytes": row_bytes,
+                                 "per_step": "64 write-row and 64 read-row segments gathered, 64 stored"},
+                      "results": out}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -482,6 +533,9 @@ def main():
         return
 
     name = args.workload
+    if name == "row_traffic":
+        bench_row_traffic(args, torch)
+        return
     if name == "gdn_1p4b":
         bench_gdn(args, sdm, synth, torch)
         return
