@@ -36,8 +36,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 
 PREFILL_WORKLOADS = ("tiny", "small", "prefill_1p4b", "long_context")
-KERNEL_SOURCES = ("sdm_scan.hip", "sdm_scan_lanes.hip", "scan_prep.hip", "scan_lanes.h", "device_common.h",
-                  "kernels.h")
+KERNEL_SOURCES = ("sdm_scan.hip", "sdm_scan_lanes.hip", "scan_prep.hip", "scan_lanes.h", "lanes_common.h",
+                  "device_common.h", "kernels.h")
 
 
 def parse():
@@ -58,7 +58,8 @@ def parse():
 
 
 # sources of the scan's backward (its counter summaries carry their hash)
-BACKWARD_SOURCES = ("sdm_scan_backward.hip", "scan_lanes.h", "device_common.h", "kernels.h")
+BACKWARD_SOURCES = ("sdm_scan_bwd_lanes.hip", "sdm_scan_backward.hip", "scan_lanes.h", "lanes_common.h",
+                    "device_common.h", "kernels.h")
 
 
 def scan_source_hash(files=KERNEL_SOURCES) -> str:
@@ -373,6 +374,8 @@ def bench_train(args, sdm, synth, torch, name):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     aws_bytes = sdm.sdm_address_backward_workspace_size(dims)
     aws = torch.empty(max(aws_bytes, 1), dtype=torch.uint8, device="cuda")
+    bws_bytes = sdm.sdm_scan_backward_workspace_size(dims)
+    bws = torch.empty(max(bws_bytes, 1), dtype=torch.uint8, device="cuda")
     nws_bytes = sdm.sdm_output_norm_gate_backward_workspace_size(dims)
     nws = torch.empty(max(nws_bytes, 1), dtype=torch.uint8, device="cuda")
     gws_bytes = sdm.sdm_gates_backward_workspace_size(dims)
@@ -401,7 +404,8 @@ def bench_train(args, sdm, synth, torch, name):
         sdm.sdm_output_norm_gate_backward(o, ex["g"], ex["gamma"], eps, dy, dims, do, dg, dgamma, nws, nws_bytes,
                                           stream)
         ev[4].record(stream)
-        sdm.sdm_scan_backward(dM, widx, wwt, ridx, rwt, dx["v"], a, b, do, xs, zs, *grads, dims, stream)
+        sdm.sdm_scan_backward(dM, widx, wwt, ridx, rwt, dx["v"], a, b, do, xs, zs, *grads, bws, bws_bytes, dims,
+                              stream)
         ev[5].record(stream)
         # the codebook is shared by both kinds: one gradient buffer receives both sums
         sdm.sdm_address_backward(dx["k"], dx["q"], dx["C_w"], dx["C_r"], widx, wwt, ridx, rwt, grads[3], grads[4],

@@ -176,6 +176,17 @@ sdm_status sdm_scan_forward_save(float *M, const int32_t *widx, const float *wwt
                                  size_t workspace_bytes, const sdm_dims *dims, sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * sdm_scan_backward_workspace_size -- bytes of device workspace
+ * sdm_scan_backward needs for these dims (uses B, T, H, W, R, d_v,
+ * in_dtype).  0 when the dims are invalid, or when they fall outside the
+ * lane-parallel backward (one (sequence, head) of its streams, of xsave or
+ * of the per-chunk partial sums would reach 2 GiB, or T * H * d_v * 4 does):
+ * sdm_scan_backward then runs its token-serial kernels, which take no
+ * workspace.  Host-only.
+ * ------------------------------------------------------------------------- */
+size_t sdm_scan_backward_workspace_size(const sdm_dims *dims);
+
+/* ---------------------------------------------------------------------------
  * sdm_scan_backward -- reverse-mode gradients of sdm_scan_forward ([P]
  * Sec. 3.1 steps 2-3, Eq. 4, differentiated; the pages print no backward
  * pass).  For a loss L with dL/do_t = dout [B,T,H,d_v] fp32 and dL/dM after
@@ -194,14 +205,21 @@ sdm_status sdm_scan_forward_save(float *M, const int32_t *widx, const float *wwt
  * adds its r_i do to G (the positions are merged, their weights summed in
  * list order).  Write slots of one token must be distinct, as in the
  * forward.  fp32 arithmetic, every sum in a fixed order (deterministic).
- * Uses B, T, H, n_sub, d_v (<= 256), W, R, in_dtype.  dM and the outputs
- * must not overlap each other or any input (SDM_ERR_INVALID_ARG).
+ * Uses B, T, H, n_sub, d_v (<= 256), W, R, in_dtype.
+ * workspace: at least sdm_scan_backward_workspace_size(dims) bytes, 16-byte
+ * aligned, owned by the caller; it holds the forwarding codes and repacked
+ * inputs of the lane-parallel pass and its per-chunk partial sums, and is
+ * overwritten.  workspace = NULL with workspace_bytes = 0 selects the
+ * token-serial kernels, which need none (same results up to the order of
+ * fp32 sums; slower: one token of a chain at a time), for callers that
+ * cannot provide it.  dM, the outputs and the workspace must not overlap
+ * each other or any input (SDM_ERR_INVALID_ARG).
  * ------------------------------------------------------------------------- */
 sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, const int32_t *ridx,
                              const float *rwt, const void *v, const float *a, const float *b,
                              const float *dout, const float *xsave, const float *zsave, float *dv,
-                             float *da, float *db, float *dw, float *dr, const sdm_dims *dims,
-                             sdm_stream_t stream);
+                             float *da, float *db, float *dw, float *dr, void *workspace,
+                             size_t workspace_bytes, const sdm_dims *dims, sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * sdm_address_backward_workspace_size -- bytes of device workspace

@@ -58,7 +58,7 @@ def load_library():
         "sdm_gdn_dense_forward": [P, P, P, P, P, P, P, D, P],
         "sdm_scan_forward_save": [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
         "sdm_scan_forward_noalloc": [P, P, P, P, P, P, P, P, P, D, P],
-        "sdm_scan_backward": [P] * 16 + [D, P],
+        "sdm_scan_backward": [P] * 17 + [ctypes.c_size_t, D, P],
         "sdm_address_backward": [P] * 10 + [D, P, P, P, P, P, ctypes.c_size_t, P],
         "sdm_gates_backward": [P] * 6 + [D, P, P, P, P, P, ctypes.c_size_t, P],
         "sdm_cow_reset": [P, D, P],
@@ -74,6 +74,8 @@ def load_library():
     lib.sdm_cow_bitmap_bytes.restype = ctypes.c_size_t
     lib.sdm_scan_workspace_size.argtypes = [D]
     lib.sdm_scan_workspace_size.restype = ctypes.c_size_t
+    lib.sdm_scan_backward_workspace_size.argtypes = [D]
+    lib.sdm_scan_backward_workspace_size.restype = ctypes.c_size_t
     lib.sdm_address_backward_workspace_size.argtypes = [D]
     lib.sdm_address_backward_workspace_size.restype = ctypes.c_size_t
     lib.sdm_gates_backward_workspace_size.argtypes = [D]
@@ -277,11 +279,16 @@ def sdm_scan_forward_save(M, widx, wwt, ridx, rwt, v, a, b, o, xsave, zsave, wor
     return st
 
 
-def sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr, dims: SdmDims,
-                      stream=None, *, check: bool = True) -> int:
+def sdm_scan_backward_workspace_size(dims: SdmDims) -> int:
+    return int(load_library().sdm_scan_backward_workspace_size(ctypes.byref(dims)))
+
+
+def sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr, workspace,
+                      workspace_bytes: int, dims: SdmDims, stream=None, *, check: bool = True) -> int:
     st = load_library().sdm_scan_backward(_ptr(dM), _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _ptr(v), _ptr(a),
                                           _ptr(b), _ptr(dout), _ptr(xsave), _ptr(zsave), _ptr(dv), _ptr(da),
-                                          _ptr(db), _ptr(dw), _ptr(dr), ctypes.byref(dims), _stream(stream))
+                                          _ptr(db), _ptr(dw), _ptr(dr), _ptr(workspace), int(workspace_bytes),
+                                          ctypes.byref(dims), _stream(stream))
     if check:
         _check(st, "sdm_scan_backward")
     return st
@@ -491,9 +498,11 @@ def scan_forward_save(M, widx, wwt, ridx, rwt, v, a, b, dims: SdmDims, o=None, w
     return o, xsave, zsave
 
 
-def scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dims: SdmDims, stream=None):
+def scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dims: SdmDims, workspace=None,
+                  stream=None):
     """Gradients of the scan; dM is updated in place (dL/dM after -> before the
-    call).  Returns (dv, da, db, dw, dr)."""
+    call).  Returns (dv, da, db, dw, dr).  The workspace is allocated here if
+    None and the dims need one."""
     import torch
     B, T, H = dims.B, dims.T, dims.H
     dev = dM.device
@@ -505,7 +514,12 @@ def scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dims: S
     db = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     dw = torch.empty((B, T, H, dims.W), dtype=torch.float32, device=dev)
     dr = torch.empty((B, T, H, dims.R), dtype=torch.float32, device=dev)
-    sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr, dims, stream)
+    need = sdm_scan_backward_workspace_size(dims)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sdm_scan_backward(dM, widx, wwt, ridx, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr, workspace, ws_bytes,
+                      dims, stream)
     return dv, da, db, dw, dr
 
 

@@ -177,6 +177,12 @@ AddrBwdLayout address_bwd_layout(int64_t BT, int64_t H, int W, int R, int n_sub,
 size_t address_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int n_sub, int half);
 hipError_t launch_address_backward(const AddrBwdArgs &args, bool bf16, void *workspace, hipStream_t stream);
 hipError_t launch_scan_backward(const BwdArgs &args, bool bf16, hipStream_t stream);
+
+// The lane-parallel backward of the scan (sdm_scan_bwd_lanes.hip): its
+// workspace (0 when the shape is outside that path; the token-serial kernels
+// of sdm_scan_backward.hip then run without one) and its launch.
+size_t scan_bwd_workspace_bytes(int64_t B, int64_t T, int64_t H, int W, int R, int d_v, bool bf16);
+hipError_t launch_scan_backward_lanes(const BwdArgs &args, bool bf16, void *workspace, hipStream_t stream);
 hipError_t launch_gdn_dense(const GdnArgs &args, bool bf16, hipStream_t stream);
 struct GateBwdArgs {
     const float *a_raw, *b_raw, *A, *dt_bias, *da, *db;

@@ -609,10 +609,19 @@ sdm_status sdm_gdn_dense_forward(float *S, const void *k, const void *q, const v
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_gdn_dense_forward launch");
 }
 
+size_t sdm_scan_backward_workspace_size(const sdm_dims *d)
+{
+    if (!d || d->B < 0 || d->T < 0 || d->H < 1 || d->W < 1 || d->R < 1 || d->W > kMaxList || d->R > kMaxList ||
+        d->d_v < 32 || d->d_v % 32 != 0 || d->d_v > 256 || (d->in_dtype != SDM_F32 && d->in_dtype != SDM_BF16))
+        return 0;
+    return sdm::scan_bwd_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v,
+                                         d->in_dtype == SDM_BF16);
+}
+
 sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, const int32_t *ridx, const float *rwt,
                              const void *v, const float *a, const float *b, const float *dout, const float *xsave,
                              const float *zsave, float *dv, float *da, float *db, float *dw, float *dr,
-                             const sdm_dims *d, sdm_stream_t stream)
+                             void *workspace, size_t workspace_bytes, const sdm_dims *d, sdm_stream_t stream)
 {
     sdm_status st = check_memory_dims(d);
     if (st != SDM_OK) return st;
@@ -656,9 +665,28 @@ sdm_status sdm_scan_backward(float *dM, const int32_t *widx, const float *wwt, c
             if (overlap(optr[i], outs[i], iptr[j], isz[j]))
                 return fail(SDM_ERR_INVALID_ARG, "a gradient output overlaps an input");
     }
+    const bool bf16 = d->in_dtype == SDM_BF16;
+    // no workspace at all: the token-serial kernels (no workspace needed)
+    const size_t need = (!workspace && workspace_bytes == 0)
+                            ? 0
+                            : sdm::scan_bwd_workspace_bytes(d->B, d->T, d->H, (int)d->W, (int)d->R, (int)d->d_v, bf16);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(SDM_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+        if (!aligned(workspace, 16)) return fail(SDM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        // the workspace is written while the inputs are read and the outputs written
+        if (overlap(workspace, need, dM, msz)) return fail(SDM_ERR_INVALID_ARG, "the workspace overlaps dM");
+        for (int i = 0; i < 5; ++i)
+            if (overlap(workspace, need, optr[i], outs[i]))
+                return fail(SDM_ERR_INVALID_ARG, "the workspace overlaps a gradient output");
+        for (int j = 0; j < 10; ++j)
+            if (overlap(workspace, need, iptr[j], isz[j]))
+                return fail(SDM_ERR_INVALID_ARG, "the workspace overlaps an input");
+    }
     sdm::BwdArgs A{dM, widx, ridx, wwt, rwt, v, a, b, dout, xsave, zsave, dv, da, db, dw, dr,
                    d->B, d->T, (int)d->H, (int)N, (int)d->d_v, (int)d->W, (int)d->R};
-    hipError_t e = sdm::launch_scan_backward(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    hipError_t e = need > 0 ? sdm::launch_scan_backward_lanes(A, bf16, workspace, as_stream(stream))
+                            : sdm::launch_scan_backward(A, bf16, as_stream(stream));
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan_backward launch");
 }
 

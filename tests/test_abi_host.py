@@ -217,10 +217,12 @@ def test_gdn_rejects_bad_arguments():
 
 def test_scan_backward_rejects_bad_arguments():
     def call(dims, **ptrs):
-        names = ("dM", "widx", "wwt", "ridx", "rwt", "v", "a", "b", "dout", "xs", "zs", "dv", "da", "db", "dw", "dr")
+        names = ("dM", "widx", "wwt", "ridx", "rwt", "v", "a", "b", "dout", "xs", "zs", "dv", "da", "db", "dw", "dr",
+                 "ws")
         p = {n: FAKE + (i << 30) for i, n in enumerate(names)}
+        ws_bytes = ptrs.pop("ws_bytes", 1 << 29)
         p.update(ptrs)
-        return sdm.sdm_scan_backward(*(p[n] for n in names), dims, stream=0, check=False)
+        return sdm.sdm_scan_backward(*(p[n] for n in names), ws_bytes, dims, stream=0, check=False)
     assert call(good_dims(d_v=512)) == sdm.SDM_ERR_UNSUPPORTED
     assert call(good_dims(W=65, k_prime=16)) == sdm.SDM_ERR_UNSUPPORTED
     assert call(good_dims(W=0)) == sdm.SDM_ERR_INVALID_ARG
@@ -232,6 +234,18 @@ def test_scan_backward_rejects_bad_arguments():
     assert call(good_dims(), dw=FAKE + (9 << 30) + 64) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(), dM=FAKE + (8 << 30)) == sdm.SDM_ERR_INVALID_ARG
     assert call(good_dims(T=0), dM=None) == sdm.SDM_OK
+    # the lane-parallel path's workspace: its size, too small, misaligned, over dM, an output or an input
+    need = sdm.sdm_scan_backward_workspace_size(good_dims())
+    assert need > 0
+    assert call(good_dims(), ws_bytes=need - 1) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws=None, ws_bytes=need) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws=FAKE + (16 << 30) + 4) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ws=FAKE + 64) == sdm.SDM_ERR_INVALID_ARG            # over dM
+    assert call(good_dims(), ws=FAKE + (14 << 30)) == sdm.SDM_ERR_INVALID_ARG    # over dw
+    assert call(good_dims(), ws=FAKE + (9 << 30)) == sdm.SDM_ERR_INVALID_ARG     # over xsave
+    # beyond the lane-parallel path's 2 GiB ranges the size is 0 (token-serial kernels)
+    assert sdm.sdm_scan_backward_workspace_size(good_dims(T=1 << 22)) == 0
+    assert sdm.sdm_scan_backward_workspace_size(good_dims(d_v=512)) == 0
 
 
 def test_scan_noalloc_rejects_beyond_scratch_on_the_host():

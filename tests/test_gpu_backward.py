@@ -4,7 +4,9 @@ the saved rows.
 
 Bar: every gradient (dM, dv, da, db, dw, dr) within 2e-3 x RMS of the
 oracle's, the scan's own bar; the forward with saving is bit-identical to
-the forward without.
+the forward without.  Both backward paths are checked: the lane-parallel one
+(with a workspace, what the training step runs) and the token-serial one
+(no workspace); the lane-parallel one gives the same bits on a second run.
 """
 import numpy as np
 import pytest
@@ -40,7 +42,20 @@ def close_rms(got, ref, what, bar=2e-3):
     assert err <= bar * scale, f"{what}: max error {err:.3g} > {bar} x RMS {scale:.3g}"
 
 
-def run_case(sdm, torch, d, x, ad, seed):
+def serial_backward(sdm, dM, ad_dev, v, a, b, dout, xs, zs, dims, d, torch):
+    """sdm_scan_backward without a workspace: the token-serial kernels."""
+    dev = dM.device
+    dv = torch.empty((d.B, d.T, d.H, d.d_v), dtype=torch.float32, device=dev)
+    da = torch.empty((d.B, d.T, d.H), dtype=torch.float32, device=dev)
+    db = torch.empty_like(da)
+    dw = torch.empty((d.B, d.T, d.H, d.W), dtype=torch.float32, device=dev)
+    dr = torch.empty((d.B, d.T, d.H, d.R), dtype=torch.float32, device=dev)
+    sdm.sdm_scan_backward(dM, ad_dev["widx"], ad_dev["wwt"], ad_dev["ridx"], ad_dev["rwt"], v, a, b, dout, xs, zs,
+                          dv, da, db, dw, dr, None, 0, dims)
+    return dv, da, db, dw, dr
+
+
+def run_case(sdm, torch, d, x, ad, seed, serial=True):
     dims = sdm.dims_from(d)
     rng = np.random.default_rng(seed)
     M0 = np.repeat(x["M0"][None], d.B, axis=0).copy()
@@ -55,9 +70,20 @@ def run_case(sdm, torch, d, x, ad, seed):
     o2 = sdm.scan_forward(M2, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]), to_dev(x["a"]),
                           to_dev(x["b"]), dims)
     dM = to_dev(dMT)
-    dv, da, db, dw, dr = sdm.scan_backward(dM, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]),
-                                           to_dev(x["a"]), to_dev(x["b"]), to_dev(dout), xs, zs, dims)
+    note(f"lane-parallel backward, workspace {sdm.sdm_scan_backward_workspace_size(dims)} bytes")
+    assert sdm.sdm_scan_backward_workspace_size(dims) > 0
+    grads = sdm.scan_backward(dM, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]),
+                              to_dev(x["a"]), to_dev(x["b"]), to_dev(dout), xs, zs, dims)
     torch.cuda.synchronize()
+    # a second run gives the same bits (every sum in a fixed order)
+    dM2 = to_dev(dMT)
+    grads2 = sdm.scan_backward(dM2, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]),
+                               to_dev(x["a"]), to_dev(x["b"]), to_dev(dout), xs, zs, dims)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dM), to_host(dM2))
+    for g1, g2 in zip(grads, grads2):
+        assert np.array_equal(to_host(g1), to_host(g2))
+    dv, da, db, dw, dr = grads
     assert np.array_equal(to_host(o), to_host(o2)) and np.array_equal(to_host(M), to_host(M2))
     # o is the read weights applied to the saved read rows
     zh = to_host(zs)                                     # [B,H,T,d_v/4,R,4]
@@ -68,6 +94,14 @@ def run_case(sdm, torch, d, x, ad, seed):
                              dM_final=dMT)
     for name, got in (("dM", dM), ("dv", dv), ("da", da), ("db", db), ("dw", dw), ("dr", dr)):
         close_rms(to_host(got), g[name], name)
+    if serial:
+        note("token-serial backward")
+        dM3 = to_dev(dMT)
+        s = serial_backward(sdm, dM3, dev, to_dev(x["v"]), to_dev(x["a"]), to_dev(x["b"]), to_dev(dout), xs, zs,
+                            dims, d, torch)
+        torch.cuda.synchronize()
+        for name, got in zip(("dM", "dv", "da", "db", "dw", "dr"), (dM3, *s)):
+            close_rms(to_host(got), g[name], name + " (token-serial)")
 
 
 CASES = {
@@ -77,6 +111,10 @@ CASES = {
     "bf16_dv96_W4_R12": (Dims(B=2, T=33, H=2, d_k=128, n_sub=8, d_v=96, k_prime=8, W=4, R=12), 16),
     "bf16_dv256_W64_R1": (Dims(B=1, T=20, H=2, d_k=128, n_sub=16, d_v=256, k_prime=16, W=64, R=1), 100),
     "T1": (Dims(B=5, T=1, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=16, R=16), None),
+    # Q = 4 (16 sub-tokens, 8 tokens per step of the lane-parallel pass), ragged T
+    "f32_dv32_W3_R4": (Dims(B=2, T=77, H=1, d_k=32, n_sub=8, d_v=32, k_prime=8, W=3, R=4, in_dtype="f32"), 12),
+    # Q = 64 (one sub-token per step), W < R
+    "bf16_dv64_W20_R40": (Dims(B=1, T=41, H=2, d_k=128, n_sub=16, d_v=64, k_prime=16, W=20, R=40), 90),
 }
 
 
@@ -107,6 +145,34 @@ def test_scan_backward_repeated_read_slots(sdm, torch):
         r[:, 0::5, :, d.R - 1] = r[:, 0::5, :, 0]
         assert any(len(set(r[b, t, h])) < d.R for b in range(d.B) for t in range(d.T) for h in range(d.H))
         run_case(sdm, torch, d, x, ad, seed=5)
+
+
+@pytest.mark.parametrize("d", [
+    Dims(B=2, T=70, H=2, d_k=128, n_sub=16, d_v=64, k_prime=8, W=16, R=16),             # Q = 16: 2 tokens per step
+    Dims(B=1, T=60, H=2, d_k=128, n_sub=32, d_v=128, k_prime=32, W=32, R=32),           # Q = 32: 1 token per step
+    Dims(B=2, T=50, H=1, d_k=32, n_sub=8, d_v=32, k_prime=4, W=4, R=4, in_dtype="f32"),  # Q = 4: 8 tokens per step
+], ids=["Q16", "Q32", "Q4"])
+def test_scan_backward_sub_token_dependencies(sdm, torch, d):
+    """Sub-tokens of one step of the lane-parallel backward that update the
+    same rows: every third token reads exactly the slots it writes (its write
+    part then takes the rows its read part just updated), every fourth reads
+    the slots the next token writes, every fifth writes the slots the
+    previous token reads (dependencies across the two tokens of a step and
+    across steps), the rest from a small pool."""
+    note(f"scan backward sub-token dependencies {d}")
+    x = synth.make_inputs(d, seed=41)
+    ad = synth.random_addressing(d, seed=41, hazard_slots=3 * max(d.W, d.R))
+    w, r = ad["widx"], ad["ridx"]
+    n = min(d.W, d.R)
+    r[:, 0::3, :, :n] = w[:, 0::3, :, :n]
+    r[:, 0:-1:4, :, :n] = w[:, 1::4, :, :n][:, :r[:, 0:-1:4].shape[1]]
+    w[:, 5::5, :, :n] = r[:, 4:-1:5, :, :n][:, :w[:, 5::5].shape[1]]
+    # write slots of one token stay distinct
+    for bb in range(d.B):
+        for t in range(d.T):
+            for h in range(d.H):
+                assert len(set(w[bb, t, h])) == d.W
+    run_case(sdm, torch, d, x, ad, seed=6)
 
 
 def test_scan_backward_with_pkm_addressing(sdm, torch):

@@ -126,6 +126,8 @@ def test_graph_capture_training_step_and_layer_edges(sdm, torch):
     gws = T.empty(max(gws_bytes, 1), dtype=T.uint8, device="cuda")
     aws_bytes = sdm.sdm_address_backward_workspace_size(dims)
     aws = T.empty(max(aws_bytes, 1), dtype=T.uint8, device="cuda")
+    bws_bytes = sdm.sdm_scan_backward_workspace_size(dims)
+    bws = T.empty(max(bws_bytes, 1), dtype=T.uint8, device="cuda")
     kx, qx, Cw = to_dev(x["k"]), to_dev(x["q"]), to_dev(x["C_w"])
     dk = T.empty((d.B, d.T, d.H, d.d_k), dtype=T.float32, device="cuda")
     dq = T.empty_like(dk)
@@ -138,7 +140,7 @@ def test_graph_capture_training_step_and_layer_edges(sdm, torch):
         sdm.sdm_scan_forward_save(M, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], xv, a_g, b_g, o, xs, zs, ws,
                                   ws_bytes, dims)
         sdm.sdm_scan_backward(dM, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], xv, a_g, b_g, dout, xs, zs,
-                              *grads, dims)
+                              *grads, bws, bws_bytes, dims)
         sdm.sdm_output_norm_gate(o, inp["g"], inp["gamma"], 1e-5, dims, y)
         sdm.sdm_output_norm_gate_backward(o, inp["g"], inp["gamma"], 1e-5, dout, dims, do_n, dg_n, dgamma, nws,
                                           nws_bytes)
