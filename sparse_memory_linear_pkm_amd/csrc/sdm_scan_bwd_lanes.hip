@@ -30,10 +30,12 @@
 //     LDS, takes rows updated in between from an LDS ring of the last 2D
 //     steps' rows, and runs sub-tokens of one step that depend on each other
 //     in rounds;
-//   - dw_j, da and db are sums over all d_v columns, held by many waves: each
-//     wave stores its chunk's partial sums per token and
-//     scan_bwd_reduce_kernel adds them over the chunks in a fixed order; it
-//     also forms dr_i = <do, Z_i> from the saved read rows.
+//   - dw_j, da and db are sums over all d_v columns, held by many waves:
+//     each wave stores its chunk's partial sums per token (with 8-wave
+//     workgroups, the waves first add their parts through LDS and the
+//     workgroup stores its row segment's), and scan_bwd_reduce_kernel adds
+//     them in a fixed order; it also forms dr_i = <do, Z_i> from the saved
+//     read rows.
 // A read slot listed at several positions of one token: its last position
 // carries the sum of their weights (in list order) and the earlier positions
 // are not stored, so G receives the term once.  Every sum has a fixed order:
@@ -58,7 +60,8 @@ struct BwdStreams {
     uint32_t *gofs;   // [chain][u][Q]: row byte offset + 2^30 (0: no row), bit 0 = superseded
     uint4 *tok;       // [chain][u][d_v/4][NTR]: read part {do chunk};
                       //   write part {a, v chunk, b} (bf16 v) or {a, b, 0, 0}{v chunk} (fp32 v)
-    float *part;      // [chain][T][d_v/4][Q + 2]: dw_j parts (j < W), then the da and db parts
+    float *part;      // [chain][T][nseg][Q + 2]: dw_j parts (j < W), then the da and db parts, per
+                      //   row segment (workgroup) when G = 8, else per 4-column chunk
 };
 
 struct BwdPrepArgs {
@@ -287,12 +290,18 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_bwd_lanes_kernel(BwdArgs A, B
     static_assert((D - 1) * NVM <= 63, "pipeline deeper than the vmcnt range");
     static_assert(G == 2 || G == 4 || G == 8, "2, 4 or 8 waves per workgroup");
     constexpr int RPW = kWave / G;               // rows of a step each wave moves
-    constexpr int PQ = Q + 2;                    // floats of a chunk's partial record
+    constexpr int PQ = Q + 2;                    // floats of a partial-sum record
+    // 8-wave workgroups add their waves' parts before storing them (an 8x
+    // smaller partial-sum stream); narrower ones, whose steps are shorter
+    // and latency-bound, store each wave's
+    constexpr bool RED = G == 8;
 
     // Row r of a step is sub-token r / Q, list position r % Q (r = the lane
     // of the compute layout).  Chunk c of row r sits at position (c + r) % G.
     __shared__ f32x4 gath[D][kWave][G];          // gathered rows of the steps in flight
     __shared__ f32x4 ring[2 * D][kWave][G];      // rows updated by the last 2D steps
+    __shared__ float red[RED ? G : 1][kWave];    // each wave's dw_j parts of the step (RED)
+    __shared__ float red2[RED ? G : 1][K][2];    // each wave's da, db parts per sub-token (RED)
 
     const uint32_t d_v = (uint32_t)A.d_v;
     const uint32_t nline = d_v / 32u;
@@ -328,8 +337,12 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_bwd_lanes_kernel(BwdArgs A, B
         make_rsrc(A.xsave + (size_t)ch * T * W * d_v, (uint32_t)((uint64_t)T * W * d_v * 4u));
     const __amdgpu_buffer_rsrc_t Vrs =
         make_rsrc(A.dv + (size_t)(bb * T * H + h) * d_v, (uint32_t)((uint64_t)((T - 1) * H + 1) * d_v * 4u));
-    const uint64_t pc = (uint64_t)T * nchunk * PQ;
+    const uint32_t nseg = RED ? nchunk / G : nchunk;        // partial-sum records per chain and token
+    const uint64_t pc = (uint64_t)T * nseg * PQ;
     const __amdgpu_buffer_rsrc_t Prs = make_rsrc(S.part + ch * pc, (uint32_t)(pc * 4u));
+    // the step's row whose dw_j parts this lane adds over the waves: row
+    // `rsum` (compute-layout lane) of wave lane % G
+    const int rsum = wave * (kWave / G) + lane / G;
     const int64_t nsteps = (U + K - 1) / K;
 
     // running byte offsets of the next loads: lane records and token records
@@ -406,6 +419,10 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_bwd_lanes_kernel(BwdArgs A, B
             const int64_t step = s0 + s;
             const int rs = (int)((uint64_t)step % (2 * D));
             wait_vmcnt<(D - 1) * NVM>();
+            // the step's records are used only from here on (otherwise the
+            // compiler may hoist their first use above the previous step's
+            // issue, with a wait tighter than the pipeline needs)
+            asm volatile("" : "+v"(lr[s].x), "+v"(lr[s].y), "+v"(xr[s]));
             const uint32_t code = ~lr[s].x;   // stored inverted: a load past the range reads "none"
             const float wj = __uint_as_float(lr[s].y);
             const uint32_t cw = code & 0x7FFFu;
@@ -484,8 +501,16 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_bwd_lanes_kernel(BwdArgs A, B
             const float dwp = __builtin_fmaf(bt, yu, dot4(dp, X));
             const float sa = group_sum1<Q>(dot4(yk, X)) - dot4(p, du);
             const float sb = group_sum1<Q>(wj * yu);
+            if constexpr (RED) {
+                red[wave][lane] = dwp;
+                if (j == 0) {
+                    red2[wave][i][0] = sa;
+                    red2[wave][i][1] = sb;
+                }
+            }
             // ---- stores: whole segments of the updated rows (every wave's
-            // chunks), this wave's chunk of dv and its partial sums ----
+            // chunks), this wave's chunk of dv, the segment's partial sums
+            // (the parts of its G waves added here) ----
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
@@ -493,16 +518,48 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_bwd_lanes_kernel(BwdArgs A, B
             {
                 const bool live = u < U && wpart;
                 const uint32_t t32 = (uint32_t)token_of(u < U ? u : U - 1);
-                const uint32_t rec = (t32 * nchunk + chunk) * (uint32_t)PQ;
                 const uint32_t ov = live && j == 0 ? t32 * (uint32_t)H * d_v * 4u + colb : kOOB;
-                const uint32_t ow = live && (uint32_t)j < W ? (rec + (uint32_t)j) * 4u : kOOB;
-                const uint32_t oab = live && j == 0 ? (rec + (uint32_t)Q) * 4u : kOOB;
                 __builtin_amdgcn_raw_buffer_store_b128(du, Vrs, ov, 0, 0);
                 // (the b32 and b64 forms take integer data: pass the bits)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dwp), Prs, ow, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    (uint32_t __attribute__((ext_vector_type(2)))){__float_as_uint(sa), __float_as_uint(sb)}, Prs, oab,
-                    0, 0);
+                if constexpr (!RED) {
+                    const uint32_t rec = (t32 * nseg + chunk) * (uint32_t)PQ;
+                    const uint32_t ow = live && (uint32_t)j < W ? (rec + (uint32_t)j) * 4u : kOOB;
+                    const uint32_t oab = live && j == 0 ? (rec + (uint32_t)Q) * 4u : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dwp), Prs, ow, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        (uint32_t __attribute__((ext_vector_type(2)))){__float_as_uint(sa), __float_as_uint(sb)}, Prs,
+                        oab, 0, 0);
+                } else {
+                    // dw_j of row rsum: the G waves' parts, added by a butterfly
+                    // over the G lanes that hold them
+                    float sdw = red[lane % G][rsum];
+                    sdw += __uint_as_float(lane_xor<1>(__float_as_uint(sdw)));
+                    if constexpr (G >= 4) sdw += __uint_as_float(lane_xor<2>(__float_as_uint(sdw)));
+                    if constexpr (G >= 8) sdw += __uint_as_float(lane_xor<4>(__float_as_uint(sdw)));
+                    const int64_t us = step * K + (rsum >> LQ);
+                    const uint32_t js = (uint32_t)(rsum & (Q - 1));
+                    const bool lw = us < U && (us & 1) && js < W && lane % G == 0;
+                    const uint32_t ts = (uint32_t)token_of(us < U ? us : U - 1);
+                    const uint32_t ow = lw ? ((ts * nseg + seg) * (uint32_t)PQ + js) * 4u : kOOB;
+                    // da, db of sub-token `lane` (wave 0, lanes < K): the waves' parts in order
+                    float ta = 0.f, tb = 0.f;
+                    const int il = lane < K ? lane : 0;
+                    if (wave == 0) {
+#pragma unroll
+                        for (int w = 0; w < G; ++w) {
+                            ta += red2[w][il][0];
+                            tb += red2[w][il][1];
+                        }
+                    }
+                    const int64_t ua = step * K + il;
+                    const bool la = wave == 0 && lane < K && ua < U && (ua & 1);
+                    const uint32_t ta32 = (uint32_t)token_of(ua < U ? ua : U - 1);
+                    const uint32_t oab = la ? ((ta32 * nseg + seg) * (uint32_t)PQ + (uint32_t)Q) * 4u : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sdw), Prs, ow, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        (uint32_t __attribute__((ext_vector_type(2)))){__float_as_uint(ta), __float_as_uint(tb)}, Prs, oab,
+                        0, 0);
+                }
             }
             // ---- issue step + D ----
             gathers(s);
@@ -515,10 +572,10 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_bwd_lanes_kernel(BwdArgs A, B
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// dw_j, da, db: the chunks' partial sums added in chunk order; dr_i = <do,
-// Z_i> with the chunks' dot products added in chunk order.  One wave per
-// token-head row (b, t, h).
-__global__ void __launch_bounds__(256) scan_bwd_reduce_kernel(BwdArgs A, const float *part, int Q)
+// dw_j, da, db: the nseg partial-sum records of a token (per chunk or per
+// row segment) added in order; dr_i = <do, Z_i> with the chunks' dot
+// products added in chunk order.  One wave per token-head row (b, t, h).
+__global__ void __launch_bounds__(256) scan_bwd_reduce_kernel(BwdArgs A, const float *part, int Q, int nseg)
 {
     const int64_t rows = A.B * A.T * A.H;
     const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kWave;
@@ -529,11 +586,11 @@ __global__ void __launch_bounds__(256) scan_bwd_reduce_kernel(BwdArgs A, const f
     const int64_t t = rem / A.H, h = rem - t * A.H;
     const int64_t ch = bb * A.H + h;
     const int nchunk = A.d_v / 4, PQ = Q + 2;
-    const float *pp = part + (ch * A.T + t) * (int64_t)nchunk * PQ;
+    const float *pp = part + (ch * A.T + t) * (int64_t)nseg * PQ;
     for (int e = lane; e < PQ; e += kWave) {
         if (e < A.W || e == Q || e == Q + 1) {
             float s = 0.f;
-            for (int c = 0; c < nchunk; ++c) s += pp[c * PQ + e];
+            for (int c = 0; c < nseg; ++c) s += pp[c * PQ + e];
             if (e < A.W) A.dw[row * A.W + e] = s;
             else if (e == Q) A.da[row] = s;
             else A.db[row] = s;
@@ -567,28 +624,6 @@ struct BwdWsLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdWsLayout bwd_ws_layout(int64_t B, int64_t T, int64_t H, int W, int R, int d_v, bool bf16)
-{
-    const size_t chains = (size_t)(B * H), U = 2 * (size_t)T;
-    const size_t q = (size_t)bwd_lanes_q(W, R), nchunk = (size_t)d_v / 4;
-    BwdWsLayout L;
-    L.lane = 0;
-    L.gofs = L.lane + align256(chains * U * q * 8);
-    L.tok = L.gofs + align256(chains * U * q * 4);
-    L.part = L.tok + align256(chains * U * nchunk * (bf16 ? 16 : 32));
-    L.total = L.part + align256(chains * (size_t)T * nchunk * (q + 2) * 4);
-    return L;
-}
-
-// every per-chain range the lanes kernel addresses with 32-bit offsets
-bool bwd_lanes_fits(int64_t T, int64_t H, int W, int R, int d_v, bool bf16)
-{
-    const uint64_t lim = 1ull << 31, U = 2 * (uint64_t)T;
-    const uint64_t q = (uint64_t)bwd_lanes_q(W, R), nchunk = (uint64_t)d_v / 4;
-    return U * q * 8 < lim && U * nchunk * (bf16 ? 16 : 32) < lim && (uint64_t)T * W * d_v * 4 < lim &&
-           (uint64_t)T * H * d_v * 4 < lim && (uint64_t)T * nchunk * (q + 2) * 4 < lim;
-}
-
 struct BwdShape {
     int G, D;
 };
@@ -601,6 +636,30 @@ BwdShape bwd_lanes_shape(int64_t chunks)
     if (chunks / 8 >= kCUs) return {8, 4};
     if (chunks / 4 >= kCUs) return {4, 4};
     return {2, 4};
+}
+
+BwdWsLayout bwd_ws_layout(int64_t B, int64_t T, int64_t H, int W, int R, int d_v, bool bf16)
+{
+    const size_t chains = (size_t)(B * H), U = 2 * (size_t)T;
+    const size_t q = (size_t)bwd_lanes_q(W, R), nchunk = (size_t)d_v / 4;
+    const int G = bwd_lanes_shape(B * H * (d_v / 4)).G;
+    const size_t nseg = G == 8 ? nchunk / 8 : nchunk;   // the kernel's partial-sum records per token
+    BwdWsLayout L;
+    L.lane = 0;
+    L.gofs = L.lane + align256(chains * U * q * 8);
+    L.tok = L.gofs + align256(chains * U * q * 4);
+    L.part = L.tok + align256(chains * U * nchunk * (bf16 ? 16 : 32));
+    L.total = L.part + align256(chains * (size_t)T * nseg * (q + 2) * 4);
+    return L;
+}
+
+// every per-chain range the lanes kernel addresses with 32-bit offsets
+bool bwd_lanes_fits(int64_t T, int64_t H, int W, int R, int d_v, bool bf16)
+{
+    const uint64_t lim = 1ull << 31, U = 2 * (uint64_t)T;
+    const uint64_t q = (uint64_t)bwd_lanes_q(W, R), nchunk = (uint64_t)d_v / 4;
+    return U * q * 8 < lim && U * nchunk * (bf16 ? 16 : 32) < lim && (uint64_t)T * W * d_v * 4 < lim &&
+           (uint64_t)T * H * d_v * 4 < lim && (uint64_t)T * nchunk * (q + 2) * 4 < lim;
 }
 
 int bwd_hash_log2(int q, int window, int lookahead)
@@ -674,7 +733,8 @@ hipError_t launch_scan_backward_lanes(const BwdArgs &A, bool bf16, void *ws, hip
     }
     if (e != hipSuccess) return e;
     const int64_t rows = A.B * A.T * A.H;
-    hipLaunchKernelGGL(scan_bwd_reduce_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, A, S.part, Q);
+    hipLaunchKernelGGL(scan_bwd_reduce_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, A, S.part, Q,
+                       sh.G == 8 ? A.d_v / 32 : A.d_v / 4);
     return hipGetLastError();
 }
 

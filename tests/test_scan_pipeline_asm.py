@@ -23,8 +23,7 @@ def _hipcc():
     return shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else None)
 
 
-@pytest.fixture(scope="module")
-def lanes_asm(tmp_path_factory):
+def _device_asm(tmp_path_factory, src):
     hipcc = _hipcc()
     if hipcc is None:
         pytest.skip("hipcc not available")
@@ -32,11 +31,21 @@ def lanes_asm(tmp_path_factory):
     sys.path.insert(0, os.path.join(ROOT, "sparse_memory_linear_pkm_amd"))
     import build as B
     flags = [f for f in B.CFLAGS if f != "-fPIC"]
-    out = str(tmp_path_factory.mktemp("asm") / "lanes.s")
-    r = subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "sdm_scan_lanes.hip"),
-                        "-o", out], capture_output=True, text=True)
+    out = str(tmp_path_factory.mktemp("asm") / (src + ".s"))
+    r = subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out],
+                       capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return open(out).read()
+
+
+@pytest.fixture(scope="module")
+def lanes_asm(tmp_path_factory):
+    return _device_asm(tmp_path_factory, "sdm_scan_lanes.hip")
+
+
+@pytest.fixture(scope="module")
+def bwd_lanes_asm(tmp_path_factory):
+    return _device_asm(tmp_path_factory, "sdm_scan_bwd_lanes.hip")
 
 
 def _kernels(asm):
@@ -57,4 +66,23 @@ def test_scan_steady_state_waits(lanes_asm):
         assert not tight, f"D={D} bf16={bf16} save={save}: waits below (D-1)*NVM = {(D - 1) * nvm}: {tight}"
         # vmcnt(0) only in the prologue (twice) and after the loop (once)
         assert waits.count(0) <= 3, f"D={D} bf16={bf16} save={save}: {waits.count(0)} full drains"
+    assert found >= 16
+
+
+def test_backward_scan_steady_state_waits(bwd_lanes_asm):
+    """The same check on the backward's lane kernel
+    (sdm_scan_bwd_lanes_kernel<Q, D, G, BF16>), whose steps issue NVM = 8 +
+    NTR vector-memory instructions (NTR = 1 for bf16 v, 2 for fp32)."""
+    pat = re.compile(r"^(_ZN3sdm25sdm_scan_bwd_lanes_kernelILi(\d+)ELi(\d+)ELi(\d+)ELb([01])E\w*):", re.M)
+    found = 0
+    for m in pat.finditer(bwd_lanes_asm):
+        end = bwd_lanes_asm.index(".Lfunc_end", m.start())
+        body = bwd_lanes_asm[m.start():end]
+        D, bf16 = int(m.group(3)), m.group(5) == "1"
+        nvm = 8 + (1 if bf16 else 2)
+        waits = [int(x) for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", body)]
+        tight = [w for w in waits if 0 < w < (D - 1) * nvm]
+        assert not tight, f"{m.group(1)}: waits below (D-1)*NVM = {(D - 1) * nvm}: {tight}"
+        assert waits.count(0) <= 3, f"{m.group(1)}: {waits.count(0)} full drains"
+        found += 1
     assert found >= 16
