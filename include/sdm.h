@@ -138,6 +138,22 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
                             const sdm_dims *dims, sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * sdm_scan_forward_gated -- sdm_scan_forward with the gates applied inside
+ * its preparation pass ([P] Sec. 3.1 step 2 and Sec. 4, as sdm_gates):
+ *   a_t = exp(-A[h] softplus(a_raw + dt_bias[h])),  b_t = sigmoid(b_raw)
+ * a_raw, b_raw [B,T,H] fp32 (the gates' pre-activations) take the place of
+ * a, b; A, dt_bias [H] fp32 (A >= 0, the decay rate itself).  The results
+ * are those of sdm_gates followed by sdm_scan_forward, bit for bit, without
+ * the separate pass over the gates.  Same workspace, dims, layout and rules
+ * as sdm_scan_forward; A and dt_bias must not overlap M, o or the workspace
+ * (SDM_ERR_INVALID_ARG).
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_scan_forward_gated(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                  const float *rwt, const void *v, const float *a_raw, const float *b_raw,
+                                  const float *A, const float *dt_bias, float *o, void *workspace,
+                                  size_t workspace_bytes, const sdm_dims *dims, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * sdm_scan_forward_noalloc -- sdm_scan_forward for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): same arguments without the

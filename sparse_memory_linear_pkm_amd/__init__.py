@@ -13,7 +13,7 @@ from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_
                       sdm_cow_materialize, sdm_gates, sdm_output_norm_gate, sdm_gdn_dense_forward,
                       sdm_scan_forward_save, sdm_scan_backward, sdm_scan_backward_workspace_size, scan_forward_save,
                       scan_backward,
-                      sdm_scan_forward_noalloc, scan_forward_noalloc,
+                      sdm_scan_forward_noalloc, scan_forward_noalloc, sdm_scan_forward_gated,
                       sdm_address_backward, sdm_address_backward_workspace_size, address_backward,
                       sdm_gates_backward, sdm_gates_backward_workspace_size, sdm_output_norm_gate_backward,
                       sdm_output_norm_gate_backward_workspace_size, gates_backward, output_norm_gate_backward,

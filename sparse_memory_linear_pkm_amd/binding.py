@@ -58,6 +58,7 @@ def load_library():
         "sdm_gdn_dense_forward": [P, P, P, P, P, P, P, D, P],
         "sdm_scan_forward_save": [P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
         "sdm_scan_forward_noalloc": [P, P, P, P, P, P, P, P, P, D, P],
+        "sdm_scan_forward_gated": [P] * 12 + [ctypes.c_size_t, D, P],
         "sdm_scan_backward": [P] * 17 + [ctypes.c_size_t, D, P],
         "sdm_address_backward": [P] * 10 + [D, P, P, P, P, P, ctypes.c_size_t, P],
         "sdm_gates_backward": [P] * 6 + [D, P, P, P, P, P, ctypes.c_size_t, P],
@@ -266,6 +267,17 @@ def sdm_output_norm_gate_backward(o, g, gamma, eps: float, dy, dims: SdmDims, do
                                                       _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "sdm_output_norm_gate_backward")
+    return st
+
+
+def sdm_scan_forward_gated(M, widx, wwt, ridx, rwt, v, a_raw, b_raw, A, dt_bias, o, workspace, workspace_bytes: int,
+                           dims: SdmDims, stream=None, *, check: bool = True) -> int:
+    st = load_library().sdm_scan_forward_gated(_ptr(M), _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _ptr(v),
+                                               _ptr(a_raw), _ptr(b_raw), _ptr(A), _ptr(dt_bias), _ptr(o),
+                                               _ptr(workspace), int(workspace_bytes), ctypes.byref(dims),
+                                               _stream(stream))
+    if check:
+        _check(st, "sdm_scan_forward_gated")
     return st
 
 

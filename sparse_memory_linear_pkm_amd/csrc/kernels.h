@@ -62,6 +62,10 @@ struct ScanArgs {
     // [B,H,T,d_v/4,R,4] the read rows after it (4-column chunks, the list
     // positions of a chunk adjacent)
     float *xsave = nullptr, *zsave = nullptr;
+    // optional (both or neither): a and b hold the gates' pre-activations
+    // a_raw, b_raw, and the preparation pass applies the gates with the
+    // per-head decay A [H] and time-step bias dt_bias [H] (gates_math.h)
+    const float *A_decay = nullptr, *dt_bias = nullptr;
 };
 
 
@@ -82,6 +86,7 @@ struct PrepArgs {
     int64_t B, T, H;
     int W, R, Q, K, window, hash_log2, d_v, bf16;   // K = tokens per scan step
     int lookahead;   // D * K - 1: superseded writes are looked for up to the end of step + D - 1
+    const float *A_decay = nullptr, *dt_bias = nullptr;   // non-null: a, b are pre-activations (ScanArgs)
 };
 
 struct DecodeArgs {

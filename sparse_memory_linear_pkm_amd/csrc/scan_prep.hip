@@ -38,7 +38,9 @@
 //                               the write offset without that bit.
 //   tok[chain][t][c], c < d_v/4: {a_t, v_t[4c .. 4c+3], b_t} as one 16-byte
 //                               record (bf16 v: 2 words) or two (fp32 v:
-//                               {a_t, b_t, 0, 0}, then the 4 values)
+//                               {a_t, b_t, 0, 0}, then the 4 values); when
+//                               the caller passes the gates' pre-activations,
+//                               a_t and b_t are formed here (gates_math.h)
 //
 // One workgroup per (b, h, block of 32 tokens).  The write lists of the block
 // and of the `window` tokens before it go into an LDS hash table keyed by
@@ -48,6 +50,7 @@
 // query does not grow with the window.
 #include "kernels.h"
 #include "device_common.h"
+#include "gates_math.h"
 
 namespace sdm {
 
@@ -201,8 +204,13 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
             const int e = min(e0 + u * kPrThreads, nt - 1);
             const int tl = e / nchunk, c = e - tl * nchunk;
             const int64_t row = row_of(t0 + tl);
-            av[u] = __float_as_uint(A.a[row]);
-            bv[u] = __float_as_uint(A.b[row]);
+            if (A.A_decay) {   // the gates from their pre-activations
+                av[u] = __float_as_uint(gate_decay(A.a[row], A.dt_bias[h], A.A_decay[h]));
+                bv[u] = __float_as_uint(gate_sigmoid(A.b[row]));
+            } else {
+                av[u] = __float_as_uint(A.a[row]);
+                bv[u] = __float_as_uint(A.b[row]);
+            }
             if (A.bf16) {
                 const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(A.v) + row * A.d_v + 4 * c);
                 vv[u] = make_uint4(v.x, v.y, 0u, 0u);

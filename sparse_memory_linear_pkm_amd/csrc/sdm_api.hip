@@ -176,7 +176,8 @@ size_t sdm_scan_workspace_size(const sdm_dims *d)
 static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
                                     const float *rwt, const void *v, const float *a, const float *b, float *o,
                                     float *xsave, float *zsave, void *workspace, size_t workspace_bytes,
-                                    const sdm_dims *d, sdm_stream_t stream, bool noalloc = false);
+                                    const sdm_dims *d, sdm_stream_t stream, bool noalloc = false,
+                                    const float *A_decay = nullptr, const float *dt_bias = nullptr);
 
 sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
                             const float *rwt, const void *v, const float *a, const float *b,
@@ -185,6 +186,18 @@ sdm_status sdm_scan_forward(float *M, const int32_t *widx, const float *wwt, con
 {
     return scan_forward_impl(M, widx, wwt, ridx, rwt, v, a, b, o, nullptr, nullptr, workspace, workspace_bytes, d,
                              stream);
+}
+
+sdm_status sdm_scan_forward_gated(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
+                                  const float *rwt, const void *v, const float *a_raw, const float *b_raw,
+                                  const float *A, const float *dt_bias, float *o, void *workspace,
+                                  size_t workspace_bytes, const sdm_dims *d, sdm_stream_t stream)
+{
+    if (d && d->B * d->T > 0 && (!A || !dt_bias)) return fail(SDM_ERR_INVALID_ARG, "A and dt_bias must be non-NULL");
+    if (d && d->B * d->T > 0 && (!aligned(A, 4) || !aligned(dt_bias, 4)))
+        return fail(SDM_ERR_INVALID_ARG, "A and dt_bias must be 4-byte aligned");
+    return scan_forward_impl(M, widx, wwt, ridx, rwt, v, a_raw, b_raw, o, nullptr, nullptr, workspace,
+                             workspace_bytes, d, stream, false, A, dt_bias);
 }
 
 sdm_status sdm_scan_forward_noalloc(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
@@ -234,7 +247,8 @@ static sdm_status scratch_address(void **out)
 static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *wwt, const int32_t *ridx,
                                     const float *rwt, const void *v, const float *a, const float *b, float *o,
                                     float *xsave, float *zsave, void *workspace, size_t workspace_bytes,
-                                    const sdm_dims *d, sdm_stream_t stream, bool noalloc)
+                                    const sdm_dims *d, sdm_stream_t stream, bool noalloc, const float *A_decay,
+                                    const float *dt_bias)
 {
     sdm_status st = check_memory_dims(d);
     if (st != SDM_OK) return st;
@@ -304,9 +318,15 @@ static sdm_status scan_forward_impl(float *M, const int32_t *widx, const float *
             overlap(zsave, zb, workspace, need))
             return fail(SDM_ERR_INVALID_ARG, "xsave or zsave overlaps another buffer");
     }
+    if (A_decay) {   // the gated form: A and dt_bias [H] are read while M, o and the workspace are written
+        const size_t hb = sizeof(float) * (size_t)d->H;
+        if (overlap(A_decay, hb, M, msz) || overlap(A_decay, hb, o, osz) || overlap(A_decay, hb, workspace, need) ||
+            overlap(dt_bias, hb, M, msz) || overlap(dt_bias, hb, o, osz) || overlap(dt_bias, hb, workspace, need))
+            return fail(SDM_ERR_INVALID_ARG, "A or dt_bias overlaps M, o or the workspace");
+    }
     if (rows == 0) return SDM_OK;
     sdm::ScanArgs A{M, widx, wwt, ridx, rwt, v, a, b, o, d->B, d->T, (int)d->H, (int)N, (int)d->d_v,
-                    (int)d->W, (int)d->R, xsave, zsave};
+                    (int)d->W, (int)d->R, xsave, zsave, A_decay, dt_bias};
     hipError_t e = sdm::launch_scan(A, d->in_dtype == SDM_BF16, workspace, workspace_bytes,
                                     as_stream(stream));
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan_forward launch");

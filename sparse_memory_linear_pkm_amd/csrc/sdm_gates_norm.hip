@@ -9,17 +9,12 @@
 // Both are streaming kernels bound by HBM bandwidth: every input element is
 // read once and every output element written once, with coalesced accesses.
 #include "device_common.h"
+#include "gates_math.h"
 #include "kernels.h"
 
 namespace sdm {
 
-// 1 / (1 + e^-x) in the form whose exponential cannot overflow (so that
-// very negative x give their subnormal values rather than 0)
-__device__ __forceinline__ float sigmoid(float x)
-{
-    const float e = expf(-fabsf(x));
-    return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
-}
+__device__ __forceinline__ float sigmoid(float x) { return gate_sigmoid(x); }
 
 // a = exp(-A[h] softplus(a_raw + dt_bias[h])), b = sigmoid(b_raw); one
 // token-head per thread.  a may be the same buffer as a_raw and b the same
@@ -29,12 +24,9 @@ __global__ void __launch_bounds__(256) sdm_gates_kernel(GateArgs G)
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= G.n) return;
     const int h = (int)(i % G.H);
-    const float z = G.a_raw[i] + G.dt_bias[h];
-    const float braw = G.b_raw[i];
-    // ln(1 + e^z) in the form whose exponential cannot overflow
-    const float sp = z > 0.f ? z + log1pf(expf(-z)) : log1pf(expf(z));
-    G.a[i] = expf(-G.A[h] * sp);
-    G.b[i] = sigmoid(braw);
+    const float araw = G.a_raw[i], braw = G.b_raw[i];
+    G.a[i] = gate_decay(araw, G.dt_bias[h], G.A[h]);
+    G.b[i] = gate_sigmoid(braw);
 }
 
 hipError_t launch_gates(const GateArgs &G, hipStream_t stream)

@@ -89,7 +89,7 @@ hipError_t launch_scan(const ScanArgs &A, bool bf16, void *ws, size_t, hipStream
                    reinterpret_cast<uint4 *>(base + L.tok)};
     PrepArgs pa{A.widx, A.ridx, A.wwt, A.rwt, A.a, A.b, A.v, st, A.B, A.T, A.H,
                 A.W, A.R, Q, K, window, scan_prep_hash_log2(A.W, window, D * K - 1), A.d_v, bf16 ? 1 : 0,
-                D * K - 1};
+                D * K - 1, A.A_decay, A.dt_bias};
     hipError_t e = launch_scan_prep(pa, stream);
     if (e != hipSuccess) return e;
     return launch_scan_lanes(A, bf16, st, Q, sh.G, D, stream);

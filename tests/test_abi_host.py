@@ -261,6 +261,21 @@ def test_scan_noalloc_rejects_beyond_scratch_on_the_host():
     assert sdm.sdm_scan_forward_noalloc(*([None] * 9), good_dims(T=0), stream=0, check=False) == sdm.SDM_OK
 
 
+def test_gated_scan_rejects_bad_arguments():
+    def call(dims, **ptrs):
+        names = ("M", "widx", "wwt", "ridx", "rwt", "v", "a_raw", "b_raw", "A", "dt", "o", "ws")
+        p = {n: FAKE + (i << 30) for i, n in enumerate(names)}
+        p.update(ptrs)
+        return sdm.sdm_scan_forward_gated(*(p[n] for n in names), 1 << 29, dims, stream=0, check=False)
+    assert call(good_dims(), A=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), dt=FAKE + (9 << 30) + 2) == sdm.SDM_ERR_INVALID_ARG    # misaligned
+    assert call(good_dims(), A=FAKE + 64) == sdm.SDM_ERR_INVALID_ARG                # A inside M
+    assert call(good_dims(), dt=FAKE + (10 << 30) + 16) == sdm.SDM_ERR_INVALID_ARG  # dt_bias inside o
+    assert call(good_dims(), dt=FAKE + (11 << 30)) == sdm.SDM_ERR_INVALID_ARG       # dt_bias over the workspace
+    assert call(good_dims(W=0)) == sdm.SDM_ERR_INVALID_ARG
+    assert sdm.sdm_scan_forward_gated(*([None] * 12), 0, good_dims(T=0), stream=0, check=False) == sdm.SDM_OK
+
+
 def test_scan_forward_save_needs_both_buffers():
     dims = good_dims()
     args = [FAKE + (i << 30) for i in range(9)]

@@ -111,6 +111,52 @@ def test_gates_in_place(sdm, torch):
     check_gates(to_host(a_t), to_host(b_t), x["a_raw"], x["b_raw"], x["A"], x["dt_bias"], d)
 
 
+@pytest.mark.parametrize("d", [
+    Dims(B=2, T=150, H=3, d_k=128, n_sub=16, d_v=64, k_prime=8, W=16, R=16),
+    Dims(B=1, T=77, H=2, d_k=32, n_sub=8, d_v=32, k_prime=8, W=8, R=5, in_dtype="f32"),
+    Dims(B=8, T=64, H=16, d_k=128, n_sub=32, d_v=128, k_prime=32, W=32, R=32),
+], ids=["small_bf16", "f32_W8_R5", "dv128_W32"])
+def test_gated_scan_equals_gates_then_scan(sdm, torch, d):
+    """sdm_scan_forward_gated (the gates applied in the scan's preparation
+    pass) gives the results of sdm_gates followed by sdm_scan_forward bit for
+    bit, also with extreme pre-activations; and both match the oracle's
+    gates followed by the oracle's scan."""
+    note(f"gated scan {d}")
+    x = synth.make_inputs(d, seed=13)
+    ad = synth.random_addressing(d, seed=13, hazard_slots=4 * max(d.W, d.R))
+    e = synth.make_layer_edge_inputs(d, seed=13)
+    a_raw, b_raw = e["a_raw"] * 3.0, e["b_raw"] * 3.0
+    fa, fb = a_raw.reshape(-1), b_raw.reshape(-1)
+    fa[:6] = [40.0, -40.0, 90.0, -90.0, 0.0, 1e-7]
+    fb[:4] = [40.0, -40.0, 100.0, -100.0]
+    dims = sdm.dims_from(d)
+    dev = {k: to_dev(v) for k, v in ad.items()}
+    M0 = np.repeat(x["M0"][None], d.B, axis=0).copy()
+    ar, br, Ad, dtd = to_dev(a_raw), to_dev(b_raw), to_dev(e["A"]), to_dev(e["dt_bias"])
+    a_d, b_d = sdm.gates(ar, br, Ad, dtd, dims)
+    M1 = to_dev(M0)
+    o1 = sdm.scan_forward(M1, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]), a_d, b_d, dims)
+    M2 = to_dev(M0)
+    o2 = torch.empty_like(o1)
+    need = sdm.sdm_scan_workspace_size(dims)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    sdm.sdm_scan_forward_gated(M2, dev["widx"], dev["wwt"], dev["ridx"], dev["rwt"], to_dev(x["v"]), ar, br, Ad, dtd,
+                               o2, ws, need, dims)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(o1), to_host(o2))
+    assert np.array_equal(to_host(M1), to_host(M2))
+    # against the oracle (gates, then the scan), the scan's bar
+    a_o, b_o = oracle.gates(a_raw, b_raw, e["A"], e["dt_bias"], d)
+    Mo = M0.copy()
+    oo = oracle.scan(Mo, ad["widx"], ad["wwt"], ad["ridx"], ad["rwt"], x["v"], a_o, b_o, d)
+    for name, got, ref in (("o", to_host(o2), oo), ("M", to_host(M2), Mo)):
+        ref = ref.astype(np.float64)
+        scale = float(np.sqrt(np.mean(ref ** 2)))
+        err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+        note(f"{name}: max |err| / RMS = {err / scale:.2e}")
+        assert err <= 2e-3 * scale
+
+
 @pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d_v,B,T,H", [(32, 1, 1, 1), (64, 2, 45, 3), (96, 1, 19, 2), (128, 3, 50, 4),
                                        (256, 1, 9, 5), (1024, 1, 3, 2), (128, 2, 0, 3)])
