@@ -18,6 +18,43 @@ namespace sdm {
 
 constexpr int kTileRows = 16;     // token rows scored together (MFMA M dimension)
 
+// B-operand fragments of one 16-sub-key tile of a [n_sub][half] bf16
+// codebook for one k-step of v_mfma_f32_16x16x32_bf16 (the caller's C
+// already offset to the k-step's first element): lane (r, kg) = (lane & 15,
+// lane >> 4) needs elements kg*8 .. +8 of sub-key tile*16 + r.  Loaded in
+// that lane order, the 4 consecutive lanes of every quad would read 4
+// different sub-key rows (128 bytes apart for d_k = 128), which the load path
+// serves one row at a time (measured: scoring alone 2.4x slower than with
+// contiguous loads); instead lane l loads piece l & 3 of row l >> 2 (each
+// quad reads 64 contiguous bytes) and ds_bpermute hands lane (r, kg) its
+// piece from lane 4r + kg.  The operands, and so the scores, are unchanged.
+// (Whole contiguous rows per load, with two exchanges and a select per
+// register, measured slower: the exchanges cost more than the loads saved.)
+// Sub-keys past n_sub (unless FULL) load a valid neighbour and are zeroed.
+template <bool FULL>
+__device__ __forceinline__ i32x4 codebook_tile_load(const uint16_t *C, int half, int n_sub, int tile)
+{
+    const int lane = lane_id();
+    const int u = tile * 16 + (lane >> 2);
+    const int e = (lane & 3) * 8;
+    if constexpr (FULL) {
+        return *reinterpret_cast<const i32x4 *>(C + (int64_t)u * half + e);
+    } else {
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(C + (int64_t)min(u, n_sub - 1) * half + e);
+        return u < n_sub ? v : (i32x4){0, 0, 0, 0};
+    }
+}
+
+__device__ __forceinline__ bf16x8 codebook_tile_frag(i32x4 raw)
+{
+    const int lane = lane_id();
+    const int src = (4 * (lane & 15) + (lane >> 4)) << 2;
+    i32x4 g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = __builtin_amdgcn_ds_bpermute(src, raw[e]);
+    return __builtin_bit_cast(bf16x8, g);
+}
+
 // fp32 half scores S[r][u] = <x_r[c*half : (c+1)*half], C[h][c][u]> for the
 // first `srows` rows of one 16-row tile, written to LDS (row stride n_sub) as
 // their order-preserving bits (score_bits), the form every comparison uses.
@@ -69,6 +106,8 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
                 av[kk] = rlive ? a : zero;
             }
         }
+        // codebook fragments: contiguous loads and a lane exchange
+        // (codebook_tile_load / codebook_tile_frag)
         for (int st0 = wave * NB; st0 * 16 < n_sub; st0 += nwaves * NB) {
             f32x4 acc[NB];
 #pragma unroll
@@ -76,18 +115,13 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
 #pragma unroll
             for (int kk = 0; kk < KMAX; ++kk) {
                 if (NK > 0 || kk < nk) {
+                    i32x4 raw[NB];
+#pragma unroll
+                    for (int t = 0; t < NB; ++t) raw[t] = codebook_tile_load<FULL>(C16 + kk * 32, half, n_sub, st0 + t);
+                    // every exchange of the round before the first MFMA
                     bf16x8 bv[NB];
 #pragma unroll
-                    for (int t = 0; t < NB; ++t) {
-                        const int u = (st0 + t) * 16 + r;   // sub-key (B column) of this lane
-                        if constexpr (FULL) {
-                            bv[t] = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)u * half + kk * 32 + kg * 8);
-                        } else {
-                            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(C16 + (int64_t)min(u, n_sub - 1) * half +
-                                                                              kk * 32 + kg * 8);
-                            bv[t] = u < n_sub ? b : zero;
-                        }
-                    }
+                    for (int t = 0; t < NB; ++t) bv[t] = codebook_tile_frag(raw[t]);
 #pragma unroll
                     for (int t = 0; t < NB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], bv[t], acc[t], 0, 0, 0);
                 }

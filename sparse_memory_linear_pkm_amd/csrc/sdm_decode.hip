@@ -95,23 +95,25 @@ __device__ __forceinline__ void score_batched(const uint16_t *const (&x)[NKIND],
                     av[q][c][kk] =
                         *reinterpret_cast<const bf16x8 *>(x[q] + (int64_t)r * row_stride + c * half + kk * 32 + kg * 8);
     }
-    // sub-keys past n_sub load a valid neighbour and are zeroed (no branches
-    // around the codebook loads)
+    // codebook fragments as in score_half_tile: contiguous loads, then a
+    // lane exchange (codebook_tile_load / codebook_tile_frag); sub-keys past
+    // n_sub load a valid neighbour and are zeroed
     for (int st0 = wave * NB; st0 * 16 < n_sub; st0 += nwaves * NB) {
+        i32x4 raw[2][NB][NK];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+                for (int t = 0; t < NB; ++t)
+                    raw[c][t][kk] = codebook_tile_load<false>(C + (int64_t)c * n_sub * half + kk * 32, half, n_sub, st0 + t);
         bf16x8 bv[2][NB][NK];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
+            for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-                for (int t = 0; t < NB; ++t) {
-                    const int u = (st0 + t) * 16 + r;
-                    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(
-                        C + ((int64_t)c * n_sub + min(u, n_sub - 1)) * half + kk * 32 + kg * 8);
-                    bv[c][t][kk] = u < n_sub ? b : zero;
-                }
-            }
-        }
+                for (int t = 0; t < NB; ++t) bv[c][t][kk] = codebook_tile_frag(raw[c][t][kk]);
 #pragma unroll
         for (int q = 0; q < NKIND; ++q) {
 #pragma unroll
