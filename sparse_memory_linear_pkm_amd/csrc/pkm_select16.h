@@ -83,14 +83,20 @@ __device__ __forceinline__ void cmpx_stage(uint32_t (&x)[4])
             }
         }
     } else {
-        const bool lower = (lane_id() & (HB >> 2)) == 0;
+        // the lower lane of a pair keeps the larger value: med3(x, y, m) with
+        // m = all ones there and 0 in the upper lane (one v_med3_u32 instead
+        // of a max, a min and a select)
+        const uint32_t m = (lane_id() & (HB >> 2)) == 0 ? 0xFFFFFFFFu : 0u;
+        // (the exchanges read the registers in the order the previous stage
+        // wrote them, so that a DPP read rarely waits on a fresh VALU write)
         uint32_t y[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = row_xor<LM>(x[r ^ RM]);
+        for (int q = 0; q < 4; ++q) y[q ^ RM] = row_xor<LM>(x[q]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t hi = x[r] > y[r] ? x[r] : y[r], lo = x[r] > y[r] ? y[r] : x[r];
-            x[r] = lower ? hi : lo;
+            const uint32_t c = hi < m ? hi : m;
+            x[r] = c > lo ? c : lo;
         }
     }
 }
