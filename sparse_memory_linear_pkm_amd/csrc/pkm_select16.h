@@ -339,18 +339,22 @@ __device__ __forceinline__ bool merge16(const HalfEntry *L0, const HalfEntry *L1
     const int g = lane_id() >> 4;
     uint32_t sb[kMaxPer];
     uint32_t m[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
+    // the staircase's candidate scores, 16 lanes x kMaxPer; the first
+    // kFirst per lane (128 entries, the whole staircase for k', n <= 32)
+    // without branches, so that all their LDS reads are in flight together
+    constexpr int kFirst = 8;
+    auto cand = [&](int i) {
         const int sp = c + kGroupLanes * i;
-        uint32_t v = 0u;
-        if (sp < nstair) {
-            const uint32_t ab = stair[sp];
-            const float sum = __uint_as_float(L0[ab >> 8].score) + __uint_as_float(L1[ab & 0xff].score);
-            v = score_bits(sum);
-        }
-        sb[i] = v;
-        m[i & 3] = v > m[i & 3] ? v : m[i & 3];
-    }
+        const uint32_t ab = stair[min(sp, nstair - 1)];
+        const float sum = __uint_as_float(L0[ab >> 8].score) + __uint_as_float(L1[ab & 0xff].score);
+        return sp < nstair ? score_bits(sum) : 0u;
+    };
+#pragma unroll
+    for (int i = 0; i < kFirst; ++i) sb[i] = cand(i);
+#pragma unroll
+    for (int i = kFirst; i < kMaxPer; ++i) sb[i] = kGroupLanes * i < nstair ? cand(i) : 0u;   // uniform
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) m[i & 3] = sb[i] > m[i & 3] ? sb[i] : m[i & 3];
     sort64_desc(m);
     const uint32_t tau = rank_value(m, n - 1);
     const uint32_t top = rank_value(m, 0);
