@@ -19,7 +19,7 @@
 
 namespace {
 
-constexpr int kWave = 64;
+[[maybe_unused]] constexpr int kWave = 64;   // (used by the device pass only)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes)
