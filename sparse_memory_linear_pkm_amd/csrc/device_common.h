@@ -220,15 +220,27 @@ __device__ __forceinline__ void wave_topn(int len, int n, Get get, uint64_t *scr
         for (int r = 0; r < NR; ++r) res[r] = lane < n ? c[r] : 0ull;
         return;
     }
+    // the candidates are read kBatch per lane at a time (clamped positions,
+    // masked values), so that their LDS reads are in flight together
+    constexpr int kBatch = 8;
     uint32_t m[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) m[r] = 0;
-    for (int p = lane; p < len; p += kWave) {
+    for (int p0 = 0; p0 < len; p0 += kBatch * kWave) {
+        uint32_t hv[kBatch][NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const uint32_t hi = (uint32_t)(get(r, p) >> 32);
-            m[r] = hi > m[r] ? hi : m[r];
+        for (int b = 0; b < kBatch; ++b) {
+            const int p = p0 + b * kWave + lane;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint32_t hi = (uint32_t)(get(r, p < len ? p : len - 1) >> 32);
+                hv[b][r] = p < len ? hi : 0u;
+            }
         }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) m[r] = hv[b][r] > m[r] ? hv[b][r] : m[r];
     }
     wave_sort_desc<NR>(m);
     uint32_t tau[NR];
@@ -239,16 +251,30 @@ __device__ __forceinline__ void wave_topn(int len, int n, Get get, uint64_t *scr
         total[r] = 0;
     }
     const int iters = (len + kWave - 1) / kWave;
-    for (int i = 0; i < iters; ++i) {
-        const int p = lane + i * kWave;
+    for (int i0 = 0; i0 < iters; i0 += kBatch) {
+        uint64_t kv[kBatch][NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const uint64_t k = p < len ? get(r, p) : 0ull;
-            const bool f = (uint32_t)(k >> 32) >= tau[r];   // tau > 0, so k != 0
-            const uint64_t ball = __ballot(f);
-            const int pos = total[r] + mbcnt64(ball);
-            if (f && pos < kWave) scratch[r * kWave + pos] = k;
-            total[r] += __popcll(ball);
+        for (int b = 0; b < kBatch; ++b) {
+            const int p = lane + (i0 + b) * kWave;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint64_t k = get(r, p < len ? p : len - 1);
+                kv[b][r] = p < len ? k : 0ull;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            if (i0 + b < iters) {   // uniform
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const uint64_t k = kv[b][r];
+                    const bool f = (uint32_t)(k >> 32) >= tau[r];   // tau > 0, so k != 0
+                    const uint64_t ball = __ballot(f);
+                    const int pos = total[r] + mbcnt64(ball);
+                    if (f && pos < kWave) scratch[r * kWave + pos] = k;
+                    total[r] += __popcll(ball);
+                }
+            }
         }
     }
     wave_lds_sync();
