@@ -52,6 +52,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time spent on the oracle baseline (0 disables it)")
     p.add_argument("--decode-steps", type=int, default=1024, help="decode steps per step (decode workload)")
+    p.add_argument("--chunks", type=int, default=None,
+                   help="prefill pipelined over this many chunks of tokens (the addressing of chunk c + 1 "
+                        "overlapping the scan of chunk c); default 32 for one-sequence layers whose T it divides, "
+                        "else 1 (no pipelining)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (for counter calibration) and exit")
     return p.parse_args()
@@ -589,12 +593,57 @@ def main():
         # the decode token of each step: the last prefill token's inputs reused
         dec = {key: dx[key][:, -1].contiguous() for key in ("k", "q", "v", "a", "b")}
 
+        # Chunked prefill (one sequence: a chunk of tokens is a contiguous
+        # slice of every [B,T,H,...] array): the addressing of chunk c + 1 runs
+        # on a second stream with at most one workgroup per CU
+        # (sdm_pkm_address_overlapped), overlapping the scan of chunk c on the
+        # main stream, whose workgroups take one CU each with room to spare.
+        # The scan over consecutive chunks gives the same bits as one call.
+        nc = args.chunks if args.chunks is not None else (32 if B == 1 and T % 32 == 0 else 1)
+        if nc < 1 or T % nc != 0 or (nc > 1 and B != 1):
+            raise SystemExit(f"--chunks {nc}: needs B == 1 and T divisible by the chunk count")
+        Tc = T // nc
+        dimsc = sdm.dims_from(d.replace(T=Tc))
+        wsc_bytes = sdm.sdm_scan_workspace_size(dimsc)
+        wsc = ws if nc == 1 else torch.empty(max(wsc_bytes, 1), dtype=torch.uint8, device="cuda")
+        addr_stream = torch.cuda.Stream()
+
+        def step_chunked(timers=None):
+            E = lambda: torch.cuda.Event(enable_timing=timers is not None)
+            ev = {k: E() for k in ("start", "init0", "init1", "scan1", "dec1")}
+            ea = [(E(), E()) for _ in range(nc)]
+            es = [(E(), E()) for _ in range(nc)]
+            ev["start"].record(stream)
+            addr_stream.wait_event(ev["start"])
+            ev["init0"].record(stream)
+            sdm.sdm_state_init(M, dx["M0"], dims, stream)
+            ev["init1"].record(stream)
+            for c in range(nc):
+                sl = slice(c * Tc, (c + 1) * Tc)
+                ea[c][0].record(addr_stream)
+                sdm.sdm_pkm_address_overlapped(dx["k"][:, sl], dx["q"][:, sl], dx["C_w"], dx["C_r"], dimsc,
+                                               widx[:, sl], wwt[:, sl], ridx[:, sl], rwt[:, sl], addr_stream)
+                ea[c][1].record(addr_stream)
+            for c in range(nc):
+                sl = slice(c * Tc, (c + 1) * Tc)
+                stream.wait_event(ea[c][1])
+                es[c][0].record(stream)
+                sdm.sdm_scan_forward(M, widx[:, sl], wwt[:, sl], ridx[:, sl], rwt[:, sl], dx["v"][:, sl],
+                                     dx["a"][:, sl], dx["b"][:, sl], o[:, sl], wsc, wsc_bytes, dimsc, stream)
+                es[c][1].record(stream)
+            ev["scan1"].record(stream)
+            sdm.sdm_decode_step(M, dec["k"], dec["q"], dx["C_w"], dx["C_r"], dec["v"], dec["a"], dec["b"], o1,
+                                None, None, dims1, stream)
+            ev["dec1"].record(stream)
+            if timers is not None:
+                timers.append((ev, ea, es))
+
         # state init and addressing are independent (one writes M, the other
         # reads k, q and the codebooks): the copy runs on a second stream,
         # concurrently with the addressing, and the scan waits for both
         init_stream = torch.cuda.Stream()
 
-        def step(timers=None):
+        def step_whole(timers=None):
             E = lambda: torch.cuda.Event(enable_timing=timers is not None)
             ev = {k: E() for k in ("start", "init0", "init1", "addr1", "scan0", "scan1", "dec1")}
             ev["start"].record(stream)
@@ -614,6 +663,7 @@ def main():
             ev["dec1"].record(stream)
             if timers is not None:
                 timers.append(ev)
+        step = step_chunked if nc > 1 else step_whole
         tokens_per_step = B * T + B
 
     for _ in range(args.warmup):
@@ -650,8 +700,11 @@ def main():
                    "d_v": d.d_v, "k_prime": d.k_prime, "W": d.W, "R": d.R, "inputs": d.in_dtype,
                    "state": "fp32", "tokens_per_step": tokens_per_step,
                    "step": ("1024 decode steps" if decode_mode else
-                            "state init (second stream, concurrent with the addressing) + PKM addressing + "
-                             "prefill scan + 1 decode token per sequence")},
+                            (f"state init + PKM addressing + prefill scan over {nc} chunks of {T // nc} tokens "
+                             "(addressing of chunk c + 1 on a second stream, one workgroup per CU, overlapping "
+                             "the scan of chunk c) + 1 decode token per sequence" if nc > 1 else
+                             "state init (second stream, concurrent with the addressing) + PKM addressing + "
+                             "prefill scan + 1 decode token per sequence"))},
         "wall_s_timed_region": wall,
     }
 
@@ -668,20 +721,34 @@ def main():
                               "avg_launch_ms": dec_ms}
         result["copy_on_write"] = decode_batches(sdm, torch, dx, per, M, o, dims1, d, nsteps, stream)
     else:
-        spans = {"sdm_state_init": ("init0", "init1"), "sdm_pkm_address": ("start", "addr1"),
-                 "sdm_scan_forward": ("scan0", "scan1"), "sdm_decode_step": ("scan1", "dec1")}
-        avg = {n: sum(ev[a].elapsed_time(ev[b]) for ev in timers) / len(timers) for n, (a, b) in spans.items()}
+        if nc > 1:
+            # per call, summed over the chunks of a step (the addressing's
+            # chunks run on the second stream, overlapped with the scan)
+            def per_step(t):
+                ev, ea, es = t
+                return {"sdm_state_init": ev["init0"].elapsed_time(ev["init1"]),
+                        "sdm_pkm_address_overlapped": sum(a.elapsed_time(b) for a, b in ea),
+                        "sdm_scan_forward": sum(a.elapsed_time(b) for a, b in es),
+                        "sdm_decode_step": ev["scan1"].elapsed_time(ev["dec1"])}
+            rows_ = [per_step(t) for t in timers]
+            avg = {k: sum(r[k] for r in rows_) / len(rows_) for k in rows_[0]}
+        else:
+            spans = {"sdm_state_init": ("init0", "init1"), "sdm_pkm_address": ("start", "addr1"),
+                     "sdm_scan_forward": ("scan0", "scan1"), "sdm_decode_step": ("scan1", "dec1")}
+            avg = {n: sum(ev[a].elapsed_time(ev[b]) for ev in timers) / len(timers) for n, (a, b) in spans.items()}
         result["kernels_ms"] = avg
         th = d.B * d.T * d.H
         scan_bytes = th * (2 * d.W + d.R) * d.d_v * 4
         scan_s = avg["sdm_scan_forward"] * 1e-3
         achieved = scan_bytes / scan_s / 1e9
+        # per launch of sdm_scan_forward: one chunk of the sequence (the whole
+        # sequence when nc = 1); the counter summary holds the bytes per launch
         traffic = measured_traffic(name)
         result["roofline"] = {"kernel": "sdm_scan_forward (scan_prep_kernel + sdm_scan_lanes_kernel)",
                               "bound": "hbm", "achieved": achieved,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                              "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
-                              "avg_launch_ms": avg["sdm_scan_forward"]}
+                              "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes / nc,
+                              "avg_launch_ms": avg["sdm_scan_forward"] / nc, "launches_per_step": nc}
         # the addressing alone, after the timed region (in the step it shares
         # the chip with the state copy on the second stream)
         reps = max(3, min(20, args.steps))

@@ -112,6 +112,20 @@ sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const 
                            float *rwt, sdm_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * sdm_pkm_address_overlapped -- sdm_pkm_address with the same arguments and
+ * results (bit for bit), launched so that each compute unit holds at most
+ * one of its workgroups: the rest of the CU's LDS and wave slots stay free
+ * for a kernel running at the same time on another stream.  For a prefill
+ * pipelined over chunks of tokens: the addressing of chunk c + 1 (this call,
+ * on a second stream) overlaps the scan of chunk c (sdm_scan_forward, whose
+ * chunks give the same results as one call over all tokens).  Alone it runs
+ * about half as fast as sdm_pkm_address.
+ * ------------------------------------------------------------------------- */
+sdm_status sdm_pkm_address_overlapped(const void *k, const void *q, const void *C_w, const void *C_r,
+                                      const sdm_dims *dims, int32_t *widx, float *wwt, int32_t *ridx,
+                                      float *rwt, sdm_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * sdm_scan_workspace_size -- bytes of device workspace sdm_scan_forward needs
  * for these dims (0 if none).  Host-only; never fails (returns 0 on bad dims).
  * ------------------------------------------------------------------------- */

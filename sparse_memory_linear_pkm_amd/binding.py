@@ -51,6 +51,7 @@ def load_library():
     sigs = {
         "sdm_state_init": [P, P, D, P],
         "sdm_pkm_address": [P, P, P, P, D, P, P, P, P, P],
+        "sdm_pkm_address_overlapped": [P, P, P, P, D, P, P, P, P, P],
         "sdm_scan_forward": [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, D, P],
         "sdm_decode_step": [P, P, P, P, P, P, P, P, P, P, P, D, P],
         "sdm_gates": [P, P, P, P, D, P, P, P],
@@ -166,6 +167,15 @@ def sdm_pkm_address(k, q, C_w, C_r, dims: SdmDims, widx, wwt, ridx, rwt, stream=
                                         _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _stream(stream))
     if check:
         _check(st, "sdm_pkm_address")
+    return st
+
+
+def sdm_pkm_address_overlapped(k, q, C_w, C_r, dims: SdmDims, widx, wwt, ridx, rwt, stream=None, *,
+                               check: bool = True) -> int:
+    st = load_library().sdm_pkm_address_overlapped(_ptr(k), _ptr(q), _ptr(C_w), _ptr(C_r), ctypes.byref(dims),
+                                                   _ptr(widx), _ptr(wwt), _ptr(ridx), _ptr(rwt), _stream(stream))
+    if check:
+        _check(st, "sdm_pkm_address_overlapped")
     return st
 
 

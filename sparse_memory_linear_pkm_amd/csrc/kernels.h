@@ -223,7 +223,9 @@ hipError_t launch_gates_backward(const GateBwdArgs &args, hipStream_t stream);
 hipError_t launch_out_norm_gate_backward(const NormBwdArgs &args, bool bf16, hipStream_t stream);
 hipError_t launch_gates(const GateArgs &args, hipStream_t stream);
 hipError_t launch_out_norm_gate(const NormArgs &args, bool bf16, hipStream_t stream);
-hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream);
+// one_per_cu: launched so that a CU holds at most one of its workgroups
+// (room for a concurrent scan on another stream); same results
+hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream, bool one_per_cu = false);
 size_t address_smem_bytes(int n_sub, int k_prime);
 hipError_t launch_scan(const ScanArgs &args, bool bf16, void *workspace, size_t ws_bytes,
                        hipStream_t stream);

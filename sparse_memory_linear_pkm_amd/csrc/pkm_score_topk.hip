@@ -178,13 +178,20 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
 
 size_t address_smem_bytes(int n_sub, int k_prime) { return addr_lds_layout(n_sub, k_prime).total; }
 
-hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream)
+// LDS a workgroup requests when it must leave room on its CU for a
+// concurrent kernel: more than half of the CU's 160 KB, so that a CU holds
+// at most one addressing workgroup, and 76 KB left for the other kernel (the
+// prefill scan's workgroups need 24-64 KB).
+constexpr size_t kOnePerCuLds = 84 * 1024;
+
+hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t stream, bool one_per_cu)
 {
     if (args.BT <= 0) return hipSuccess;
     const int64_t ntiles = (args.BT + kTileRows - 1) / kTileRows;
     const int64_t grid = ntiles * 2 * args.H;
     if (ntiles > INT32_MAX || grid > UINT32_MAX) return hipErrorInvalidValue;
-    const size_t smem = address_smem_bytes(args.n_sub, args.k_prime);
+    size_t smem = address_smem_bytes(args.n_sub, args.k_prime);
+    if (one_per_cu && smem < kOnePerCuLds) smem = kOnePerCuLds;   // the extra LDS is never touched
     auto launch = [&](auto kern) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;

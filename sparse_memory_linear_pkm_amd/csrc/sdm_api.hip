@@ -129,9 +129,27 @@ sdm_status sdm_state_init(float *M, const float *M0, const sdm_dims *d, sdm_stre
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_state_init launch");
 }
 
+static sdm_status address_impl(const void *k, const void *q, const void *C_w, const void *C_r, const sdm_dims *d,
+                               int32_t *widx, float *wwt, int32_t *ridx, float *rwt, sdm_stream_t stream,
+                               bool one_per_cu);
+
 sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const void *C_r,
                            const sdm_dims *d, int32_t *widx, float *wwt, int32_t *ridx, float *rwt,
                            sdm_stream_t stream)
+{
+    return address_impl(k, q, C_w, C_r, d, widx, wwt, ridx, rwt, stream, false);
+}
+
+sdm_status sdm_pkm_address_overlapped(const void *k, const void *q, const void *C_w, const void *C_r,
+                                      const sdm_dims *d, int32_t *widx, float *wwt, int32_t *ridx, float *rwt,
+                                      sdm_stream_t stream)
+{
+    return address_impl(k, q, C_w, C_r, d, widx, wwt, ridx, rwt, stream, true);
+}
+
+static sdm_status address_impl(const void *k, const void *q, const void *C_w, const void *C_r, const sdm_dims *d,
+                               int32_t *widx, float *wwt, int32_t *ridx, float *rwt, sdm_stream_t stream,
+                               bool one_per_cu)
 {
     sdm_status st = check_method_dims(d, true);
     if (st != SDM_OK) return st;
@@ -160,7 +178,7 @@ sdm_status sdm_pkm_address(const void *k, const void *q, const void *C_w, const 
     A.d_k = (int)d->d_k;
     A.n_sub = (int)d->n_sub;
     A.k_prime = (int)d->k_prime;
-    hipError_t e = sdm::launch_pkm_address(A, d->in_dtype == SDM_BF16, as_stream(stream));
+    hipError_t e = sdm::launch_pkm_address(A, d->in_dtype == SDM_BF16, as_stream(stream), one_per_cu);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_pkm_address launch");
 }
 

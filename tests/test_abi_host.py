@@ -80,6 +80,19 @@ def test_address_rejects_null_and_misaligned():
     assert addr(good_dims(), ridx=FAKE) == sdm.SDM_ERR_INVALID_ARG
 
 
+def test_address_overlapped_validates_like_address():
+    """sdm_pkm_address_overlapped shares sdm_pkm_address's checks."""
+    def call(dims, k=FAKE, q=FAKE + (1 << 32), widx=FAKE + (2 << 32), ridx=FAKE + (3 << 32)):
+        return sdm.sdm_pkm_address_overlapped(k, q, FAKE + (4 << 32), FAKE + (5 << 32), dims, widx,
+                                              FAKE + (6 << 32), ridx, FAKE + (7 << 32), stream=0, check=False)
+    assert call(good_dims(), k=None) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), q=FAKE + 2) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(), ridx=FAKE + (2 << 32)) == sdm.SDM_ERR_INVALID_ARG
+    assert call(good_dims(W=65, k_prime=16)) == sdm.SDM_ERR_UNSUPPORTED
+    assert sdm.sdm_pkm_address_overlapped(None, None, None, None, good_dims(T=0), None, None, None, None, stream=0,
+                                          check=False) == sdm.SDM_OK
+
+
 def scan(dims, **ptrs):
     base = FAKE
     step = 1 << 34
