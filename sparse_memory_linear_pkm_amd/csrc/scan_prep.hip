@@ -42,12 +42,15 @@
 //                               the caller passes the gates' pre-activations,
 //                               a_t and b_t are formed here (gates_math.h)
 //
-// One workgroup per (b, h, block of 32 tokens).  The write lists of the block
-// and of the `window` tokens before it go into an LDS hash table keyed by
-// slot (open addressing, linear probing; one bucket per (token, position), so
-// a slot written by several tokens has several buckets); every query probes
-// for its slot and keeps the latest writer inside its window, so the cost per
-// query does not grow with the window.
+// One workgroup per (b, h, block of 32 tokens).  The write lists of the block,
+// of the `window` tokens before it and of the look-ahead after it go into an
+// LDS hash table keyed by slot, with chained buckets: entry (local token r,
+// position j) sits at index r * Q + j of an entry array holding its slot and
+// the next entry of its bucket, and is put at the head of its bucket with one
+// atomic exchange (no retries, so a thread's inserts are all in flight at
+// once).  Every query walks its slot's bucket and keeps the latest writer
+// inside its window, so the cost per query does not grow with the window; a
+// thread walks the buckets of its queries together.
 #include "kernels.h"
 #include "device_common.h"
 #include "gates_math.h"
@@ -56,16 +59,24 @@ namespace sdm {
 
 constexpr int kPrBlock = 32;      // tokens per workgroup
 constexpr int kPrThreads = 256;
-constexpr int kPrBatch = 8;       // loads a thread issues together
-constexpr int32_t kPrEmpty = INT32_MIN;
+constexpr int kPrBatch = 8;       // slots to insert a thread loads together
+constexpr int kPrQBatch = 4;      // queries (and token records) a thread loads together
+constexpr uint32_t kPrNone = 0xFFFFFFFFu;   // end of a bucket's chain
 constexpr uint32_t kRowBias = 0x40000000u;
 
 int scan_prep_hash_log2(int W, int window, int lookahead)
 {
     const int entries = (kPrBlock + window + lookahead) * W;
     int lg = 6;
-    while ((1 << lg) < 2 * entries) ++lg;   // load factor <= 1/2
+    while ((1 << lg) < 2 * entries) ++lg;   // at least two buckets per entry
     return lg;
+}
+
+// bucket heads, then the entries {slot, next entry of the bucket}
+static size_t scan_prep_smem(const PrepArgs &A)
+{
+    return sizeof(uint32_t) * ((size_t)1 << A.hash_log2) +
+           sizeof(uint2) * (size_t)(kPrBlock + A.window + A.lookahead) * (size_t)A.Q;
 }
 
 __device__ __forceinline__ uint32_t pr_hash(int32_t slot, int lg)
@@ -77,9 +88,10 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lg = A.hash_log2;
-    const uint32_t hmask = (1u << lg) - 1u;
-    int32_t *keys = reinterpret_cast<int32_t *>(smem);
-    uint32_t *vals = reinterpret_cast<uint32_t *>(smem + sizeof(int32_t) * (1u << lg));
+    const uint32_t nbucket = 1u << lg;
+    uint32_t *heads = reinterpret_cast<uint32_t *>(smem);
+    uint2 *ent = reinterpret_cast<uint2 *>(smem + sizeof(uint32_t) * nbucket);
+    const int qlog = __builtin_ctz((unsigned)A.Q);   // Q is a power of two
     const int tid = threadIdx.x;
     const int nblk = (int)((A.T + kPrBlock - 1) / kPrBlock);
     const int64_t ch = blockIdx.x / nblk;
@@ -94,10 +106,13 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
     const uint32_t rowb = (uint32_t)A.d_v * 4u;
     auto row_of = [&](int64_t t) { return (bb * A.T + t) * A.H + h; };
 
-    for (uint32_t e = tid; e <= hmask; e += kPrThreads) keys[e] = kPrEmpty;
-    // each thread's slots of kPrBatch entries are loaded together before any
-    // of them is inserted (the loads are in flight at once); the first batch
-    // is loaded while the table is cleared
+    const int ntok = (int)(thi - t0);
+    const int nq = ntok * Q;               // (token, position) queries
+    const int nchunk = A.d_v / 4;
+    const int nt = ntok * nchunk;          // token records
+    // Every load of the first batch of each phase (the slots to insert, the
+    // query inputs, the token records) is issued before the table is
+    // cleared, so the workgroup waits for one round trip instead of three.
     const int nins = nrows * W;
     int32_t sl[kPrBatch];
     auto load_batch = [&](int e0) {
@@ -108,99 +123,26 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
             sl[u] = e < nins ? A.widx[row_of(tlo + r) * W + j] : 0;
         }
     };
-    load_batch(tid);
-    __syncthreads();
-    for (int e0 = tid; e0 < nins; e0 += kPrThreads * kPrBatch) {
-        if (e0 != tid) load_batch(e0);
+    int32_t ws[kPrQBatch], rs[kPrQBatch];
+    float wv[kPrQBatch], rv[kPrQBatch];
+    auto load_queries = [&](int e0) {
 #pragma unroll
-        for (int u = 0; u < kPrBatch; ++u) {
-            const int e = e0 + u * kPrThreads;
-            if (e >= nins) break;
-            const int r = e / W, j = e - r * W;
-            uint32_t b = pr_hash(sl[u], lg);
-            while (true) {
-                const int32_t old = atomicCAS(&keys[b], kPrEmpty, sl[u]);
-                if (old == kPrEmpty) {
-                    vals[b] = ((uint32_t)r << 6) | (uint32_t)j;
-                    break;
-                }
-                b = (b + 1) & hmask;
-            }
-        }
-    }
-    __syncthreads();
-    // latest writer of `slot` among local tokens [lo, hi] (local = t - tlo), as
-    // (local token << 6 | position), or -1
-    auto latest = [&](int32_t slot, int lo, int hi) {
-        int best = -1;
-        uint32_t b = pr_hash(slot, lg);
-        while (true) {
-            const int32_t k = keys[b];
-            if (k == kPrEmpty) break;
-            if (k == slot) {
-                const int v = (int)vals[b];
-                const int r = v >> 6;
-                if (r >= lo && r <= hi && v > best) best = v;
-            }
-            b = (b + 1) & hmask;
-        }
-        return best;
-    };
-    const int ntok = (int)(thi - t0);
-    // (token, position) queries, kPrBatch per thread at a time: their inputs
-    // are loaded together, then the table is probed and the records written
-    const int nq = ntok * Q;
-    for (int e0 = tid; e0 < nq; e0 += kPrThreads * kPrBatch) {
-        int32_t ws[kPrBatch], rs[kPrBatch];
-        float wv[kPrBatch], rv[kPrBatch];
-#pragma unroll
-        for (int u = 0; u < kPrBatch; ++u) {
+        for (int u = 0; u < kPrQBatch; ++u) {
             const int e = e0 + u * kPrThreads;
             const int tl = e / Q, j = e - tl * Q;
-            const int64_t row = row_of(t0 + tl);
+            const int64_t row = row_of(t0 + (e < nq ? tl : 0));
             const bool okw = e < nq && j < W, okr = e < nq && j < R;
             ws[u] = okw ? A.widx[row * W + j] : 0;
             wv[u] = okw ? A.wwt[row * W + j] : 0.f;
             rs[u] = okr ? A.ridx[row * R + j] : 0;
             rv[u] = okr ? A.rwt[row * R + j] : 0.f;
         }
+    };
+    uint32_t av[kPrQBatch], bv[kPrQBatch];
+    uint4 vv[kPrQBatch];
+    auto load_records = [&](int e0) {
 #pragma unroll
-        for (int u = 0; u < kPrBatch; ++u) {
-            const int e = e0 + u * kPrThreads;
-            if (e >= nq) break;
-            const int tl = e / Q, j = e - tl * Q;
-            const int64_t t = t0 + tl;
-            const int ul = (int)(t - tlo);              // local index of this token
-            const int lo = ul - win > 0 ? ul - win : 0;
-            uint32_t cw = 0x7FFFu, cr = 0xFFFFu, gw = 0u, gr = 0u;
-            if (j < W) {
-                const int v = latest(ws[u], lo, ul - 1);
-                if (v >= 0) cw = (uint32_t)((ul - (v >> 6)) * 64 + (v & 63));
-                const int64_t last = (t / A.K) * A.K + look;   // <= t + look
-                const int hi = (int)((last < tend - 1 ? last : tend - 1) - tlo);
-                gw = (uint32_t)ws[u] * rowb + kRowBias;
-                if (hi > ul && latest(ws[u], ul + 1, hi) >= 0) gw |= 1u;
-            }
-            if (j < R) {
-                const int v = latest(rs[u], lo, ul);
-                if (v >= 0) cr = (uint32_t)((ul - (v >> 6)) * 64 + (v & 63));
-                gr = (uint32_t)rs[u] * rowb + kRowBias;
-            }
-            const int64_t s = (ch * A.T + t) * Q + j;
-            A.st.lane[s] = make_uint4(~(cw | (cr << 16)), __float_as_uint(wv[u]), __float_as_uint(rv[u]),
-                                      gw & ~1u);
-            A.st.gofs[s] = make_uint2(gw, gr);
-        }
-    }
-    // token records: a_t and the 4-column chunks of v_t (kPrBatch per thread
-    // at a time, loads first)
-    const int nchunk = A.d_v / 4;
-    const int nt = ntok * nchunk;
-    for (int e0 = tid; e0 < nt; e0 += kPrThreads * kPrBatch) {
-        uint32_t av[kPrBatch], bv[kPrBatch];
-        uint4 vv[kPrBatch];
-#pragma unroll
-        for (int u = 0; u < kPrBatch; ++u) {
+        for (int u = 0; u < kPrQBatch; ++u) {
             const int e = min(e0 + u * kPrThreads, nt - 1);
             const int tl = e / nchunk, c = e - tl * nchunk;
             const int64_t row = row_of(t0 + tl);
@@ -218,8 +160,103 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
                 vv[u] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(A.v) + row * A.d_v + 4 * c);
             }
         }
+    };
+    load_batch(tid);
+    load_queries(tid);
+    load_records(tid);
+    for (uint32_t e = tid; e < nbucket; e += kPrThreads) heads[e] = kPrNone;
+    __syncthreads();
+    for (int e0 = tid; e0 < nins; e0 += kPrThreads * kPrBatch) {
+        if (e0 != tid) load_batch(e0);
 #pragma unroll
         for (int u = 0; u < kPrBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            if (e >= nins) break;
+            const int r = e / W, j = e - r * W;
+            const uint32_t idx = ((uint32_t)r << qlog) | (uint32_t)j;
+            ent[idx].x = (uint32_t)sl[u];
+            ent[idx].y = atomicExch(&heads[pr_hash(sl[u], lg)], idx);
+        }
+    }
+    __syncthreads();
+    for (int e0 = tid; e0 < nq; e0 += kPrThreads * kPrQBatch) {
+        if (e0 != tid) load_queries(e0);
+        // per query: the chains of its write slot and of its read slot; the
+        // latest earlier writer of each inside the window (entry index, or
+        // -1), and whether the write slot is written again in the look-ahead
+        uint32_t cw[kPrQBatch], cr[kPrQBatch];
+        int bw[kPrQBatch], br[kPrQBatch], ul[kPrQBatch], lo[kPrQBatch], hi[kPrQBatch];
+        bool later[kPrQBatch];
+#pragma unroll
+        for (int u = 0; u < kPrQBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            const int tl = e / Q, j = e - tl * Q;
+            const int64_t t = t0 + tl;
+            ul[u] = (int)(t - tlo);
+            lo[u] = ul[u] - win > 0 ? ul[u] - win : 0;
+            const int64_t last = (t / A.K) * A.K + look;   // <= t + look
+            hi[u] = (int)((last < tend - 1 ? last : tend - 1) - tlo);
+            cw[u] = e < nq && j < W ? heads[pr_hash(ws[u], lg)] : kPrNone;
+            cr[u] = e < nq && j < R ? heads[pr_hash(rs[u], lg)] : kPrNone;
+            bw[u] = br[u] = -1;
+            later[u] = false;
+        }
+        while (true) {
+            uint2 ew[kPrQBatch], er[kPrQBatch];
+#pragma unroll
+            for (int u = 0; u < kPrQBatch; ++u) {
+                ew[u] = ent[cw[u] == kPrNone ? 0u : cw[u]];
+                er[u] = ent[cr[u] == kPrNone ? 0u : cr[u]];
+            }
+            bool more = false;
+#pragma unroll
+            for (int u = 0; u < kPrQBatch; ++u) {
+                if (cw[u] != kPrNone) {
+                    if ((int32_t)ew[u].x == ws[u]) {
+                        const int r = (int)(cw[u] >> qlog);
+                        if (r >= lo[u] && r < ul[u] && (int)cw[u] > bw[u]) bw[u] = (int)cw[u];
+                        if (r > ul[u] && r <= hi[u]) later[u] = true;
+                    }
+                    cw[u] = ew[u].y;
+                }
+                if (cr[u] != kPrNone) {
+                    if ((int32_t)er[u].x == rs[u]) {
+                        const int r = (int)(cr[u] >> qlog);
+                        if (r >= lo[u] && r <= ul[u] && (int)cr[u] > br[u]) br[u] = (int)cr[u];
+                    }
+                    cr[u] = er[u].y;
+                }
+                more = more || cw[u] != kPrNone || cr[u] != kPrNone;
+            }
+            if (!more) break;
+        }
+#pragma unroll
+        for (int u = 0; u < kPrQBatch; ++u) {
+            const int e = e0 + u * kPrThreads;
+            if (e >= nq) break;
+            const int tl = e / Q, j = e - tl * Q;
+            const int64_t t = t0 + tl;
+            uint32_t code_w = 0x7FFFu, code_r = 0xFFFFu, gw = 0u, gr = 0u;
+            if (j < W) {
+                if (bw[u] >= 0) code_w = (uint32_t)((ul[u] - (bw[u] >> qlog)) * 64 + (bw[u] & (Q - 1)));
+                gw = (uint32_t)ws[u] * rowb + kRowBias;
+                if (later[u]) gw |= 1u;
+            }
+            if (j < R) {
+                if (br[u] >= 0) code_r = (uint32_t)((ul[u] - (br[u] >> qlog)) * 64 + (br[u] & (Q - 1)));
+                gr = (uint32_t)rs[u] * rowb + kRowBias;
+            }
+            const int64_t s = (ch * A.T + t) * Q + j;
+            A.st.lane[s] = make_uint4(~(code_w | (code_r << 16)), __float_as_uint(wv[u]), __float_as_uint(rv[u]),
+                                      gw & ~1u);
+            A.st.gofs[s] = make_uint2(gw, gr);
+        }
+    }
+    // token records: a_t and the 4-column chunks of v_t
+    for (int e0 = tid; e0 < nt; e0 += kPrThreads * kPrQBatch) {
+        if (e0 != tid) load_records(e0);
+#pragma unroll
+        for (int u = 0; u < kPrQBatch; ++u) {
             const int e = e0 + u * kPrThreads;
             if (e >= nt) break;
             const int tl = e / nchunk, c = e - tl * nchunk;
@@ -236,13 +273,15 @@ __global__ void __launch_bounds__(kPrThreads) scan_prep_kernel(PrepArgs A)
 
 hipError_t launch_scan_prep(const PrepArgs &A, hipStream_t stream)
 {
-    if (A.window < 0 || A.window > 511 || A.W > 64 || A.R > 64 || A.Q > 64 || A.hash_log2 > 14 ||
+    if (A.window < 0 || A.window > 511 || A.W > 64 || A.R > 64 || A.Q > 64 || (A.Q & (A.Q - 1)) != 0 ||
+        A.Q < A.W || A.Q < A.R || A.hash_log2 > 14 ||
         A.K < 1 || kPrBlock % A.K != 0 || A.lookahead < A.K - 1 || A.lookahead > 511)
         return hipErrorInvalidValue;
     const int64_t nblk = (A.T + kPrBlock - 1) / kPrBlock;
     const int64_t grid = A.B * A.H * nblk;
     if (grid == 0) return hipSuccess;
-    const size_t smem = (sizeof(int32_t) + sizeof(uint32_t)) * ((size_t)1 << A.hash_log2);
+    const size_t smem = scan_prep_smem(A);
+    if (smem > 160 * 1024) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute((const void *)scan_prep_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;

@@ -52,8 +52,9 @@ namespace {
 
 constexpr int kBpBlock = 32;      // sub-tokens per preparation workgroup
 constexpr int kBpThreads = 256;
-constexpr int kBpBatch = 8;       // loads a thread issues together
-constexpr int32_t kBpEmpty = INT32_MIN;
+constexpr int kBpBatch = 8;       // slots to insert a thread loads together
+constexpr int kBpQBatch = 4;      // queries (and sub-token records) a thread loads together
+constexpr uint32_t kBpNone = 0xFFFFFFFFu;   // end of a bucket's chain
 
 struct BwdStreams {
     uint2 *lane;      // [chain][u][Q]: {~forwarding code, weight}
@@ -78,18 +79,36 @@ __device__ __forceinline__ uint32_t bp_hash(int32_t slot, int lg)
     return ((uint32_t)slot * 0x9E3779B1u) >> (32 - lg);
 }
 
+// sub-token u: token T - 1 - u/2, its read list (u even) or write list (u
+// odd).  Plain functions of values: a list length selected between two
+// variables that a lambda holds (by reference or by value) compiles to a
+// two-entry table in scratch memory and a dependent load per use.
+__device__ __forceinline__ int64_t bp_row(int64_t u, int64_t bb, int64_t T, int64_t H, int64_t h)
+{
+    return (bb * T + (T - 1 - (u >> 1))) * H + h;
+}
+
+__device__ __forceinline__ int bp_len(int64_t u, int W, int R)
+{
+    return (u & 1) ? W : R;
+}
+
 // Preparation pass.  One workgroup per (chain, block of 32 sub-tokens).  The
 // lists of the block, of the `window` sub-tokens before it and of the
-// `lookahead` sub-tokens after it go into an LDS hash table keyed by slot
-// (one bucket per (sub-token, position)); each (sub-token, position) query
-// probes for its slot once.
+// `lookahead` sub-tokens after it go into an LDS hash table keyed by slot,
+// with chained buckets: entry (local sub-token r, position j) sits at index
+// r * Q + j of an entry array holding its slot and the next entry of its
+// bucket, and is put at the head of its bucket with one atomic exchange.
+// Each (sub-token, position) query walks its slot's bucket once; a thread
+// walks the buckets of its queries together.
 __global__ void __launch_bounds__(kBpThreads) scan_bwd_prep_kernel(BwdPrepArgs A)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lg = A.hash_log2;
-    const uint32_t hmask = (1u << lg) - 1u;
-    int32_t *keys = reinterpret_cast<int32_t *>(smem);
-    uint32_t *vals = reinterpret_cast<uint32_t *>(smem + sizeof(int32_t) * (1u << lg));
+    const uint32_t nbucket = 1u << lg;
+    uint32_t *heads = reinterpret_cast<uint32_t *>(smem);
+    uint2 *ent = reinterpret_cast<uint2 *>(smem + sizeof(uint32_t) * nbucket);
+    const int qlog = __builtin_ctz((unsigned)A.Q);   // Q is a power of two
     const int tid = threadIdx.x;
     const int64_t U = 2 * A.T;
     const int64_t nblk = (U + kBpBlock - 1) / kBpBlock;
@@ -102,50 +121,35 @@ __global__ void __launch_bounds__(kBpThreads) scan_bwd_prep_kernel(BwdPrepArgs A
     const int64_t uend = uhi + A.lookahead < U ? uhi + A.lookahead : U;
     const int nsub = (int)(uend - ulo);
     const uint32_t rowb = (uint32_t)A.d_v * 4u;
-    // sub-token u: token T - 1 - u/2, its read list (u even) or write list (u odd)
-    auto row_of = [&](int64_t u) { return (bb * A.T + (A.T - 1 - (u >> 1))) * A.H + h; };
-    auto len_of = [&](int64_t u) { return (u & 1) ? W : R; };
+    const int64_t T = A.T, H = A.H;
+    auto row_of = [bb, T, H, h](int64_t u) { return bp_row(u, bb, T, H, h); };
+    auto len_of = [W, R](int64_t u) { return bp_len(u, W, R); };
 
-    for (uint32_t e = tid; e <= hmask; e += kBpThreads) keys[e] = kBpEmpty;
-    __syncthreads();
+    const int ntok = (int)(uhi - u0);
+    const int nq = ntok * Q;               // (sub-token, position) queries
+    const int nchunk = A.d_v / 4;
+    const int nt = ntok * nchunk;          // sub-token records
+    // The first batch of each phase's loads (the slots to insert, the query
+    // inputs, the sub-token records) is issued before the table is cleared,
+    // so the workgroup waits for one round trip instead of three.
     const int nins = nsub * Q;
-    for (int e0 = tid; e0 < nins; e0 += kBpThreads * kBpBatch) {
-        int32_t sl[kBpBatch];
-        bool ok[kBpBatch];
+    int32_t sl[kBpBatch];
+    auto load_batch = [&](int e0) {
 #pragma unroll
         for (int k = 0; k < kBpBatch; ++k) {
             const int e = e0 + k * kBpThreads;
             const int r = e / Q, j = e - r * Q;
             const int64_t u = ulo + r;
-            ok[k] = e < nins && j < len_of(u);
-            const int64_t row = row_of(ok[k] ? u : ulo);
-            sl[k] = ok[k] ? ((u & 1) ? A.widx[row * W + j] : A.ridx[row * R + j]) : 0;
+            const bool ok = e < nins && j < len_of(u);
+            const int64_t row = row_of(ok ? u : ulo);
+            sl[k] = ok ? ((u & 1) ? A.widx[row * W + j] : A.ridx[row * R + j]) : 0;
         }
+    };
+    int32_t ss[kBpQBatch];
+    float wv[kBpQBatch];
+    auto load_queries = [&](int e0) {
 #pragma unroll
-        for (int k = 0; k < kBpBatch; ++k) {
-            if (!ok[k]) continue;
-            const int e = e0 + k * kBpThreads;
-            const int r = e / Q, j = e - r * Q;
-            uint32_t b = bp_hash(sl[k], lg);
-            while (true) {
-                const int32_t old = atomicCAS(&keys[b], kBpEmpty, sl[k]);
-                if (old == kBpEmpty) {
-                    vals[b] = ((uint32_t)r << 6) | (uint32_t)j;
-                    break;
-                }
-                b = (b + 1) & hmask;
-            }
-        }
-    }
-    __syncthreads();
-
-    const int ntok = (int)(uhi - u0);
-    const int nq = ntok * Q;
-    for (int e0 = tid; e0 < nq; e0 += kBpThreads * kBpBatch) {
-        int32_t ss[kBpBatch];
-        float wv[kBpBatch];
-#pragma unroll
-        for (int k = 0; k < kBpBatch; ++k) {
+        for (int k = 0; k < kBpQBatch; ++k) {
             const int e = e0 + k * kBpThreads;
             const int tl = e / Q, j = e - tl * Q;
             const int64_t u = u0 + tl;
@@ -154,66 +158,11 @@ __global__ void __launch_bounds__(kBpThreads) scan_bwd_prep_kernel(BwdPrepArgs A
             ss[k] = on ? ((u & 1) ? A.widx[row * W + j] : A.ridx[row * R + j]) : 0;
             wv[k] = on ? ((u & 1) ? A.wwt[row * W + j] : A.rwt[row * R + j]) : 0.f;
         }
+    };
+    uint4 r0[kBpQBatch], r1[kBpQBatch];
+    auto load_records = [&](int e0) {
 #pragma unroll
-        for (int k = 0; k < kBpBatch; ++k) {
-            const int e = e0 + k * kBpThreads;
-            if (e >= nq) break;
-            const int tl = e / Q, j = e - tl * Q;
-            const int64_t u = u0 + tl;
-            const int ul = (int)(u - ulo);
-            uint32_t code = 0x7FFFu, go = 0u;
-            float wt = 0.f;
-            if (j < len_of(u)) {
-                const int32_t slot = ss[k];
-                wt = wv[k];
-                const int lo = ul - win > 0 ? ul - win : 0;
-                // the look-ahead ends with the step D - 1 steps after this one
-                const int64_t last = (u / A.K) * A.K + A.lookahead;
-                const int hi = (int)((last < uend - 1 ? last : uend - 1) - ulo);
-                int best = -1;
-                bool later_same = false, later_other = false, dup = false;
-                uint32_t b = bp_hash(slot, lg);
-                while (true) {
-                    const int32_t key = keys[b];
-                    if (key == kBpEmpty) break;
-                    if (key == slot) {
-                        const int v = (int)vals[b];
-                        const int r = v >> 6, p = v & 63;
-                        if (r >= lo && r < ul && v > best) best = v;
-                        if (r == ul && p != j) {
-                            dup = true;
-                            if (p > j) later_same = true;
-                        }
-                        if (r > ul && r <= hi) later_other = true;
-                    }
-                    b = (b + 1) & hmask;
-                }
-                if (best >= 0) code = (uint32_t)((ul - (best >> 6)) * 64 + (best & 63));
-                go = (uint32_t)slot * rowb + kRowBias;
-                if (later_same || later_other) go |= 1u;
-                if (!(u & 1) && dup && !later_same) {
-                    // the last position of a repeated read slot: the sum of
-                    // the positions' weights, in list order
-                    const int64_t row = row_of(u);
-                    float s = 0.f;
-                    for (int p = 0; p < R; ++p)
-                        if (A.ridx[row * R + p] == slot) s += A.rwt[row * R + p];
-                    wt = s;
-                }
-            }
-            const int64_t sidx = (ch * U + u) * Q + j;
-            A.st.lane[sidx] = make_uint2(~code, __float_as_uint(wt));
-            A.st.gofs[sidx] = go;
-        }
-    }
-
-    // token records (loads of kBpBatch records first, then the stores)
-    const int nchunk = A.d_v / 4;
-    const int nt = ntok * nchunk;
-    for (int e0 = tid; e0 < nt; e0 += kBpThreads * kBpBatch) {
-        uint4 r0[kBpBatch], r1[kBpBatch];
-#pragma unroll
-        for (int k = 0; k < kBpBatch; ++k) {
+        for (int k = 0; k < kBpQBatch; ++k) {
             const int e = min(e0 + k * kBpThreads, nt - 1);
             const int tl = e / nchunk, c = e - tl * nchunk;
             const int64_t u = u0 + tl;
@@ -234,8 +183,109 @@ __global__ void __launch_bounds__(kBpThreads) scan_bwd_prep_kernel(BwdPrepArgs A
                 r1[k] = make_uint4(0u, 0u, 0u, 0u);
             }
         }
+    };
+    load_batch(tid);
+    load_queries(tid);
+    load_records(tid);
+    for (uint32_t e = tid; e < nbucket; e += kBpThreads) heads[e] = kBpNone;
+    __syncthreads();
+    for (int e0 = tid; e0 < nins; e0 += kBpThreads * kBpBatch) {
+        if (e0 != tid) load_batch(e0);
 #pragma unroll
         for (int k = 0; k < kBpBatch; ++k) {
+            const int e = e0 + k * kBpThreads;   // entry index r * Q + j
+            if (e >= nins) break;
+            const int r = e / Q, j = e - r * Q;
+            if (j >= len_of(ulo + r)) continue;
+            ent[e].x = (uint32_t)sl[k];
+            ent[e].y = atomicExch(&heads[bp_hash(sl[k], lg)], (uint32_t)e);
+        }
+    }
+    __syncthreads();
+
+    for (int e0 = tid; e0 < nq; e0 += kBpThreads * kBpQBatch) {
+        if (e0 != tid) load_queries(e0);
+        // per query: the latest earlier entry of its slot inside the window
+        // (entry index, or -1); another position of the same sub-token with
+        // the slot (dup), a later one (later_same); a later sub-token in the
+        // look-ahead with it (later_other)
+        uint32_t cur[kBpQBatch];
+        int best[kBpQBatch], ul[kBpQBatch], lo[kBpQBatch], hi[kBpQBatch];
+        bool later_same[kBpQBatch], later_other[kBpQBatch], dup[kBpQBatch];
+#pragma unroll
+        for (int k = 0; k < kBpQBatch; ++k) {
+            const int e = e0 + k * kBpThreads;
+            const int tl = e / Q, j = e - tl * Q;
+            const int64_t u = u0 + tl;
+            ul[k] = (int)(u - ulo);
+            lo[k] = ul[k] - win > 0 ? ul[k] - win : 0;
+            // the look-ahead ends with the step D - 1 steps after this one
+            const int64_t last = (u / A.K) * A.K + A.lookahead;
+            hi[k] = (int)((last < uend - 1 ? last : uend - 1) - ulo);
+            cur[k] = e < nq && j < len_of(u) ? heads[bp_hash(ss[k], lg)] : kBpNone;
+            best[k] = -1;
+            later_same[k] = later_other[k] = dup[k] = false;
+        }
+        while (true) {
+            uint2 en[kBpQBatch];
+#pragma unroll
+            for (int k = 0; k < kBpQBatch; ++k) en[k] = ent[cur[k] == kBpNone ? 0u : cur[k]];
+            bool more = false;
+#pragma unroll
+            for (int k = 0; k < kBpQBatch; ++k) {
+                if (cur[k] != kBpNone) {
+                    if ((int32_t)en[k].x == ss[k]) {
+                        const int v = (int)cur[k];
+                        const int r = v >> qlog, p = v & (Q - 1);
+                        const int j = (e0 + k * kBpThreads) & (Q - 1);
+                        if (r >= lo[k] && r < ul[k] && v > best[k]) best[k] = v;
+                        if (r == ul[k] && p != j) {
+                            dup[k] = true;
+                            if (p > j) later_same[k] = true;
+                        }
+                        if (r > ul[k] && r <= hi[k]) later_other[k] = true;
+                    }
+                    cur[k] = en[k].y;
+                }
+                more = more || cur[k] != kBpNone;
+            }
+            if (!more) break;
+        }
+#pragma unroll
+        for (int k = 0; k < kBpQBatch; ++k) {
+            const int e = e0 + k * kBpThreads;
+            if (e >= nq) break;
+            const int tl = e / Q, j = e - tl * Q;
+            const int64_t u = u0 + tl;
+            uint32_t code = 0x7FFFu, go = 0u;
+            float wt = 0.f;
+            if (j < len_of(u)) {
+                const int32_t slot = ss[k];
+                wt = wv[k];
+                if (best[k] >= 0) code = (uint32_t)((ul[k] - (best[k] >> qlog)) * 64 + (best[k] & (Q - 1)));
+                go = (uint32_t)slot * rowb + kRowBias;
+                if (later_same[k] || later_other[k]) go |= 1u;
+                if (!(u & 1) && dup[k] && !later_same[k]) {
+                    // the last position of a repeated read slot: the sum of
+                    // the positions' weights, in list order
+                    const int64_t row = row_of(u);
+                    float s = 0.f;
+                    for (int p = 0; p < R; ++p)
+                        if (A.ridx[row * R + p] == slot) s += A.rwt[row * R + p];
+                    wt = s;
+                }
+            }
+            const int64_t sidx = (ch * U + u) * Q + j;
+            A.st.lane[sidx] = make_uint2(~code, __float_as_uint(wt));
+            A.st.gofs[sidx] = go;
+        }
+    }
+
+    // sub-token records
+    for (int e0 = tid; e0 < nt; e0 += kBpThreads * kBpQBatch) {
+        if (e0 != tid) load_records(e0);
+#pragma unroll
+        for (int k = 0; k < kBpQBatch; ++k) {
             const int e = e0 + k * kBpThreads;
             if (e >= nt) break;
             const int tl = e / nchunk, c = e - tl * nchunk;
@@ -575,8 +625,15 @@ __global__ void __launch_bounds__(64 * G) sdm_scan_bwd_lanes_kernel(BwdArgs A, B
 // dw_j, da, db: the nseg partial-sum records of a token (per chunk or per
 // row segment) added in order; dr_i = <do, Z_i> with the chunks' dot
 // products added in chunk order.  One wave per token-head row (b, t, h).
-__global__ void __launch_bounds__(256) scan_bwd_reduce_kernel(BwdArgs A, const float *part, int Q, int nseg)
+// One wave per (b, t, h).  For dr_i = <do, Z_i>, P = 64 / Q lanes share read
+// position i: lane (g, i) = (lane / Q, lane % Q) adds the chunks g, g + P,
+// g + 2P, ... with several loads in flight (each chunk's Q lanes read
+// consecutive 16-byte pieces), then the P lanes add their sums in a fixed
+// butterfly.
+template <int Q>
+__global__ void __launch_bounds__(256) scan_bwd_reduce_kernel(BwdArgs A, const float *part, int nseg)
 {
+    constexpr int P = kWave / Q;
     const int64_t rows = A.B * A.T * A.H;
     const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kWave;
     if (row >= rows) return;   // whole waves
@@ -596,17 +653,23 @@ __global__ void __launch_bounds__(256) scan_bwd_reduce_kernel(BwdArgs A, const f
             else A.db[row] = s;
         }
     }
-    if (lane < A.R) {
-        const float *Z = A.zsave + ((ch * A.T + t) * (int64_t)nchunk * A.R + lane) * 4;
+    const int i = lane % Q, g = lane / Q;
+    float s = 0.f;
+    if (i < A.R) {
+        const float *Z = A.zsave + ((ch * A.T + t) * (int64_t)nchunk * A.R + i) * 4;
         const float *dop = A.dout + row * A.d_v;
-        float s = 0.f;
-        for (int c = 0; c < nchunk; ++c) {
+#pragma unroll 8
+        for (int c = g; c < nchunk; c += P) {
             const f32x4 z = *reinterpret_cast<const f32x4 *>(Z + (int64_t)c * A.R * 4);
             const f32x4 dv = *reinterpret_cast<const f32x4 *>(dop + 4 * c);
             s += dot4(dv, z);
         }
-        A.dr[row * A.R + lane] = s;
     }
+    if constexpr (P >= 2) s += __uint_as_float(lane_xor<Q>(__float_as_uint(s)));
+    if constexpr (P >= 4) s += __uint_as_float(lane_xor<2 * Q>(__float_as_uint(s)));
+    if constexpr (P >= 8) s += __uint_as_float(lane_xor<4 * Q>(__float_as_uint(s)));
+    if constexpr (P >= 16) s += __uint_as_float(lane_xor<8 * Q>(__float_as_uint(s)));
+    if (g == 0 && i < A.R) A.dr[row * A.R + i] = s;
 }
 
 namespace {
@@ -716,7 +779,10 @@ hipError_t launch_scan_backward_lanes(const BwdArgs &A, bool bf16, void *ws, hip
                   A.W, A.R, Q, K, window, lookahead, bwd_hash_log2(Q, window, lookahead), A.d_v, bf16 ? 1 : 0};
     if (P.hash_log2 > 14) return hipErrorInvalidValue;
     const int64_t nblk = (2 * A.T + kBpBlock - 1) / kBpBlock;
-    const size_t smem = (sizeof(int32_t) + sizeof(uint32_t)) * ((size_t)1 << P.hash_log2);
+    // bucket heads, then the entries {slot, next entry of the bucket}
+    const size_t smem = sizeof(uint32_t) * ((size_t)1 << P.hash_log2) +
+                        sizeof(uint2) * (size_t)(kBpBlock + window + lookahead) * (size_t)Q;
+    if (smem > 160 * 1024) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute((const void *)scan_bwd_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)smem);
     if (e != hipSuccess) return e;
@@ -733,8 +799,15 @@ hipError_t launch_scan_backward_lanes(const BwdArgs &A, bool bf16, void *ws, hip
     }
     if (e != hipSuccess) return e;
     const int64_t rows = A.B * A.T * A.H;
-    hipLaunchKernelGGL(scan_bwd_reduce_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, A, S.part, Q,
-                       sh.G == 8 ? A.d_v / 32 : A.d_v / 4);
+    const int nseg = sh.G == 8 ? A.d_v / 32 : A.d_v / 4;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    switch (Q) {
+    case 4: hipLaunchKernelGGL(scan_bwd_reduce_kernel<4>, grid, dim3(256), 0, stream, A, S.part, nseg); break;
+    case 8: hipLaunchKernelGGL(scan_bwd_reduce_kernel<8>, grid, dim3(256), 0, stream, A, S.part, nseg); break;
+    case 16: hipLaunchKernelGGL(scan_bwd_reduce_kernel<16>, grid, dim3(256), 0, stream, A, S.part, nseg); break;
+    case 32: hipLaunchKernelGGL(scan_bwd_reduce_kernel<32>, grid, dim3(256), 0, stream, A, S.part, nseg); break;
+    default: hipLaunchKernelGGL(scan_bwd_reduce_kernel<64>, grid, dim3(256), 0, stream, A, S.part, nseg); break;
+    }
     return hipGetLastError();
 }
 
