@@ -3,7 +3,7 @@
 // "Sparse Delta Memory: Scaling the State of Linear RNNs through Sparsity",
 // Sec. 3.1 steps 1-3 for a single token.
 //
-// One workgroup (16 waves) per (head h, tile of TS consecutive sequences):
+// One workgroup (12 waves) per (head h, tile of TS consecutive sequences):
 // the sequences of a tile share the head's codebooks, so the tile reads them
 // once (the 16-row MFMA tile has TS real rows).
 //   A. the 4*TS half-score vectors (write/read x half 0/1 x sequence) on bf16
@@ -24,7 +24,9 @@
 
 namespace sdm {
 
-constexpr int kDecWaves = 16;
+// 12 waves: at 16 the 128-register limit per lane made the kernel spill
+// inside the scoring loop (scratch reloads that drained the loads in flight)
+constexpr int kDecWaves = 12;
 
 struct DecodeLds {
     // byte offsets into dynamic LDS
