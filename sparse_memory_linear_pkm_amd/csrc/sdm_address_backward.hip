@@ -203,6 +203,111 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_dx_kernel(AddrBwdArgs A, 
     }
 }
 
+// 1, wide form (when a 16-byte piece of a codebook row, 8 bf16 or 4 fp32
+// features, never straddles the two halves and d_k / 8 resp. d_k / 4 is a
+// power of two): each lane loads 16 bytes of a codebook row per list entry
+// instead of one element.  Lane (g, f) = (lane / NF, lane % NF) takes feature
+// piece f of list entries g, g + EG, g + 2 EG, ... (EG = 64 / NF; KB of them
+// at most), summed in that order; the EG partial sums of a piece are then
+// added by a fixed butterfly (every lane of the piece ends with the same
+// bits).  The entries' offsets and dsc come from the lanes holding them
+// (ds_bpermute).
+template <bool BF16, int NF, int KB>
+__global__ void __launch_bounds__(256) sdm_address_bwd_dx_wide_kernel(AddrBwdArgs A, float *dsc_ws)
+{
+    constexpr int FPL = BF16 ? 8 : 4;     // features per 16-byte piece
+    constexpr int EG = kWave / NF;        // entry groups
+    constexpr int esz = BF16 ? 2 : 4;
+    const int64_t rows = A.rows;
+    const int64_t wpk = (rows + kAbDxRows - 1) / kAbDxRows;   // waves per kind
+    const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    if (gw >= 2 * wpk) return;                 // whole waves
+    const int kind = (int)(gw / wpk);
+    const int64_t r0 = (gw - (int64_t)kind * wpk) * kAbDxRows;
+    const int64_t r1 = min(rows, r0 + kAbDxRows);
+    const int lane = lane_id();
+    const int n = kind ? A.R : A.W;
+    const int32_t *idx = kind ? A.ridx : A.widx;
+    const float *wt = kind ? A.rwt : A.wwt;
+    const float *dwt = kind ? A.dr : A.dw;
+    const void *C = kind ? A.C_r : A.C_w;
+    const int ns = A.n_sub, half = A.d_k / 2;
+    const int g = lane / NF, f = lane % NF;
+    const int e0 = f * FPL;                    // this lane's first feature
+    const bool hi = e0 >= half;
+    const uint32_t col = (uint32_t)(hi ? e0 - half : e0) * esz;
+    const int jl = lane < n ? lane : 0;
+    float wl = wt[r0 * n + jl], gl = dwt[r0 * n + jl];
+    int32_t sl = idx[r0 * n + jl];
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t rn = r + 1 < r1 ? r + 1 : r;
+        const float wn = wt[rn * n + jl], gn = dwt[rn * n + jl];
+        const int32_t sn = idx[rn * n + jl];
+        const int h = (int)(r % A.H);
+        const float w = lane < n ? wl : 0.f, gg = lane < n ? gl : 0.f;
+        const float mean = wave_sum_f32(w * gg);
+        const float ds = w * (gg - mean);
+        if (lane < n) dsc_ws[(kind ? rows * A.W : 0) + r * n + lane] = ds;
+        // entries past the list and slots outside the memory add exactly nothing
+        const bool ok = lane < n && sl >= 0 && sl < ns * ns;
+        const float dsl = ok ? ds : 0.f;
+        const int32_t s = ok ? sl : 0;
+        // byte offsets (in the head's codebook) of this entry's rows of half 0 and half 1
+        const int32_t off0 = (s / ns) * half * esz;
+        const int32_t off1 = (ns + s % ns) * half * esz;
+        const __amdgpu_buffer_rsrc_t Crs = make_rsrc(static_cast<const unsigned char *>(C) +
+                                                         (int64_t)h * 2 * ns * half * esz,
+                                                     (uint32_t)(2 * ns * half * esz));
+        uint4 raw[KB];
+        float dj[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int j = k * EG + g;
+            const int src = j < n ? j : 0;
+            const int o0 = __builtin_amdgcn_ds_bpermute(src * 4, off0);
+            const int o1 = __builtin_amdgcn_ds_bpermute(src * 4, off1);
+            const float d = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(dsl)));
+            dj[k] = j < n ? d : 0.f;
+            const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(Crs, (uint32_t)(hi ? o1 : o0) + col, 0, 0);
+            raw[k] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+        }
+        float acc[FPL];
+#pragma unroll
+        for (int e = 0; e < FPL; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+            for (int e = 0; e < FPL; ++e) {
+                float c;
+                if constexpr (BF16)
+                    c = __uint_as_float((e & 1) ? (wd[e >> 1] & 0xFFFF0000u) : (wd[e >> 1] << 16));
+                else
+                    c = __uint_as_float(wd[e]);
+                acc[e] = __builtin_fmaf(dj[k], c, acc[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < FPL; ++e) {
+            if constexpr (NF <= 1) acc[e] += __uint_as_float(lane_xor<1>(__float_as_uint(acc[e])));
+            if constexpr (NF <= 2) acc[e] += __uint_as_float(lane_xor<2>(__float_as_uint(acc[e])));
+            if constexpr (NF <= 4) acc[e] += __uint_as_float(lane_xor<4>(__float_as_uint(acc[e])));
+            if constexpr (NF <= 8) acc[e] += __uint_as_float(lane_xor<8>(__float_as_uint(acc[e])));
+            if constexpr (NF <= 16) acc[e] += __uint_as_float(lane_xor<16>(__float_as_uint(acc[e])));
+            if constexpr (NF <= 32) acc[e] += __uint_as_float(lane_xor<32>(__float_as_uint(acc[e])));
+        }
+        if (g == 0) {
+            float *dx = (kind ? A.dq : A.dk) + r * A.d_k + e0;
+#pragma unroll
+            for (int e = 0; e < FPL; e += 4)
+                *reinterpret_cast<f32x4 *>(dx + e) = (f32x4){acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+        }
+        wl = wn;
+        gl = gn;
+        sl = sn;
+    }
+}
+
 namespace {
 
 // the pieces of the workspace for one launch
@@ -581,7 +686,39 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
     } while (0)
 #define SDM_AB_ACC(BF, M)                                                                                     \
     hipLaunchKernelGGL((sdm_address_bwd_accum_kernel<BF, M>), dim3((unsigned)b4), dim3(256), 0, stream, A, S)
-    if (bf16) {
+    // the wide dx form: 16-byte codebook pieces within one half, a power-of-two
+    // number of pieces per row, 16-byte aligned codebooks and outputs
+    const int fpl = bf16 ? 8 : 4, nf = A.d_k / fpl;
+    auto al16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    // entries per lane group: ceil(max(W, R) / (64 / nf)), held in registers (at most 8)
+    const int epg = nf >= 1 ? (maxn + kWave / nf - 1) / (kWave / nf) : 0;
+    const bool wide = A.d_k % fpl == 0 && half % fpl == 0 && nf >= 2 && nf <= kWave && (nf & (nf - 1)) == 0 &&
+                      epg <= 8 && al16(A.C_w) && al16(A.C_r) && al16(A.dk) && al16(A.dq);
+#define SDM_AB_DXW_KB(BF, F, KB)                                                                              \
+    hipLaunchKernelGGL((sdm_address_bwd_dx_wide_kernel<BF, F, KB>), dim3((unsigned)b1), dim3(256), 0, stream, A, \
+                       S.dsc)
+#define SDM_AB_DXW(BF, F)                                                                                     \
+    do {                                                                                                      \
+        if (epg <= 1) SDM_AB_DXW_KB(BF, F, 1);                                                                \
+        else if (epg <= 2) SDM_AB_DXW_KB(BF, F, 2);                                                           \
+        else if (epg <= 4) SDM_AB_DXW_KB(BF, F, 4);                                                           \
+        else SDM_AB_DXW_KB(BF, F, 8);                                                                         \
+    } while (0)
+    if (wide) {
+        if (bf16) {
+            if (nf == 8) SDM_AB_DXW(true, 8);
+            else if (nf == 16) SDM_AB_DXW(true, 16);
+            else if (nf == 32) SDM_AB_DXW(true, 32);
+            else SDM_AB_DXW(true, 64);
+        } else {
+            if (nf == 2) SDM_AB_DXW(false, 2);
+            else if (nf == 4) SDM_AB_DXW(false, 4);
+            else if (nf == 8) SDM_AB_DXW(false, 8);
+            else if (nf == 16) SDM_AB_DXW(false, 16);
+            else if (nf == 32) SDM_AB_DXW(false, 32);
+            else SDM_AB_DXW(false, 64);
+        }
+    } else if (bf16) {
         if (nm <= 1) SDM_AB_DX(true, 1);
         else if (nm <= 2) SDM_AB_DX(true, 2);
         else if (nm <= 4) SDM_AB_DX(true, 4);
@@ -615,6 +752,8 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
     else
         hipLaunchKernelGGL(sdm_address_bwd_pieces_kernel<4>, dim3((unsigned)b5), dim3(256), 0, stream, A, S);
 #undef SDM_AB_DX
+#undef SDM_AB_DXW
+#undef SDM_AB_DXW_KB
 #undef SDM_AB_ACC
     return hipGetLastError();
 }

@@ -81,6 +81,13 @@ CASES = {
     "f32_dk48": (Dims(B=1, T=50, H=2, d_k=48, n_sub=20, d_v=32, k_prime=6, W=5, R=3, in_dtype="f32"), False),
     "bf16_two_ranges": (Dims(B=1, T=64, H=2, d_k=128, n_sub=300, d_v=32, k_prime=32, W=32, R=32), True),
     "bf16_dk256": (Dims(B=1, T=40, H=1, d_k=256, n_sub=128, d_v=32, k_prime=64, W=64, R=1), False),
+    # the dx pass in its wide form (16-byte codebook pieces): 8 pieces per row
+    # (8 entry groups), one piece group per row (d_k = 512: one entry group),
+    # and fp32 with 8 and 2 pieces per row
+    "bf16_dk64": (Dims(B=1, T=50, H=2, d_k=64, n_sub=40, d_v=32, k_prime=16, W=16, R=9), False),
+    "bf16_dk512": (Dims(B=1, T=24, H=1, d_k=512, n_sub=24, d_v=32, k_prime=8, W=8, R=8), True),
+    "f32_dk32": (Dims(B=1, T=60, H=2, d_k=32, n_sub=24, d_v=32, k_prime=8, W=8, R=5, in_dtype="f32"), False),
+    "f32_dk8": (Dims(B=2, T=33, H=1, d_k=8, n_sub=10, d_v=32, k_prime=4, W=4, R=7, in_dtype="f32"), True),
 }
 
 
@@ -111,3 +118,33 @@ def test_address_backward_full_size_small_layer(sdm, torch):
     d = synth.PRESETS["small"].dims
     note(f"address backward full size {d}")
     run_case(sdm, torch, d, seed=41, shared=True)
+
+
+def test_address_backward_unaligned_outputs(sdm, torch):
+    """dk and dq 4 bytes past a 16-byte boundary (the C ABI asks only for 4):
+    the dx pass then takes its element-wise form, with the same results up
+    to the order of the sums."""
+    d = Dims(B=2, T=70, H=2, d_k=128, n_sub=48, d_v=32, k_prime=16, W=16, R=16)
+    note(f"address backward, unaligned dk/dq {d}")
+    x = synth.make_inputs(d, seed=5, separate_read_codebook=True, m0=False)
+    dims = sdm.dims_from(d)
+    k, q, Cw, Cr = (to_dev(x[n]) for n in ("k", "q", "C_w", "C_r"))
+    widx, wwt, ridx, rwt = sdm.pkm_address(k, q, Cw, Cr, dims)
+    rng = np.random.default_rng(5)
+    dw = rng.normal(0, 1, (d.B, d.T, d.H, d.W)).astype(np.float32)
+    dr = rng.normal(0, 1, (d.B, d.T, d.H, d.R)).astype(np.float32)
+    nx = d.B * d.T * d.H * d.d_k
+    big = torch.zeros(2 * nx + 8, dtype=torch.float32, device="cuda")
+    dk, dq = big[1:1 + nx], big[nx + 5:2 * nx + 5]     # 4 bytes past 16-byte boundaries
+    assert dk.data_ptr() % 16 == 4 and dq.data_ptr() % 16 == 4
+    dCw = torch.empty((d.H, 2, d.n_sub, d.d_k // 2), dtype=torch.float32, device="cuda")
+    dCr = torch.empty_like(dCw)
+    need = sdm.sdm_address_backward_workspace_size(dims)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    sdm.sdm_address_backward(k, q, Cw, Cr, widx, wwt, ridx, rwt, to_dev(dw), to_dev(dr), dims, dk, dq, dCw, dCr,
+                             ws, need)
+    torch.cuda.synchronize()
+    ok, oq, _, _ = oracle.address_backward(x["k"], x["q"], x["C_w"], x["C_r"], to_host(widx), to_host(wwt),
+                                           to_host(ridx), to_host(rwt), dw, dr, d)
+    close_rms(to_host(dk).reshape(ok.shape), ok, "dk")
+    close_rms(to_host(dq).reshape(oq.shape), oq, "dq")
