@@ -471,23 +471,31 @@ __global__ void __launch_bounds__(256) sdm_address_bwd_key_prefix_kernel(AddrBwd
     }
 }
 
-// 2d. stable scatter: one wave per (kind, head, chunk) walks its entries 64
-// at a time in token-then-list order (the next 64 loaded while the current
-// ones are placed); the combined entries that select the same sub-key find
-// each other with one ballot per key bit and take consecutive places after
-// the sub-key's running offset (in LDS), in lane order.  A combined entry's
-// dsc is its first member's plus the others' in lane order, read from LDS.
-__global__ void __launch_bounds__(64) sdm_address_bwd_scatter_kernel(AddrBwdArgs A, AbWs S, int key_bits)
+// 2d. stable scatter: one workgroup per (kind, head, chunk) of one wave
+// placing both halves' entries, or (when there are few chunks, so that the
+// latency of each wave's dependent chain of running offsets is what counts)
+// of two waves, wave c placing half c's (the halves' sorts are independent).
+// A wave walks its entries 64 at a time in token-then-list order (the next 64
+// loaded while the current ones are placed); the combined entries that select
+// the same sub-key find each other with one ballot per key bit and take
+// consecutive places after the sub-key's running offset (in LDS), in lane
+// order.  A combined entry's dsc is its first member's plus the others' in
+// lane order, read from LDS.
+__global__ void __launch_bounds__(2 * kWave) sdm_address_bwd_scatter_kernel(AddrBwdArgs A, AbWs S, int key_bits)
 {
     extern __shared__ int32_t ctr[];   // [2][n_sub]
-    __shared__ float dsl[kWave];
+    __shared__ float dsl_all[2][kWave];
     int kind, h;
     int64_t ch;
     chunk_unit(A, S, kind, h, ch);
     const int ns = A.n_sub, n = kind ? A.R : A.W;
     const int32_t N = ns * ns;
     const int lane = lane_id();
-    for (int c = 0; c < 2; ++c) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const bool split = blockDim.x > kWave;
+    const int c0 = split ? wave : 0, c1 = split ? wave + 1 : 2;   // the halves this wave places
+    float *dsl = dsl_all[wave];
+    for (int c = c0; c < c1; ++c) {
         const int32_t *cr = cnt_row(A, S, kind, h, c, ch);
         const int32_t *st = S.start + (int64_t)((kind * A.H + h) * 2 + c) * (ns + 1);
         for (int u = lane; u < ns; u += kWave) ctr[c * ns + u] = st[u] + cr[u];
@@ -497,8 +505,7 @@ __global__ void __launch_bounds__(64) sdm_address_bwd_scatter_kernel(AddrBwdArgs
     const int64_t f0 = ch * kAbChunk, f1 = min(total, f0 + kAbChunk);
     const int32_t *idx = kind ? A.ridx : A.widx;
     const float *dsc = S.dsc + (kind ? A.rows * A.W : 0);
-    int2 *out[2];
-    for (int c = 0; c < 2; ++c) out[c] = S.sorted + (kind ? S.sorted1 : 0) + (int64_t)(h * 2 + c) * total;
+    int2 *out0 = S.sorted + (kind ? S.sorted1 : 0) + (int64_t)(h * 2) * total;
     const uint64_t below = (1ull << lane) - 1ull;
     // the list entry of this lane in the group of 64 starting at fb (a valid
     // entry past the end)
@@ -519,8 +526,7 @@ __global__ void __launch_bounds__(64) sdm_address_bwd_scatter_kernel(AddrBwdArgs
         const uint64_t valid = __builtin_amdgcn_ballot_w64(ok) & same_row(bt, fb, n);
         const int32_t row = (int32_t)(e / n);
         dsl[lane] = ds;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = c0; c < c1; ++c) {
             const int key = ok ? (c ? sl % ns : sl / ns) : 0;
             const uint64_t eq = same_key(key, key_bits);
             const uint64_t grp = eq & valid;
@@ -535,7 +541,7 @@ __global__ void __launch_bounds__(64) sdm_address_bwd_scatter_kernel(AddrBwdArgs
             const int rank = __builtin_popcountll(peers & below);
             const int base = ctr[c * ns + key];
             if (lead) {
-                out[c][base + rank] = make_int2(row, __float_as_int(gs));
+                out0[(int64_t)c * total + base + rank] = make_int2(row, __float_as_int(gs));
                 if (rank == 0) ctr[c * ns + key] = base + __builtin_popcountll(peers);
             }
         }
@@ -734,8 +740,12 @@ hipError_t launch_address_backward(const AddrBwdArgs &A, bool bf16, void *ws, hi
     hipLaunchKernelGGL(sdm_address_bwd_chunk_prefix_kernel, dim3((unsigned)(((ns + 255) / 256) * segs)), dim3(256), 0,
                        stream, A, S);
     hipLaunchKernelGGL(sdm_address_bwd_key_prefix_kernel, dim3((unsigned)segs), dim3(256), 0, stream, A, S);
-    hipLaunchKernelGGL(sdm_address_bwd_scatter_kernel, dim3((unsigned)chunks), dim3(kWave), hist_bytes, stream, A, S,
-                       key_bits);
+    // two waves per chunk (one per half) when the chunks are few: measured
+    // 179 -> 111 us on the small layer (1,024 chunks), but 1.11 -> 1.22 ms on
+    // the 1.4B layer (16,384 chunks), where more waves only add scattered stores
+    const int scatter_threads = chunks < 2048 ? 2 * kWave : kWave;
+    hipLaunchKernelGGL(sdm_address_bwd_scatter_kernel, dim3((unsigned)chunks), dim3(scatter_threads), hist_bytes,
+                       stream, A, S, key_bits);
     if (bf16) {
         if (hm <= 1) SDM_AB_ACC(true, 1);
         else if (hm <= 2) SDM_AB_ACC(true, 2);
