@@ -242,21 +242,6 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
         if (out && r < nb && lane < n) out[((size_t)(b0 + r) * A.H + h) * n + lane] = slot[0];
     }
     __syncthreads();
-    // read position j of row r is also written by the token at write
-    // position mpos (the lists hold distinct slots), else -1
-    for (int r = wave; r < TS; r += kDecWaves) {
-        const int s = lidx[(TS + r) * kWave + lane];
-        const i32x4 *wl = reinterpret_cast<const i32x4 *>(lidx + r * kWave);   // the write list, 4 at a time
-        int m = -1;
-        for (int jw = 0; jw < A.W; jw += 4) {
-            const i32x4 w4 = wl[jw / 4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = (s >= 0 && w4[e] == s) ? jw + e : m;
-        }
-        mpos[r * kWave + lane] = m;
-    }
-    __syncthreads();
-
     // D. the write and the read
     constexpr int K = kWave / Q;
     constexpr uint32_t kOOB = 0x80000000u;
@@ -269,18 +254,13 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
     // PB passes of a wave at a time, all their loads issued first; one row
     // (sequence) per pass, so the buffer resources are uniform
     constexpr int PB = 4;
-    if constexpr (COW) {
-        // every bit this step reads was taken before the last barrier: mark
-        // the rows the step writes
-        for (int r = wave; r < nb; r += kDecWaves) {
-            const int s = lidx[r * kWave + lane];
-            if (lane < A.W && s >= 0 && s < A.N)
-                atomicOr(A.touched + ((size_t)(b0 + r) * A.H + h) * wpb + ((uint32_t)s >> 5), 1u << (s & 31));
-        }
-    }
-    for (int p0 = wave; p0 < npass; p0 += kDecWaves * PB) {
-        f32x4 xw[PB], xr[PB], v4[PB];
-        int mm[PB];
+    // The update's loads of one round of PB passes per wave.  The first
+    // round is issued before the matching of read to write positions below,
+    // so that its latency overlaps that phase and its barrier; a read row
+    // the token also writes is loaded all the same (its value is then taken
+    // from the lane that computes the new row, not from memory).
+    f32x4 xw[PB], xr[PB], v4[PB];
+    auto load_round = [&](int p0) {
 #pragma unroll
         for (int t = 0; t < PB; ++t) {
             const int pass = min(p0 + t * kDecWaves, npass - 1);
@@ -292,9 +272,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
                 make_rsrc(A.M + bh * A.N * d_v, (uint32_t)((uint64_t)A.N * d_v * 4u));
             const uint32_t col4 = (uint32_t)chunk * 16u;
             const int sw = lidx[r * kWave + j], sr = lidx[(TS + r) * kWave + j];
-            mm[t] = mpos[r * kWave + j];
             const uint32_t offw = (live && j < A.W) ? (uint32_t)sw * d_v * 4u + col4 : kOOB;
-            const uint32_t offr = (live && j < A.R && mm[t] < 0) ? (uint32_t)sr * d_v * 4u + col4 : kOOB;
+            const uint32_t offr = (live && j < A.R) ? (uint32_t)sr * d_v * 4u + col4 : kOOB;
             if constexpr (COW) {
                 // each row from M if the sequence has written it, else from M0
                 // (the other load is out of range: no memory access, zeros)
@@ -320,6 +299,40 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
             } else {
                 v4[t] = __builtin_amdgcn_raw_buffer_load_b128(Vrs, live ? (uint32_t)chunk * vbytes : kOOB, 0, 0);
             }
+        }
+    };
+    load_round(wave);
+    // read position j of row r is also written by the token at write
+    // position mpos (the lists hold distinct slots), else -1
+    for (int r = wave; r < TS; r += kDecWaves) {
+        const int s = lidx[(TS + r) * kWave + lane];
+        const i32x4 *wl = reinterpret_cast<const i32x4 *>(lidx + r * kWave);   // the write list, 4 at a time
+        int m = -1;
+        for (int jw = 0; jw < A.W; jw += 4) {
+            const i32x4 w4 = wl[jw / 4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = (s >= 0 && w4[e] == s) ? jw + e : m;
+        }
+        mpos[r * kWave + lane] = m;
+    }
+    __syncthreads();
+
+    if constexpr (COW) {
+        // every bit this step reads was taken before the last barrier: mark
+        // the rows the step writes
+        for (int r = wave; r < nb; r += kDecWaves) {
+            const int s = lidx[r * kWave + lane];
+            if (lane < A.W && s >= 0 && s < A.N)
+                atomicOr(A.touched + ((size_t)(b0 + r) * A.H + h) * wpb + ((uint32_t)s >> 5), 1u << (s & 31));
+        }
+    }
+    for (int p0 = wave; p0 < npass; p0 += kDecWaves * PB) {
+        if (p0 != wave) load_round(p0);
+        int mm[PB];
+#pragma unroll
+        for (int t = 0; t < PB; ++t) {
+            const int pass = min(p0 + t * kDecWaves, npass - 1);
+            mm[t] = mpos[(pass / npr) * kWave + j];
         }
 #pragma unroll
         for (int t = 0; t < PB; ++t) {
