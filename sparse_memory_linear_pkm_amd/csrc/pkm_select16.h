@@ -186,6 +186,15 @@ __device__ __forceinline__ void push_ge_f32(uint32_t &m, float x, float t)
     asm volatile("v_cmp_ge_f32 vcc, %1, %2\n\tv_addc_co_u32 %0, vcc, %0, %0, vcc" : "+v"(m) : "v"(x), "v"(t) : "vcc");
 }
 
+// max(a, b, c) of fp32 values that are never NaN, in one instruction
+// (fmaxf would also quiet each operand first, an extra instruction per value).
+__device__ __forceinline__ float max3_f32(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Per-row survivor buffers of a wave: 4 rows x 64 entries.
 struct RowBuf {
     uint32_t *buf;   // [4][64]
@@ -231,13 +240,36 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
     const int c = lane_id() & (kGroupLanes - 1);
     const uint32_t *Sr = S + (size_t)row_g * sst;
     const int nch = (n_sub + 63) >> 6;   // 64 candidates of a row per chunk, 4 per lane
+    // Maxima over the chunks, kMaxBatch chunks' LDS reads in flight together
+    // (chunk positions clamped to the last one: a chunk read twice leaves a
+    // maximum unchanged).
+    constexpr int kMaxBatch = 4;
     float mf[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    for (int i = 0; i < nch; ++i) {
-        const float4 v = *reinterpret_cast<const float4 *>(Sr + 64 * i + 4 * c);
-        mf[0] = fmaxf(mf[0], v.x);
-        mf[1] = fmaxf(mf[1], v.y);
-        mf[2] = fmaxf(mf[2], v.z);
-        mf[3] = fmaxf(mf[3], v.w);
+    auto fold = [&](const float4 (&v)[kMaxBatch]) {
+        mf[0] = max3_f32(mf[0], v[0].x, v[1].x);
+        mf[1] = max3_f32(mf[1], v[0].y, v[1].y);
+        mf[2] = max3_f32(mf[2], v[0].z, v[1].z);
+        mf[3] = max3_f32(mf[3], v[0].w, v[1].w);
+        mf[0] = max3_f32(mf[0], v[2].x, v[3].x);
+        mf[1] = max3_f32(mf[1], v[2].y, v[3].y);
+        mf[2] = max3_f32(mf[2], v[2].z, v[3].z);
+        mf[3] = max3_f32(mf[3], v[2].w, v[3].w);
+    };
+    if (nch % kMaxBatch == 0) {   // uniform: no clamping needed
+        for (int i0 = 0; i0 < nch; i0 += kMaxBatch) {
+            float4 v[kMaxBatch];
+#pragma unroll
+            for (int b = 0; b < kMaxBatch; ++b) v[b] = *reinterpret_cast<const float4 *>(Sr + 64 * (i0 + b) + 4 * c);
+            fold(v);
+        }
+    } else {
+        for (int i0 = 0; i0 < nch; i0 += kMaxBatch) {
+            float4 v[kMaxBatch];
+#pragma unroll
+            for (int b = 0; b < kMaxBatch; ++b)
+                v[b] = *reinterpret_cast<const float4 *>(Sr + 64 * min(i0 + b, nch - 1) + 4 * c);
+            fold(v);
+        }
     }
     // an all-padding group (-inf) maps below every finite score
     uint32_t m[4];
@@ -248,26 +280,41 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
     const uint32_t top = rank_value(m, 0);
     const float tauf = __uint_as_float(raw_of_score_bits(tau));
     // candidates reaching tau: word w holds chunks 8w .. 8w + 7, candidate
-    // (chunk i, k) at bit 31 - (4 (i - 8w) + k) (shifted in from the right
-    // in order, then left-aligned)
+    // (chunk i, k) at bit 31 - (4 (i - 8w) + k).  All 8 chunks of a word are
+    // read before the first compare (positions past the row clamped to its
+    // last chunk and compared with +inf, which no score reaches, so their
+    // bits are 0).
     uint32_t mask[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         if (8 * w < nch) {   // uniform
+            float4 v[8];
             uint32_t mw = 0u;
+            if (8 * w + 8 <= nch) {   // uniform: a whole word
 #pragma unroll
-            for (int k8 = 0; k8 < 8; ++k8) {
-                const int i = 8 * w + k8;
-                if (i < nch) {   // uniform
-                    const float4 v = *reinterpret_cast<const float4 *>(Sr + 64 * i + 4 * c);
-                    push_ge_f32(mw, v.x, tauf);
-                    push_ge_f32(mw, v.y, tauf);
-                    push_ge_f32(mw, v.z, tauf);
-                    push_ge_f32(mw, v.w, tauf);
+                for (int k8 = 0; k8 < 8; ++k8)
+                    v[k8] = *reinterpret_cast<const float4 *>(Sr + 64 * (8 * w + k8) + 4 * c);
+#pragma unroll
+                for (int k8 = 0; k8 < 8; ++k8) {
+                    push_ge_f32(mw, v[k8].x, tauf);
+                    push_ge_f32(mw, v[k8].y, tauf);
+                    push_ge_f32(mw, v[k8].z, tauf);
+                    push_ge_f32(mw, v[k8].w, tauf);
+                }
+            } else {
+#pragma unroll
+                for (int k8 = 0; k8 < 8; ++k8)
+                    v[k8] = *reinterpret_cast<const float4 *>(Sr + 64 * min(8 * w + k8, nch - 1) + 4 * c);
+#pragma unroll
+                for (int k8 = 0; k8 < 8; ++k8) {
+                    const float t = 8 * w + k8 < nch ? tauf : INFINITY;   // uniform
+                    push_ge_f32(mw, v[k8].x, t);
+                    push_ge_f32(mw, v[k8].y, t);
+                    push_ge_f32(mw, v[k8].z, t);
+                    push_ge_f32(mw, v[k8].w, t);
                 }
             }
-            const int pushed = 4 * min(8, nch - 8 * w);
-            mask[w] = pushed < 32 ? mw << (32 - pushed) : mw;
+            mask[w] = mw;
         }
     }
     const uint32_t total = compact_row<4>(mask, rb, [&](int q) {
