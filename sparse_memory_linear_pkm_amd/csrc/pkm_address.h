@@ -112,18 +112,30 @@ __device__ __forceinline__ void score_half_tile(const void *x, int64_t row_strid
             f32x4 acc[NB];
 #pragma unroll
             for (int t = 0; t < NB; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            // with a compile-time k-step count every load of the round is
+            // issued before the first exchange (one memory round trip per
+            // round instead of one per k-step); the MFMAs still accumulate
+            // the k-steps in order, so the scores are unchanged
+            constexpr int KL = NK > 0 ? NK : 1;   // k-steps loaded together
 #pragma unroll
-            for (int kk = 0; kk < KMAX; ++kk) {
-                if (NK > 0 || kk < nk) {
-                    i32x4 raw[NB];
+            for (int kk0 = 0; kk0 < KMAX; kk0 += KL) {
+                if (NK > 0 || kk0 < nk) {
+                    i32x4 raw[KL][NB];
 #pragma unroll
-                    for (int t = 0; t < NB; ++t) raw[t] = codebook_tile_load<FULL>(C16 + kk * 32, half, n_sub, st0 + t);
-                    // every exchange of the round before the first MFMA
-                    bf16x8 bv[NB];
+                    for (int j = 0; j < KL; ++j)
 #pragma unroll
-                    for (int t = 0; t < NB; ++t) bv[t] = codebook_tile_frag(raw[t]);
+                        for (int t = 0; t < NB; ++t)
+                            raw[j][t] = codebook_tile_load<FULL>(C16 + (kk0 + j) * 32, half, n_sub, st0 + t);
 #pragma unroll
-                    for (int t = 0; t < NB; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk], bv[t], acc[t], 0, 0, 0);
+                    for (int j = 0; j < KL; ++j) {
+                        // every exchange of the k-step before its first MFMA
+                        bf16x8 bv[NB];
+#pragma unroll
+                        for (int t = 0; t < NB; ++t) bv[t] = codebook_tile_frag(raw[j][t]);
+#pragma unroll
+                        for (int t = 0; t < NB; ++t)
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[kk0 + j], bv[t], acc[t], 0, 0, 0);
+                    }
                 }
             }
             // D[i][j]: lane holds column j = lane & 15 (sub-key), rows 4*(lane>>4) + e

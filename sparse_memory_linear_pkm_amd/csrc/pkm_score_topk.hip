@@ -36,15 +36,22 @@ struct AddrLds {
     int sst;   // row stride of S in elements
 };
 
+// The two half lists are kept in registers while the score tile is in use
+// and written to LDS only for the merge, into the tile's space (free by
+// then), so a workgroup's LDS is the tile, the survivor buffers, the one-row
+// routines' scratch and the staircase: 39 KB for n_sub = 512 (four
+// workgroups per CU), 71 KB for n_sub = 1024 (two).
 __host__ __device__ inline AddrLds addr_lds_layout(int n_sub, int kp)
 {
     AddrLds o;
     // rows padded with zeros to a multiple of 64 candidates, plus 4 elements
     // so that consecutive rows start in different LDS banks
     o.sst = ((n_sub + 63) / 64) * 64 + 4;
-    o.S = 0;                                                      // uint32 [16][sst]
-    o.L = o.S + sizeof(uint32_t) * kTileRows * (size_t)o.sst;     // HalfEntry [2][16][kp]
-    o.buf = o.L + sizeof(HalfEntry) * 2 * kTileRows * (size_t)kp; // uint32 [16][64] survivors
+    const size_t tile = sizeof(uint32_t) * kTileRows * (size_t)o.sst;       // uint32 [16][sst]
+    const size_t lists = sizeof(HalfEntry) * 2 * kTileRows * (size_t)kp;   // HalfEntry [2][16][kp]
+    o.S = 0;
+    o.L = 0;                                                      // aliases the tile (merge only)
+    o.buf = ((tile > lists ? tile : lists) + 15) / 16 * 16;       // uint32 [16][64] survivors
     o.scratch = o.buf + sizeof(uint32_t) * kTileRows * 64;        // uint64 [4][64] (one-row routines)
     o.stair = o.scratch + sizeof(uint64_t) * kAddrWaves * kWave;
     o.total = o.stair + sizeof(uint16_t) * kMaxStair;
@@ -118,31 +125,50 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
     const int row_g = wave + kAddrWaves * g;
     const RowBuf rb{buf + wave * kAddrWaves * 64};
 
+    // the half lists of this lane's row, entries 4 c16 .. 4 c16 + 3
+    HalfEntry hl[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         score_half_tile<BF16, kScoreNB, NK, true, FULL>(xb, row_stride, nrows, kTileRows,
                                                        Cb + (int64_t)c * n_sub * half * esz, c, half, n_sub, S,
                                                        sst);
         __syncthreads();
-        const bool bad = half_topk16(S, sst, row_g, n_sub, kp, rb, L + (c * kTileRows + row_g) * kp);
-        // rows the fast path could not vouch for: the exact one-row routine
+        const bool bad = half_topk16(S, sst, row_g, n_sub, kp, rb, hl[c]);
+        // rows the fast path could not vouch for: the exact one-row routine,
+        // its list handed to the row's lane group through the wave's scratch
         const uint64_t bb = __ballot(bad);
         for (int gg = 0; gg < kAddrWaves; ++gg) {
             if ((bb >> (16 * gg)) & 0xFFFFull) {
                 const int rows1[1] = {wave + kAddrWaves * gg};
                 uint64_t keys[1];
                 half_topk<1, true>(S, rows1, n_sub, kp, wscr, keys, sst);
-                if (lane < kp) {
-                    HalfEntry e;
-                    e.score = __float_as_uint(key_score(keys[0]));
-                    e.index = key_index(keys[0]);
-                    L[(c * kTileRows + rows1[0]) * kp + lane] = e;
+                wave_lds_sync();
+                if (lane < kp)
+                    wscr[lane] = ((uint64_t)key_index(keys[0]) << 32) | __float_as_uint(key_score(keys[0]));
+                wave_lds_sync();
+                if (g == gg) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 4 * c16 + r;
+                        const uint64_t e = wscr[j < kp ? j : 0];
+                        hl[c][r].score = (uint32_t)e;
+                        hl[c][r].index = (uint32_t)(e >> 32);
+                    }
                 }
                 wave_lds_sync();
             }
         }
-        __syncthreads();
+        __syncthreads();   // the tile is free: every wave has finished reading it
     }
+    // both lists into LDS for the merge (each wave reads only its own rows)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 4 * c16 + r;
+            if (j < kp) L[(c * kTileRows + row_g) * kp + j] = hl[c][r];
+        }
+    wave_lds_sync();
 
     int slot[4];
     float wt[4];

@@ -229,13 +229,14 @@ __device__ __forceinline__ uint32_t compact_row(const uint32_t (&mask)[NMW], Row
 
 // Top-k' of one half for the 4 rows of this wave (row of lane group g =
 // row_g): S holds the row's raw fp32 scores at S + row_g * sst, -inf from
-// n_sub up to the next multiple of 64.  Lane j < k' of the row's list is
-// written to Lrow[j] (best first).  Returns true if this lane's row must be
-// redone by the exact one-row routine.  Scores are compared as floats while
+// n_sub up to the next multiple of 64.  Lane c of the row's group receives
+// entries 4c .. 4c + 3 of the row's list (best first) in ent[] (entries past
+// k' are undefined).  Returns true if this lane's row must be redone by the
+// exact one-row routine (ent[] is then undefined).  Scores are compared as floats while
 // scanning (the same order as score_bits for finite values) and as
 // score_bits in the sorts.
 __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_g, int n_sub, int kp, RowBuf rb,
-                                            HalfEntry *Lrow)
+                                            HalfEntry (&ent)[4])
 {
     const int c = lane_id() & (kGroupLanes - 1);
     const uint32_t *Sr = S + (size_t)row_g * sst;
@@ -328,11 +329,11 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
     const uint32_t sh = key_shift(top - tau, ib);
     uint32_t key[4];
     const uint4 e = *reinterpret_cast<const uint4 *>(rb.buf + g * 64 + 4 * c);
-    const uint32_t ent[4] = {e.x, e.y, e.z, e.w};
+    const uint32_t sv[4] = {e.x, e.y, e.z, e.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const uint32_t j = (uint32_t)(4 * c + r);
-        const uint32_t p = j < total ? ent[r] : 0u;
+        const uint32_t p = j < total ? sv[r] : 0u;
         const uint32_t s = score_bits(__uint_as_float(Sr[p]));
         key[r] = j < total ? ((((s - tau) >> sh) + 1u) << ib) | (imask - p) : 0u;
     }
@@ -361,13 +362,8 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
     const bool row_bad = ((bb >> (16 * g)) & 0xFFFFull) != 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int j = 4 * c + r;
-        if (!row_bad && j < kp) {
-            HalfEntry he;
-            he.score = raw_of_score_bits(s[r]);
-            he.index = p[r];
-            Lrow[j] = he;
-        }
+        ent[r].score = raw_of_score_bits(s[r]);
+        ent[r].index = p[r];
     }
     return row_bad;
 }
