@@ -484,46 +484,51 @@ def bench_row_traffic(args, torch):
     no arithmetic and no dependence between steps (libsdm_bench.so).  Run on
     the long-context layer's table (16 chains of 2^20 rows of 512 bytes) with
     the segment sizes the scan can use (32, 64, 128 bytes: 2, 4, 8 waves per
-    workgroup), and with the same bytes split over 4x the chains (4x the
-    workgroups) at 32 bytes.  Bytes per workgroup and step: 64 rows x 3 x
-    segment."""
+    workgroup); with 4x or 2x the waves per workgroup, each extra group moving
+    its own rows (more requests in flight per CU); with the same bytes split
+    over 4x and 16x the chains at 32 bytes; and on a 16 GiB table split into
+    32, 64 and 128 chains at 128 bytes (more CUs each moving whole lines).
+    Bytes per workgroup and step: 64 rows x 3 x segment per token group."""
     import ctypes
     path = os.path.join(ROOT, "sparse_memory_linear_pkm_amd", "libsdm_bench.so")
     if not os.path.exists(path):
         raise ImportError(f"{path} not found: build it with `python -m sparse_memory_linear_pkm_amd.build`")
     lib = ctypes.CDLL(path)
     fn = lib.sdm_bench_row_traffic
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
-                   ctypes.c_uint32, ctypes.c_void_p]
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
     fn.restype = ctypes.c_int
     row_bytes = 512
-    M = torch.zeros(16 * (1 << 20) * row_bytes // 4, dtype=torch.float32, device="cuda")
+    M = torch.zeros(128 * (1 << 18) * row_bytes // 4, dtype=torch.float32, device="cuda")   # 16 GiB
     stream = torch.cuda.current_stream()
-    configs = [(16, 20, 32), (16, 20, 64), (16, 20, 128), (64, 18, 32), (256, 16, 32)]
+    # (chains, log2 rows per chain, segment bytes, token groups)
+    configs = [(16, 20, 32, 1), (16, 20, 64, 1), (16, 20, 128, 1), (16, 20, 32, 4), (16, 20, 128, 2),
+               (64, 18, 32, 1), (256, 16, 32, 1), (32, 20, 128, 1), (64, 19, 128, 1), (128, 18, 128, 1)]
     steps = max(1024, args.steps * 1024)
     out = []
-    for chains, lg, seg in configs:
+    for chains, lg, seg, tg in configs:
         wgs = chains * row_bytes // seg
-        nbytes = wgs * steps * 64 * 3 * seg
-        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, 1024, 1, stream.cuda_stream)
+        nbytes = wgs * tg * steps * 64 * 3 * seg
+        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, tg, 1024, 1, stream.cuda_stream)
         assert rc == 0, rc
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, steps, 7, stream.cuda_stream)
+        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, tg, steps, 7, stream.cuda_stream)
         e1.record(stream)
         torch.cuda.synchronize()
         assert rc == 0, rc
         ms = e0.elapsed_time(e1)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        out.append({"chains": chains, "rows_per_chain": 1 << lg, "segment_bytes": seg, "workgroups": wgs,
-                    "waves": wgs * seg // 16, "steps": steps, "bytes": nbytes, "ms": ms, "GB/s": gbs,
-                    "frac_of_hbm_peak": gbs / HBM_PEAK_GBS})
+        out.append({"chains": chains, "rows_per_chain": 1 << lg, "segment_bytes": seg, "token_groups": tg,
+                    "workgroups": wgs, "waves": wgs * seg // 16 * tg, "steps": steps, "bytes": nbytes, "ms": ms,
+                    "GB/s": gbs, "GB/s_per_workgroup": gbs / wgs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS})
     print(json.dumps({"metric": "scan access-pattern bandwidth (random row-segment gathers and stores, no arithmetic)",
                       "unit": "GB/s", "n_gpus": 1, "peak": HBM_PEAK_GBS, "data": "synthetic",
                       "config": {"workload": "row_traffic", "row_bytes": row_bytes,
-                                 "per_step": "64 write-row and 64 read-row segments gathered, 64 stored"},
+                                 "per_step": "64 write-row and 64 read-row segments gathered, 64 stored, "
+                                             "per token group"},
                       "results": out}), flush=True)
 
 

@@ -13,7 +13,9 @@
 // step with one 16-byte LDS-destination buffer load per lane, D steps are in
 // flight, and the write rows' segments are stored back from LDS -- with row
 // indices drawn by a hash instead of slot lists, and no arithmetic between
-// the load and the store.
+// the load and the store.  With P > 1 token groups a workgroup runs P such
+// streams of independent rows on the same segment (P times the waves and the
+// rows in flight per CU).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,21 +75,24 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// grid: chains * (row_bytes / (16 G)) workgroups of G waves; rows per chain
-// must be a power of two.
-template <int G, int D>
-__global__ void __launch_bounds__(64 * G) row_traffic_kernel(float *M, uint32_t nrows_log2, uint32_t row_bytes,
-                                                             uint32_t steps, uint32_t seed)
+// grid: chains * (row_bytes / (16 G)) workgroups of G * P waves (P token
+// groups of G waves, each group moving its own rows); rows per chain must be
+// a power of two.
+template <int G, int P, int D>
+__global__ void __launch_bounds__(64 * G * P) row_traffic_kernel(float *M, uint32_t nrows_log2, uint32_t row_bytes,
+                                                                 uint32_t steps, uint32_t seed)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int RPW = kWave / G;
     constexpr int NVM = 3;   // two gathers and one store per step
-    __shared__ f32x4 gath[D][2][kWave][G];
+    __shared__ f32x4 gath_all[P][D][2][kWave][G];
     const uint32_t nline = row_bytes / 128u;   // 128-byte lines per row
     uint32_t grp, part;
     xcd_place(blockIdx.x, (uint32_t)gridDim.x / (8u / G), 8u / G, grp, part);
     const uint32_t chain = grp / nline, seg = (grp % nline) * (8u / G) + part;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int wave_all = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int tg = wave_all / G, wave = wave_all % G;   // token group, wave within it
+    auto &gath = gath_all[tg];
     const int lane = (int)(threadIdx.x & 63);
     const uint32_t rr = (uint32_t)(wave * RPW + lane / G);   // row of the step this lane moves
     const uint32_t piece = (uint32_t)(lane % G);
@@ -97,7 +102,7 @@ __global__ void __launch_bounds__(64 * G) row_traffic_kernel(float *M, uint32_t 
     const uint32_t rmask = (1u << nrows_log2) - 1u;
     const uint32_t col = seg * 16u * G + piece * 16u;
     auto offset = [&](uint32_t step, uint32_t kind) {
-        const uint32_t row = mix(seed ^ mix(chain * 0x9E3779B1u + step * 0x85EBCA6Bu + (rr * 2u + kind) * 0xC2B2AE35u)) &
+        const uint32_t row = mix(seed ^ mix(chain * 0x9E3779B1u + step * 0x85EBCA6Bu + (rr * 2u + kind + 1024u * (uint32_t)tg) * 0xC2B2AE35u)) &
                              rmask;
         return row * row_bytes + col;
     };
@@ -136,13 +141,13 @@ __global__ void __launch_bounds__(64 * G) row_traffic_kernel(float *M, uint32_t 
 #endif
 }
 
-template <int G>
+template <int G, int P>
 hipError_t launch_g(float *M, int64_t chains, int nrows_log2, int row_bytes, int64_t steps, uint32_t seed,
                     hipStream_t st)
 {
     const int64_t wgs = chains * (row_bytes / (16 * G));
-    hipLaunchKernelGGL((row_traffic_kernel<G, 4>), dim3((unsigned)wgs), dim3(64 * G), 0, st, M, (uint32_t)nrows_log2,
-                       (uint32_t)row_bytes, (uint32_t)steps, seed);
+    hipLaunchKernelGGL((row_traffic_kernel<G, P, 4>), dim3((unsigned)wgs), dim3(64 * G * P), 0, st, M,
+                       (uint32_t)nrows_log2, (uint32_t)row_bytes, (uint32_t)steps, seed);
     return hipGetLastError();
 }
 
@@ -155,20 +160,23 @@ extern "C" {
 // bytes, contents overwritten with values read from it): per step and
 // workgroup, 64 write rows and 64 read rows of one seg_bytes-byte segment
 // are gathered and the 64 write-row segments stored back.  seg_bytes = 32,
-// 64 or 128 (G = 2, 4 or 8 waves per workgroup); row_bytes a multiple of
-// 128 (whole lines); one chain below 2 GiB.  Returns 0 or a HIP error code (-1 for
-// invalid arguments).  Bytes moved: chains * row_bytes / seg_bytes * steps *
-// 64 * 3 * seg_bytes.
-int sdm_bench_row_traffic(float *M, int64_t chains, int nrows_log2, int row_bytes, int seg_bytes, int64_t steps,
-                          uint32_t seed, hipStream_t stream)
+// 64 or 128 (G = 2, 4 or 8 waves per workgroup); token_groups = P streams of
+// independent rows per workgroup (1, or 4 with 32-byte and 2 with 128-byte
+// segments); row_bytes a multiple of 128 (whole lines); one chain below
+// 2 GiB.  Returns 0 or a HIP error code (-1 for invalid arguments).  Bytes
+// moved: chains * row_bytes / seg_bytes * P * steps * 64 * 3 * seg_bytes.
+int sdm_bench_row_traffic(float *M, int64_t chains, int nrows_log2, int row_bytes, int seg_bytes, int token_groups,
+                          int64_t steps, uint32_t seed, hipStream_t stream)
 {
     if (!M || chains < 1 || nrows_log2 < 6 || nrows_log2 > 24 || row_bytes < 128 || row_bytes % 128 ||
         steps < 1 || steps > (1 << 30) || ((uint64_t)row_bytes << nrows_log2) >= (1ull << 31))
         return -1;
-    switch (seg_bytes) {
-    case 32: return (int)launch_g<2>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
-    case 64: return (int)launch_g<4>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
-    case 128: return (int)launch_g<8>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
+    switch (seg_bytes * 8 + token_groups) {
+    case 32 * 8 + 1: return (int)launch_g<2, 1>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
+    case 32 * 8 + 4: return (int)launch_g<2, 4>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
+    case 64 * 8 + 1: return (int)launch_g<4, 1>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
+    case 128 * 8 + 1: return (int)launch_g<8, 1>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
+    case 128 * 8 + 2: return (int)launch_g<8, 2>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
     default: return -1;
     }
 }
