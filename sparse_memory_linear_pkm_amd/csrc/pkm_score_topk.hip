@@ -9,7 +9,9 @@
 //   1. for each half c: the [16 x d_k/2] x [d_k/2 x n_sub] score tile on bf16
 //      MFMA (fp32 accumulation) into LDS;
 //   2. each wave takes 4 of the 16 rows, one per 16-lane group: exact top-k'
-//      of the half (pkm_select16.h);
+//      of the half (pkm_select16.h); with 1024 sub-keys per half the half is
+//      scored and selected in two parts of 512 and the two exact part lists
+//      merged, which halves the tile and doubles the workgroups a CU holds;
 //   3. each wave: exact top-n of the outer-sum candidates of its 4 rows
 //      (staircase-pruned, with an exact fallback), softmax, store slots and
 //      weights.
@@ -60,11 +62,16 @@ __host__ __device__ inline AddrLds addr_lds_layout(int n_sub, int kp)
 
 // Codebook loads a wave issues together in the scoring (sub-key tiles).
 constexpr int kScoreNB = 4;
+// Sub-keys per part of a half in the split form.
+constexpr int kSplit = 512;
 
 // NK: compile-time k-steps of the scoring tile (d_k = 64 * NK), 0 = any d_k.
 // FULL: n_sub is a multiple of 16 * kScoreNB (no bounds checks in the scoring).
-template <bool BF16, int NK, bool FULL>
-__global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, int ntiles)
+// SPLIT: each half scored and selected in two parts of kSplit sub-keys
+// (n_sub = 2 kSplit, k' <= 32), so that the tile, and the workgroup's LDS,
+// is half as large.
+template <bool BF16, int NK, bool FULL, bool SPLIT>
+__global__ void __launch_bounds__(256, SPLIT ? 4 : 1) pkm_score_topk_kernel(AddressArgs args, int ntiles)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     // id -> (kind, h, tile): groups of (head, kind) pairs are pinned to one XCD.
@@ -96,7 +103,7 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
     const int lane = lane_id();
     const int g = lane >> 4, c16 = lane & (kGroupLanes - 1);
 
-    const AddrLds lay = addr_lds_layout(n_sub, kp);
+    const AddrLds lay = addr_lds_layout(SPLIT ? kSplit : n_sub, kp);
     const int sst = lay.sst;
     uint32_t *S = reinterpret_cast<uint32_t *>(smem + lay.S);
     HalfEntry *L = reinterpret_cast<HalfEntry *>(smem + lay.L);
@@ -116,9 +123,10 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
     // the padding of every score row past n_sub holds -inf (below every real
     // score; the scoring never writes it)
     {
-        const int padw = sst - n_sub;
+        const int tcols = SPLIT ? kSplit : n_sub;   // sub-keys in the tile
+        const int padw = sst - tcols;
         for (int e = threadIdx.x; e < kTileRows * padw; e += blockDim.x)
-            S[(e / padw) * sst + n_sub + e % padw] = 0xFF800000u;
+            S[(e / padw) * sst + tcols + e % padw] = 0xFF800000u;
     }
 
     // rows of this wave: wave + 4 g for lane group g
@@ -127,38 +135,62 @@ __global__ void __launch_bounds__(256) pkm_score_topk_kernel(AddressArgs args, i
 
     // the half lists of this lane's row, entries 4 c16 .. 4 c16 + 3
     HalfEntry hl[2][4];
+    // SPLIT: each half's sub-keys in parts of kSplit, one part in the tile at
+    // a time; the part lists are exact and merge_sorted16 takes the best k'
+    // of their union (the same list, in the same order, as one selection over
+    // the whole half)
+    constexpr int kParts = SPLIT ? 2 : 1;
+    const int ncols = SPLIT ? kSplit : n_sub;   // sub-keys per part
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        score_half_tile<BF16, kScoreNB, NK, true, FULL>(xb, row_stride, nrows, kTileRows,
-                                                       Cb + (int64_t)c * n_sub * half * esz, c, half, n_sub, S,
-                                                       sst);
-        __syncthreads();
-        const bool bad = half_topk16(S, sst, row_g, n_sub, kp, rb, hl[c]);
-        // rows the fast path could not vouch for: the exact one-row routine,
-        // its list handed to the row's lane group through the wave's scratch
-        const uint64_t bb = __ballot(bad);
-        for (int gg = 0; gg < kAddrWaves; ++gg) {
-            if ((bb >> (16 * gg)) & 0xFFFFull) {
-                const int rows1[1] = {wave + kAddrWaves * gg};
-                uint64_t keys[1];
-                half_topk<1, true>(S, rows1, n_sub, kp, wscr, keys, sst);
-                wave_lds_sync();
-                if (lane < kp)
-                    wscr[lane] = ((uint64_t)key_index(keys[0]) << 32) | __float_as_uint(key_score(keys[0]));
-                wave_lds_sync();
-                if (g == gg) {
+        HalfEntry part_l[kParts][4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 4 * c16 + r;
-                        const uint64_t e = wscr[j < kp ? j : 0];
-                        hl[c][r].score = (uint32_t)e;
-                        hl[c][r].index = (uint32_t)(e >> 32);
+        for (int pt = 0; pt < kParts; ++pt) {
+            // (the split form loads two sub-key tiles per round instead of four:
+            // fewer registers, so that four of its workgroups fit a CU)
+            score_half_tile<BF16, SPLIT ? 2 : kScoreNB, NK, true, FULL>(
+                xb, row_stride, nrows, kTileRows, Cb + ((int64_t)c * n_sub + (int64_t)pt * ncols) * half * esz, c,
+                half, ncols, S, sst);
+            __syncthreads();
+            HalfEntry(&pl)[4] = part_l[pt];
+            const bool bad = half_topk16(S, sst, row_g, ncols, kp, rb, pl);
+            // rows the fast path could not vouch for: the exact one-row
+            // routine, its list handed to the row's lane group through the
+            // wave's scratch
+            const uint64_t bb = __ballot(bad);
+            for (int gg = 0; gg < kAddrWaves; ++gg) {
+                if ((bb >> (16 * gg)) & 0xFFFFull) {
+                    const int rows1[1] = {wave + kAddrWaves * gg};
+                    uint64_t keys[1];
+                    half_topk<1, true>(S, rows1, ncols, kp, wscr, keys, sst);
+                    wave_lds_sync();
+                    if (lane < kp)
+                        wscr[lane] = ((uint64_t)key_index(keys[0]) << 32) | __float_as_uint(key_score(keys[0]));
+                    wave_lds_sync();
+                    if (g == gg) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = 4 * c16 + r;
+                            const uint64_t e = wscr[j < kp ? j : 0];
+                            pl[r].score = (uint32_t)e;
+                            pl[r].index = (uint32_t)(e >> 32);
+                        }
                     }
+                    wave_lds_sync();
                 }
-                wave_lds_sync();
             }
+            if (SPLIT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pl[r].index += (uint32_t)(pt * ncols);
+            }
+            __syncthreads();   // the tile is free: every wave has finished reading it
         }
-        __syncthreads();   // the tile is free: every wave has finished reading it
+        if constexpr (SPLIT) {
+            merge_sorted16(part_l[0], part_l[kParts - 1], kp, hl[c]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hl[c][r] = part_l[0][r];
+        }
     }
     // both lists into LDS for the merge (each wave reads only its own rows)
 #pragma unroll
@@ -216,7 +248,13 @@ hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t st
     const int64_t ntiles = (args.BT + kTileRows - 1) / kTileRows;
     const int64_t grid = ntiles * 2 * args.H;
     if (ntiles > INT32_MAX || grid > UINT32_MAX) return hipErrorInvalidValue;
-    size_t smem = address_smem_bytes(args.n_sub, args.k_prime);
+    // halves of 1024 sub-keys selected in two parts of 512 (LDS 40 KB instead
+    // of 72 KB: four workgroups per CU instead of two).  Not in the
+    // one-per-CU launch: there the occupancy is fixed and the split form's
+    // extra selection work only makes it longer (measured: the long-context
+    // step's overlapped addressing 232 -> 345 ms and its scan 1-2% slower).
+    const bool split = !one_per_cu && bf16 && args.d_k == 128 && args.n_sub == 2 * kSplit && args.k_prime <= 32;
+    size_t smem = address_smem_bytes(split ? kSplit : args.n_sub, args.k_prime);
     if (one_per_cu && smem < kOnePerCuLds) smem = kOnePerCuLds;   // the extra LDS is never touched
     auto launch = [&](auto kern) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -227,11 +265,13 @@ hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t st
     hipError_t e;
     const bool full = args.n_sub % (16 * kScoreNB) == 0;
     if (!bf16)
-        e = launch(pkm_score_topk_kernel<false, 0, false>);
+        e = launch(pkm_score_topk_kernel<false, 0, false, false>);
+    else if (split)
+        e = launch(pkm_score_topk_kernel<true, 2, true, true>);
     else if (args.d_k == 128)
-        e = full ? launch(pkm_score_topk_kernel<true, 2, true>) : launch(pkm_score_topk_kernel<true, 2, false>);
+        e = full ? launch(pkm_score_topk_kernel<true, 2, true, false>) : launch(pkm_score_topk_kernel<true, 2, false, false>);
     else
-        e = full ? launch(pkm_score_topk_kernel<true, 0, true>) : launch(pkm_score_topk_kernel<true, 0, false>);
+        e = full ? launch(pkm_score_topk_kernel<true, 0, true, false>) : launch(pkm_score_topk_kernel<true, 0, false, false>);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

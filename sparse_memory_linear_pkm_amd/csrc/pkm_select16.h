@@ -368,6 +368,73 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
     return row_bad;
 }
 
+// Compare-exchange stage of 64-bit keys (element i = 4c + r): i and i ^ M
+// are compared and the lower index keeps the larger key; M in {1, 2, 4, 8,
+// 16, 32}.
+template <int M>
+__device__ __forceinline__ void cmpx64_stage(uint64_t (&x)[4])
+{
+    constexpr int LM = M >> 2, RM = M & 3;
+    if constexpr (LM == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if ((r & RM) == 0) {
+                const uint64_t a = x[r], b = x[r ^ RM];
+                x[r] = a > b ? a : b;
+                x[r ^ RM] = a > b ? b : a;
+            }
+        }
+    } else {
+        const bool lower = (lane_id() & LM) == 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t lo = row_xor<LM>((uint32_t)x[r]), hi = row_xor<LM>((uint32_t)(x[r] >> 32));
+            const uint64_t y = ((uint64_t)hi << 32) | lo;
+            const bool take = (y > x[r]) == lower;
+            x[r] = take ? y : x[r];
+        }
+    }
+}
+
+// The best kp (<= 32) of two sorted lists of kp entries each (best first in
+// the total order score descending, index ascending), one list per 16-lane
+// group as half_topk16 leaves them (lane c: entries 4c .. 4c + 3).  The
+// first list followed by the second in reverse is a bitonic sequence of 64
+// keys; six half-cleaner stages sort it, and its first kp elements are the
+// answer, exact (the keys are the full (score, index) order).  Lane c
+// receives entries 4c .. 4c + 3 of the result in out[].
+__device__ __forceinline__ void merge_sorted16(const HalfEntry (&a)[4], const HalfEntry (&b)[4], int kp,
+                                               HalfEntry (&out)[4])
+{
+    const int c = lane_id() & (kGroupLanes - 1);
+    uint64_t ka[4], kb[4], x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool live = 4 * c + r < kp;
+        ka[r] = live ? score_key(__uint_as_float(a[r].score), a[r].index) : 0ull;
+        kb[r] = live ? score_key(__uint_as_float(b[r].score), b[r].index) : 0ull;
+    }
+    // element 32 + 4k + r (lane 8 + k) = second list's entry 31 - 4k - r,
+    // held by lane 7 - k in register 3 - r: a row_mirror of the registers in
+    // reverse order
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t lo = row_xor<15>((uint32_t)kb[3 - r]), hi = row_xor<15>((uint32_t)(kb[3 - r] >> 32));
+        x[r] = c < 8 ? ka[r] : (((uint64_t)hi << 32) | lo);
+    }
+    cmpx64_stage<32>(x);
+    cmpx64_stage<16>(x);
+    cmpx64_stage<8>(x);
+    cmpx64_stage<4>(x);
+    cmpx64_stage<2>(x);
+    cmpx64_stage<1>(x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        out[r].score = __float_as_uint(key_score(x[r]));
+        out[r].index = key_index(x[r]);
+    }
+}
+
 // Merge of the two half lists of the 4 rows of this wave into the best n
 // slots and their softmax weights.  L0, L1: this lane's row's k' entries of
 // half 0 and half 1.  On success lane (c, r) holds rank 4c + r: slot[r],

@@ -104,6 +104,27 @@ def test_address_identity_codebook_bit_exact(sdm, torch):
     np.testing.assert_allclose(grw, orw, rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("n_sub", [1024, 512])
+def test_address_integer_scores_bit_exact(sdm, torch, n_sub):
+    """Codebook and inputs in {-1, 0, 1}: every half score is a small integer,
+    exact in fp32 whatever the summation order, so scores tie very often and
+    the lists (ties to the lower index, at both levels) must equal the
+    oracle's bit for bit.  n_sub = 1024 exercises the selection of each half
+    in two parts of 512 sub-keys and their merge; 512 the one-part form."""
+    d = Dims(B=1, T=40, H=2, d_k=128, n_sub=n_sub, d_v=32, k_prime=32, W=32, R=32)
+    note(f"address integer scores n_sub={n_sub}")
+    g = np.random.default_rng(11)
+    tern = lambda shape: synth.f32_to_bf16_bits(g.integers(-1, 2, size=shape).astype(np.float32))
+    x = {"k": tern((d.B, d.T, d.H, d.d_k)), "q": tern((d.B, d.T, d.H, d.d_k))}
+    x["C_w"] = x["C_r"] = tern((d.H, 2, d.n_sub, d.d_k // 2))
+    gw, gww, gr, grw = run_address(sdm, torch, x, d)
+    ow, oww, orr, orw = oracle.address(x["k"], x["q"], x["C_w"], x["C_r"], d)
+    np.testing.assert_array_equal(gw, ow)
+    np.testing.assert_array_equal(gr, orr)
+    np.testing.assert_allclose(gww, oww, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(grw, orw, rtol=0, atol=1e-6)
+
+
 # ---------------------------------------------------------------------------
 SCAN_CASES = {
     # name: (dims, hazard slot pool or None)
