@@ -144,6 +144,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 4 : 1) pkm_score_topk_kernel(Addr
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         HalfEntry part_l[kParts][4];
+        uint32_t part_n[kParts];   // entries of each part's list (the row's)
 #pragma unroll
         for (int pt = 0; pt < kParts; ++pt) {
             // (the split form loads two sub-key tiles per round instead of four:
@@ -153,7 +154,16 @@ __global__ void __launch_bounds__(256, SPLIT ? 4 : 1) pkm_score_topk_kernel(Addr
                 half, ncols, S, sst);
             __syncthreads();
             HalfEntry(&pl)[4] = part_l[pt];
-            const bool bad = half_topk16(S, sst, row_g, ncols, kp, rb, pl);
+            // the second part lists only candidates at or above the first
+            // part's k'-th score: the first part alone has k' at or above it,
+            // and on equal scores its lower sub-keys come first
+            uint32_t floor_bits = 0u;
+            if (pt > 0) {
+                const uint32_t sc[4] = {part_l[0][0].score, part_l[0][1].score, part_l[0][2].score,
+                                        part_l[0][3].score};
+                floor_bits = score_bits(__uint_as_float(rank_value(sc, kp - 1)));
+            }
+            const bool bad = half_topk16(S, sst, row_g, ncols, kp, rb, pl, part_n[pt], pt > 0, floor_bits);
             // rows the fast path could not vouch for: the exact one-row
             // routine, its list handed to the row's lane group through the
             // wave's scratch
@@ -175,6 +185,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 4 : 1) pkm_score_topk_kernel(Addr
                             pl[r].score = (uint32_t)e;
                             pl[r].index = (uint32_t)(e >> 32);
                         }
+                        part_n[pt] = (uint32_t)kp;
                     }
                     wave_lds_sync();
                 }
@@ -186,7 +197,7 @@ __global__ void __launch_bounds__(256, SPLIT ? 4 : 1) pkm_score_topk_kernel(Addr
             __syncthreads();   // the tile is free: every wave has finished reading it
         }
         if constexpr (SPLIT) {
-            merge_sorted16(part_l[0], part_l[kParts - 1], kp, hl[c]);
+            merge_sorted16(part_l[0], part_l[kParts - 1], kp, (int)part_n[kParts - 1], hl[c]);
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) hl[c][r] = part_l[0][r];

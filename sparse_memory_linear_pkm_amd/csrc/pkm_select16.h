@@ -232,11 +232,17 @@ __device__ __forceinline__ uint32_t compact_row(const uint32_t (&mask)[NMW], Row
 // n_sub up to the next multiple of 64.  Lane c of the row's group receives
 // entries 4c .. 4c + 3 of the row's list (best first) in ent[] (entries past
 // k' are undefined).  Returns true if this lane's row must be redone by the
-// exact one-row routine (ent[] is then undefined).  Scores are compared as floats while
+// exact one-row routine (ent[] is then undefined).
+// With use_floor (uniform over the wave), the threshold is floor_bits (the
+// row's, as score bits) instead of the k'-th group maximum: only candidates
+// at or above it are listed, `count` of them (at most k'; entries past count
+// are undefined).  A caller that needs only the candidates above a score
+// already known to have k' others at or above it skips the threshold sort.  Scores are compared as floats while
 // scanning (the same order as score_bits for finite values) and as
 // score_bits in the sorts.
 __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_g, int n_sub, int kp, RowBuf rb,
-                                            HalfEntry (&ent)[4])
+                                            HalfEntry (&ent)[4], uint32_t &count, bool use_floor = false,
+                                            uint32_t floor_bits = 0u)
 {
     const int c = lane_id() & (kGroupLanes - 1);
     const uint32_t *Sr = S + (size_t)row_g * sst;
@@ -276,9 +282,19 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
     uint32_t m[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) m[r] = score_bits(mf[r]);
-    sort64_desc(m);
-    const uint32_t tau = rank_value(m, kp - 1);
-    const uint32_t top = rank_value(m, 0);
+    uint32_t tau, top;
+    if (use_floor) {
+        uint32_t mx = m[0] > m[1] ? m[0] : m[1];
+        mx = mx > m[2] ? mx : m[2];
+        mx = mx > m[3] ? mx : m[3];
+        top = group_max16(mx);
+        tau = floor_bits;
+        top = top > tau ? top : tau;   // no candidate reaches tau: none survives
+    } else {
+        sort64_desc(m);
+        tau = rank_value(m, kp - 1);
+        top = rank_value(m, 0);
+    }
     const float tauf = __uint_as_float(raw_of_score_bits(tau));
     // candidates reaching tau: word w holds chunks 8w .. 8w + 7, candidate
     // (chunk i, k) at bit 31 - (4 (i - 8w) + k).  All 8 chunks of a word are
@@ -365,6 +381,7 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
         ent[r].score = raw_of_score_bits(s[r]);
         ent[r].index = p[r];
     }
+    count = total < (uint32_t)kp ? total : (uint32_t)kp;
     return row_bad;
 }
 
@@ -396,23 +413,23 @@ __device__ __forceinline__ void cmpx64_stage(uint64_t (&x)[4])
     }
 }
 
-// The best kp (<= 32) of two sorted lists of kp entries each (best first in
-// the total order score descending, index ascending), one list per 16-lane
-// group as half_topk16 leaves them (lane c: entries 4c .. 4c + 3).  The
+// The best kp (<= 32) of two sorted lists, the first of kp entries and the
+// second of nb <= kp (best first in the total order score descending, index
+// ascending), one list per 16-lane group as half_topk16 leaves them (lane c:
+// entries 4c .. 4c + 3; nb is the row's, the same in its 16 lanes).  The
 // first list followed by the second in reverse is a bitonic sequence of 64
 // keys; six half-cleaner stages sort it, and its first kp elements are the
 // answer, exact (the keys are the full (score, index) order).  Lane c
 // receives entries 4c .. 4c + 3 of the result in out[].
-__device__ __forceinline__ void merge_sorted16(const HalfEntry (&a)[4], const HalfEntry (&b)[4], int kp,
+__device__ __forceinline__ void merge_sorted16(const HalfEntry (&a)[4], const HalfEntry (&b)[4], int kp, int nb,
                                                HalfEntry (&out)[4])
 {
     const int c = lane_id() & (kGroupLanes - 1);
     uint64_t ka[4], kb[4], x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const bool live = 4 * c + r < kp;
-        ka[r] = live ? score_key(__uint_as_float(a[r].score), a[r].index) : 0ull;
-        kb[r] = live ? score_key(__uint_as_float(b[r].score), b[r].index) : 0ull;
+        ka[r] = 4 * c + r < kp ? score_key(__uint_as_float(a[r].score), a[r].index) : 0ull;
+        kb[r] = 4 * c + r < nb ? score_key(__uint_as_float(b[r].score), b[r].index) : 0ull;
     }
     // element 32 + 4k + r (lane 8 + k) = second list's entry 31 - 4k - r,
     // held by lane 7 - k in register 3 - r: a row_mirror of the registers in
