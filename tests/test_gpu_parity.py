@@ -73,6 +73,10 @@ ADDRESS_CASES = {
     "sep_codebook": (Dims(B=2, T=19, H=3, d_k=64, n_sub=40, d_v=32, k_prime=12, W=9, R=30), dict(sep=True)),
     "kprime_below_W": (Dims(B=1, T=33, H=2, d_k=128, n_sub=64, d_v=32, k_prime=5, W=20, R=25), {}),
     "fp32_wide": (Dims(B=1, T=40, H=2, d_k=24, n_sub=50, d_v=32, k_prime=10, W=7, R=3, in_dtype="f32"), {}),
+    # 1024 sub-keys per half: the two-part selection, with k' below 32 and
+    # below W (the PKM approximation), and separate codebooks
+    "split_kp16_W20": (Dims(B=1, T=33, H=2, d_k=128, n_sub=1024, d_v=32, k_prime=16, W=20, R=9), {}),
+    "split_kp5_sep": (Dims(B=2, T=21, H=1, d_k=128, n_sub=1024, d_v=32, k_prime=5, W=3, R=25), dict(sep=True)),
 }
 
 
@@ -104,15 +108,15 @@ def test_address_identity_codebook_bit_exact(sdm, torch):
     np.testing.assert_allclose(grw, orw, rtol=0, atol=1e-6)
 
 
-@pytest.mark.parametrize("n_sub", [1024, 512])
-def test_address_integer_scores_bit_exact(sdm, torch, n_sub):
+@pytest.mark.parametrize("n_sub,kp", [(1024, 32), (512, 32), (1024, 12)])
+def test_address_integer_scores_bit_exact(sdm, torch, n_sub, kp):
     """Codebook and inputs in {-1, 0, 1}: every half score is a small integer,
     exact in fp32 whatever the summation order, so scores tie very often and
     the lists (ties to the lower index, at both levels) must equal the
     oracle's bit for bit.  n_sub = 1024 exercises the selection of each half
     in two parts of 512 sub-keys and their merge; 512 the one-part form."""
-    d = Dims(B=1, T=40, H=2, d_k=128, n_sub=n_sub, d_v=32, k_prime=32, W=32, R=32)
-    note(f"address integer scores n_sub={n_sub}")
+    d = Dims(B=1, T=40, H=2, d_k=128, n_sub=n_sub, d_v=32, k_prime=kp, W=32, R=kp)
+    note(f"address integer scores n_sub={n_sub} k'={kp}")
     g = np.random.default_rng(11)
     tern = lambda shape: synth.f32_to_bf16_bits(g.integers(-1, 2, size=shape).astype(np.float32))
     x = {"k": tern((d.B, d.T, d.H, d.d_k)), "q": tern((d.B, d.T, d.H, d.d_k))}
