@@ -82,3 +82,21 @@ def test_chunked_pipelined_prefill_equals_one_call(sdm, torch, d, nc):
     for name, a, b in (("widx", w1, w2), ("wwt", ww1, ww2), ("ridx", r1, r2), ("rwt", rw1, rw2), ("o", o1, o2),
                        ("M", M1, M2)):
         assert np.array_equal(to_host(a), to_host(b)), name
+
+
+@pytest.mark.parametrize("n_sub,kp", [(1024, 32), (1024, 8), (512, 32)])
+def test_overlapped_addressing_equals_address(sdm, torch, n_sub, kp):
+    """sdm_pkm_address_overlapped (one workgroup per CU; for 1024 sub-keys
+    per half the one-part selection) returns the same slots and weights, bit
+    for bit, as sdm_pkm_address (for 1024 sub-keys per half the selection in
+    two parts of 512 and their merge)."""
+    d = Dims(B=2, T=300, H=3, d_k=128, n_sub=n_sub, d_v=32, k_prime=kp, W=32, R=kp)
+    note(f"overlapped vs plain addressing {d}")
+    x = synth.make_inputs_torch(d, seed=23, m0=False)
+    dims = sdm.dims_from(d)
+    a = sdm.pkm_address(x["k"], x["q"], x["C_w"], x["C_r"], dims)
+    b = [torch.empty_like(t) for t in a]
+    sdm.sdm_pkm_address_overlapped(x["k"], x["q"], x["C_w"], x["C_r"], dims, *b)
+    torch.cuda.synchronize()
+    for ta, tb, name in zip(a, b, ("widx", "wwt", "ridx", "rwt")):
+        np.testing.assert_array_equal(to_host(ta), to_host(tb), err_msg=name)
