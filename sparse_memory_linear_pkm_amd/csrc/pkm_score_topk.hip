@@ -9,9 +9,10 @@
 //   1. for each half c: the [16 x d_k/2] x [d_k/2 x n_sub] score tile on bf16
 //      MFMA (fp32 accumulation) into LDS;
 //   2. each wave takes 4 of the 16 rows, one per 16-lane group: exact top-k'
-//      of the half (pkm_select16.h); with 1024 sub-keys per half the half is
-//      scored and selected in two parts of 512 and the two exact part lists
-//      merged, which halves the tile and doubles the workgroups a CU holds;
+//      of the half (pkm_select16.h); with 1024 or more sub-keys per half the
+//      half is scored and selected in parts of 512 and the exact part lists
+//      merged, which keeps the tile at 512 sub-keys and four workgroups on a
+//      CU;
 //   3. each wave: exact top-n of the outer-sum candidates of its 4 rows
 //      (staircase-pruned, with an exact fallback), softmax, store slots and
 //      weights.
@@ -67,12 +68,14 @@ constexpr int kSplit = 512;
 
 // NK: compile-time k-steps of the scoring tile (d_k = 64 * NK), 0 = any d_k.
 // FULL: n_sub is a multiple of 16 * kScoreNB (no bounds checks in the scoring).
-// SPLIT: each half scored and selected in two parts of kSplit sub-keys
-// (n_sub = 2 kSplit, k' <= 32), so that the tile, and the workgroup's LDS,
-// is half as large.
-template <bool BF16, int NK, bool FULL, bool SPLIT>
-__global__ void __launch_bounds__(256, SPLIT ? 4 : 1) pkm_score_topk_kernel(AddressArgs args, int ntiles)
+// PARTS != 1: each half scored and selected in parts of kSplit sub-keys
+// (n_sub a multiple of kSplit, at least two parts, k' <= 32), so that the
+// tile, and the workgroup's LDS, is that of n_sub = kSplit; PARTS = 2 fixes
+// two parts (n_sub = 1024) at compile time, 0 takes n_sub / kSplit.
+template <bool BF16, int NK, bool FULL, int PARTS>
+__global__ void __launch_bounds__(256, PARTS != 1 ? 4 : 1) pkm_score_topk_kernel(AddressArgs args, int ntiles)
 {
+    constexpr bool SPLIT = PARTS != 1;
     extern __shared__ __align__(16) unsigned char smem[];
     // id -> (kind, h, tile): groups of (head, kind) pairs are pinned to one XCD.
     const int npairs = 2 * args.H;
@@ -136,71 +139,76 @@ __global__ void __launch_bounds__(256, SPLIT ? 4 : 1) pkm_score_topk_kernel(Addr
     // the half lists of this lane's row, entries 4 c16 .. 4 c16 + 3
     HalfEntry hl[2][4];
     // SPLIT: each half's sub-keys in parts of kSplit, one part in the tile at
-    // a time; the part lists are exact and merge_sorted16 takes the best k'
-    // of their union (the same list, in the same order, as one selection over
+    // a time; each part's list is exact, and merge_sorted16 folds it into the
+    // best k' so far (the same list, in the same order, as one selection over
     // the whole half)
-    constexpr int kParts = SPLIT ? 2 : 1;
+    const int nparts = PARTS > 0 ? PARTS : n_sub / kSplit;
     const int ncols = SPLIT ? kSplit : n_sub;   // sub-keys per part
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        HalfEntry part_l[kParts][4];
-        uint32_t part_n[kParts];   // entries of each part's list (the row's)
-#pragma unroll
-        for (int pt = 0; pt < kParts; ++pt) {
-            // (the split form loads two sub-key tiles per round instead of four:
-            // fewer registers, so that four of its workgroups fit a CU)
-            score_half_tile<BF16, SPLIT ? 2 : kScoreNB, NK, true, FULL>(
-                xb, row_stride, nrows, kTileRows, Cb + ((int64_t)c * n_sub + (int64_t)pt * ncols) * half * esz, c,
-                half, ncols, S, sst);
-            __syncthreads();
-            HalfEntry(&pl)[4] = part_l[pt];
-            // the second part lists only candidates at or above the first
-            // part's k'-th score: the first part alone has k' at or above it,
-            // and on equal scores its lower sub-keys come first
-            uint32_t floor_bits = 0u;
-            if (pt > 0) {
-                const uint32_t sc[4] = {part_l[0][0].score, part_l[0][1].score, part_l[0][2].score,
-                                        part_l[0][3].score};
-                floor_bits = score_bits(__uint_as_float(rank_value(sc, kp - 1)));
-            }
-            const bool bad = half_topk16(S, sst, row_g, ncols, kp, rb, pl, part_n[pt], pt > 0, floor_bits);
-            // rows the fast path could not vouch for: the exact one-row
-            // routine, its list handed to the row's lane group through the
-            // wave's scratch
-            const uint64_t bb = __ballot(bad);
-            for (int gg = 0; gg < kAddrWaves; ++gg) {
-                if ((bb >> (16 * gg)) & 0xFFFFull) {
-                    const int rows1[1] = {wave + kAddrWaves * gg};
-                    uint64_t keys[1];
-                    half_topk<1, true>(S, rows1, ncols, kp, wscr, keys, sst);
-                    wave_lds_sync();
-                    if (lane < kp)
-                        wscr[lane] = ((uint64_t)key_index(keys[0]) << 32) | __float_as_uint(key_score(keys[0]));
-                    wave_lds_sync();
-                    if (g == gg) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = 4 * c16 + r;
-                            const uint64_t e = wscr[j < kp ? j : 0];
-                            pl[r].score = (uint32_t)e;
-                            pl[r].index = (uint32_t)(e >> 32);
-                        }
-                        part_n[pt] = (uint32_t)kp;
-                    }
-                    wave_lds_sync();
-                }
-            }
-            if (SPLIT) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pl[r].index += (uint32_t)(pt * ncols);
-            }
-            __syncthreads();   // the tile is free: every wave has finished reading it
+    // one part of half c: score it, select it, fold it into hl[c]
+    auto do_part = [&](const int c, const int pt) __attribute__((always_inline)) {
+        // (the split form loads two sub-key tiles per round instead of four:
+        // fewer registers, so that four of its workgroups fit a CU)
+        score_half_tile<BF16, SPLIT ? 2 : kScoreNB, NK, true, FULL>(
+            xb, row_stride, nrows, kTileRows, Cb + ((int64_t)c * n_sub + (int64_t)pt * ncols) * half * esz, c,
+            half, ncols, S, sst);
+        __syncthreads();
+        HalfEntry pl[4];
+        uint32_t pn;   // entries of this part's list (the row's)
+        // a later part lists only candidates at or above the k'-th score
+        // so far: the earlier parts alone have k' at or above it, and on
+        // equal scores their lower sub-keys come first
+        uint32_t floor_bits = 0u;
+        if (pt > 0) {
+            const uint32_t sc[4] = {hl[c][0].score, hl[c][1].score, hl[c][2].score, hl[c][3].score};
+            floor_bits = score_bits(__uint_as_float(rank_value(sc, kp - 1)));
         }
-        if constexpr (SPLIT) {
-            merge_sorted16(part_l[0], part_l[kParts - 1], kp, (int)part_n[kParts - 1], hl[c]);
+        const bool bad = half_topk16(S, sst, row_g, ncols, kp, rb, pl, pn, pt > 0, floor_bits);
+        // rows the fast path could not vouch for: the exact one-row
+        // routine, its list handed to the row's lane group through the
+        // wave's scratch
+        const uint64_t bb = __ballot(bad);
+        for (int gg = 0; gg < kAddrWaves; ++gg) {
+            if ((bb >> (16 * gg)) & 0xFFFFull) {
+                const int rows1[1] = {wave + kAddrWaves * gg};
+                uint64_t keys[1];
+                half_topk<1, true>(S, rows1, ncols, kp, wscr, keys, sst);
+                wave_lds_sync();
+                if (lane < kp)
+                    wscr[lane] = ((uint64_t)key_index(keys[0]) << 32) | __float_as_uint(key_score(keys[0]));
+                wave_lds_sync();
+                if (g == gg) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 4 * c16 + r;
+                        const uint64_t e = wscr[j < kp ? j : 0];
+                        pl[r].score = (uint32_t)e;
+                        pl[r].index = (uint32_t)(e >> 32);
+                    }
+                    pn = (uint32_t)kp;
+                }
+                wave_lds_sync();
+            }
+        }
+        __syncthreads();   // the tile is free: every wave has finished reading it
+        if (pt == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hl[c][r] = pl[r];
         } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) hl[c][r] = part_l[0][r];
+            for (int r = 0; r < 4; ++r) pl[r].index += (uint32_t)(pt * ncols);
+            HalfEntry m[4];
+            merge_sorted16(hl[c], pl, kp, (int)pn, m);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hl[c][r] = m[r];
+        }
+    };
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        if constexpr (PARTS > 0) {
+#pragma unroll
+            for (int pt = 0; pt < PARTS; ++pt) do_part(c, pt);
+        } else {
+            for (int pt = 0; pt < nparts; ++pt) do_part(c, pt);
         }
     }
     // both lists into LDS for the merge (each wave reads only its own rows)
@@ -259,12 +267,13 @@ hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t st
     const int64_t ntiles = (args.BT + kTileRows - 1) / kTileRows;
     const int64_t grid = ntiles * 2 * args.H;
     if (ntiles > INT32_MAX || grid > UINT32_MAX) return hipErrorInvalidValue;
-    // halves of 1024 sub-keys selected in two parts of 512 (LDS 40 KB instead
-    // of 72 KB: four workgroups per CU instead of two).  Not in the
+    // halves of 1024 or more sub-keys selected in parts of 512 (LDS 40 KB
+    // instead of 72 KB or more: four workgroups per CU instead of two or one).  Not in the
     // one-per-CU launch: there the occupancy is fixed and the split form's
     // extra selection work only makes it longer (measured: the long-context
     // step's overlapped addressing 232 -> 345 ms and its scan 1-2% slower).
-    const bool split = !one_per_cu && bf16 && args.d_k == 128 && args.n_sub == 2 * kSplit && args.k_prime <= 32;
+    const bool split = !one_per_cu && bf16 && args.d_k == 128 && args.n_sub >= 2 * kSplit &&
+                       args.n_sub % kSplit == 0 && args.k_prime <= 32;
     size_t smem = address_smem_bytes(split ? kSplit : args.n_sub, args.k_prime);
     if (one_per_cu && smem < kOnePerCuLds) smem = kOnePerCuLds;   // the extra LDS is never touched
     auto launch = [&](auto kern) {
@@ -276,13 +285,15 @@ hipError_t launch_pkm_address(const AddressArgs &args, bool bf16, hipStream_t st
     hipError_t e;
     const bool full = args.n_sub % (16 * kScoreNB) == 0;
     if (!bf16)
-        e = launch(pkm_score_topk_kernel<false, 0, false, false>);
+        e = launch(pkm_score_topk_kernel<false, 0, false, 1>);
+    else if (split && args.n_sub == 2 * kSplit)
+        e = launch(pkm_score_topk_kernel<true, 2, true, 2>);
     else if (split)
-        e = launch(pkm_score_topk_kernel<true, 2, true, true>);
+        e = launch(pkm_score_topk_kernel<true, 2, true, 0>);
     else if (args.d_k == 128)
-        e = full ? launch(pkm_score_topk_kernel<true, 2, true, false>) : launch(pkm_score_topk_kernel<true, 2, false, false>);
+        e = full ? launch(pkm_score_topk_kernel<true, 2, true, 1>) : launch(pkm_score_topk_kernel<true, 2, false, 1>);
     else
-        e = full ? launch(pkm_score_topk_kernel<true, 0, true, false>) : launch(pkm_score_topk_kernel<true, 0, false, false>);
+        e = full ? launch(pkm_score_topk_kernel<true, 0, true, 1>) : launch(pkm_score_topk_kernel<true, 0, false, 1>);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

@@ -108,13 +108,14 @@ def test_address_identity_codebook_bit_exact(sdm, torch):
     np.testing.assert_allclose(grw, orw, rtol=0, atol=1e-6)
 
 
-@pytest.mark.parametrize("n_sub,kp", [(1024, 32), (512, 32), (1024, 12)])
+@pytest.mark.parametrize("n_sub,kp", [(1024, 32), (512, 32), (1024, 12), (2048, 32), (1536, 20)])
 def test_address_integer_scores_bit_exact(sdm, torch, n_sub, kp):
     """Codebook and inputs in {-1, 0, 1}: every half score is a small integer,
     exact in fp32 whatever the summation order, so scores tie very often and
     the lists (ties to the lower index, at both levels) must equal the
-    oracle's bit for bit.  n_sub = 1024 exercises the selection of each half
-    in two parts of 512 sub-keys and their merge; 512 the one-part form."""
+    oracle's bit for bit.  n_sub = 1024, 1536 and 2048 exercise the selection
+    of each half in two, three and four parts of 512 sub-keys and their
+    merges; 512 the one-part form."""
     d = Dims(B=1, T=40, H=2, d_k=128, n_sub=n_sub, d_v=32, k_prime=kp, W=32, R=kp)
     note(f"address integer scores n_sub={n_sub} k'={kp}")
     g = np.random.default_rng(11)

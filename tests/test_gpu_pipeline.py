@@ -84,12 +84,12 @@ def test_chunked_pipelined_prefill_equals_one_call(sdm, torch, d, nc):
         assert np.array_equal(to_host(a), to_host(b)), name
 
 
-@pytest.mark.parametrize("n_sub,kp", [(1024, 32), (1024, 8), (512, 32)])
+@pytest.mark.parametrize("n_sub,kp", [(1024, 32), (1024, 8), (512, 32), (2048, 32)])
 def test_overlapped_addressing_equals_address(sdm, torch, n_sub, kp):
-    """sdm_pkm_address_overlapped (one workgroup per CU; for 1024 sub-keys
-    per half the one-part selection) returns the same slots and weights, bit
-    for bit, as sdm_pkm_address (for 1024 sub-keys per half the selection in
-    two parts of 512 and their merge)."""
+    """sdm_pkm_address_overlapped (one workgroup per CU, the one-part
+    selection) returns the same slots and weights, bit for bit, as
+    sdm_pkm_address (for 1024 or more sub-keys per half the selection in parts
+    of 512 and their merges)."""
     d = Dims(B=2, T=300, H=3, d_k=128, n_sub=n_sub, d_v=32, k_prime=kp, W=32, R=kp)
     note(f"overlapped vs plain addressing {d}")
     x = synth.make_inputs_torch(d, seed=23, m0=False)
