@@ -22,10 +22,11 @@
 //   1. group maxima: every lane folds its candidates into 4 running maxima
 //      (64 per row); tau = the n-th largest of them, found by sorting the 64.
 //      At least n candidates reach tau (one per group maximum above it), so
-//      the n best all do;
+//      the n best all do.  (A later part of a half split in parts instead
+//      takes the n-th best score of the earlier parts as tau.)
 //   2. the candidates that reach tau (typically 1.1-1.4 n) are compacted into
-//      a per-row LDS buffer (a per-lane bit mask, one LDS atomic per lane to
-//      reserve space, then the set bits);
+//      a per-row LDS buffer (a per-lane bit mask, a prefix sum of the lanes'
+//      counts over the row group's DPP row, then the set bits);
 //   3. the survivors are sorted as 32-bit keys: the score bits above tau,
 //      shifted right just enough to leave room for the index in the low
 //      bits.  Where the shift drops bits, two different scores can share a
