@@ -488,7 +488,11 @@ def bench_row_traffic(args, torch):
     its own rows (more requests in flight per CU); with the same bytes split
     over 4x and 16x the chains at 32 bytes; and on a 16 GiB table split into
     32, 64 and 128 chains at 128 bytes (more CUs each moving whole lines).
-    Bytes per workgroup and step: 64 rows x 3 x segment per token group."""
+    On the long-context table at 32 and 128 bytes also three variants: the
+    gathers alone (the stores issued past the buffer range), and the gathers
+    non-temporal or at device scope (bypassing the CU's L1).  Bytes per
+    workgroup and step: 64 rows x 3 x segment per token group (x 2 for the
+    gathers alone)."""
     import ctypes
     path = os.path.join(ROOT, "sparse_memory_linear_pkm_amd", "libsdm_bench.so")
     if not os.path.exists(path):
@@ -496,32 +500,36 @@ def bench_row_traffic(args, torch):
     lib = ctypes.CDLL(path)
     fn = lib.sdm_bench_row_traffic
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                   ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+                   ctypes.c_int, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
     fn.restype = ctypes.c_int
     row_bytes = 512
     M = torch.zeros(128 * (1 << 18) * row_bytes // 4, dtype=torch.float32, device="cuda")   # 16 GiB
     stream = torch.cuda.current_stream()
-    # (chains, log2 rows per chain, segment bytes, token groups)
-    configs = [(16, 20, 32, 1), (16, 20, 64, 1), (16, 20, 128, 1), (16, 20, 32, 4), (16, 20, 128, 2),
-               (64, 18, 32, 1), (256, 16, 32, 1), (32, 20, 128, 1), (64, 19, 128, 1), (128, 18, 128, 1)]
+    # (chains, log2 rows per chain, segment bytes, token groups, variant)
+    configs = [(16, 20, 32, 1, 0), (16, 20, 64, 1, 0), (16, 20, 128, 1, 0), (16, 20, 32, 4, 0), (16, 20, 128, 2, 0),
+               (64, 18, 32, 1, 0), (256, 16, 32, 1, 0), (32, 20, 128, 1, 0), (64, 19, 128, 1, 0),
+               (128, 18, 128, 1, 0), (16, 20, 32, 1, 1), (16, 20, 32, 1, 2), (16, 20, 32, 1, 3),
+               (16, 20, 128, 1, 1), (16, 20, 128, 1, 2), (16, 20, 128, 1, 3)]
+    variants = {0: "scan form", 1: "gathers only", 2: "gathers non-temporal", 3: "gathers at device scope"}
     steps = max(1024, args.steps * 1024)
     out = []
-    for chains, lg, seg, tg in configs:
+    for chains, lg, seg, tg, var in configs:
         wgs = chains * row_bytes // seg
-        nbytes = wgs * tg * steps * 64 * 3 * seg
-        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, tg, 1024, 1, stream.cuda_stream)
+        nbytes = wgs * tg * steps * 64 * (2 if var == 1 else 3) * seg
+        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, tg, var, 1024, 1, stream.cuda_stream)
         assert rc == 0, rc
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, tg, steps, 7, stream.cuda_stream)
+        rc = fn(M.data_ptr(), chains, lg, row_bytes, seg, tg, var, steps, 7, stream.cuda_stream)
         e1.record(stream)
         torch.cuda.synchronize()
         assert rc == 0, rc
         ms = e0.elapsed_time(e1)
         gbs = nbytes / (ms * 1e-3) / 1e9
         out.append({"chains": chains, "rows_per_chain": 1 << lg, "segment_bytes": seg, "token_groups": tg,
+                    "variant": variants[var],
                     "workgroups": wgs, "waves": wgs * seg // 16 * tg, "steps": steps, "bytes": nbytes, "ms": ms,
                     "GB/s": gbs, "GB/s_per_workgroup": gbs / wgs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS})
     print(json.dumps({"metric": "scan access-pattern bandwidth (random row-segment gathers and stores, no arithmetic)",

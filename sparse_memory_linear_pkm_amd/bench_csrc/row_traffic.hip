@@ -15,7 +15,10 @@
 // indices drawn by a hash instead of slot lists, and no arithmetic between
 // the load and the store.  With P > 1 token groups a workgroup runs P such
 // streams of independent rows on the same segment (P times the waves and the
-// rows in flight per CU).
+// rows in flight per CU).  Two variants isolate what the rate depends on: the
+// gathers alone (every store goes past the buffer range, so it is issued but
+// moves nothing), and the gathers with another cache policy (non-temporal, or
+// device scope, which bypasses the CU's vector L1).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,7 +81,9 @@ __device__ __forceinline__ void static_for(F &&f)
 // grid: chains * (row_bytes / (16 G)) workgroups of G * P waves (P token
 // groups of G waves, each group moving its own rows); rows per chain must be
 // a power of two.
-template <int G, int P, int D>
+// LA: cache-policy bits of the gathers (0, 2 = nt, 17 = sc0 sc1); ST: the
+// write rows are stored (else the stores go past the range).
+template <int G, int P, int D, int LA, bool ST>
 __global__ void __launch_bounds__(64 * G * P) row_traffic_kernel(float *M, uint32_t nrows_log2, uint32_t row_bytes,
                                                                  uint32_t steps, uint32_t seed)
 {
@@ -112,10 +117,10 @@ __global__ void __launch_bounds__(64 * G * P) row_traffic_kernel(float *M, uint3
         ofw[sl] = step < steps ? ow : 0x80000000u;   // past the range: dropped
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             Mrs, (__attribute__((address_space(3))) void *)&gath[sl][0][wave * RPW][0], 16,
-            step < steps ? ow : 0x80000000u, 0, 0, 0);
+            step < steps ? ow : 0x80000000u, 0, 0, LA);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             Mrs, (__attribute__((address_space(3))) void *)&gath[sl][1][wave * RPW][0], 16,
-            step < steps ? orr : 0x80000000u, 0, 0, 0);
+            step < steps ? orr : 0x80000000u, 0, 0, LA);
     };
     static_for<0, D>([&](auto s_c) __attribute__((always_inline)) {
         constexpr int s = decltype(s_c)::value;
@@ -133,7 +138,7 @@ __global__ void __launch_bounds__(64 * G * P) row_traffic_kernel(float *M, uint3
                          : "=&v"(x)
                          : "v"((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) f32x4 *)&gath[s][0][rr][piece])
                          : "memory");
-            __builtin_amdgcn_raw_buffer_store_b128(x, Mrs, ofw[s], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(x, Mrs, ST ? ofw[s] : 0x80000000u, 0, 0);
             gathers(s, step + D);
         });
     }
@@ -141,12 +146,12 @@ __global__ void __launch_bounds__(64 * G * P) row_traffic_kernel(float *M, uint3
 #endif
 }
 
-template <int G, int P>
+template <int G, int P, int LA = 0, bool ST = true>
 hipError_t launch_g(float *M, int64_t chains, int nrows_log2, int row_bytes, int64_t steps, uint32_t seed,
                     hipStream_t st)
 {
     const int64_t wgs = chains * (row_bytes / (16 * G));
-    hipLaunchKernelGGL((row_traffic_kernel<G, P, 4>), dim3((unsigned)wgs), dim3(64 * G * P), 0, st, M,
+    hipLaunchKernelGGL((row_traffic_kernel<G, P, 4, LA, ST>), dim3((unsigned)wgs), dim3(64 * G * P), 0, st, M,
                        (uint32_t)nrows_log2, (uint32_t)row_bytes, (uint32_t)steps, seed);
     return hipGetLastError();
 }
@@ -163,14 +168,30 @@ extern "C" {
 // 64 or 128 (G = 2, 4 or 8 waves per workgroup); token_groups = P streams of
 // independent rows per workgroup (1, or 4 with 32-byte and 2 with 128-byte
 // segments); row_bytes a multiple of 128 (whole lines); one chain below
-// 2 GiB.  Returns 0 or a HIP error code (-1 for invalid arguments).  Bytes
-// moved: chains * row_bytes / seg_bytes * P * steps * 64 * 3 * seg_bytes.
+// 2 GiB.  variant: 0 = the scan's form; with one token group and 32- or
+// 128-byte segments also 1 = gathers only (the stores go past the range),
+// 2 = gathers non-temporal, 3 = gathers at device scope (L1 bypassed).
+// Returns 0 or a HIP error code (-1 for invalid arguments).  Bytes moved:
+// chains * row_bytes / seg_bytes * P * steps * 64 * (3, or 2 for variant 1)
+// * seg_bytes.
 int sdm_bench_row_traffic(float *M, int64_t chains, int nrows_log2, int row_bytes, int seg_bytes, int token_groups,
-                          int64_t steps, uint32_t seed, hipStream_t stream)
+                          int variant, int64_t steps, uint32_t seed, hipStream_t stream)
 {
     if (!M || chains < 1 || nrows_log2 < 6 || nrows_log2 > 24 || row_bytes < 128 || row_bytes % 128 ||
-        steps < 1 || steps > (1 << 30) || ((uint64_t)row_bytes << nrows_log2) >= (1ull << 31))
+        steps < 1 || steps > (1 << 30) || ((uint64_t)row_bytes << nrows_log2) >= (1ull << 31) || variant < 0 ||
+        variant > 3 || (variant != 0 && (token_groups != 1 || (seg_bytes != 32 && seg_bytes != 128))))
         return -1;
+    if (variant != 0) {
+        const bool g2 = seg_bytes == 32;
+        switch (variant) {
+        case 1: return (int)(g2 ? launch_g<2, 1, 0, false>(M, chains, nrows_log2, row_bytes, steps, seed, stream)
+                                : launch_g<8, 1, 0, false>(M, chains, nrows_log2, row_bytes, steps, seed, stream));
+        case 2: return (int)(g2 ? launch_g<2, 1, 2>(M, chains, nrows_log2, row_bytes, steps, seed, stream)
+                                : launch_g<8, 1, 2>(M, chains, nrows_log2, row_bytes, steps, seed, stream));
+        default: return (int)(g2 ? launch_g<2, 1, 17>(M, chains, nrows_log2, row_bytes, steps, seed, stream)
+                                 : launch_g<8, 1, 17>(M, chains, nrows_log2, row_bytes, steps, seed, stream));
+        }
+    }
     switch (seg_bytes * 8 + token_groups) {
     case 32 * 8 + 1: return (int)launch_g<2, 1>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
     case 32 * 8 + 4: return (int)launch_g<2, 4>(M, chains, nrows_log2, row_bytes, steps, seed, stream);
