@@ -20,11 +20,13 @@
 //
 // Selection of the n best of a row's candidates (n <= 64):
 //   1. group maxima: every lane folds its candidates into 4 running maxima
-//      (64 per row); tau = the n-th largest of them, found by sorting the 64.
-//      At least n candidates reach tau (one per group maximum above it), so
-//      the n best all do.  (A later part of a half split in parts instead
-//      takes the n-th best score of the earlier parts as tau.)
-//   2. the candidates that reach tau (typically 1.1-1.4 n) are compacted into
+//      (64 per row); tau = the n-th largest of them, found by sorting the 64,
+//      or for n <= 32 (when every maximum is a real candidate) the 32nd
+//      largest, found with a shorter network (tau32_top).  At least n
+//      candidates reach tau (one per group maximum above it), so the n best
+//      all do.  (A later part of a half split in parts instead takes the n-th
+//      best score of the earlier parts as tau.)
+//   2. the candidates that reach tau (typically 1.1-1.4 x 32) are compacted into
 //      a per-row LDS buffer (a per-lane bit mask, a prefix sum of the lanes'
 //      counts over the row group's DPP row, then the set bits);
 //   3. the survivors are sorted as 32-bit keys: the score bits above tau,
@@ -113,6 +115,40 @@ __device__ __forceinline__ void sort64_desc(uint32_t (&x)[4])
     cmpx_stage<15>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
     cmpx_stage<31>(x); cmpx_stage<8>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
     cmpx_stage<63>(x); cmpx_stage<16>(x); cmpx_stage<8>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+}
+
+// The 32nd largest (tau) and the largest (top) of each 16-lane row's 64
+// values, in every lane of the row (x is overwritten).  The two halves of 32
+// (lanes 0-7, lanes 8-15) are sorted descending, then element i is compared
+// with element 63 - i: the larger of each pair are the 32 largest of the 64
+// (a bitonic half-cleaner), and every lane holds such a pair, lanes c and
+// 15 - c the same ones.  So the minimum and maximum over each half of the
+// row's lanes are the 32nd largest and the largest: the last five stages of
+// a full sort and the readout of ranks are not needed.
+__device__ __forceinline__ void tau32_top(uint32_t (&x)[4], uint32_t &tau, uint32_t &top)
+{
+    cmpx_stage<1>(x);
+    cmpx_stage<3>(x); cmpx_stage<1>(x);
+    cmpx_stage<7>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+    cmpx_stage<15>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+    cmpx_stage<31>(x); cmpx_stage<8>(x); cmpx_stage<4>(x); cmpx_stage<2>(x); cmpx_stage<1>(x);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t y = row_xor<15>(x[3 - r]);   // element 63 - (4c + r)
+        const uint32_t mx = x[r] > y ? x[r] : y;
+        lo = mx < lo ? mx : lo;
+        hi = mx > hi ? mx : hi;
+    }
+    uint32_t t;
+    t = row_xor<1>(lo); lo = t < lo ? t : lo;
+    t = row_xor<1>(hi); hi = t > hi ? t : hi;
+    t = row_xor<2>(lo); lo = t < lo ? t : lo;
+    t = row_xor<2>(hi); hi = t > hi ? t : hi;
+    t = row_xor<4>(lo); lo = t < lo ? t : lo;
+    t = row_xor<4>(hi); hi = t > hi ? t : hi;
+    tau = lo;
+    top = hi;
 }
 
 // The value lane 16 g + c0 (c0 uniform) holds, in every lane of row group g
@@ -291,6 +327,10 @@ __device__ __forceinline__ bool half_topk16(const uint32_t *S, int sst, int row_
         top = group_max16(mx);
         tau = floor_bits;
         top = top > tau ? top : tau;   // no candidate reaches tau: none survives
+    } else if (kp <= 32 && n_sub >= 64) {
+        // every group maximum is a real score: the 32nd largest of them is
+        // reached by at least 32 >= k' candidates
+        tau32_top(m, tau, top);
     } else {
         sort64_desc(m);
         tau = rank_value(m, kp - 1);
@@ -483,9 +523,16 @@ __device__ __forceinline__ bool merge16(const HalfEntry *L0, const HalfEntry *L1
     for (int i = kFirst; i < kMaxPer; ++i) sb[i] = kGroupLanes * i < nstair ? cand(i) : 0u;   // uniform
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) m[i & 3] = sb[i] > m[i & 3] ? sb[i] : m[i & 3];
-    sort64_desc(m);
-    const uint32_t tau = rank_value(m, n - 1);
-    const uint32_t top = rank_value(m, 0);
+    uint32_t tau, top;
+    if (n <= 32 && nstair >= 64) {
+        // every group maximum is a candidate: the 32nd largest of them is
+        // reached by at least 32 >= n candidates
+        tau32_top(m, tau, top);
+    } else {
+        sort64_desc(m);
+        tau = rank_value(m, n - 1);
+        top = rank_value(m, 0);
+    }
     uint32_t mask[1] = {0u};
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) mask[0] |= (sb[i] >= tau && sb[i] != 0u) ? 1u << i : 0u;
