@@ -81,7 +81,7 @@ typedef struct {
 } sdm_dims;
 
 /* Limits of this implementation (SDM_ERR_UNSUPPORTED beyond them):
- *   W, R <= 64;  k_prime <= 64;  k_prime <= n_sub <= 2048;
+ *   B < 2^31;  W, R <= 64;  k_prime <= 64;  k_prime <= n_sub <= 2048;
  *   d_v a multiple of 32 and <= 1024;  n_sub^2 * d_v * 4 <= 2 GiB (one (b, h) memory);
  *   bf16: d_k/2 a multiple of 32, d_k <= 512;
  *   fp32: d_k <= 512.

@@ -61,6 +61,7 @@ sdm_status check_memory_dims(const sdm_dims *d)
         return fail(SDM_ERR_INVALID_ARG, "need B >= 0, H >= 1, n_sub >= 1, d_v >= 1 (got B=%lld H=%lld n_sub=%lld d_v=%lld)",
                     (long long)d->B, (long long)d->H, (long long)d->n_sub, (long long)d->d_v);
     if (d->n_sub > 46340) return fail(SDM_ERR_INVALID_ARG, "n_sub^2 must fit in int32");
+    if (d->B > 0x7FFFFFFF) return fail(SDM_ERR_UNSUPPORTED, "B must be < 2^31 (got %lld)", (long long)d->B);
     if (d->d_v % 32 != 0 || d->d_v > kMaxDv)
         return fail(SDM_ERR_UNSUPPORTED, "d_v must be a multiple of 32 and <= %lld (got %lld)",
                     (long long)kMaxDv, (long long)d->d_v);
@@ -387,6 +388,7 @@ sdm_status sdm_cow_reset(uint32_t *touched, const sdm_dims *d, sdm_stream_t stre
     if (!d) return fail(SDM_ERR_INVALID_ARG, "dims is NULL");
     if (d->B < 0 || d->H < 1 || d->n_sub < 1) return fail(SDM_ERR_INVALID_ARG, "need B >= 0, H >= 1, n_sub >= 1");
     if (d->n_sub > 46340) return fail(SDM_ERR_INVALID_ARG, "n_sub^2 must fit in int32");
+    if (d->B > 0x7FFFFFFF) return fail(SDM_ERR_UNSUPPORTED, "B must be < 2^31 (got %lld)", (long long)d->B);
     if (d->B == 0) return SDM_OK;
     if (!touched || !aligned(touched, 4)) return fail(SDM_ERR_INVALID_ARG, "NULL or misaligned bitmap");
     sdm::CowArgs A{nullptr, nullptr, touched, d->B, d->H, d->n_sub * d->n_sub, d->d_v};

@@ -19,15 +19,18 @@ __global__ void __launch_bounds__(256) sdm_state_init_kernel(InitArgs A)
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const f32x4 *src = reinterpret_cast<const f32x4 *>(A.M0);
     f32x4 *dst = reinterpret_cast<f32x4 *>(A.M);
+    // copies in a block-rotated order (copy (k + blockIdx.x) mod B k-th), so
+    // that the stores in flight at any moment spread over all B copies (the
+    // copies of one chunk are a large power-of-two stride apart and would
+    // otherwise tend to hit the same HBM channel together)
+    const uint32_t nb = (uint32_t)A.B;   // B < 2^31 (checked by the caller)
+    const uint32_t b0 = blockIdx.x % nb;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
         const f32x4 x = __builtin_nontemporal_load(src + i);
-        // copies in a block-rotated order, so that the stores in flight at
-        // any moment spread over all B copies (the copies of one chunk are
-        // a large power-of-two stride apart and would otherwise tend to hit
-        // the same HBM channel together)
-        for (int64_t k = 0; k < A.B; ++k) {
-            const int64_t b = (k + blockIdx.x) % A.B;
-            __builtin_nontemporal_store(x, dst + b * n4 + i);
+        uint32_t b = b0;
+        for (uint32_t k = 0; k < nb; ++k) {
+            __builtin_nontemporal_store(x, dst + (int64_t)b * n4 + i);
+            b = b + 1u == nb ? 0u : b + 1u;
         }
     }
 }

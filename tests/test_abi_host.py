@@ -133,6 +133,8 @@ def test_state_init_rejects_overlap():
     d = good_dims()
     assert sdm.sdm_state_init(FAKE, FAKE + 16, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
     assert sdm.sdm_state_init(None, FAKE, d, stream=0, check=False) == sdm.SDM_ERR_INVALID_ARG
+    big = good_dims(B=1 << 31)
+    assert sdm.sdm_state_init(FAKE, FAKE + (1 << 40), big, stream=0, check=False) == sdm.SDM_ERR_UNSUPPORTED
 
 
 def test_workspace_size_is_host_only():
