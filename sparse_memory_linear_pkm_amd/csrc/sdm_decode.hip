@@ -263,10 +263,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) sdm_decode_kernel(DecodeArgs A
     auto load_round = [&](int p0) {
 #pragma unroll
         for (int t = 0; t < PB; ++t) {
-            const int pass = min(p0 + t * kDecWaves, npass - 1);
+            // passes past the last are neither loaded nor used (uniform)
+            if (p0 + t * kDecWaves >= npass) break;
+            const int pass = p0 + t * kDecWaves;
             const int r = pass / npr;
             const int chunk = (pass - r * npr) * K + i;
-            const bool live = p0 + t * kDecWaves < npass && chunk < nchunk;
+            const bool live = chunk < nchunk;
             const size_t bh = (size_t)(b0 + r) * A.H + h;
             const __amdgpu_buffer_rsrc_t Mrs =
                 make_rsrc(A.M + bh * A.N * d_v, (uint32_t)((uint64_t)A.N * d_v * 4u));
