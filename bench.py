@@ -53,9 +53,9 @@ def parse():
                    help="minimum CPU time spent on the oracle baseline (0 disables it)")
     p.add_argument("--decode-steps", type=int, default=1024, help="decode steps per step (decode workload)")
     p.add_argument("--chunks", type=int, default=None,
-                   help="prefill pipelined over this many chunks of tokens (the addressing of chunk c + 1 "
-                        "overlapping the scan of chunk c); default 32 for one-sequence layers whose T it divides, "
-                        "else 1 (no pipelining)")
+                   help="prefill pipelined over this many equal chunks of tokens (the addressing of chunk c + 1 "
+                        "overlapping the scan of chunk c); default for one-sequence layers: chunks growing from "
+                        "16,384 tokens by 1.5x up to 131,072 (sdm.prefill_chunks); 1 = no pipelining")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (for counter calibration) and exit")
     return p.parse_args()
@@ -74,10 +74,11 @@ def scan_source_hash(files=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, backward: bool = False):
+def measured_traffic(workload: str, backward: bool = False, launches: int = 1):
     """HBM bytes per launch of the scan (or of the scan's backward) from the
-    committed counter summary, if it was taken on the current kernel
-    source; else None."""
+    committed counter summary, if it was taken on the current kernel source
+    (and, for a step of several launches, with the same number of launches
+    per step: the average per launch); else None."""
     stem = "sdm_scan_backward" if backward else "sdm_scan"
     path = os.path.join(ROOT, "profiles", f"{stem}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
@@ -91,6 +92,10 @@ def measured_traffic(workload: str, backward: bool = False):
     if kv.get(key) != scan_source_hash(BACKWARD_SOURCES if backward else KERNEL_SOURCES):
         return None
     try:
+        if launches > 1:
+            if int(kv["launches_per_step"]) != launches:
+                return None
+            return float(kv["hbm_bytes_per_step"]) / launches
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
@@ -625,12 +630,19 @@ def main():
         # (sdm_pkm_address_overlapped), overlapping the scan of chunk c on the
         # main stream, whose workgroups take one CU each with room to spare.
         # The scan over consecutive chunks gives the same bits as one call.
-        nc = args.chunks if args.chunks is not None else (32 if B == 1 and T % 32 == 0 else 1)
-        if nc < 1 or T % nc != 0 or (nc > 1 and B != 1):
-            raise SystemExit(f"--chunks {nc}: needs B == 1 and T divisible by the chunk count")
-        Tc = T // nc
-        dimsc = sdm.dims_from(d.replace(T=Tc))
-        wsc_bytes = sdm.sdm_scan_workspace_size(dimsc)
+        # Default: chunks growing from 16,384 tokens (sdm.prefill_chunks);
+        # --chunks N: N equal chunks.
+        if args.chunks is not None:
+            nc = args.chunks
+            if nc < 1 or T % nc != 0 or (nc > 1 and B != 1):
+                raise SystemExit(f"--chunks {nc}: needs B == 1 and T divisible by the chunk count")
+            chunks = [T // nc] * nc
+        else:
+            chunks = sdm.prefill_chunks(T) if B == 1 and T > 0 else [T]
+        nc = len(chunks)
+        bounds = [(sum(chunks[:c]), sum(chunks[:c + 1])) for c in range(nc)]
+        dimsc = [sdm.dims_from(d.replace(T=n)) for n in chunks]
+        wsc_bytes = max(sdm.sdm_scan_workspace_size(x) for x in dimsc)
         wsc = ws if nc == 1 else torch.empty(max(wsc_bytes, 1), dtype=torch.uint8, device="cuda")
         addr_stream = torch.cuda.Stream()
 
@@ -644,18 +656,18 @@ def main():
             ev["init0"].record(stream)
             sdm.sdm_state_init(M, dx["M0"], dims, stream)
             ev["init1"].record(stream)
-            for c in range(nc):
-                sl = slice(c * Tc, (c + 1) * Tc)
+            for c, (t0, t1) in enumerate(bounds):
+                sl = slice(t0, t1)
                 ea[c][0].record(addr_stream)
-                sdm.sdm_pkm_address_overlapped(dx["k"][:, sl], dx["q"][:, sl], dx["C_w"], dx["C_r"], dimsc,
+                sdm.sdm_pkm_address_overlapped(dx["k"][:, sl], dx["q"][:, sl], dx["C_w"], dx["C_r"], dimsc[c],
                                                widx[:, sl], wwt[:, sl], ridx[:, sl], rwt[:, sl], addr_stream)
                 ea[c][1].record(addr_stream)
-            for c in range(nc):
-                sl = slice(c * Tc, (c + 1) * Tc)
+            for c, (t0, t1) in enumerate(bounds):
+                sl = slice(t0, t1)
                 stream.wait_event(ea[c][1])
                 es[c][0].record(stream)
                 sdm.sdm_scan_forward(M, widx[:, sl], wwt[:, sl], ridx[:, sl], rwt[:, sl], dx["v"][:, sl],
-                                     dx["a"][:, sl], dx["b"][:, sl], o[:, sl], wsc, wsc_bytes, dimsc, stream)
+                                     dx["a"][:, sl], dx["b"][:, sl], o[:, sl], wsc, wsc_bytes, dimsc[c], stream)
                 es[c][1].record(stream)
             ev["scan1"].record(stream)
             sdm.sdm_decode_step(M, dec["k"], dec["q"], dx["C_w"], dx["C_r"], dec["v"], dec["a"], dec["b"], o1,
@@ -726,7 +738,8 @@ def main():
                    "d_v": d.d_v, "k_prime": d.k_prime, "W": d.W, "R": d.R, "inputs": d.in_dtype,
                    "state": "fp32", "tokens_per_step": tokens_per_step,
                    "step": ("1024 decode steps" if decode_mode else
-                            (f"state init + PKM addressing + prefill scan over {nc} chunks of {T // nc} tokens "
+                            (f"state init + PKM addressing + prefill scan over {nc} chunks of "
+                             f"{', '.join(str(n) for n in chunks)} tokens "
                              "(addressing of chunk c + 1 on a second stream, one workgroup per CU, overlapping "
                              "the scan of chunk c) + 1 decode token per sequence" if nc > 1 else
                              "state init (second stream, concurrent with the addressing) + PKM addressing + "
@@ -767,9 +780,10 @@ def main():
         scan_bytes = th * (2 * d.W + d.R) * d.d_v * 4
         scan_s = avg["sdm_scan_forward"] * 1e-3
         achieved = scan_bytes / scan_s / 1e9
-        # per launch of sdm_scan_forward: one chunk of the sequence (the whole
-        # sequence when nc = 1); the counter summary holds the bytes per launch
-        traffic = measured_traffic(name)
+        # per launch of sdm_scan_forward: one chunk of the sequence on average
+        # (the whole sequence when nc = 1); the counter summary holds the bytes
+        # per launch, or per step of nc launches
+        traffic = measured_traffic(name, launches=nc)
         result["roofline"] = {"kernel": "sdm_scan_forward (scan_prep_kernel + sdm_scan_lanes_kernel)",
                               "bound": "hbm", "achieved": achieved,
                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

@@ -20,8 +20,9 @@ from .binding import (SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED, SDM_ERR_
                       sdm_status_string,
                       sdm_last_error, sdm_version, state_init, pkm_address, scan_forward, decode_step,
                       gates, output_norm_gate, gdn_dense_forward)
+from .pipeline import prefill_chunks
 
 __all__ = [n for n in dir() if n.startswith(("sdm_", "SDM_", "Sdm")) or n in (
     "dims_from", "lib_path", "load_library", "state_init", "pkm_address", "scan_forward",
     "decode_step", "gates", "output_norm_gate", "gdn_dense_forward", "scan_forward_save", "scan_backward",
-    "address_backward", "gates_backward", "output_norm_gate_backward", "scan_forward_noalloc")]
+    "address_backward", "gates_backward", "output_norm_gate_backward", "scan_forward_noalloc", "prefill_chunks")]

@@ -97,8 +97,8 @@ def test_fullsize_prefill_layer(sdm, torch, name):
 def test_fullsize_long_context_prefix(sdm, torch):
     """The 1M-token layer on the GPU; the oracle replays a 65,536-token prefix
     of two chains (a prefix of the recurrence is itself exact), and the
-    benchmark's pipelined form of the whole step equals the one-call prefill
-    bit for bit."""
+    benchmark's pipelined form of the whole step (sdm.prefill_chunks) equals
+    the one-call prefill bit for bit."""
     p = synth.PRESETS["long_context"]
     d = p.dims
     note(f"full-size long_context {d}")
@@ -126,18 +126,19 @@ def test_fullsize_long_context_prefix(sdm, torch):
     np.testing.assert_array_equal(to_host(o[:, :Tp]), to_host(op))
     del op
     _free(torch)
-    # the step as the benchmark runs it: 32 chunks of 32,768 tokens, each
-    # chunk's addressing on a second stream with at most one workgroup per CU
-    # (sdm_pkm_address_overlapped), each chunk's scan on the main stream once
-    # its addressing is done; every output equals the one-call prefill's
-    note("full-size long_context pipelined over 32 chunks")
-    nc = 32
-    Tc = d.T // nc
-    dimsc = sdm.dims_from(d.replace(T=Tc))
+    # the step as the benchmark runs it: the chunks of sdm.prefill_chunks
+    # (growing from 16,384 tokens), each chunk's addressing on a second
+    # stream with at most one workgroup per CU (sdm_pkm_address_overlapped),
+    # each chunk's scan on the main stream once its addressing is done; every
+    # output equals the one-call prefill's
+    chunks = sdm.prefill_chunks(d.T)
+    note(f"full-size long_context pipelined over {len(chunks)} chunks")
+    bounds = [(sum(chunks[:c]), sum(chunks[:c + 1])) for c in range(len(chunks))]
+    dimsc = [sdm.dims_from(d.replace(T=n)) for n in chunks]
     lists2 = tuple(torch.empty_like(t) for t in lists)
     M2 = sdm.state_init(x["M0"], dims)
     o2 = torch.empty_like(o)
-    ws_bytes = sdm.sdm_scan_workspace_size(dimsc)
+    ws_bytes = max(sdm.sdm_scan_workspace_size(dc) for dc in dimsc)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
@@ -145,18 +146,18 @@ def test_fullsize_long_context_prefix(sdm, torch):
     start.record(main)
     side.wait_event(start)
     done = []
-    for c in range(nc):
-        sl = slice(c * Tc, (c + 1) * Tc)
-        sdm.sdm_pkm_address_overlapped(x["k"][:, sl], x["q"][:, sl], x["C_w"], x["C_r"], dimsc,
+    for c, (t0, t1) in enumerate(bounds):
+        sl = slice(t0, t1)
+        sdm.sdm_pkm_address_overlapped(x["k"][:, sl], x["q"][:, sl], x["C_w"], x["C_r"], dimsc[c],
                                        *(t[:, sl] for t in lists2), side)
         e = torch.cuda.Event()
         e.record(side)
         done.append(e)
-    for c in range(nc):
-        sl = slice(c * Tc, (c + 1) * Tc)
+    for c, (t0, t1) in enumerate(bounds):
+        sl = slice(t0, t1)
         main.wait_event(done[c])
         sdm.sdm_scan_forward(M2, *(t[:, sl] for t in lists2), x["v"][:, sl], x["a"][:, sl], x["b"][:, sl],
-                             o2[:, sl], ws, ws_bytes, dimsc, main)
+                             o2[:, sl], ws, ws_bytes, dimsc[c], main)
     torch.cuda.synchronize()
     for name, a, b in zip(("widx", "wwt", "ridx", "rwt"), lists, lists2):
         assert torch.equal(a, b), name
